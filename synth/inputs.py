@@ -1,0 +1,76 @@
+"""Seeded synthetic Q/K/V with planted needle blocks.
+
+Recipe (stated once, used by the tests and the bench):
+  * numpy ``Generator(PCG64(seed))``; Q [b, n_q, h_q, d], then K, then V
+    [b, n_kv, h_kv, d], each ``standard_normal`` in float32;
+  * per sequence, ``n_needles`` needle blocks drawn without replacement,
+    uniformly from blocks [N_init, n_blk - N_local);
+  * per sequence and KV group g, the mean query direction
+    u_g = normalise(sum over tokens t and heads h of group g of Q[t, h, :])
+    is added, times 0.5, to every K row of each needle block;
+  * the arrays are then cast to the I/O dtype (torch's bf16 cast rounds to
+    nearest even); fp32 configs stay fp32.
+Decode workloads draw the whole cache the same way and the single query of
+each sequence from the same generator (Q is drawn first).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .configs import Config
+
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def needle_blocks(cfg: Config, rng: np.random.Generator) -> np.ndarray:
+    """[batch, n_needles] needle block ids per sequence (sorted)."""
+    lo, hi = cfg.N_init, cfg.n_blk - cfg.N_local
+    out = np.zeros((cfg.batch, cfg.n_needles), dtype=np.int64)
+    for b in range(cfg.batch):
+        if cfg.n_needles:
+            out[b] = np.sort(rng.choice(np.arange(lo, hi), size=cfg.n_needles, replace=False))
+    return out
+
+
+def make_inputs(cfg: Config, seed: int | None = None, n_kv: int | None = None,
+                batch: int | None = None):
+    """Return dict(q, k, v) as contiguous CPU torch tensors in the I/O dtype,
+    plus ``needles`` [batch, n_needles].
+
+    ``n_kv`` and ``batch`` override the config (tests use smaller variants).
+    """
+    from dataclasses import replace
+    seed = cfg.seed if seed is None else seed
+    n_kv = cfg.n_kv if n_kv is None else n_kv
+    if batch is not None and batch != cfg.batch:
+        cfg = replace(cfg, batch=batch)
+    n_q = 1 if cfg.decode else n_kv
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((cfg.batch, n_q, cfg.h_q, cfg.d), dtype=np.float32)
+    k = rng.standard_normal((cfg.batch, n_kv, cfg.h_kv, cfg.d), dtype=np.float32)
+    v = rng.standard_normal((cfg.batch, n_kv, cfg.h_kv, cfg.d), dtype=np.float32)
+    sub = cfg if n_kv == cfg.n_kv else _with_nkv(cfg, n_kv)
+    needles = needle_blocks(sub, rng)
+    G = cfg.G
+    for b in range(cfg.batch):
+        for g in range(cfg.h_kv):
+            u = q[b, :, g * G:(g + 1) * G, :].astype(np.float64).sum(axis=(0, 1))
+            nrm = np.linalg.norm(u)
+            if nrm == 0.0:
+                continue
+            shift = (0.5 * u / nrm).astype(np.float32)
+            for blk in needles[b]:
+                k[b, blk * cfg.B:(blk + 1) * cfg.B, g, :] += shift
+    dt = _TORCH_DT[cfg.io]
+    return {
+        "q": torch.from_numpy(q).to(dt).contiguous(),
+        "k": torch.from_numpy(k).to(dt).contiguous(),
+        "v": torch.from_numpy(v).to(dt).contiguous(),
+        "needles": needles,
+    }
+
+
+def _with_nkv(cfg: Config, n_kv: int) -> Config:
+    from dataclasses import replace
+    return replace(cfg, n_kv=n_kv, n_q=(1 if cfg.decode else n_kv))
