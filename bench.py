@@ -1,0 +1,402 @@
+#!/usr/bin/env python3
+"""Benchmark of the InfLLM-V2 sparse-attention forward path on one MI355X.
+
+Default workload (the headline line): MiniCPM-style GQA layer prefill at 32k
+tokens (b=1, n=32768, h_q=32, h_kv=2, d=128, bf16, B=64, l_C1=32, s_C1=16,
+l=5, s=4, N_init=1, N_local=2, k=16) on seeded synthetic inputs with planted
+needle blocks.  One step = the whole hot path: compress_k -> block_scores ->
+topk_select -> sparse_attn, inputs resident in HBM, outputs preallocated.
+The same JSON line also carries the 128k prefill and the 16-sequence decode
+step (both secondary, fewer steps), the dense-attention time on the same
+input, the roofline of the dominant kernel, and the fp64 CPU oracle timed on a
+bounded sample of the workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import trainable_block_sparse_amd as tbs  # noqa: E402
+from synth import CONFIGS, make_inputs  # noqa: E402
+
+METRIC = "sparse-attn prefill tokens/s at 32k/128k + decode µs/token; % of MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "trainable_block_sparse_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def problem_of(cfg, **kw) -> tbs.Problem:
+    n_q = 1 if cfg.decode else cfg.n_kv
+    p = dict(batch=cfg.batch, n_q=n_q, n_kv=cfg.n_kv, h_kv=cfg.h_kv, G=cfg.G, d=cfg.d,
+             q_pos0=cfg.n_kv - n_q, B=cfg.B, l_C1=cfg.l_C1, s_C1=cfg.s_C1, l=cfg.l, s=cfg.s,
+             k=cfg.k, N_init=cfg.N_init, N_local=cfg.N_local, dtype=cfg.io)
+    p.update(kw)
+    return tbs.Problem(**p)
+
+
+# --------------------------------------------------------------------------
+# algorithmic work (what the method must do; no padding, masking or re-sweeps)
+# --------------------------------------------------------------------------
+
+def visible_kernels(p, l_C1=32, s_C1=16):
+    return np.where(p >= l_C1 - 1, (p - l_C1 + 1) // s_C1 + 1, 0)
+
+
+def selection_flops_per_pass(cfg, positions):
+    """b * h_q * 2d * sum_p |V(p)|  (one pass over the visible kernels)."""
+    return float(cfg.batch * cfg.h_q * 2 * cfg.d * visible_kernels(positions).sum())
+
+
+def attention_flops(cfg, positions, budget):
+    """b * h_q * 4d * sum_p keys(p), keys(p) = (|I(p)|-1)*B + (p mod B) + 1."""
+    b_p = positions // cfg.B
+    nsel = np.minimum(b_p + 1, budget)
+    keys = (nsel - 1) * cfg.B + positions % cfg.B + 1
+    return float(cfg.batch * cfg.h_q * 4 * cfg.d * keys.sum())
+
+
+def decode_bytes(cfg, budget):
+    """Algorithmic HBM bytes of one decode step: K^C1 of every visible kernel,
+    the selected K and V blocks, Q and O."""
+    L = cfg.n_kv
+    n_c1 = (L - cfg.l_C1) // cfg.s_C1 + 1
+    nsel = min((L - 1) // cfg.B + 1, budget)
+    kc1 = n_c1 * cfg.d * 2
+    kv = nsel * cfg.B * cfg.d * 2 * 2
+    qo = 2 * cfg.G * cfg.d * 2
+    return float(cfg.batch * cfg.h_kv * (kc1 + kv + qo))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------
+# timed runs
+# --------------------------------------------------------------------------
+
+class StageTimer:
+    """Per-stage HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, names):
+        self.names = names
+        self.ms = {n: 0.0 for n in names}
+        self.pending = []
+
+    def step(self, fns):
+        s = torch.cuda.current_stream()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        evs[0].record(s)
+        for i, fn in enumerate(fns):
+            fn()
+            evs[i + 1].record(s)
+        self.pending.append(evs)
+
+    def collect(self):
+        torch.cuda.synchronize()
+        for evs in self.pending:
+            for i, n in enumerate(self.names):
+                self.ms[n] += evs[i].elapsed_time(evs[i + 1])
+        steps = len(self.pending)
+        self.pending = []
+        return {n: v / steps for n, v in self.ms.items()}
+
+
+def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None):
+    log(f"[bench] {cfg.name}: generating inputs")
+    x = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
+    del x
+    lp = problem_of(cfg)
+    n_blk, bud, n_c1 = tbs.n_blocks(lp), tbs.budget(lp), tbs.n_kernels(lp)
+    Kc1 = torch.empty((lp.batch, lp.h_kv, n_c1, lp.d), dtype=Q.dtype, device=dev)
+    S = torch.empty((lp.batch, lp.h_kv, lp.n_q, n_blk), dtype=torch.float32, device=dev)
+    idx = torch.empty((lp.batch, lp.h_kv, lp.n_q, bud), dtype=torch.int32, device=dev)
+    nsel = torch.empty((lp.batch, lp.h_kv, lp.n_q), dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((lp.batch, lp.h_q, lp.n_q), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(max(tbs.block_scores_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(tbs.sparse_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    fns = [
+        lambda: tbs.compress_k(lp, K, Kc1),
+        lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s),
+        lambda: tbs.topk_select(lp, S, idx, nsel),
+        lambda: tbs.sparse_attn(lp, Q, K, V, idx, nsel, O, lse, ws_a),
+    ]
+    names = ["compress_k", "block_scores", "topk_select", "sparse_attn"]
+    log(f"[bench] {cfg.name}: warmup {warmup}")
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    timer = StageTimer(names)
+    log(f"[bench] {cfg.name}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        timer.step(fns)
+    stage = timer.collect()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    ms = sum(stage.values())
+    pos = np.arange(cfg.n_kv)
+    out = dict(ms_per_step=ms, wall_ms_per_step=wall, stages_ms=stage,
+               tokens_per_s=cfg.batch * cfg.n_q / (ms / 1e3),
+               sel_flops_2pass=2 * selection_flops_per_pass(cfg, pos),
+               attn_flops=attention_flops(cfg, pos, bud))
+    out["algo_tflops"] = (out["sel_flops_2pass"] + out["attn_flops"]) / (ms / 1e3) / 1e12
+    out["frac_of_bf16_peak"] = out["algo_tflops"] / PEAK_BF16_TFLOPS
+    if with_dense:
+        dsteps = dense_steps or max(1, steps // 2)
+        ws_d = torch.empty(max(tbs.dense_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
+        Od = torch.empty_like(Q)
+        log(f"[bench] {cfg.name}: dense attention x{dsteps}")
+        tbs.dense_attn(lp, Q, K, V, Od, lse, ws_d)
+        dt = StageTimer(["dense_attn"])
+        for _ in range(dsteps):
+            dt.step([lambda: tbs.dense_attn(lp, Q, K, V, Od, lse, ws_d)])
+        out["dense_ms"] = dt.collect()["dense_attn"]
+        out["speedup_vs_dense"] = out["dense_ms"] / ms
+    del Q, K, V, S, O
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode(cfg, steps, warmup):
+    log(f"[bench] {cfg.name}: generating the KV cache")
+    x = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
+    del x
+    lp = problem_of(cfg)
+    prev = problem_of(cfg, n_kv=cfg.n_kv - 1, q_pos0=cfg.n_kv - 2, kv_cap=cfg.n_kv)
+    n_blk, bud, n_c1 = tbs.n_blocks(lp), tbs.budget(lp), tbs.n_kernels(lp)
+    n_prev = tbs.n_kernels(prev)
+    lp.c1_cap = prev.c1_cap = n_c1
+    Kc1 = torch.empty((lp.batch, lp.h_kv, n_c1, lp.d), dtype=Q.dtype, device=dev)
+    tbs.compress_k(prev, K, Kc1)           # the cache before this step
+    S = torch.empty((lp.batch, lp.h_kv, 1, n_blk), dtype=torch.float32, device=dev)
+    idx = torch.empty((lp.batch, lp.h_kv, 1, bud), dtype=torch.int32, device=dev)
+    nsel = torch.empty((lp.batch, lp.h_kv, 1), dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((lp.batch, lp.h_q, 1), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(max(tbs.block_scores_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(tbs.sparse_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    fns = [
+        lambda: tbs.compress_k(lp, K, Kc1, c1_begin=n_prev, c1_end=n_c1),
+        lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s),
+        lambda: tbs.topk_select(lp, S, idx, nsel),
+        lambda: tbs.sparse_attn(lp, Q, K, V, idx, nsel, O, lse, ws_a),
+    ]
+    names = ["compress_append", "block_scores", "topk_select", "sparse_attn"]
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    timer = StageTimer(names)
+    log(f"[bench] {cfg.name}: timing {steps} steps (per-stage events)")
+    for _ in range(steps):
+        timer.step(fns)
+    stage = timer.collect()
+    # the whole step without events in between
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        for fn in fns:
+            fn()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    nbytes = decode_bytes(cfg, bud)
+    out = dict(step_us=step_ms * 1e3, us_per_token=step_ms * 1e3 / cfg.batch,
+               stages_us={k: v * 1e3 for k, v in stage.items()}, algo_bytes=nbytes,
+               algo_GBps=nbytes / (step_ms / 1e3) / 1e9)
+    out["frac_of_hbm_peak"] = out["algo_GBps"] / PEAK_HBM_GBS
+    del Q, K, V
+    torch.cuda.empty_cache()
+    return out
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, as it stands, on a bounded sample
+# --------------------------------------------------------------------------
+
+def cpu_baseline(cfg, budget_s=15.0):
+    import oracle as orc
+    from threadpoolctl import threadpool_info
+    x = make_inputs(cfg)
+    op = orc.Problem(G=cfg.G, h_kv=cfg.h_kv, d=cfg.d, B=cfg.B, l_C1=cfg.l_C1, s_C1=cfg.s_C1,
+                     l=cfg.l, s=cfg.s, k=cfg.k, N_init=cfg.N_init, N_local=cfg.N_local,
+                     io=cfg.io)
+    Q = x["q"][0].double().numpy()
+    K = x["k"][0].double().numpy()
+    V = x["v"][0].double().numpy()
+    t0 = time.perf_counter()
+    Kc1 = orc.compress_k(K[None], op)[0]
+    t_comp = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    rows_done, t_rows = 0, 0.0
+    while t_rows < budget_s and rows_done < cfg.n_q:
+        rows = np.sort(rng.choice(cfg.n_q, size=16, replace=False))
+        t1 = time.perf_counter()
+        orc.forward_rows(Q, K, V, rows, op, Kc1=Kc1, mode="sparse")
+        t_rows += time.perf_counter() - t1
+        rows_done += 16
+    per_row = t_rows / rows_done
+    total = t_comp + per_row * cfg.n_q * cfg.batch
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": cfg.batch * cfg.n_q / total, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{cfg.name}: compress_k over all {cfg.n_kv} keys ({t_comp:.1f} s) + "
+                       f"{rows_done} uniformly sampled query rows (selection, top-k, attention; "
+                       f"{t_rows:.1f} s), extrapolated to {cfg.batch * cfg.n_q} rows")}
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tr.get(f"{workload}/{kernel}")
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="skip the 128k and decode lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the path shards by KV group / batch / query range, see the design notes); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    tbs.lib()
+
+    cfg = CONFIGS["prefill32k"]
+    main_res = bench_prefill(cfg, args.steps, args.warmup, with_dense=not args.no_dense)
+    log(f"[bench] prefill32k: {main_res['ms_per_step']:.3f} ms/step, stages {main_res['stages_ms']}")
+
+    # roofline of the dominant kernel
+    stages = main_res["stages_ms"]
+    dom = max(stages, key=stages.get)
+    pos = np.arange(cfg.n_kv)
+    if dom == "block_scores":
+        flops = main_res["sel_flops_2pass"]
+    elif dom == "sparse_attn":
+        flops = main_res["attn_flops"]
+    else:
+        flops = None
+    if flops is not None:
+        ach = flops / (stages[dom] / 1e3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                "traffic": traffic_for(dom, "prefill32k"),
+                "per_launch_algorithmic": flops, "avg_launch_ms": stages[dom]}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": None, "traffic": traffic_for(dom, "prefill32k")}
+
+    extra = {}
+    if not args.no_extra:
+        c3 = CONFIGS["prefill128k"]
+        r3 = bench_prefill(c3, max(2, args.steps // 5), 1, with_dense=not args.no_dense,
+                           dense_steps=1)
+        extra["prefill128k"] = {k: v for k, v in r3.items()}
+        log(f"[bench] prefill128k: {r3['ms_per_step']:.3f} ms/step")
+        c4 = CONFIGS["decode"]
+        r4 = bench_decode(c4, max(20, args.steps * 5), args.warmup)
+        extra["decode"] = r4
+        log(f"[bench] decode: {r4['step_us']:.1f} us/step")
+        c5 = CONFIGS["dense_switch"]
+        r5 = bench_dense_switch(c5, args.steps, args.warmup)
+        extra["dense_switch"] = r5
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(cfg)
+
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, 32 planted needle blocks)",
+        "config": {"workload": "prefill32k: b=1 n=32768 h_q=32 h_kv=2 d=128 bf16 B=64 "
+                               "l_C1=32 s_C1=16 l=5 s=4 N_init=1 N_local=2 k=16",
+                   "global_batch": cfg.batch, "seq_len": cfg.n_kv, "parallelism": "none (1 GPU)"},
+        "stages_ms": main_res["stages_ms"],
+        "algo_tflops": main_res["algo_tflops"],
+        "frac_of_bf16_peak": main_res["frac_of_bf16_peak"],
+        "dense_ms": main_res.get("dense_ms"),
+        "speedup_vs_dense": main_res.get("speedup_vs_dense"),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_dense_switch(cfg, steps, warmup):
+    """Short sequences: the switch selects dense attention; the sparse path is
+    timed beside it on the same input (they must agree)."""
+    log(f"[bench] {cfg.name}: inputs")
+    x = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
+    lp = problem_of(cfg)
+    assert tbs.use_dense(lp)
+    ws_d = torch.empty(max(tbs.dense_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((lp.batch, lp.h_q, lp.n_q), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        tbs.dense_attn(lp, Q, K, V, O, lse, ws_d)
+    t = StageTimer(["dense_attn"])
+    for _ in range(steps):
+        t.step([lambda: tbs.dense_attn(lp, Q, K, V, O, lse, ws_d)])
+    dense_ms = t.collect()["dense_attn"]
+    flops = attention_flops(cfg, np.arange(cfg.n_kv), 10 ** 9)
+    return {"dense_ms": dense_ms, "tokens_per_s": cfg.batch * cfg.n_q / (dense_ms / 1e3),
+            "algo_tflops": flops / (dense_ms / 1e3) / 1e12}
+
+
+if __name__ == "__main__":
+    main()

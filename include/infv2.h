@@ -1,0 +1,161 @@
+/*
+ * infv2.h -- C ABI of the InfLLM-V2 sparse-attention forward path on MI355X.
+ *
+ * The method: InfLLM-V2 dense-sparse switchable attention, as described on
+ *  - the papernotes.org note "InfLLM-V2: Dense-Sparse Switchable Attention for
+ *    Seamless Short-to-Long Adaptation", 方法详解 > 关键设计 2-4 (key designs 2-4);
+ *  - the paperlayer.ai summary of arXiv 2509.24663v1, "A IMPLEMENTATION DETAIL";
+ *  - the OpenBMB blog "技术Blog-4 | 新一代InfLLM：可训练的稀疏注意力机制",
+ *    动态上下文块选择 (semantic kernels, top-k sharing, efficient top-k).
+ *
+ * Conventions for every entry point
+ *  - All pointers are DEVICE pointers except `prob` (host).  Buffers are
+ *    row-major and contiguous with the layouts stated per call; every device
+ *    pointer must be 16-byte aligned.
+ *  - The caller owns and frees every buffer, workspaces included.  The
+ *    library keeps no state besides a thread-local error string: it never
+ *    allocates, never synchronises and never writes an input.
+ *  - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream).  Calls return once the work is enqueued.
+ *  - Return value: INFV2_OK, or a negative status; infv2_last_error() then
+ *    holds a message for the calling thread.  Nothing is enqueued when a
+ *    call returns an argument, support or workspace error.
+ *  - Entry points are reentrant; no C++ exception crosses this boundary.
+ *
+ * Notation (the pages'): B block size; l_C1, s_C1 stage-1 kernel length and
+ * stride; l, s stage-3 max-pool length and stride (in kernels); k top-k; N_init,
+ * N_local; G query heads per KV group; h_q = G*h_kv; d head dimension.
+ */
+#ifndef INFV2_H
+#define INFV2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  INFV2_OK = 0,
+  INFV2_E_ARG = -1,          /* null/misaligned pointer, inconsistent sizes   */
+  INFV2_E_UNSUPPORTED = -2,  /* valid for the method, no kernel instance      */
+  INFV2_E_WORKSPACE = -3,    /* workspace too small                           */
+  INFV2_E_HIP = -4           /* a HIP launch failed (message holds the error) */
+};
+
+enum { INFV2_BF16 = 0, INFV2_F32 = 1 };
+
+/* One attention layer call.  Query token t of a sequence sits at absolute
+ * position p = q_pos0 + t (prefill: q_pos0 = 0, n_q = n_kv; decode:
+ * q_pos0 = L-1, n_q = 1, n_kv = L, the cache length INCLUDING the new token).
+ * Head h belongs to KV group g = h / G (the G heads of a group are adjacent). */
+typedef struct infv2_problem {
+  int32_t batch;             /* b: sequences                                   */
+  int32_t n_q;               /* query tokens per sequence                      */
+  int32_t q_pos0;            /* absolute position of query token 0             */
+  int32_t n_kv;              /* keys per sequence (q_pos0 + n_q <= n_kv)       */
+  int32_t h_kv;              /* KV heads (groups)                              */
+  int32_t G;                 /* query heads per group                          */
+  int32_t d;                 /* head dimension                                 */
+  int32_t B;                 /* KV block size                                  */
+  int32_t l_C1, s_C1;        /* stage-1 kernel length / stride (tokens)        */
+  int32_t l, s;              /* stage-3 max-pool length / stride (kernels)     */
+  int32_t k;                 /* top-k blocks besides init and local            */
+  int32_t N_init, N_local;   /* always-attended initial / local blocks         */
+  int32_t dtype;             /* INFV2_BF16 or INFV2_F32: Q, K, V, K^C1 and O   */
+  float scale;               /* softmax scale; 0 selects 1/sqrt(d)             */
+  int64_t kv_cap;            /* token rows allocated in K and V; 0 -> n_kv     */
+  int64_t c1_cap;            /* kernel rows allocated in K^C1; 0 -> n_C1       */
+} infv2_problem;
+
+/* Derived sizes.  n_C1 = floor((n_kv - l_C1)/s_C1) + 1 complete kernels
+ * (0 if n_kv < l_C1); n_blk = ceil(n_kv / B); budget = N_init + N_local + k. */
+int32_t infv2_n_kernels(const infv2_problem* prob);
+int32_t infv2_n_blocks(const infv2_problem* prob);
+int32_t infv2_budget(const infv2_problem* prob);
+
+/* 1 when ceil(n_kv/B) <= N_init + N_local + k: every causal block is in the
+ * budget and the sparse path equals dense causal attention (papernotes note,
+ * 整体框架 flowchart; OpenBMB blog, 语义核: short inputs degrade to standard
+ * attention).  0 otherwise, -1 on a bad argument. */
+int infv2_use_dense(const infv2_problem* prob);
+
+/* Checks that `prob` describes a problem the library can run (shapes, the
+ * max-pool parameters l and s equal the count and stride of the kernels that
+ * intersect a block, B a multiple of the attention key tile, ...).  Returns
+ * INFV2_OK, INFV2_E_ARG or INFV2_E_UNSUPPORTED; enqueues nothing. */
+int infv2_check_problem(const infv2_problem* prob);
+
+/* Stage 1 (papernotes note, 关键设计 3; OpenBMB blog, 语义核): mean-pool the keys
+ * of each kernel,  K^C1[b][g][j][:] = (1/l_C1) * sum_{u<l_C1} K[b][j*s_C1+u][g][:],
+ * for kernels j in [c1_begin, c1_end).  The sum is exact (compensated fp64)
+ * and rounded once, to nearest even, to the I/O dtype.  Prefill passes
+ * [0, n_C1); a decode step appends the kernels that the new tokens completed.
+ *   K   : [batch][kv_cap][h_kv][d]   (input)
+ *   Kc1 : [batch][h_kv][c1_cap][d]   (output rows c1_begin..c1_end-1 only)
+ * Requires 0 <= c1_begin <= c1_end <= n_C1 <= c1_cap. */
+int infv2_compress_k(const infv2_problem* prob, const void* K, void* Kc1,
+                     int32_t c1_begin, int32_t c1_end, void* stream);
+
+/* Stages 2-3 with the exact two-pass log-sum-exp (papernotes note, 关键设计 3
+ * and 4; OpenBMB blog, 高效Top-K实现).  For query token t (position p), group g:
+ *   z[h][j]     = scale * Q[b][t][h][:] . K^C1[b][g][j][:]   for visible j,
+ *                 i.e. j*s_C1 + l_C1 - 1 <= p (a kernel is causal when its
+ *                 last token is);
+ *   S^C1[h][j]  = exp(z[h][j] - lse[h]),  lse[h] = log sum_j exp(z[h][j]);
+ *   S^shared[j] = sum over the G heads of g of S^C1[h][j]   (kept on chip);
+ *   S^cmp[blk]  = max of S^shared over the visible kernels that intersect
+ *                 block blk (-inf when there is none).
+ *   Q     : [batch][n_q][h_q][d]
+ *   Kc1   : [batch][h_kv][c1_cap][d]  (rows 0..n_C1-1 valid)
+ *   S_cmp : [batch][h_kv][n_q][n_blk] fp32 (output).  Entries for blocks
+ *           0..floor(p/B) are written; entries after the query's own block are
+ *           left untouched.
+ *   ws    : workspace of infv2_block_scores_workspace(prob) bytes (may be
+ *           NULL when that size is 0). */
+size_t infv2_block_scores_workspace(const infv2_problem* prob);
+int infv2_block_scores(const infv2_problem* prob, const void* Q, const void* Kc1,
+                       float* S_cmp, void* ws, size_t ws_bytes, void* stream);
+
+/* Block selection (papernotes note, 关键设计 2; OpenBMB blog, Top-K块共享):
+ *   I(p) = I_init  u  I_local(p)  u  top-k(p),
+ * I_init = {0..N_init-1}, I_local(p) = {b_p-N_local+1..b_p} with b_p = floor(p/B),
+ * top-k = the k best remaining causal blocks by S^cmp; ties go to the lower
+ * block index.  One set per (token, group), shared by the group's heads.
+ *   S_cmp : [batch][h_kv][n_q][n_blk] fp32 (input, as written above)
+ *   idx   : [batch][h_kv][n_q][budget] int32 (output): I(p) ascending, padded
+ *           with -1; |I(p)| = min(b_p + 1, budget)
+ *   n_sel : [batch][h_kv][n_q] int32 (output): |I(p)|. */
+int infv2_topk_select(const infv2_problem* prob, const float* S_cmp, int32_t* idx,
+                      int32_t* n_sel, void* stream);
+
+/* Block-sparse attention (paperlayer.ai summary, A IMPLEMENTATION DETAIL):
+ * for each query token and head, softmax attention over the keys
+ * T(p) = {t <= p : floor(t/B) in I(p)}, returning O and the natural-log LSE.
+ *   Q     : [batch][n_q][h_q][d]        K, V : [batch][kv_cap][h_kv][d]
+ *   idx, n_sel : as written by infv2_topk_select (any ascending sets of
+ *           distinct causal blocks whose last entry is b_p are accepted)
+ *   O     : [batch][n_q][h_q][d] I/O dtype (output, rounded once)
+ *   lse   : [batch][h_q][n_q] fp32 (output; may be NULL)
+ *   ws    : workspace of infv2_sparse_attn_workspace(prob) bytes. */
+size_t infv2_sparse_attn_workspace(const infv2_problem* prob);
+int infv2_sparse_attn(const infv2_problem* prob, const void* Q, const void* K,
+                      const void* V, const int32_t* idx, const int32_t* n_sel,
+                      void* O, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Dense causal attention (the fallback of the switch, and the baseline):
+ * the same as infv2_sparse_attn with T(p) = {0..p}.  Layouts as above;
+ * ws: workspace of infv2_dense_attn_workspace(prob) bytes. */
+size_t infv2_dense_attn_workspace(const infv2_problem* prob);
+int infv2_dense_attn(const infv2_problem* prob, const void* Q, const void* K,
+                     const void* V, void* O, float* lse, void* ws, size_t ws_bytes,
+                     void* stream);
+
+const char* infv2_status_string(int status);
+const char* infv2_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* INFV2_H */

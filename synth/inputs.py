@@ -3,8 +3,9 @@
 Recipe (stated once, used by the tests and the bench):
   * numpy ``Generator(PCG64(seed))``; Q [b, n_q, h_q, d], then K, then V
     [b, n_kv, h_kv, d], each ``standard_normal`` in float32;
-  * per sequence, ``n_needles`` needle blocks drawn without replacement,
-    uniformly from blocks [N_init, n_blk - N_local);
+  * per sequence, ``n_needles`` needle blocks (fewer if a shortened variant
+    has fewer blocks) drawn without replacement, uniformly from blocks
+    [N_init, n_blk - N_local);
   * per sequence and KV group g, the mean query direction
     u_g = normalise(sum over tokens t and heads h of group g of Q[t, h, :])
     is added, times 0.5, to every K row of each needle block;
@@ -26,10 +27,11 @@ _TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 def needle_blocks(cfg: Config, rng: np.random.Generator) -> np.ndarray:
     """[batch, n_needles] needle block ids per sequence (sorted)."""
     lo, hi = cfg.N_init, cfg.n_blk - cfg.N_local
-    out = np.zeros((cfg.batch, cfg.n_needles), dtype=np.int64)
+    count = max(0, min(cfg.n_needles, hi - lo))   # shortened variants have fewer blocks
+    out = np.zeros((cfg.batch, count), dtype=np.int64)
     for b in range(cfg.batch):
-        if cfg.n_needles:
-            out[b] = np.sort(rng.choice(np.arange(lo, hi), size=cfg.n_needles, replace=False))
+        if count:
+            out[b] = np.sort(rng.choice(np.arange(lo, hi), size=count, replace=False))
     return out
 
 

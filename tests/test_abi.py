@@ -1,0 +1,111 @@
+"""The C ABI library loads, exports every declared symbol, and its host-side
+validation rejects bad arguments without touching a device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import trainable_block_sparse_amd as tbs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "infv2.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(infv2_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tbs.LIB_PATH):
+        from trainable_block_sparse_amd.build import build
+        build()
+    return tbs.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(tbs.EXPORTED)
+
+
+def _prob(**kw):
+    base = dict(batch=1, n_q=4096, n_kv=4096, h_kv=2, G=16, d=128, k=16)
+    base.update(kw)
+    return tbs.Problem(**base)
+
+
+def _status(L, p):
+    return L.infv2_check_problem(ctypes.byref(p.to_c()))
+
+
+def test_derived_sizes(L):
+    p = _prob(n_kv=131072, n_q=1, q_pos0=131071)
+    assert tbs.n_kernels(p) == 8191
+    assert tbs.n_blocks(p) == 2048
+    assert tbs.budget(p) == 19
+    assert tbs.n_kernels(_prob(n_kv=31, n_q=31)) == 0
+    assert tbs.n_kernels(_prob(n_kv=32, n_q=32)) == 1
+
+
+def test_dense_switch_rule(L):
+    assert tbs.use_dense(_prob(k=64))                  # 64 blocks <= 67
+    assert not tbs.use_dense(_prob(k=16))              # 64 blocks > 19
+    assert tbs.use_dense(_prob(n_kv=19 * 64, n_q=19 * 64))
+    assert not tbs.use_dense(_prob(n_kv=19 * 64 + 1, n_q=19 * 64 + 1))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(n_q=4097), tbs.INFV2_E_ARG),                 # q_pos0 + n_q > n_kv
+    (dict(q_pos0=-1), tbs.INFV2_E_ARG),
+    (dict(l=4), tbs.INFV2_E_ARG),                      # max-pool length must be 5
+    (dict(s=5), tbs.INFV2_E_ARG),
+    (dict(B=60), tbs.INFV2_E_ARG),                     # B not a multiple of s_C1
+    (dict(N_local=0), tbs.INFV2_E_ARG),
+    (dict(scale=-1.0), tbs.INFV2_E_ARG),
+    (dict(kv_cap=100), tbs.INFV2_E_ARG),
+    (dict(l_C1=24, l=5, s=4), tbs.INFV2_E_UNSUPPORTED),  # not a power of two
+    (dict(d=260), tbs.INFV2_E_UNSUPPORTED),
+    (dict(dtype="f32", G=4, d=64), 0),
+    (dict(dtype="f32", G=4, d=64, n_kv=131072, n_q=131072), tbs.INFV2_E_UNSUPPORTED),
+])
+def test_check_problem(L, kw, status):
+    assert _status(L, _prob(**kw)) == status
+
+
+def test_calls_reject_null_and_misaligned_pointers_before_any_launch(L):
+    p = _prob()
+    pc = ctypes.byref(p.to_c())
+    assert L.infv2_compress_k(pc, None, None, 0, 1, None) == tbs.INFV2_E_ARG
+    assert b"NULL" in L.infv2_last_error()
+    assert L.infv2_compress_k(pc, 16, 17, 0, 1, None) == tbs.INFV2_E_ARG
+    assert b"aligned" in L.infv2_last_error()
+    assert L.infv2_compress_k(pc, 16, 32, 0, 10 ** 6, None) == tbs.INFV2_E_ARG
+    assert L.infv2_topk_select(pc, None, 16, 16, None) == tbs.INFV2_E_ARG
+    assert L.infv2_block_scores(pc, 16, 16, None, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_sparse_attn(pc, 16, 16, 16, 16, 16, None, None, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_dense_attn(pc, 16, 16, 16, 16, None, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_check_problem(None) == tbs.INFV2_E_ARG
+
+
+def test_workspace_sizes_and_errors(L):
+    dec = _prob(batch=16, n_q=1, q_pos0=131071, n_kv=131072)
+    pc = ctypes.byref(dec.to_c())
+    need = L.infv2_block_scores_workspace(pc)
+    assert need >= 16 * 2 * 16 * 8191 * 4
+    assert L.infv2_block_scores(pc, 16, 16, 16, 16, need - 1, None) == tbs.INFV2_E_WORKSPACE
+    need_a = L.infv2_sparse_attn_workspace(pc)
+    assert need_a >= 16 * 2 * 19 * 16 * 128 * 4
+    assert L.infv2_sparse_attn(pc, 16, 16, 16, 16, 16, 16, None, 16, 0, None) \
+        == tbs.INFV2_E_WORKSPACE
+    pre = _prob(n_q=32768, n_kv=32768)
+    assert L.infv2_block_scores_workspace(ctypes.byref(pre.to_c())) == 0
+    assert L.infv2_dense_attn_workspace(ctypes.byref(pre.to_c())) == 2 * 128 * 32768 * 2
+    for s in (0, -1, -2, -3, -4, 7):
+        assert L.infv2_status_string(s)

@@ -1,0 +1,258 @@
+// Host side of the C ABI declared in include/infv2.h: argument validation,
+// workspace sizing and kernel dispatch.  No allocation, no synchronisation.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "common.hpp"
+
+namespace infv2 {
+hipError_t launch_compress_k(const infv2_problem& p, const void* K, void* Kc1, int c1_begin,
+                             int c1_end, int64_t kv_cap, int64_t c1_cap, hipStream_t stream);
+bool scores_fast_shape(const infv2_problem& p);
+size_t scores_workspace(const infv2_problem& p, int n_c1);
+size_t scores_generic_lds(const infv2_problem& p, int n_c1);
+hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void* Kc1,
+                               float* S_cmp, void* ws, int n_c1, int n_blk, int64_t c1_cap,
+                               float scale, hipStream_t stream);
+hipError_t launch_topk(const infv2_problem& p, const float* S_cmp, int32_t* idx, int32_t* n_sel,
+                       int n_blk, int budget, hipStream_t stream);
+bool attn_fast_shape(const infv2_problem& p);
+size_t attn_workspace(const infv2_problem& p, int budget, bool sparse);
+hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, const void* V,
+                       const int32_t* idx, const int32_t* n_sel, void* O, float* lse, void* ws,
+                       int budget, int64_t kv_cap, float scale, hipStream_t stream);
+}  // namespace infv2
+
+using namespace infv2;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return INFV2_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(INFV2_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int n_c1_of(const infv2_problem& p) {
+  return p.n_kv < p.l_C1 ? 0 : (p.n_kv - p.l_C1) / p.s_C1 + 1;
+}
+int n_blk_of(const infv2_problem& p) { return (p.n_kv + p.B - 1) / p.B; }
+int budget_of(const infv2_problem& p) { return p.N_init + p.N_local + p.k; }
+int64_t kv_cap_of(const infv2_problem& p) { return p.kv_cap ? p.kv_cap : p.n_kv; }
+int64_t c1_cap_of(const infv2_problem& p) { return p.c1_cap ? p.c1_cap : n_c1_of(p); }
+float scale_of(const infv2_problem& p) {
+  return p.scale != 0.0f ? p.scale : 1.0f / sqrtf((float)p.d);
+}
+
+// Shape and parameter checks shared by every entry point.
+int check(const infv2_problem* pp) {
+  if (!pp) return fail(INFV2_E_ARG, "prob is NULL");
+  const infv2_problem& p = *pp;
+  if (p.batch < 1 || p.n_q < 1 || p.n_kv < 1 || p.h_kv < 1 || p.G < 1 || p.d < 1)
+    return fail(INFV2_E_ARG, "batch, n_q, n_kv, h_kv, G and d must be >= 1");
+  if (p.q_pos0 < 0 || (int64_t)p.q_pos0 + p.n_q > p.n_kv)
+    return fail(INFV2_E_ARG, "need 0 <= q_pos0 and q_pos0 + n_q <= n_kv (got %d + %d > %d)",
+                p.q_pos0, p.n_q, p.n_kv);
+  if (p.dtype != INFV2_BF16 && p.dtype != INFV2_F32)
+    return fail(INFV2_E_ARG, "dtype must be INFV2_BF16 or INFV2_F32");
+  if (p.B < 1 || p.l_C1 < 1 || p.s_C1 < 1 || p.k < 0 || p.N_init < 0 || p.N_local < 1)
+    return fail(INFV2_E_ARG, "need B, l_C1, s_C1, N_local >= 1 and k, N_init >= 0");
+  if (p.B % p.s_C1 != 0)
+    return fail(INFV2_E_ARG, "B (%d) must be a multiple of s_C1 (%d)", p.B, p.s_C1);
+  // stage-3 parameters must be the stride and count of the kernels that
+  // intersect one block: s = B/s_C1, l = B/s_C1 + floor((l_C1-1)/s_C1)
+  const int s_expect = p.B / p.s_C1;
+  const int l_expect = s_expect + (p.l_C1 - 1) / p.s_C1;
+  if (p.s != s_expect || p.l != l_expect)
+    return fail(INFV2_E_ARG,
+                "max-pool (l=%d, s=%d) must equal the count and stride of the kernels "
+                "intersecting a block (l=%d, s=%d)",
+                p.l, p.s, l_expect, s_expect);
+  if (!(p.scale >= 0.0f) || isinf(p.scale))
+    return fail(INFV2_E_ARG, "scale must be finite and >= 0 (0 selects 1/sqrt(d))");
+  if (p.kv_cap != 0 && p.kv_cap < p.n_kv)
+    return fail(INFV2_E_ARG, "kv_cap (%lld) < n_kv (%d)", (long long)p.kv_cap, p.n_kv);
+  if (p.c1_cap != 0 && p.c1_cap < n_c1_of(p))
+    return fail(INFV2_E_ARG, "c1_cap (%lld) < n_C1 (%d)", (long long)p.c1_cap, n_c1_of(p));
+  if (budget_of(p) < 1) return fail(INFV2_E_ARG, "N_init + N_local + k must be >= 1");
+  if ((int64_t)p.G * p.h_kv > 4096) return fail(INFV2_E_ARG, "h_q too large");
+  // kernel instances
+  if (!is_pow2(p.l_C1))
+    return fail(INFV2_E_UNSUPPORTED, "l_C1 (%d) must be a power of two (exact mean)", p.l_C1);
+  if (p.d > 256 || p.d % 8 != 0)
+    return fail(INFV2_E_UNSUPPORTED, "d (%d) must be a multiple of 8 and <= 256", p.d);
+  if (p.dtype == INFV2_BF16 && p.d % 8 != 0)
+    return fail(INFV2_E_UNSUPPORTED, "bf16 rows must be 16-byte multiples");
+  if (!scores_fast_shape(p) && scores_generic_lds(p, n_c1_of(p)) > 60 * 1024)
+    return fail(INFV2_E_UNSUPPORTED,
+                "n_C1 = %d too large for the generic selection kernel (shape G=%d d=%d dtype=%d)",
+                n_c1_of(p), p.G, p.d, p.dtype);
+  return INFV2_OK;
+}
+
+#define CHECK_PTR(ptr)                                                          \
+  do {                                                                          \
+    if (!(ptr)) return fail(INFV2_E_ARG, "%s is NULL", #ptr);                   \
+    if (!aligned16(ptr)) return fail(INFV2_E_ARG, "%s is not 16-byte aligned", #ptr); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t infv2_n_kernels(const infv2_problem* p) { return p ? n_c1_of(*p) : -1; }
+int32_t infv2_n_blocks(const infv2_problem* p) { return p ? n_blk_of(*p) : -1; }
+int32_t infv2_budget(const infv2_problem* p) { return p ? budget_of(*p) : -1; }
+
+int infv2_use_dense(const infv2_problem* p) {
+  if (check(p) != INFV2_OK) return -1;
+  return n_blk_of(*p) <= budget_of(*p) ? 1 : 0;
+}
+
+int infv2_check_problem(const infv2_problem* p) {
+  const int st = check(p);
+  return st == INFV2_OK ? ok() : st;
+}
+
+int infv2_compress_k(const infv2_problem* p, const void* K, void* Kc1, int32_t c1_begin,
+                     int32_t c1_end, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(K);
+  CHECK_PTR(Kc1);
+  const int n_c1 = n_c1_of(*p);
+  if (c1_begin < 0 || c1_begin > c1_end || c1_end > n_c1)
+    return fail(INFV2_E_ARG, "need 0 <= c1_begin <= c1_end <= n_C1 (%d..%d, n_C1=%d)",
+                c1_begin, c1_end, n_c1);
+  return hip_status(launch_compress_k(*p, K, Kc1, c1_begin, c1_end, kv_cap_of(*p), c1_cap_of(*p),
+                                      (hipStream_t)stream),
+                    "infv2_compress_k");
+}
+
+size_t infv2_block_scores_workspace(const infv2_problem* p) {
+  if (check(p) != INFV2_OK) return 0;
+  return scores_workspace(*p, n_c1_of(*p));
+}
+
+int infv2_block_scores(const infv2_problem* p, const void* Q, const void* Kc1, float* S_cmp,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(Q);
+  CHECK_PTR(S_cmp);
+  const int n_c1 = n_c1_of(*p);
+  if (n_c1 > 0) CHECK_PTR(Kc1);
+  const size_t need = scores_workspace(*p, n_c1);
+  if (need) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need)
+      return fail(INFV2_E_WORKSPACE, "block_scores workspace %zu < %zu bytes", ws_bytes, need);
+  }
+  return hip_status(launch_block_scores(*p, Q, Kc1, S_cmp, ws, n_c1, n_blk_of(*p), c1_cap_of(*p),
+                                        scale_of(*p), (hipStream_t)stream),
+                    "infv2_block_scores");
+}
+
+int infv2_topk_select(const infv2_problem* p, const float* S_cmp, int32_t* idx, int32_t* n_sel,
+                      void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(S_cmp);
+  CHECK_PTR(idx);
+  CHECK_PTR(n_sel);
+  return hip_status(
+      launch_topk(*p, S_cmp, idx, n_sel, n_blk_of(*p), budget_of(*p), (hipStream_t)stream),
+      "infv2_topk_select");
+}
+
+size_t infv2_sparse_attn_workspace(const infv2_problem* p) {
+  if (check(p) != INFV2_OK) return 0;
+  return attn_workspace(*p, budget_of(*p), true);
+}
+
+int infv2_sparse_attn(const infv2_problem* p, const void* Q, const void* K, const void* V,
+                      const int32_t* idx, const int32_t* n_sel, void* O, float* lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(Q);
+  CHECK_PTR(K);
+  CHECK_PTR(V);
+  CHECK_PTR(idx);
+  CHECK_PTR(n_sel);
+  CHECK_PTR(O);
+  if (lse && !aligned16(lse)) return fail(INFV2_E_ARG, "lse is not 16-byte aligned");
+  const size_t need = attn_workspace(*p, budget_of(*p), true);
+  if (need) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need)
+      return fail(INFV2_E_WORKSPACE, "sparse_attn workspace %zu < %zu bytes", ws_bytes, need);
+  }
+  return hip_status(launch_attn(*p, Q, K, V, idx, n_sel, O, lse, ws, budget_of(*p), kv_cap_of(*p),
+                                scale_of(*p), (hipStream_t)stream),
+                    "infv2_sparse_attn");
+}
+
+size_t infv2_dense_attn_workspace(const infv2_problem* p) {
+  if (check(p) != INFV2_OK) return 0;
+  return attn_workspace(*p, budget_of(*p), false);
+}
+
+int infv2_dense_attn(const infv2_problem* p, const void* Q, const void* K, const void* V,
+                     void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(Q);
+  CHECK_PTR(K);
+  CHECK_PTR(V);
+  CHECK_PTR(O);
+  if (lse && !aligned16(lse)) return fail(INFV2_E_ARG, "lse is not 16-byte aligned");
+  const size_t need = attn_workspace(*p, budget_of(*p), false);
+  if (need) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need)
+      return fail(INFV2_E_WORKSPACE, "dense_attn workspace %zu < %zu bytes", ws_bytes, need);
+  }
+  return hip_status(launch_attn(*p, Q, K, V, nullptr, nullptr, O, lse, ws, budget_of(*p),
+                                kv_cap_of(*p), scale_of(*p), (hipStream_t)stream),
+                    "infv2_dense_attn");
+}
+
+const char* infv2_status_string(int status) {
+  switch (status) {
+    case INFV2_OK: return "ok";
+    case INFV2_E_ARG: return "invalid argument";
+    case INFV2_E_UNSUPPORTED: return "unsupported problem";
+    case INFV2_E_WORKSPACE: return "workspace too small";
+    case INFV2_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* infv2_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

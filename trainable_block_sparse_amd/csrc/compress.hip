@@ -1,0 +1,104 @@
+// Stage 1 of the block representation: mean-pooled keys K^C1.
+//
+// papernotes.org InfLLM-V2 note, 方法详解 > 关键设计 3 (three-stage compression,
+// stage 1 with kernel length l_C1 and stride s_C1); OpenBMB blog
+// "技术Blog-4 | 新一代InfLLM：可训练的稀疏注意力机制", 动态上下文块选择 > 语义核 (kernels
+// overlap, keys only, representation = mean of the kernel's keys).
+//
+// The kernel is HBM-bound: every key row is read by l_C1/s_C1 kernels, so the
+// second read hits L2.  Threads run along d so that each 32-token segment is
+// read as contiguous rows.  The sum of the l_C1 keys is carried as an fp64
+// pair (hi, lo) with TwoSum, which is exact for any inputs of this format, and
+// rounded ONCE to the I/O dtype, to nearest even.
+#include "common.hpp"
+
+namespace infv2 {
+
+// Round (hi + lo) to a binary format with P significant bits and fp32's
+// exponent range, to nearest even; |lo| <= ulp(hi)/2 (a TwoSum pair).
+template <int P>
+__device__ __forceinline__ double round_pair(double hi, double lo) {
+  if (hi == 0.0 || !__builtin_isfinite(hi)) return hi + lo;
+  int e;
+  (void)__builtin_frexp(hi, &e);             // hi = m * 2^e, 0.5 <= |m| < 1
+  int qexp = e - P;
+  if (qexp < -126 - P + 1) qexp = -126 - P + 1;   // subnormal quantum
+  const double scaled = __builtin_ldexp(hi, -qexp);
+  double r = __builtin_rint(scaled);         // ties to even
+  const double delta = scaled - r;           // exact
+  if ((delta == 0.5 || delta == -0.5) && lo != 0.0) {
+    // hi sits exactly on a midpoint: the sign of lo decides the direction.
+    if ((lo > 0.0) == (delta > 0.0)) r += (delta > 0.0) ? 1.0 : -1.0;
+  }
+  return __builtin_ldexp(r, qexp);
+}
+
+template <typename T> __device__ __forceinline__ double load_f64(const T* p);
+template <> __device__ __forceinline__ double load_f64<uint16_t>(const uint16_t* p) {
+  return (double)bf16_bits_to_f32(*p);
+}
+template <> __device__ __forceinline__ double load_f64<float>(const float* p) {
+  return (double)*p;
+}
+
+template <typename T> __device__ __forceinline__ void store_rounded(T* p, double hi, double lo);
+template <> __device__ __forceinline__ void store_rounded<uint16_t>(uint16_t* p, double hi, double lo) {
+  const float r = (float)round_pair<8>(hi, lo);      // exact: 8 bits fit fp32
+  *p = (uint16_t)(__float_as_uint(r) >> 16);          // exact: low half is zero
+}
+template <> __device__ __forceinline__ void store_rounded<float>(float* p, double hi, double lo) {
+  *p = (float)round_pair<24>(hi, lo);                 // exact conversion
+}
+
+// grid: x = kernel groups of (blockDim / d) kernels, y = h_kv, z = batch.
+template <typename T>
+__global__ void __launch_bounds__(256) compress_k_kernel(
+    const T* __restrict__ K, T* __restrict__ Kc1, int c1_begin, int c1_end, int h_kv, int d,
+    int64_t kv_cap, int64_t c1_cap, int l_C1, int s_C1, double inv_l) {
+  const int per_blk = blockDim.x / d;
+  const int local = threadIdx.x / d;
+  const int di = threadIdx.x % d;
+  if (local >= per_blk) return;
+  const int j = c1_begin + blockIdx.x * per_blk + local;
+  if (j >= c1_end) return;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const size_t row_stride = (size_t)h_kv * d;
+  const T* src = K + ((size_t)b * kv_cap + (size_t)j * s_C1) * row_stride + (size_t)g * d + di;
+  double hi = 0.0, lo = 0.0;
+  for (int u = 0; u < l_C1; ++u) {
+    const double x = load_f64<T>(src + (size_t)u * row_stride);
+    const double t = hi + x;
+    const double bp = t - hi;
+    lo += (hi - (t - bp)) + (x - bp);       // TwoSum error, accumulated exactly
+    hi = t;                                  // for the magnitudes of one kernel
+  }
+  // renormalise the pair so that |lo| <= ulp(hi)/2, then scale by 1/l_C1
+  // (a power of two: exact)
+  const double t = hi + lo;
+  const double bp = t - hi;
+  const double e = (hi - (t - bp)) + (lo - bp);
+  T* dst = Kc1 + (((size_t)b * h_kv + g) * c1_cap + j) * d + di;
+  store_rounded<T>(dst, t * inv_l, e * inv_l);
+}
+
+hipError_t launch_compress_k(const infv2_problem& p, const void* K, void* Kc1, int c1_begin,
+                             int c1_end, int64_t kv_cap, int64_t c1_cap, hipStream_t stream) {
+  if (c1_end <= c1_begin) return hipSuccess;
+  const int per_blk = 256 / p.d;
+  const int n = c1_end - c1_begin;
+  dim3 grid((n + per_blk - 1) / per_blk, p.h_kv, p.batch);
+  dim3 block(per_blk * p.d);
+  const double inv_l = 1.0 / (double)p.l_C1;
+  if (p.dtype == INFV2_BF16) {
+    hipLaunchKernelGGL(compress_k_kernel<uint16_t>, grid, block, 0, stream,
+                       (const uint16_t*)K, (uint16_t*)Kc1, c1_begin, c1_end, p.h_kv, p.d, kv_cap,
+                       c1_cap, p.l_C1, p.s_C1, inv_l);
+  } else {
+    hipLaunchKernelGGL(compress_k_kernel<float>, grid, block, 0, stream, (const float*)K,
+                       (float*)Kc1, c1_begin, c1_end, p.h_kv, p.d, kv_cap, c1_cap, p.l_C1,
+                       p.s_C1, inv_l);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace infv2

@@ -1,0 +1,603 @@
+// Stages 2-3 of block selection: compressed scores, head-group sum, max-pool.
+//
+// papernotes.org InfLLM-V2 note, 方法详解 > 关键设计 3 (S^C1 = Softmax(Q K^C1^T),
+// S^shared = sum over the G heads of a group, S^cmp = max-pool with l, s) and
+// 关键设计 4 (fused head-group summation: S^C1 never reaches HBM; the normaliser
+// comes from an exact log-sum-exp computed in an earlier sweep).  OpenBMB blog
+// "技术Blog-4 | 新一代InfLLM：可训练的稀疏注意力机制", 动态上下文块选择 > 语义核 (block
+// score = max over the kernels intersecting the block) and 高效Top-K实现.
+//
+// Three kernels:
+//  * scores_prefill_kernel -- bf16, G = 16, d = 128, B = 64, l_C1 = 32,
+//    s_C1 = 16.  One workgroup = 16 query tokens x 16 heads of one group (256
+//    MFMA rows).  Q stays in registers; K^C1 streams through LDS in chunks of
+//    64 kernels.  The log-sum-exp is exact and takes two sweeps (row maximum,
+//    then the sum of 2^(z*c - max)); a third sweep forms S^C1, sums the 16
+//    heads (8 in-lane + one cross-half exchange), max-pools into blocks and
+//    writes S^cmp.  Neither S^C1 nor S^shared is written to memory.
+//  * scores_split_{logits,pool}_kernel -- few query tokens (decode): the kernel
+//    axis is split over workgroups; the first writes scaled logits and
+//    per-chunk (max, sum) partials, the second merges the partials into the
+//    exact log-sum-exp and forms S^shared / S^cmp for its chunk.
+//  * scores_generic_kernel -- any shape and fp32 I/O: fp64 arithmetic, one
+//    workgroup per (token, group).  Correctness path for the fp32 workload.
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace infv2 {
+
+constexpr int SEL_D = 128;
+constexpr int SEL_G = 16;
+constexpr int SEL_CHUNK = 64;                 // kernels per LDS chunk
+constexpr int SEL_ROW_BYTES = SEL_D * 2;      // one K^C1 row, bf16
+constexpr int SEL_TOK_WAVE = 4;               // tokens per wave (2 MFMA row blocks)
+constexpr int SEL_TOK_WG = 16;                // tokens per workgroup
+
+struct ScoresArgs {
+  const uint16_t* Q;
+  const uint16_t* Kc1;
+  float* S_cmp;
+  int n_q, q_pos0, h_kv, n_c1, n_blk, tiles;
+  int64_t c1_cap;
+  float c;  // scale * log2(e)
+};
+
+// kernel j is causal for position p when its last token j*16+31 <= p
+__device__ __forceinline__ int last_visible_kernel(int p) { return p >= 31 ? (p - 31) >> 4 : -1; }
+
+template <int PASS>
+__device__ __forceinline__ void scores_chunk(const ScoresArgs& a, const uint8_t* kb, int chunk,
+                                             bool masked, const bf16x8 (&qf)[2][8],
+                                             const int (&jm)[4], float (&M)[2][16],
+                                             float (&W)[2][16], float (&sbuf)[4][SEL_CHUNK + 1],
+                                             int lane) {
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][nt][i] = 0.f;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int row = 32 * nt + col;
+      const int c16 = 2 * ks + half;
+      const u32x4 raw = *(const u32x4*)(kb + row * SEL_ROW_BYTES + ((c16 ^ (row & 15)) << 4));
+      const bf16x8 bfrag = as_bf16x8(raw);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) acc[rb][nt] = mfma32(qf[rb][ks], bfrag, acc[rb][nt]);
+    }
+  }
+  const int j_base = chunk * SEL_CHUNK;
+  if constexpr (PASS == 0) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float z = acc[rb][nt][i];
+          if (masked && j_base + 32 * nt + col > jm[2 * rb + (i >> 3)]) z = kNegInf;
+          M[rb][i] = fmaxf(M[rb][i], z);
+        }
+  } else if constexpr (PASS == 1) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float e = fast_exp2(__builtin_fmaf(acc[rb][nt][i], a.c, -M[rb][i]));
+          if (masked && j_base + 32 * nt + col > jm[2 * rb + (i >> 3)]) e = 0.f;
+          W[rb][i] += e;
+        }
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float part0 = 0.f, part1 = 0.f;  // tokens 2rb and 2rb+1, this lane's 8 heads
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float e = fast_exp2(__builtin_fmaf(acc[rb][nt][i], a.c, -M[rb][i]));
+          if (masked && j_base + 32 * nt + col > jm[2 * rb + (i >> 3)]) e = 0.f;
+          if (i < 8) part0 = __builtin_fmaf(e, W[rb][i], part0);
+          else       part1 = __builtin_fmaf(e, W[rb][i], part1);
+        }
+        // lanes l and l^32 hold the other 8 heads of the same (token, kernel)
+        const float send = half ? part0 : part1;
+        const float recv = __shfl_xor(send, 32, 64);
+        const float mine = (half ? part1 : part0) + recv;
+        const int tl = 2 * rb + half;
+        const int j = j_base + 32 * nt + col;
+        sbuf[tl][1 + 32 * nt + col] = (j > jm[tl]) ? kNegInf : mine;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256, 2) scores_prefill_kernel(ScoresArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][SEL_CHUNK * SEL_ROW_BYTES];
+  __shared__ float sbuf_all[4][SEL_TOK_WAVE][SEL_CHUNK + 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int tile = a.tiles - 1 - (int)(blockIdx.x % a.tiles);   // long rows first
+  const int bg = blockIdx.x / a.tiles;
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int wg_t0 = tile * SEL_TOK_WG;
+  const int t0 = wg_t0 + wave * SEL_TOK_WAVE;
+  const int hq = a.h_kv * SEL_G;
+  float (&sbuf)[4][SEL_CHUNK + 1] = sbuf_all[wave];
+
+  // ---- Q fragments (A operand: rows = (token, head), k = d) ----
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int tok = t0 + 2 * rb + ((lane & 31) >> 4);
+    const int head = g * SEL_G + (lane & 15);
+    const bool ok = tok < a.n_q;
+    const uint16_t* qrow = a.Q + (((size_t)b * a.n_q + (ok ? tok : 0)) * hq + head) * SEL_D;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *(const u32x4*)(qrow + 16 * ks + 8 * (lane >> 5));
+      qf[rb][ks] = as_bf16x8(v);
+    }
+  }
+  int jm[4];
+#pragma unroll
+  for (int tl = 0; tl < 4; ++tl) {
+    const int tok = t0 + tl;
+    jm[tl] = tok < a.n_q ? last_visible_kernel(a.q_pos0 + tok) : -1;
+  }
+  const int wg_last = min(wg_t0 + SEL_TOK_WG - 1, a.n_q - 1);
+  const int jmax_wg = last_visible_kernel(a.q_pos0 + wg_last);
+  const int jmin_wg = last_visible_kernel(a.q_pos0 + wg_t0);
+  const int nchunks = jmax_wg < 0 ? 0 : (jmax_wg + 2 + SEL_CHUNK - 1) / SEL_CHUNK;
+
+  float M[2][16], W[2][16];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { M[rb][i] = kNegInf; W[rb][i] = 0.f; }
+
+  const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
+
+  // stage one chunk of 64 K^C1 rows (16 KB): 4 x 16 B per thread, XOR-swizzled
+  auto stage_load = [&](int chunk, u32x4 (&st)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      const int row = u >> 4, c16 = u & 15;
+      const int j = chunk * SEL_CHUNK + row;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (j < a.n_c1) v = *(const u32x4*)(kc1 + (size_t)j * SEL_D + c16 * 8);
+      st[i] = v;
+    }
+  };
+  auto stage_store = [&](uint8_t* kb, const u32x4 (&st)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = tid + 256 * i;
+      const int row = u >> 4, c16 = u & 15;
+      *(u32x4*)(kb + row * SEL_ROW_BYTES + ((c16 ^ (row & 15)) << 4)) = st[i];
+    }
+  };
+
+  auto run_pass = [&](auto pass_tag) {
+    constexpr int PASS = decltype(pass_tag)::value;
+    if (nchunks == 0) return;
+    u32x4 st[4];
+    stage_load(0, st);
+    stage_store(kbuf[0], st);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      const bool more = c + 1 < nchunks;
+      if (more) stage_load(c + 1, st);
+      const bool masked = c * SEL_CHUNK + SEL_CHUNK - 1 > jmin_wg;
+      scores_chunk<PASS>(a, kbuf[c & 1], c, masked, qf, jm, M, W, sbuf, lane);
+      if constexpr (PASS == 2) {
+        // max-pool: block c*16+bb takes kernels c*64+4bb-1 .. c*64+4bb+3,
+        // i.e. sbuf[tl][4bb .. 4bb+4] (sbuf[tl][0] carries kernel c*64-1)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int tl = lane >> 4, bb = lane & 15;
+        float v = sbuf[tl][4 * bb];
+#pragma unroll
+        for (int q = 1; q < 5; ++q) v = fmaxf(v, sbuf[tl][4 * bb + q]);
+        const int tok = t0 + tl;
+        const int blk = c * (SEL_CHUNK / 4) + bb;
+        if (tok < a.n_q && blk <= (a.q_pos0 + tok) >> 6)
+          a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_blk + blk] = v;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < 4) sbuf[lane][0] = sbuf[lane][SEL_CHUNK];
+      }
+      if (more) stage_store(kbuf[(c + 1) & 1], st);
+      __syncthreads();
+    }
+  };
+
+
+  // sweep 1: exact row maximum of z (raw dot products)
+  run_pass(std::integral_constant<int, 0>{});
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float m = M[rb][i];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      // log2-domain reference; rows without a visible kernel keep -inf and
+      // are masked in every chunk
+      M[rb][i] = (m == kNegInf) ? 0.f : m * a.c;
+    }
+  // sweep 2: s = sum 2^(z*c - max)  ->  lse = max + log2(s)
+  run_pass(std::integral_constant<int, 1>{});
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = W[rb][i];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
+      W[rb][i] = s > 0.f ? 1.0f / s : 0.f;
+    }
+  // sweep 3: S^C1 = 2^(z*c - max) / s, head-group sum, max-pool, S^cmp
+  if (lane < 4) sbuf[lane][0] = kNegInf;
+  run_pass(std::integral_constant<int, 2>{});
+  // blocks with no visible kernel in the causal range
+  {
+    const int tl = lane >> 4;
+    const int tok = t0 + tl;
+    if (tok < a.n_q) {
+      const int b_p = (a.q_pos0 + tok) >> 6;
+      float* row = a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_blk;
+      for (int blk = nchunks * (SEL_CHUNK / 4) + (lane & 15); blk <= b_p; blk += 16)
+        row[blk] = kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K selection for few query tokens (decode).
+// ---------------------------------------------------------------------------
+constexpr int SPLIT_CK = 256;   // kernels per workgroup
+
+struct SplitArgs {
+  const uint16_t* Q;
+  const uint16_t* Kc1;
+  float* S_cmp;
+  float* logits;    // [batch*n_q][h_kv][16][n_c1p]  (z*c, -inf when invisible)
+  float2* part;     // [batch*n_q][h_kv][nch][16]    (chunk max, chunk sum)
+  int n_q, q_pos0, h_kv, n_c1, n_c1p, n_blk, nch;
+  int64_t c1_cap;
+  float c;
+};
+
+// grid: x = chunk, y = group, z = batch*n_q token.  4 waves x 64 kernels.
+__global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
+  __shared__ float red_m[4][16], red_s[4][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+  const int b = bt / a.n_q, t = bt % a.n_q;
+  const int p = a.q_pos0 + t;
+  const int jmax = last_visible_kernel(p);
+  const int hq = a.h_kv * SEL_G;
+  // A operand: Q rows = heads (lane & 15), k = d
+  bf16x8 qf[4];
+  const uint16_t* qrow = a.Q + (((size_t)b * a.n_q + t) * hq + g * SEL_G + (lane & 15)) * SEL_D;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(qrow + 32 * ks + 8 * (lane >> 4)));
+  const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
+  const int jw = chunk * SPLIT_CK + wave * 64;
+  f32x4 acc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int j = jw + 16 * nt + (lane & 15);
+    const bool ok = j < a.n_c1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *(const u32x4*)(kc1 + (size_t)j * SEL_D + 32 * ks + 8 * (lane >> 4));
+      acc[nt] = mfma16(qf[ks], as_bf16x8(v), acc[nt]);
+    }
+  }
+  // C layout: lane holds heads 4*(lane>>4)+i, kernel jw + 16*nt + (lane&15)
+  float* lrow = a.logits + ((size_t)bt * a.h_kv + g) * SEL_G * a.n_c1p;
+  float mloc[4], sloc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * (lane >> 4) + i;
+    float m = kNegInf;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int j = jw + 16 * nt + (lane & 15);
+      const float zc = (j <= jmax) ? acc[nt][i] * a.c : kNegInf;
+      acc[nt][i] = zc;
+      if (j < a.n_c1p) lrow[(size_t)h * a.n_c1p + j] = zc;
+      m = fmaxf(m, zc);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    mloc[i] = m;
+  }
+  if ((lane & 15) == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red_m[wave][4 * (lane >> 4) + i] = mloc[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * (lane >> 4) + i;
+    const float mc = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+    float s = 0.f;
+    if (mc != kNegInf) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) s += fast_exp2(acc[nt][i] - mc);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+    sloc[i] = s;
+    mloc[i] = mc;
+  }
+  if ((lane & 15) == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red_s[wave][4 * (lane >> 4) + i] = sloc[i];
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
+    const float mc = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+    const float s = red_s[0][h] + red_s[1][h] + red_s[2][h] + red_s[3][h];
+    a.part[(((size_t)bt * a.h_kv + g) * a.nch + chunk) * SEL_G + h] = make_float2(mc, s);
+  }
+}
+
+// grid as above; 256 threads = 256 kernels of the chunk (+ the carry kernel).
+__global__ void __launch_bounds__(256) scores_split_pool_kernel(SplitArgs a) {
+  __shared__ float Mh[SEL_G], Wh[SEL_G];
+  __shared__ float sh[SPLIT_CK + 1];
+  const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+  const int b = bt / a.n_q, t = bt % a.n_q;
+  const int p = a.q_pos0 + t;
+  const int jmax = last_visible_kernel(p);
+  const int b_p = p >> 6;
+  if (threadIdx.x < SEL_G) {
+    const int h = threadIdx.x;
+    const float2* pr = a.part + ((size_t)bt * a.h_kv + g) * a.nch * SEL_G + h;
+    float m = kNegInf;
+    for (int c = 0; c < a.nch; ++c) m = fmaxf(m, pr[(size_t)c * SEL_G].x);
+    float s = 0.f;
+    if (m != kNegInf)
+      for (int c = 0; c < a.nch; ++c) {
+        const float2 v = pr[(size_t)c * SEL_G];
+        if (v.x != kNegInf) s += v.y * fast_exp2(v.x - m);
+      }
+    Mh[h] = (m == kNegInf) ? 0.f : m;
+    Wh[h] = s > 0.f ? 1.0f / s : 0.f;
+  }
+  __syncthreads();
+  const float* lrow = a.logits + ((size_t)bt * a.h_kv + g) * SEL_G * a.n_c1p;
+  const int j0 = chunk * SPLIT_CK;
+  for (int x = threadIdx.x; x <= SPLIT_CK; x += blockDim.x) {
+    const int j = j0 - 1 + x;       // x = 0 is the carry kernel j0-1
+    float v = kNegInf;
+    if (j >= 0 && j <= jmax) {
+      v = 0.f;
+#pragma unroll
+      for (int h = 0; h < SEL_G; ++h)
+        v = __builtin_fmaf(fast_exp2(lrow[(size_t)h * a.n_c1p + j] - Mh[h]), Wh[h], v);
+    }
+    sh[x] = v;
+  }
+  __syncthreads();
+  float* row = a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_blk;
+  const int nblk_chunk = SPLIT_CK / 4;
+  if (threadIdx.x < nblk_chunk) {
+    const int bb = threadIdx.x;
+    const int blk = chunk * nblk_chunk + bb;
+    float v = sh[4 * bb];
+#pragma unroll
+    for (int q = 1; q < 5; ++q) v = fmaxf(v, sh[4 * bb + q]);
+    if (blk <= b_p) row[blk] = v;
+  }
+  if (chunk == a.nch - 1)
+    for (int blk = a.nch * nblk_chunk + threadIdx.x; blk <= b_p; blk += blockDim.x)
+      row[blk] = kNegInf;
+}
+
+// ---------------------------------------------------------------------------
+// Generic selection: any G, d, B, l_C1, s_C1 and fp32 or bf16 I/O; fp64 math.
+// One workgroup per (token, group).  Dynamic LDS: (n_vis + 1) doubles + G
+// doubles.
+// ---------------------------------------------------------------------------
+struct GenericScoresArgs {
+  const void* Q;
+  const void* Kc1;
+  float* S_cmp;
+  int dtype, n_q, q_pos0, h_kv, G, d, n_c1, n_blk, B, l_C1, s_C1;
+  int64_t c1_cap;
+  double scale;
+};
+
+template <typename T> __device__ __forceinline__ double ld(const T* p, size_t i);
+template <> __device__ __forceinline__ double ld<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ double ld<uint16_t>(const uint16_t* p, size_t i) {
+  return (double)bf16_bits_to_f32(p[i]);
+}
+
+__device__ double block_reduce_max(double v, double* red) {
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  double r = red[0];
+  for (int i = 1; i < nw; ++i) r = fmax(r, red[i]);
+  return r;
+}
+__device__ double block_reduce_sum(double v, double* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  double r = 0.0;
+  for (int i = 0; i < nw; ++i) r += red[i];
+  return r;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) scores_generic_kernel(GenericScoresArgs a) {
+  extern __shared__ double dyn[];
+  __shared__ double red[8];
+  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int p = a.q_pos0 + t;
+  const int jmax = p >= a.l_C1 - 1 ? (p - a.l_C1 + 1) / a.s_C1 : -1;
+  const int nv = min(jmax + 1, a.n_c1);
+  double* lse = dyn;            // [G]
+  double* shared_s = dyn + a.G; // [nv]
+  const T* Q = (const T*)a.Q;
+  const T* K = (const T*)a.Kc1;
+  const int hq = a.h_kv * a.G;
+  const T* kbase = K + ((size_t)b * a.h_kv + g) * a.c1_cap * a.d;
+  for (int h = 0; h < a.G; ++h) {
+    const T* q = Q + (((size_t)b * a.n_q + t) * hq + g * a.G + h) * a.d;
+    double m = -__builtin_huge_val();
+    for (int j = threadIdx.x; j < nv; j += blockDim.x) {
+      double z = 0.0;
+      for (int i = 0; i < a.d; ++i) z += ld<T>(q, i) * ld<T>(kbase, (size_t)j * a.d + i);
+      m = fmax(m, z * a.scale);
+    }
+    m = block_reduce_max(m, red);
+    double s = 0.0;
+    for (int j = threadIdx.x; j < nv; j += blockDim.x) {
+      double z = 0.0;
+      for (int i = 0; i < a.d; ++i) z += ld<T>(q, i) * ld<T>(kbase, (size_t)j * a.d + i);
+      s += exp(z * a.scale - m);
+    }
+    s = block_reduce_sum(s, red);
+    if (threadIdx.x == 0) lse[h] = nv > 0 ? m + log(s) : -__builtin_huge_val();
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < nv; j += blockDim.x) {
+    double acc = 0.0;
+    for (int h = 0; h < a.G; ++h) {
+      const T* q = Q + (((size_t)b * a.n_q + t) * hq + g * a.G + h) * a.d;
+      double z = 0.0;
+      for (int i = 0; i < a.d; ++i) z += ld<T>(q, i) * ld<T>(kbase, (size_t)j * a.d + i);
+      acc += exp(z * a.scale - lse[h]);
+    }
+    shared_s[j] = acc;
+  }
+  __syncthreads();
+  const int b_p = p / a.B;
+  float* row = a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_blk;
+  for (int blk = threadIdx.x; blk <= b_p; blk += blockDim.x) {
+    // kernels whose span [j*s_C1, j*s_C1+l_C1-1] meets [blk*B, blk*B+B-1]
+    const int lo_num = blk * a.B - a.l_C1 + 1;
+    int jlo = lo_num <= 0 ? 0 : (lo_num + a.s_C1 - 1) / a.s_C1;
+    int jhi = (blk * a.B + a.B - 1) / a.s_C1;
+    if (jhi > nv - 1) jhi = nv - 1;
+    double v = -__builtin_huge_val();
+    for (int j = jlo; j <= jhi; ++j) v = fmax(v, shared_s[j]);
+    row[blk] = (float)v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+bool scores_fast_shape(const infv2_problem& p) {
+  return p.dtype == INFV2_BF16 && p.G == SEL_G && p.d == SEL_D && p.B == 64 && p.l_C1 == 32 &&
+         p.s_C1 == 16;
+}
+bool scores_use_split(const infv2_problem& p) { return scores_fast_shape(p) && p.n_q <= 4; }
+
+size_t scores_workspace(const infv2_problem& p, int n_c1) {
+  if (!scores_use_split(p)) return 0;
+  const int n_c1p = (n_c1 + 63) & ~63;
+  const int nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
+  const size_t rows = (size_t)p.batch * p.n_q * p.h_kv;
+  return rows * SEL_G * (size_t)n_c1p * sizeof(float) + rows * nch * SEL_G * sizeof(float2);
+}
+
+size_t scores_generic_lds(const infv2_problem& p, int n_c1) {
+  return (size_t)(n_c1 + p.G + 1) * sizeof(double);
+}
+
+hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void* Kc1,
+                               float* S_cmp, void* ws, int n_c1, int n_blk, int64_t c1_cap,
+                               float scale, hipStream_t stream) {
+  if (scores_use_split(p)) {
+    SplitArgs a;
+    a.Q = (const uint16_t*)Q;
+    a.Kc1 = (const uint16_t*)Kc1;
+    a.S_cmp = S_cmp;
+    a.n_q = p.n_q;
+    a.q_pos0 = p.q_pos0;
+    a.h_kv = p.h_kv;
+    a.n_c1 = n_c1;
+    a.n_c1p = (n_c1 + 63) & ~63;
+    a.n_blk = n_blk;
+    a.nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
+    a.c1_cap = c1_cap;
+    a.c = scale * kLog2e;
+    const size_t rows = (size_t)p.batch * p.n_q * p.h_kv;
+    a.logits = (float*)ws;
+    a.part = (float2*)((char*)ws + rows * SEL_G * (size_t)a.n_c1p * sizeof(float));
+    dim3 grid(a.nch, p.h_kv, p.batch * p.n_q);
+    hipLaunchKernelGGL(scores_split_logits_kernel, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(scores_split_pool_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (scores_fast_shape(p)) {
+    ScoresArgs a;
+    a.Q = (const uint16_t*)Q;
+    a.Kc1 = (const uint16_t*)Kc1;
+    a.S_cmp = S_cmp;
+    a.n_q = p.n_q;
+    a.q_pos0 = p.q_pos0;
+    a.h_kv = p.h_kv;
+    a.n_c1 = n_c1;
+    a.n_blk = n_blk;
+    a.tiles = (p.n_q + SEL_TOK_WG - 1) / SEL_TOK_WG;
+    a.c1_cap = c1_cap;
+    a.c = scale * kLog2e;
+    dim3 grid((unsigned)a.tiles * p.h_kv * p.batch);
+    hipLaunchKernelGGL(scores_prefill_kernel, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  GenericScoresArgs a;
+  a.Q = Q;
+  a.Kc1 = Kc1;
+  a.S_cmp = S_cmp;
+  a.dtype = p.dtype;
+  a.n_q = p.n_q;
+  a.q_pos0 = p.q_pos0;
+  a.h_kv = p.h_kv;
+  a.G = p.G;
+  a.d = p.d;
+  a.n_c1 = n_c1;
+  a.n_blk = n_blk;
+  a.B = p.B;
+  a.l_C1 = p.l_C1;
+  a.s_C1 = p.s_C1;
+  a.c1_cap = c1_cap;
+  a.scale = scale;
+  dim3 grid(p.n_q, p.h_kv, p.batch);
+  const size_t lds = scores_generic_lds(p, n_c1);
+  if (p.dtype == INFV2_F32)
+    hipLaunchKernelGGL(scores_generic_kernel<float>, grid, dim3(256), lds, stream, a);
+  else
+    hipLaunchKernelGGL(scores_generic_kernel<uint16_t>, grid, dim3(256), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace infv2
