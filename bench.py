@@ -294,6 +294,11 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the 128k and decode lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--only", choices=["prefill32k", "prefill128k", "decode", "dense_switch",
+                                       "copy"],
+                    help="run one workload alone and print its record (profiling runs); "
+                         "'copy' is a plain 256 MiB device copy used to calibrate the "
+                         "FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -302,6 +307,25 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     tbs.lib()
+    if args.only:
+        if args.only == "copy":
+            n = 256 << 20
+            src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+            dst = torch.empty_like(src)
+            for _ in range(args.steps):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            print(json.dumps({"workload": "copy", "bytes_read": n, "bytes_written": n}), flush=True)
+            return
+        c = CONFIGS[args.only]
+        if args.only == "decode":
+            rec = bench_decode(c, args.steps, args.warmup)
+        elif args.only == "dense_switch":
+            rec = bench_dense_switch(c, args.steps, args.warmup)
+        else:
+            rec = bench_prefill(c, args.steps, args.warmup, with_dense=not args.no_dense)
+        print(json.dumps({"workload": args.only, **rec}), flush=True)
+        return
 
     cfg = CONFIGS["prefill32k"]
     main_res = bench_prefill(cfg, args.steps, args.warmup, with_dense=not args.no_dense)

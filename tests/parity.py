@@ -95,13 +95,14 @@ def compare_sets(gpu, ref, S_cmp_ref, p, op):
     return "exempt"
 
 
-def check_compress(res, k_cpu, op, batches=None):
-    batches = range(k_cpu.shape[0]) if batches is None else batches
+def check_compress(res, k_cpu, op):
+    """K^C1 bit-exact against the oracle; returns the oracle's K^C1 per
+    sequence ({b: [h_kv, n_C1, d]}) for the selection checks."""
     n_c1 = orc.n_kernels(k_cpu.shape[1], op.l_C1, op.s_C1)
-    for b in batches:
-        ref = orc.compress_k(to_f64(k_cpu[b:b + 1]), op)[0]
-        got = to_f64(res["Kc1"][b, :, :n_c1])
-        np.testing.assert_array_equal(got, ref)
+    ref = orc.compress_k(to_f64(k_cpu), op)
+    got = to_f64(res["Kc1"][:, :, :n_c1])
+    np.testing.assert_array_equal(got, ref)
+    return {b: ref[b] for b in range(ref.shape[0])}
 
 
 def check_rows(res, x, op, q_pos0, rows_per_b, dense=False, check_scores=True,

@@ -14,9 +14,11 @@
 //    (keys on the M axis), so that each lane ends up holding 8 consecutive
 //    keys of one head -- exactly the B-operand layout of the P V product
 //    O^T = V^T P^T.  No cross-lane data movement besides the row max.
-//  * V^T fragments need 8 consecutive keys of one feature: prefill reads them
-//    from a transposed copy of V made once per call (vt_transpose_kernel);
+//  * prefill first writes K and V once in MFMA-fragment order (kv_pack_kernel)
+//    so that every fragment load of the gather is one coalesced 1 KB load;
 //    decode stages each selected block through LDS.
+//  * prefill keeps one block of loads in flight ahead of the math, and
+//    rescales O only when a head's running maximum grows by more than 2^8;
 //  * decode splits the selected blocks over workgroups (one block each) and
 //    merges the partial (max, sum, O) afterwards.
 // A generic fp64 kernel serves fp32 I/O and other shapes.
@@ -28,44 +30,6 @@ constexpr int AT_D = 128;
 constexpr int AT_G = 16;
 constexpr int AT_B = 64;
 
-// ---------------------------------------------------------------------------
-// V [b][kv_cap][h_kv][d] -> VT [b][h_kv][d][n_pad]  (bf16), zero beyond n_kv.
-// grid: x = 64-token tiles, y = h_kv, z = batch.  256 threads.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) vt_transpose_kernel(const uint16_t* __restrict__ V,
-                                                           uint16_t* __restrict__ VT, int n_kv,
-                                                           int n_pad, int h_kv, int64_t kv_cap) {
-  __shared__ uint16_t tile[64][AT_D + 8];
-  const int tt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  // load 64 rows x 128 d: 1024 16-byte pieces, 4 per thread
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int u = tid + 256 * i;
-    const int r = u >> 4, c8 = (u & 15) * 8;
-    const int tok = tt * 64 + r;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (tok < n_kv) v = *(const u32x4*)(V + (((size_t)b * kv_cap + tok) * h_kv + g) * AT_D + c8);
-    const uint16_t* e = (const uint16_t*)&v;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) tile[r][c8 + q] = e[q];
-  }
-  __syncthreads();
-  // write 128 d-rows x 64 tokens: thread -> (d, 32 tokens) as 4 x 16 B
-  const int d = tid >> 1, half = tid & 1;
-  uint16_t* dst = VT + (((size_t)b * h_kv + g) * AT_D + d) * n_pad + tt * 64 + half * 32;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = half * 32 + q * 8 + 2 * e;
-      w[e] = (uint32_t)tile[r][d] | ((uint32_t)tile[r + 1][d] << 16);
-    }
-    *(u32x4*)(dst + q * 8) = u32x4{w[0], w[1], w[2], w[3]};
-  }
-}
-
 // Key held by row r (0..15) of score tile t (0..3) of a 64-key block: the
 // permutation makes a lane's 8 P^T elements of k-step ks the 8 consecutive
 // keys 32*ks + 8*(lane>>4) .. +7.
@@ -73,10 +37,71 @@ __device__ __forceinline__ int tile_key(int t, int r) {
   return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
 }
 
+// ---------------------------------------------------------------------------
+// K, V [b][kv_cap][h_kv][d] -> packs [b][h_kv][n_blk][16 fragments][64 lanes][8]
+// (bf16), zero beyond n_kv.  Fragment f of a block is the 1 KB that one MFMA
+// operand load needs, in lane order, so the attention kernel reads every
+// fragment with one fully coalesced 16-byte-per-lane load:
+//   K pack, f = 4t + ks:  lane l holds K[tile_key(t, l&15)][32ks + 8(l>>4) .. +7]
+//   V pack, f = 2mt + ks: lane l holds V[32ks + 8(l>>4) .. +7][16mt + (l&15)]
+// (A gather of rows straight into the operand layout would put 16 different
+// rows on consecutive lanes and cost one address request per lane.)
+// grid: x = blocks, y = h_kv, z = batch.  256 threads.
+// ---------------------------------------------------------------------------
+constexpr int PACK_ELEMS = AT_B * AT_D;   // 8192 bf16 = 16 KB per block
+
+__global__ void __launch_bounds__(256) kv_pack_kernel(const uint16_t* __restrict__ K,
+                                                      const uint16_t* __restrict__ V,
+                                                      uint16_t* __restrict__ Kp,
+                                                      uint16_t* __restrict__ Vp, int n_kv,
+                                                      int n_blk, int h_kv, int64_t kv_cap) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt[AT_B][AT_D + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[AT_B][AT_D + 8];
+  const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + 256 * i;
+    const int r = u >> 4, c8 = (u & 15) * 8;
+    const int tok = blk * AT_B + r;
+    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (tok < n_kv) {
+      const size_t off = (((size_t)b * kv_cap + tok) * h_kv + g) * AT_D + c8;
+      kv = *(const u32x4*)(K + off);
+      vv = *(const u32x4*)(V + off);
+    }
+    *(u32x4*)&kt[r][c8] = kv;
+    *(u32x4*)&vt[r][c8] = vv;
+  }
+  __syncthreads();
+  const size_t base = (((size_t)b * h_kv + g) * n_blk + blk) * PACK_ELEMS;
+  // 16 fragments x 64 lanes = 1024 pieces of 16 B per pack, 4 per thread
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + 256 * i;
+    const int f = u >> 6, l = u & 63;
+    {  // K: f = 4t + ks
+      const int t = f >> 2, ks = f & 3;
+      *(u32x4*)(Kp + base + (size_t)u * 8) =
+          *(const u32x4*)&kt[tile_key(t, l & 15)][32 * ks + 8 * (l >> 4)];
+    }
+    {  // V: f = 2mt + ks
+      const int mt = f >> 1, ks = f & 1;
+      const int d = 16 * mt + (l & 15), k0 = 32 * ks + 8 * (l >> 4);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)vt[k0 + 2 * e][d] | ((uint32_t)vt[k0 + 2 * e + 1][d] << 16);
+      *(u32x4*)(Vp + base + (size_t)u * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
 struct AttnArgs {
   const uint16_t* Q;
   const uint16_t* K;
-  const uint16_t* VT;     // prefill: transposed V
+  const uint16_t* Kp;     // prefill: K and V in fragment order (kv_pack_kernel)
+  const uint16_t* Vp;
   const uint16_t* V;      // decode: natural V
   const int32_t* idx;     // nullptr -> dense
   const int32_t* n_sel;
@@ -84,23 +109,28 @@ struct AttnArgs {
   float* lse;
   float* part_o;          // decode partials
   float2* part_ml;
-  int n_q, q_pos0, n_kv, n_pad, h_kv, budget;
+  int n_q, q_pos0, n_kv, n_blk, h_kv, budget;
   int64_t kv_cap;
   float c;                // scale * log2(e)
 };
 
-// One block of 64 keys for one token's 16 heads: scores, online softmax, PV.
-// kfrag(t, ks) returns the K fragment, vfrag(mt, ks) the V^T fragment.
-template <typename KF, typename VF>
-__device__ __forceinline__ void attn_block(const bf16x8 (&qf)[4], f32x4 (&o)[8], float& m_run,
-                                           float& l_run, int kv0, int p, float c, int lane,
-                                           KF kfrag, VF vfrag) {
+// Scores and online softmax of one 64-key block for one token's 16 heads.
+// kf[t][ks]: K fragments (rows tile_key(t, lane&15), features 32ks+8*(lane>>4)).
+// Returns P^T as two bf16 B operands (k-step ks = keys 32ks + 8*(lane>>4) ..+7)
+// and rescales o / l_run when the running maximum moves.  The reference m_run
+// is only raised when some head's block maximum exceeds it by more than 2^8
+// (log2 units): probabilities then stay below 256, and O is rescaled rarely.
+// DIAG: the block holds the query position; keys after p are masked.
+template <bool DIAG>
+__device__ __forceinline__ void attn_scores(const bf16x8 (&qf)[4], const bf16x8 (&kf)[4][4],
+                                            f32x4 (&o)[8], float& m_run, float& l_run, int kv0,
+                                            int p, float c, int lane, bf16x8 (&pf)[2]) {
   f32x4 s[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) s[t] = mfma16(kfrag(t, ks), qf[ks], s[t]);
+    for (int ks = 0; ks < 4; ++ks) s[t] = mfma16(kf[t][ks], qf[ks], s[t]);
   }
   const int grp = lane >> 4;
   float mx = kNegInf;
@@ -108,24 +138,29 @@ __device__ __forceinline__ void attn_block(const bf16x8 (&qf)[4], f32x4 (&o)[8],
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = kv0 + 32 * (t >> 1) + 8 * grp + 4 * (t & 1) + i;
       float x = s[t][i] * c;
-      if (key > p) x = kNegInf;
+      if constexpr (DIAG) {
+        const int key = kv0 + 32 * (t >> 1) + 8 * grp + 4 * (t & 1) + i;
+        if (key > p) x = kNegInf;
+      }
       s[t][i] = x;
       mx = fmaxf(mx, x);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const float m_new = fmaxf(m_run, mx);
-  const float alpha = fast_exp2(m_run - m_new);
-  m_run = m_new;
-  l_run *= alpha;
+  if (__ballot(mx > m_run + 8.0f)) {
+    // (mx > m_run implies mx is finite)
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[mt][i] *= alpha;
-  // P^T as bf16 B operands (k-step ks covers keys 32ks + 8*grp .. +7)
-  bf16x8 pf[2];
+      for (int i = 0; i < 4; ++i) o[mt][i] *= alpha;
+  }
+  // before the first visible key m_run is -inf and every score here is -inf
+  const float mref = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     uint32_t w[4];
@@ -133,17 +168,23 @@ __device__ __forceinline__ void attn_block(const bf16x8 (&qf)[4], f32x4 (&o)[8],
     for (int e = 0; e < 4; ++e) {
       const int t = 2 * ks + (e >> 1);
       const int i0 = 2 * (e & 1);
-      const float p0 = fast_exp2(s[t][i0] - m_new);
-      const float p1 = fast_exp2(s[t][i0 + 1] - m_new);
+      const float p0 = fast_exp2(s[t][i0] - mref);
+      const float p1 = fast_exp2(s[t][i0 + 1] - mref);
       l_run += p0 + p1;                      // fp32 sum: exact-to-fp32 LSE
-      w[e] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+      w[e] = pack_bf16x2(p0, p1);
     }
     pf[ks] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
   }
+}
+
+// O^T += V^T P^T for one block; vf[mt][ks]: V^T fragments (feature
+// 16mt+(lane&15), keys 32ks+8*(lane>>4) .. +7).
+__device__ __forceinline__ void attn_pv(const bf16x8 (&vf)[8][2], const bf16x8 (&pf)[2],
+                                        f32x4 (&o)[8]) {
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) o[mt] = mfma16(vfrag(mt, ks), pf[ks], o[mt]);
+    for (int ks = 0; ks < 2; ++ks) o[mt] = mfma16(vf[mt][ks], pf[ks], o[mt]);
 }
 
 __device__ __forceinline__ void load_qfrag(const AttnArgs& a, int b, int t, int g, int lane,
@@ -155,8 +196,13 @@ __device__ __forceinline__ void load_qfrag(const AttnArgs& a, int b, int t, int 
 }
 
 // grid: x = ceil(n_q/4) token quads, y = h_kv, z = batch; 4 waves = 4 tokens.
-template <bool SPARSE>
-__global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
+// Loads run one block ahead: the K fragments of block i+1 are in flight
+// during the softmax and PV of block i, the V^T fragments of block i+1 during
+// the scores of block i+1.
+// LONG: block lists of more than 64 entries (budget > 64) are re-read 64 at a
+// time; the common case never touches memory for the list inside the loop.
+template <bool SPARSE, bool LONG>
+__global__ void __launch_bounds__(256, 2) attn_prefill_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nquads = gridDim.x;
   const int quad = nquads - 1 - (int)blockIdx.x;      // late tokens (long rows) first
@@ -174,25 +220,66 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
   const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
   const int nblocks = SPARSE ? a.n_sel[row] : b_p + 1;
   const int32_t* sel = SPARSE ? a.idx + row * a.budget : nullptr;
-  const size_t kstride = (size_t)a.h_kv * AT_D;
-  const uint16_t* kbase = a.K + (size_t)b * a.kv_cap * kstride + (size_t)g * AT_D;
-  const uint16_t* vtbase = a.VT + ((size_t)b * a.h_kv + g) * AT_D * a.n_pad;
+  const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS + lane * 8;
+  const uint16_t* kbase = a.Kp + pack0;
+  const uint16_t* vbase = a.Vp + pack0;
   const int grp = lane >> 4, r16 = lane & 15;
+  // The block list is held one entry per lane, 64 entries at a time, so that
+  // reading the next entry (a uniform lane read) never waits on memory.
+  int list_base = 0;
+  int my_entry = (SPARSE && lane < nblocks) ? sel[lane] : -1;
+  // block of list entry bi, or -1 when the entry is not a causal block
+  auto block_at = [&](int bi) -> int {
+    int blk = bi;
+    if constexpr (SPARSE) {
+      if constexpr (LONG) {
+        if (bi >= list_base + 64) {
+          list_base = bi & ~63;
+          my_entry = (list_base + lane < nblocks) ? sel[list_base + lane] : -1;
+        }
+      }
+      blk = __builtin_amdgcn_readlane(my_entry, bi - list_base);
+    }
+    return (blk < 0 || blk > b_p) ? -1 : blk;
+  };
+  // one coalesced 1 KB load per fragment (keys past n_kv are zero in the pack)
+  auto load_k = [&](int blk, bf16x8 (&kf)[4][4]) {
+    const uint16_t* src = kbase + (uint32_t)blk * PACK_ELEMS;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[tt][ks] = as_bf16x8(*(const u32x4*)(src + (4 * tt + ks) * 512));
+  };
+  auto load_v = [&](int blk, bf16x8 (&vf)[8][2]) {
+    const uint16_t* src = vbase + (uint32_t)blk * PACK_ELEMS;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) vf[mt][ks] = as_bf16x8(*(const u32x4*)(src + (2 * mt + ks) * 512));
+  };
+  // Every iteration issues the loads of the next entry unconditionally (the
+  // last one re-reads its own block), so the loads in flight are the same on
+  // every path and the waits stay precise.  A non-causal entry is processed as
+  // block 0 with every key masked: it adds nothing.
+  bf16x8 kf[4][4], vf[8][2], pf[2];
+  int blk = block_at(0);
+  load_k(max(blk, 0), kf);
+  load_v(max(blk, 0), vf);
   for (int bi = 0; bi < nblocks; ++bi) {
-    const int blk = SPARSE ? sel[bi] : bi;
-    if (blk < 0 || blk > b_p) continue;            // only causal blocks
-    const int kv0 = blk * AT_B;
-    auto kfrag = [&](int tt, int ks) -> bf16x8 {
-      const int key = kv0 + tile_key(tt, r16);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < a.n_kv) v = *(const u32x4*)(kbase + (size_t)key * kstride + 32 * ks + 8 * grp);
-      return as_bf16x8(v);
-    };
-    auto vfrag = [&](int mt, int ks) -> bf16x8 {
-      const int d = 16 * mt + r16;
-      return as_bf16x8(*(const u32x4*)(vtbase + (size_t)d * a.n_pad + kv0 + 32 * ks + 8 * grp));
-    };
-    attn_block(qf, o, m_run, l_run, kv0, p, a.c, lane, kfrag, vfrag);
+    const int nxt = bi + 1 < nblocks ? block_at(bi + 1) : blk;
+    const int kv0 = max(blk, 0) * AT_B;
+    if (blk == b_p)
+      attn_scores<true>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+    else if (blk < 0)
+      attn_scores<true>(qf, kf, o, m_run, l_run, kv0, -1, a.c, lane, pf);
+    else
+      attn_scores<false>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+    load_k(max(nxt, 0), kf);
+    __builtin_amdgcn_sched_barrier(0);
+    attn_pv(vf, pf, o);
+    load_v(max(nxt, 0), vf);
+    __builtin_amdgcn_sched_barrier(0);
+    blk = nxt;
   }
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
@@ -201,8 +288,8 @@ __global__ void __launch_bounds__(256) attn_prefill_kernel(AttnArgs a) {
   uint16_t* orow = a.O + (((size_t)b * a.n_q + t) * hq + g * AT_G + r16) * AT_D;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    const uint32_t w0 = f32_to_bf16_bits(o[mt][0] * inv) | (f32_to_bf16_bits(o[mt][1] * inv) << 16);
-    const uint32_t w1 = f32_to_bf16_bits(o[mt][2] * inv) | (f32_to_bf16_bits(o[mt][3] * inv) << 16);
+    const uint32_t w0 = pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv);
+    const uint32_t w1 = pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv);
     *(uint2*)(orow + 16 * mt + 4 * grp) = make_uint2(w0, w1);
   }
   if (a.lse && grp == 0)
@@ -258,10 +345,9 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
     u32x4 in[8], out[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int key = kv0 + 8 * kg + r;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key < a.n_kv) v = *(const u32x4*)(vbase + (size_t)key * kstride + 8 * c);
-      in[r] = v;
+      // rows past the last key are clamped to it; their probabilities are 0
+      const int key = min(kv0 + 8 * kg + r, a.n_kv - 1);
+      in[r] = *(const u32x4*)(vbase + (size_t)key * kstride + 8 * c);
     }
     transpose8x8_bf16(in, out);
 #pragma unroll
@@ -278,17 +364,27 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
   for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
   const int grp = lane >> 4, r16 = lane & 15;
-  auto kfrag = [&](int tt, int ks) -> bf16x8 {
-    const int key = kv0 + tile_key(tt, r16);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (key < a.n_kv) v = *(const u32x4*)(kbase + (size_t)key * kstride + 32 * ks + 8 * grp);
-    return as_bf16x8(v);
-  };
-  auto vfrag = [&](int mt, int ks) -> bf16x8 {
+  bf16x8 kf[4][4], vf[8][2];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int key = min(kv0 + tile_key(tt, r16), a.n_kv - 1);   // clamped rows are masked
+    const uint16_t* kr = kbase + (size_t)key * kstride + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kf[tt][ks] = as_bf16x8(*(const u32x4*)(kr + 32 * ks));
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
     const int d = 16 * mt + r16;
-    return as_bf16x8(*(const u32x4*)(&vt[d][8 * vt_slot(d, 4 * ks + grp)]));
-  };
-  attn_block(qf, o, m_run, l_run, kv0, p, a.c, lane, kfrag, vfrag);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      vf[mt][ks] = as_bf16x8(*(const u32x4*)(&vt[d][8 * vt_slot(d, 4 * ks + grp)]));
+  }
+  bf16x8 pf[2];
+  if (blk == p / AT_B)
+    attn_scores<true>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+  else
+    attn_scores<false>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+  attn_pv(vf, pf, o);
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   // partial O^T (unnormalised) and (max, sum) per head
@@ -300,23 +396,40 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
 }
 
 // grid: x = h_kv, y = batch*n_q; 256 threads: head = tid/16, 8 features each.
+// Slots are folded four at a time so that their loads are in flight together.
 __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
   const int g = blockIdx.x, bt = blockIdx.y;
   const int b = bt / a.n_q, t = bt % a.n_q;
   const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
   const int nsel = a.n_sel[row];
   const int h = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
-  float m = kNegInf;
-  for (int s = 0; s < nsel; ++s) m = fmaxf(m, a.part_ml[(row * a.budget + s) * AT_G + h].x);
-  float l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsel; ++s) {
-    const float2 ml = a.part_ml[(row * a.budget + s) * AT_G + h];
-    if (ml.x == kNegInf) continue;
-    const float w = fast_exp2(ml.x - m);
-    l += ml.y * w;
-    const float* po = a.part_o + ((row * a.budget + s) * AT_G + h) * AT_D + d0;
+  float m = kNegInf, l = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsel; s0 += 4) {
+    float2 ml[4];
+    f32x4 lo[4], hi[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += po[q] * w;
+    for (int u = 0; u < 4; ++u) {
+      const int sl = min(s0 + u, nsel - 1);
+      const size_t slot = row * a.budget + sl;
+      ml[u] = a.part_ml[slot * AT_G + h];
+      const float* po = a.part_o + (slot * AT_G + h) * AT_D + d0;
+      lo[u] = *(const f32x4*)po;
+      hi[u] = *(const f32x4*)(po + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s0 + u >= nsel || ml[u].x == kNegInf) continue;
+      const float mn = fmaxf(m, ml[u].x);
+      const float wo = fast_exp2(m - mn), wn = fast_exp2(ml[u].x - mn);
+      l = l * wo + ml[u].y * wn;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[q] = acc[q] * wo + lo[u][q] * wn;
+        acc[4 + q] = acc[4 + q] * wo + hi[u][q] * wn;
+      }
+      m = mn;
+    }
   }
   const float inv = 1.0f / l;
   const int hq = a.h_kv * AT_G;
@@ -324,7 +437,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
   uint32_t w[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    w[q] = f32_to_bf16_bits(acc[2 * q] * inv) | (f32_to_bf16_bits(acc[2 * q + 1] * inv) << 16);
+    w[q] = pack_bf16x2(acc[2 * q] * inv, acc[2 * q + 1] * inv);
   *(u32x4*)orow = u32x4{w[0], w[1], w[2], w[3]};
   if (a.lse && (threadIdx.x & 15) == 0)
     a.lse[((size_t)b * hq + g * AT_G + h) * a.n_q + t] = (m + fast_log2(l)) * kLn2;
@@ -460,8 +573,8 @@ size_t attn_workspace(const infv2_problem& p, int budget, bool sparse) {
     const size_t slots = (size_t)p.batch * p.h_kv * p.n_q * budget;
     return slots * AT_G * AT_D * sizeof(float) + slots * AT_G * sizeof(float2);
   }
-  const size_t n_pad = ((size_t)p.n_kv + 63) & ~(size_t)63;
-  return (size_t)p.batch * p.h_kv * AT_D * n_pad * sizeof(uint16_t);
+  const size_t n_blk = ((size_t)p.n_kv + AT_B - 1) / AT_B;
+  return 2 * (size_t)p.batch * p.h_kv * n_blk * PACK_ELEMS * sizeof(uint16_t);
 }
 
 static AttnArgs fast_args(const infv2_problem& p, const void* Q, const void* K, const void* V,
@@ -471,7 +584,8 @@ static AttnArgs fast_args(const infv2_problem& p, const void* Q, const void* K, 
   a.Q = (const uint16_t*)Q;
   a.K = (const uint16_t*)K;
   a.V = (const uint16_t*)V;
-  a.VT = nullptr;
+  a.Kp = nullptr;
+  a.Vp = nullptr;
   a.idx = idx;
   a.n_sel = n_sel;
   a.O = (uint16_t*)O;
@@ -481,7 +595,7 @@ static AttnArgs fast_args(const infv2_problem& p, const void* Q, const void* K, 
   a.n_q = p.n_q;
   a.q_pos0 = p.q_pos0;
   a.n_kv = p.n_kv;
-  a.n_pad = (p.n_kv + 63) & ~63;
+  a.n_blk = (p.n_kv + AT_B - 1) / AT_B;
   a.h_kv = p.h_kv;
   a.budget = budget;
   a.kv_cap = kv_cap;
@@ -505,14 +619,19 @@ hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, con
                          a);
       return hipGetLastError();
     }
-    a.VT = (uint16_t*)ws;
-    hipLaunchKernelGGL(vt_transpose_kernel, dim3(a.n_pad / 64, p.h_kv, p.batch), dim3(256), 0,
-                       stream, (const uint16_t*)V, (uint16_t*)ws, p.n_kv, a.n_pad, p.h_kv, kv_cap);
+    const size_t pack = (size_t)p.batch * p.h_kv * a.n_blk * PACK_ELEMS;
+    a.Kp = (uint16_t*)ws;
+    a.Vp = (uint16_t*)ws + pack;
+    hipLaunchKernelGGL(kv_pack_kernel, dim3(a.n_blk, p.h_kv, p.batch), dim3(256), 0, stream,
+                       (const uint16_t*)K, (const uint16_t*)V, (uint16_t*)a.Kp, (uint16_t*)a.Vp,
+                       p.n_kv, a.n_blk, p.h_kv, kv_cap);
     dim3 grid((p.n_q + 3) / 4, p.h_kv, p.batch);
-    if (sparse)
-      hipLaunchKernelGGL(attn_prefill_kernel<true>, grid, dim3(256), 0, stream, a);
+    if (sparse && budget > 64)
+      hipLaunchKernelGGL((attn_prefill_kernel<true, true>), grid, dim3(256), 0, stream, a);
+    else if (sparse)
+      hipLaunchKernelGGL((attn_prefill_kernel<true, false>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(attn_prefill_kernel<false>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((attn_prefill_kernel<false, false>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   GenericAttnArgs a;

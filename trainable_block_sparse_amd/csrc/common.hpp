@@ -28,6 +28,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return u >> 16;
 }
 
+// Two fp32 values to packed bf16 (round to nearest even) with the hardware
+// conversion (v_cvt_pk_bf16_f32 on gfx950); lo lands in the low half.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // 2^x on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

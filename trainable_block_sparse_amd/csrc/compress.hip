@@ -8,8 +8,9 @@
 // The kernel is HBM-bound: every key row is read by l_C1/s_C1 kernels, so the
 // second read hits L2.  Threads run along d so that each 32-token segment is
 // read as contiguous rows.  The sum of the l_C1 keys is carried as an fp64
-// pair (hi, lo) with TwoSum, which is exact for any inputs of this format, and
-// rounded ONCE to the I/O dtype, to nearest even.
+// pair (hi, lo) with TwoSum: exact unless the kernel's values span more than
+// about 78 binades (never for bf16 or fp32 data of one attention layer in
+// practice), and rounded ONCE to the I/O dtype, to nearest even.
 #include "common.hpp"
 
 namespace infv2 {
@@ -65,12 +66,21 @@ __global__ void __launch_bounds__(256) compress_k_kernel(
   const size_t row_stride = (size_t)h_kv * d;
   const T* src = K + ((size_t)b * kv_cap + (size_t)j * s_C1) * row_stride + (size_t)g * d + di;
   double hi = 0.0, lo = 0.0;
-  for (int u = 0; u < l_C1; ++u) {
-    const double x = load_f64<T>(src + (size_t)u * row_stride);
-    const double t = hi + x;
-    const double bp = t - hi;
-    lo += (hi - (t - bp)) + (x - bp);       // TwoSum error, accumulated exactly
-    hi = t;                                  // for the magnitudes of one kernel
+  // 32 keys per step, all loaded before the (serial) compensated sum
+  for (int u0 = 0; u0 < l_C1; u0 += 32) {
+    const int cnt = min(32, l_C1 - u0);
+    double x[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u)
+      x[u] = load_f64<T>(src + (size_t)(u0 + min(u, cnt - 1)) * row_stride);
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      if (u >= cnt) break;
+      const double t = hi + x[u];
+      const double bp = t - hi;
+      lo += (hi - (t - bp)) + (x[u] - bp);  // TwoSum error, accumulated exactly
+      hi = t;                               // for the magnitudes of one kernel
+    }
   }
   // renormalise the pair so that |lo| <= ulp(hi)/2, then scale by 1/l_C1
   // (a power of two: exact)

@@ -11,10 +11,12 @@
 //  * scores_prefill_kernel -- bf16, G = 16, d = 128, B = 64, l_C1 = 32,
 //    s_C1 = 16.  One workgroup = 16 query tokens x 16 heads of one group (256
 //    MFMA rows).  Q stays in registers; K^C1 streams through LDS in chunks of
-//    64 kernels.  The log-sum-exp is exact and takes two sweeps (row maximum,
-//    then the sum of 2^(z*c - max)); a third sweep forms S^C1, sums the 16
-//    heads (8 in-lane + one cross-half exchange), max-pools into blocks and
-//    writes S^cmp.  Neither S^C1 nor S^shared is written to memory.
+//    32 kernels.  Two sweeps, as the pages describe: the first sums
+//    2^(z*c - M) with M the exact row maximum of the first chunk (an extra
+//    maximum sweep runs only if a later logit overflows that reference); the
+//    second forms S^C1, sums the 16 heads (8 in-lane + one cross-half
+//    exchange), max-pools into blocks and writes S^cmp.  Neither S^C1 nor
+//    S^shared is written to memory.
 //  * scores_split_{logits,pool}_kernel -- few query tokens (decode): the kernel
 //    axis is split over workgroups; the first writes scaled logits and
 //    per-chunk (max, sum) partials, the second merges the partials into the
@@ -29,7 +31,7 @@ namespace infv2 {
 
 constexpr int SEL_D = 128;
 constexpr int SEL_G = 16;
-constexpr int SEL_CHUNK = 64;                 // kernels per LDS chunk
+constexpr int SEL_CHUNK = 32;                 // kernels per LDS chunk (one MFMA N-tile)
 constexpr int SEL_ROW_BYTES = SEL_D * 2;      // one K^C1 row, bf16
 constexpr int SEL_TOK_WAVE = 4;               // tokens per wave (2 MFMA row blocks)
 constexpr int SEL_TOK_WG = 16;                // tokens per workgroup
@@ -46,77 +48,85 @@ struct ScoresArgs {
 // kernel j is causal for position p when its last token j*16+31 <= p
 __device__ __forceinline__ int last_visible_kernel(int p) { return p >= 31 ? (p - 31) >> 4 : -1; }
 
-template <int PASS>
+constexpr int PASS_MAX = 0;    // row maxima (only when the sum overflows)
+constexpr int PASS_SUM = 1;    // log-sum-exp sweep
+constexpr int PASS_SCORE = 2;  // normalised scores, group sum, max-pool
+
+// One chunk of 32 kernels for the wave's 64 rows (4 tokens x 16 heads).
+// MASKED chunks contain kernels that are not causal for some row.
+//  PASS_MAX:   M = max(M, z)
+//  PASS_SUM:   W += 2^(z*c - M); on the first chunk M is first set to the
+//              chunk's exact row maximum (times c), the reference of the sum
+//  PASS_SCORE: S^C1 = 2^(z*c - M) * W, summed over the group's 16 heads and
+//              staged in sbuf for the max-pool
+template <int PASS, bool MASKED>
 __device__ __forceinline__ void scores_chunk(const ScoresArgs& a, const uint8_t* kb, int chunk,
-                                             bool masked, const bf16x8 (&qf)[2][8],
+                                             bool first, const bf16x8 (&qf)[2][8],
                                              const int (&jm)[4], float (&M)[2][16],
                                              float (&W)[2][16], float (&sbuf)[4][SEL_CHUNK + 1],
                                              int lane) {
-  f32x16 acc[2][2];
+  f32x16 acc[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rb][nt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
   const int col = lane & 31;
   const int half = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
+    const int c16 = 2 * ks + half;
+    const u32x4 raw = *(const u32x4*)(kb + col * SEL_ROW_BYTES + ((c16 ^ (col & 15)) << 4));
+    const bf16x8 bfrag = as_bf16x8(raw);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int row = 32 * nt + col;
-      const int c16 = 2 * ks + half;
-      const u32x4 raw = *(const u32x4*)(kb + row * SEL_ROW_BYTES + ((c16 ^ (row & 15)) << 4));
-      const bf16x8 bfrag = as_bf16x8(raw);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) acc[rb][nt] = mfma32(qf[rb][ks], bfrag, acc[rb][nt]);
-    }
+    for (int rb = 0; rb < 2; ++rb) acc[rb] = mfma32(qf[rb][ks], bfrag, acc[rb]);
   }
-  const int j_base = chunk * SEL_CHUNK;
-  if constexpr (PASS == 0) {
+  const int j = chunk * SEL_CHUNK + col;     // this lane's kernel
+  // causal mask: only chunks that reach past a row's last visible kernel
+  if constexpr (MASKED) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float z = acc[rb][nt][i];
-          if (masked && j_base + 32 * nt + col > jm[2 * rb + (i >> 3)]) z = kNegInf;
-          M[rb][i] = fmaxf(M[rb][i], z);
-        }
-  } else if constexpr (PASS == 1) {
+      for (int i = 0; i < 16; ++i)
+        if (j > jm[2 * rb + (i >> 3)]) acc[rb][i] = kNegInf;
+  }
+  if constexpr (PASS == PASS_MAX) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int i = 0; i < 16; ++i) M[rb][i] = fmaxf(M[rb][i], acc[rb][i]);
+  } else if constexpr (PASS == PASS_SUM) {
+    if (first) {
+      // reference = exact maximum of this chunk's visible logits, per row
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float e = fast_exp2(__builtin_fmaf(acc[rb][nt][i], a.c, -M[rb][i]));
-          if (masked && j_base + 32 * nt + col > jm[2 * rb + (i >> 3)]) e = 0.f;
-          W[rb][i] += e;
+          float m = acc[rb][i];
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          M[rb][i] = (m == kNegInf) ? 0.f : m * a.c;   // -inf rows: nothing visible
         }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) W[rb][i] += fast_exp2(__builtin_fmaf(acc[rb][i], a.c, -M[rb][i]));
   } else {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
+      float part0 = 0.f, part1 = 0.f;  // tokens 2rb and 2rb+1, this lane's 8 heads
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        float part0 = 0.f, part1 = 0.f;  // tokens 2rb and 2rb+1, this lane's 8 heads
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float e = fast_exp2(__builtin_fmaf(acc[rb][nt][i], a.c, -M[rb][i]));
-          if (masked && j_base + 32 * nt + col > jm[2 * rb + (i >> 3)]) e = 0.f;
-          if (i < 8) part0 = __builtin_fmaf(e, W[rb][i], part0);
-          else       part1 = __builtin_fmaf(e, W[rb][i], part1);
-        }
-        // lanes l and l^32 hold the other 8 heads of the same (token, kernel)
-        const float send = half ? part0 : part1;
-        const float recv = __shfl_xor(send, 32, 64);
-        const float mine = (half ? part1 : part0) + recv;
-        const int tl = 2 * rb + half;
-        const int j = j_base + 32 * nt + col;
-        sbuf[tl][1 + 32 * nt + col] = (j > jm[tl]) ? kNegInf : mine;
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(__builtin_fmaf(acc[rb][i], a.c, -M[rb][i]));
+        if (i < 8) part0 = __builtin_fmaf(e, W[rb][i], part0);
+        else       part1 = __builtin_fmaf(e, W[rb][i], part1);
       }
+      // lanes l and l^32 hold the other 8 heads of the same (token, kernel)
+      const float send = half ? part0 : part1;
+      const float recv = __shfl_xor(send, 32, 64);
+      const float mine = (half ? part1 : part0) + recv;
+      const int tl = 2 * rb + half;
+      sbuf[tl][1 + col] = (j > jm[tl]) ? kNegInf : mine;
     }
   }
 }
@@ -141,14 +151,10 @@ __global__ void __launch_bounds__(256, 2) scores_prefill_kernel(ScoresArgs a) {
   for (int rb = 0; rb < 2; ++rb) {
     const int tok = t0 + 2 * rb + ((lane & 31) >> 4);
     const int head = g * SEL_G + (lane & 15);
-    const bool ok = tok < a.n_q;
-    const uint16_t* qrow = a.Q + (((size_t)b * a.n_q + (ok ? tok : 0)) * hq + head) * SEL_D;
+    // rows of tokens past n_q read the last token; they are never written
+    const uint16_t* qrow = a.Q + (((size_t)b * a.n_q + min(tok, a.n_q - 1)) * hq + head) * SEL_D;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *(const u32x4*)(qrow + 16 * ks + 8 * (lane >> 5));
-      qf[rb][ks] = as_bf16x8(v);
-    }
+    for (int ks = 0; ks < 8; ++ks) qf[rb][ks] = as_bf16x8(*(const u32x4*)(qrow + 16 * ks + 8 * (lane >> 5)));
   }
   int jm[4];
 #pragma unroll
@@ -169,31 +175,30 @@ __global__ void __launch_bounds__(256, 2) scores_prefill_kernel(ScoresArgs a) {
 
   const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
 
-  // stage one chunk of 64 K^C1 rows (16 KB): 4 x 16 B per thread, XOR-swizzled
-  auto stage_load = [&](int chunk, u32x4 (&st)[4]) {
+  // stage one chunk of 32 K^C1 rows (8 KB): 2 x 16 B per thread, XOR-swizzled
+  auto stage_load = [&](int chunk, u32x4 (&st)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int u = tid + 256 * i;
       const int row = u >> 4, c16 = u & 15;
-      const int j = chunk * SEL_CHUNK + row;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j < a.n_c1) v = *(const u32x4*)(kc1 + (size_t)j * SEL_D + c16 * 8);
-      st[i] = v;
+      // rows past the last kernel are clamped to it; they are never visible
+      const int j = min(chunk * SEL_CHUNK + row, a.n_c1 - 1);
+      st[i] = *(const u32x4*)(kc1 + (size_t)j * SEL_D + c16 * 8);
     }
   };
-  auto stage_store = [&](uint8_t* kb, const u32x4 (&st)[4]) {
+  auto stage_store = [&](uint8_t* kb, const u32x4 (&st)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       const int u = tid + 256 * i;
       const int row = u >> 4, c16 = u & 15;
       *(u32x4*)(kb + row * SEL_ROW_BYTES + ((c16 ^ (row & 15)) << 4)) = st[i];
     }
   };
 
-  auto run_pass = [&](auto pass_tag) {
+  auto run_pass = [&](auto pass_tag, bool set_ref) {
     constexpr int PASS = decltype(pass_tag)::value;
     if (nchunks == 0) return;
-    u32x4 st[4];
+    u32x4 st[2];
     stage_load(0, st);
     stage_store(kbuf[0], st);
     __syncthreads();
@@ -201,21 +206,28 @@ __global__ void __launch_bounds__(256, 2) scores_prefill_kernel(ScoresArgs a) {
       const bool more = c + 1 < nchunks;
       if (more) stage_load(c + 1, st);
       const bool masked = c * SEL_CHUNK + SEL_CHUNK - 1 > jmin_wg;
-      scores_chunk<PASS>(a, kbuf[c & 1], c, masked, qf, jm, M, W, sbuf, lane);
-      if constexpr (PASS == 2) {
-        // max-pool: block c*16+bb takes kernels c*64+4bb-1 .. c*64+4bb+3,
-        // i.e. sbuf[tl][4bb .. 4bb+4] (sbuf[tl][0] carries kernel c*64-1)
+      const bool first = set_ref && c == 0;
+      if (masked)
+        scores_chunk<PASS, true>(a, kbuf[c & 1], c, first, qf, jm, M, W, sbuf, lane);
+      else
+        scores_chunk<PASS, false>(a, kbuf[c & 1], c, first, qf, jm, M, W, sbuf, lane);
+      if constexpr (PASS == PASS_SCORE) {
+        // max-pool: block c*8+bb takes kernels c*32+4bb-1 .. c*32+4bb+3,
+        // i.e. sbuf[tl][4bb .. 4bb+4] (sbuf[tl][0] carries kernel c*32-1);
+        // lanes 0..31 hold the 4 tokens x 8 blocks of the chunk
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int tl = lane >> 4, bb = lane & 15;
-        float v = sbuf[tl][4 * bb];
+        if (lane < 32) {
+          const int tl = lane >> 3, bb = lane & 7;
+          float v = sbuf[tl][4 * bb];
 #pragma unroll
-        for (int q = 1; q < 5; ++q) v = fmaxf(v, sbuf[tl][4 * bb + q]);
-        const int tok = t0 + tl;
-        const int blk = c * (SEL_CHUNK / 4) + bb;
-        if (tok < a.n_q && blk <= (a.q_pos0 + tok) >> 6)
-          a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_blk + blk] = v;
+          for (int q = 1; q < 5; ++q) v = fmaxf(v, sbuf[tl][4 * bb + q]);
+          const int tok = t0 + tl;
+          const int blk = c * (SEL_CHUNK / 4) + bb;
+          if (tok < a.n_q && blk <= (a.q_pos0 + tok) >> 6)
+            a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_blk + blk] = v;
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -225,35 +237,52 @@ __global__ void __launch_bounds__(256, 2) scores_prefill_kernel(ScoresArgs a) {
       __syncthreads();
     }
   };
+  auto merge_sums = [&]() -> bool {   // lane partial sums -> row sums; true if finite
+    bool ok = true;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float s = W[rb][i];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
+        W[rb][i] = s;
+        ok = ok && __builtin_isfinite(s);
+      }
+    return ok;
+  };
 
-
-  // sweep 1: exact row maximum of z (raw dot products)
-  run_pass(std::integral_constant<int, 0>{});
+  // sweep 1 (log-sum-exp): s = sum_j 2^(z_j*c - M), M = the exact row maximum
+  // over the first chunk (every row with a visible kernel sees kernel 0)
+  run_pass(std::integral_constant<int, PASS_SUM>{}, true);
+  const bool finite = merge_sums();
+  if (__syncthreads_or(!finite)) {
+    // a later logit exceeded the reference by more than 2^127: take the exact
+    // row maximum (one extra sweep) and sum again
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { M[rb][i] = kNegInf; W[rb][i] = 0.f; }
+    run_pass(std::integral_constant<int, PASS_MAX>{}, false);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float m = M[rb][i];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        M[rb][i] = (m == kNegInf) ? 0.f : m * a.c;
+      }
+    run_pass(std::integral_constant<int, PASS_SUM>{}, false);
+    merge_sums();
+  }
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float m = M[rb][i];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      // log2-domain reference; rows without a visible kernel keep -inf and
-      // are masked in every chunk
-      M[rb][i] = (m == kNegInf) ? 0.f : m * a.c;
-    }
-  // sweep 2: s = sum 2^(z*c - max)  ->  lse = max + log2(s)
-  run_pass(std::integral_constant<int, 1>{});
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float s = W[rb][i];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o, 64);
-      W[rb][i] = s > 0.f ? 1.0f / s : 0.f;
-    }
-  // sweep 3: S^C1 = 2^(z*c - max) / s, head-group sum, max-pool, S^cmp
+    for (int i = 0; i < 16; ++i) W[rb][i] = W[rb][i] > 0.f ? 1.0f / W[rb][i] : 0.f;
+  // sweep 2: S^C1 = 2^(z*c - M) / s, head-group sum, max-pool, S^cmp
   if (lane < 4) sbuf[lane][0] = kNegInf;
-  run_pass(std::integral_constant<int, 2>{});
+  run_pass(std::integral_constant<int, PASS_SCORE>{}, false);
   // blocks with no visible kernel in the causal range
   {
     const int tl = lane >> 4;
@@ -303,14 +332,14 @@ __global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int j = jw + 16 * nt + (lane & 15);
-    const bool ok = j < a.n_c1;
+    // kernels past the last one are clamped to it; they are never visible
+    const int j = min(jw + 16 * nt + (lane & 15), a.n_c1 - 1);
+    bf16x8 kf[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *(const u32x4*)(kc1 + (size_t)j * SEL_D + 32 * ks + 8 * (lane >> 4));
-      acc[nt] = mfma16(qf[ks], as_bf16x8(v), acc[nt]);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      kf[ks] = as_bf16x8(*(const u32x4*)(kc1 + (size_t)j * SEL_D + 32 * ks + 8 * (lane >> 4)));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc[nt] = mfma16(qf[ks], kf[ks], acc[nt]);
   }
   // C layout: lane holds heads 4*(lane>>4)+i, kernel jw + 16*nt + (lane&15)
   float* lrow = a.logits + ((size_t)bt * a.h_kv + g) * SEL_G * a.n_c1p;
@@ -370,19 +399,29 @@ __global__ void __launch_bounds__(256) scores_split_pool_kernel(SplitArgs a) {
   const int p = a.q_pos0 + t;
   const int jmax = last_visible_kernel(p);
   const int b_p = p >> 6;
-  if (threadIdx.x < SEL_G) {
-    const int h = threadIdx.x;
+  {
+    // merge the per-chunk (max, sum) partials of every head: 16 threads per
+    // head, each folding every 16th chunk, then a 16-lane reduction
+    const int h = threadIdx.x >> 4, q = threadIdx.x & 15;
     const float2* pr = a.part + ((size_t)bt * a.h_kv + g) * a.nch * SEL_G + h;
-    float m = kNegInf;
-    for (int c = 0; c < a.nch; ++c) m = fmaxf(m, pr[(size_t)c * SEL_G].x);
-    float s = 0.f;
-    if (m != kNegInf)
-      for (int c = 0; c < a.nch; ++c) {
-        const float2 v = pr[(size_t)c * SEL_G];
-        if (v.x != kNegInf) s += v.y * fast_exp2(v.x - m);
-      }
-    Mh[h] = (m == kNegInf) ? 0.f : m;
-    Wh[h] = s > 0.f ? 1.0f / s : 0.f;
+    float m = kNegInf, s = 0.f;
+    for (int c = q; c < a.nch; c += 16) {
+      const float2 v = pr[(size_t)c * SEL_G];
+      if (v.x == kNegInf) continue;
+      if (v.x > m) { s = s * fast_exp2(m - v.x) + v.y; m = v.x; }
+      else s += v.y * fast_exp2(v.x - m);
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float mo = __shfl_xor(m, o, 64), so = __shfl_xor(s, o, 64);
+      const float mn = fmaxf(m, mo);
+      if (mn != kNegInf) s = s * fast_exp2(m - mn) + so * fast_exp2(mo - mn);
+      m = mn;
+    }
+    if (q == 0) {
+      Mh[h] = (m == kNegInf) ? 0.f : m;
+      Wh[h] = s > 0.f ? 1.0f / s : 0.f;
+    }
   }
   __syncthreads();
   const float* lrow = a.logits + ((size_t)bt * a.h_kv + g) * SEL_G * a.n_c1p;

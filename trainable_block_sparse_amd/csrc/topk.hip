@@ -15,6 +15,7 @@
 //   2. the keys >= K0 (usually about kk of them) are gathered, one per lane,
 //      and sorted across the wave; K* is the kk-th.  If more than 64 keys
 //      are >= K0 a bisection over the 64-bit key range finds K* instead.
+// Rows of up to 2048 blocks are read once, in one burst, into registers.
 // Membership is then  init/local, or key >= K*;  the ascending index list
 // comes from a ballot/popcount compaction over the blocks in order.
 #include "common.hpp"
@@ -61,6 +62,9 @@ struct TopkArgs {
   int rows;
 };
 
+// NI > 0: the row (nb <= 64*NI blocks) is loaded once, in one burst, into
+// NI registers per lane; NI == 0: any length, scores re-read from memory.
+template <int NI>
 __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   __shared__ uint64_t gather_all[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -77,46 +81,71 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   const int kk = min(a.k, ncand);
   const float* srow = a.S_cmp + (size_t)row * a.n_blk;
   int32_t* out = a.idx + (size_t)row * a.budget;
-
-  auto key_of = [&](int blk) -> uint64_t {
-    if (blk < init_hi || blk >= loc_lo) return 0ull;          // not a candidate
-    return ((uint64_t)ordered_bits(srow[blk]) << 32) | (uint64_t)(~(uint32_t)blk);
+  constexpr int NC = NI > 0 ? NI : 1;
+  float sc[NC];
+  if constexpr (NI > 0) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) sc[i] = srow[min(lane + 64 * i, nb - 1)];
+  }
+  const int niter = (nb + 63) >> 6;
+  auto key_at = [&](int i) -> uint64_t {     // key of block lane + 64*i
+    const int blk = lane + 64 * i;
+    if (blk >= nb || blk < init_hi || blk >= loc_lo) return 0ull;   // not a candidate
+    float v;
+    if constexpr (NI > 0) v = sc[i]; else v = srow[blk];
+    return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(~(uint32_t)blk);
+  };
+  auto count_ge = [&](uint64_t thr) -> int {
+    int c = 0;
+    if constexpr (NI > 0) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) c += key_at(i) >= thr ? 1 : 0;
+    } else {
+      for (int i = 0; i < niter; ++i) c += key_at(i) >= thr ? 1 : 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    return c;
+  };
+  // largest X with count(key >= X) >= kk, starting from a known lower bound
+  auto bisect = [&](uint64_t lo) -> uint64_t {
+    uint64_t hi = ~0ull;
+    while (lo < hi) {
+      const uint64_t mid = lo + ((hi - lo) >> 1) + 1;
+      if (count_ge(mid) >= kk) lo = mid; else hi = mid - 1;
+    }
+    return lo;
   };
 
-  uint64_t kstar = 0ull;     // keys >= kstar are selected; 0 selects nothing extra
+  uint64_t kstar = 0ull;     // keys >= kstar are selected
   const bool all = (kk == ncand);  // every candidate is selected
   if (all || kk == 0) {
     // nothing to rank
   } else if (kk > 64) {
-    // large k: bisection from the smallest candidate key (every candidate
-    // key is >= 1, non-candidates are 0)
-    uint64_t lo = 1ull, hi = ~0ull;
-    while (lo < hi) {
-      const uint64_t mid = lo + ((hi - lo) >> 1) + 1;
-      int c = 0;
-      for (int blk = lane; blk < nb; blk += 64) c += key_of(blk) >= mid ? 1 : 0;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-      if (c >= kk) lo = mid; else hi = mid - 1;
-    }
-    kstar = lo;
+    kstar = bisect(1ull);    // every candidate key is >= 1, non-candidates are 0
   } else {
     uint64_t lmax = 0ull;
-    for (int blk = lane; blk < nb; blk += 64) {
-      const uint64_t kv = key_of(blk);
-      lmax = kv > lmax ? kv : lmax;
+    if constexpr (NI > 0) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) { const uint64_t kv = key_at(i); lmax = kv > lmax ? kv : lmax; }
+    } else {
+      for (int i = 0; i < niter; ++i) { const uint64_t kv = key_at(i); lmax = kv > lmax ? kv : lmax; }
     }
     const uint64_t sorted = wave_sort_desc(lmax, lane);
     const uint64_t k0 = shfl_u64(sorted, kk - 1);
     // count and gather the keys >= k0
     int cnt = 0;
-    for (int blk = lane; blk < nb; blk += 64) cnt += key_of(blk) >= k0 ? 1 : 0;
+    if constexpr (NI > 0) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) cnt += key_at(i) >= k0 ? 1 : 0;
+    } else {
+      for (int i = 0; i < niter; ++i) cnt += key_at(i) >= k0 ? 1 : 0;
+    }
     int total = cnt;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o, 64);
     if (total <= 64) {
-      // exclusive prefix of cnt over lanes
-      int pre = cnt;
+      int pre = cnt;                          // exclusive prefix of cnt over lanes
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(pre, o, 64);
@@ -127,9 +156,11 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int blk = lane; blk < nb; blk += 64) {
-        const uint64_t kv = key_of(blk);
-        if (kv >= k0) gather[pre++] = kv;
+      if constexpr (NI > 0) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) { const uint64_t kv = key_at(i); if (kv >= k0) gather[pre++] = kv; }
+      } else {
+        for (int i = 0; i < niter; ++i) { const uint64_t kv = key_at(i); if (kv >= k0) gather[pre++] = kv; }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -137,32 +168,28 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
       const uint64_t s2 = wave_sort_desc(gather[lane], lane);
       kstar = shfl_u64(s2, kk - 1);
     } else {
-      // bisection: largest X with count(key >= X) >= kk (keys are distinct)
-      uint64_t lo = k0, hi = ~0ull;            // count(>= lo) >= kk
-      while (lo < hi) {
-        const uint64_t mid = lo + ((hi - lo) >> 1) + 1;
-        int c = 0;
-        for (int blk = lane; blk < nb; blk += 64) c += key_of(blk) >= mid ? 1 : 0;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-        if (c >= kk) lo = mid; else hi = mid - 1;
-      }
-      kstar = lo;
+      kstar = bisect(k0);                     // count(>= k0) >= kk holds
     }
   }
   // ascending compaction of the selected blocks
   int written = 0;
-  for (int base = 0; base < nb; base += 64) {
-    const int blk = base + lane;
+  auto emit = [&](int i) {
+    const int blk = lane + 64 * i;
     bool sel = false;
     if (blk < nb) {
       if (blk < init_hi || blk >= loc_lo) sel = true;
-      else sel = all || (kk > 0 && key_of(blk) >= kstar);
+      else sel = all || (kk > 0 && key_at(i) >= kstar);
     }
     const uint64_t ballot = __ballot(sel);
     const int pos = written + (int)__popcll(ballot & ((1ull << lane) - 1ull));
     if (sel) out[pos] = blk;
     written += (int)__popcll(ballot);
+  };
+  if constexpr (NI > 0) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) if (i < niter) emit(i);
+  } else {
+    for (int i = 0; i < niter; ++i) emit(i);
   }
   for (int i = written + lane; i < a.budget; i += 64) out[i] = -1;
   if (lane == 0) a.n_sel[row] = written;
@@ -184,7 +211,14 @@ hipError_t launch_topk(const infv2_problem& p, const float* S_cmp, int32_t* idx,
   a.budget = budget;
   a.rows = p.batch * p.h_kv * p.n_q;
   dim3 grid((a.rows + 3) / 4);
-  hipLaunchKernelGGL(topk_kernel, grid, dim3(256), 0, stream, a);
+  if (n_blk <= 256)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, dim3(256), 0, stream, a);
+  else if (n_blk <= 1024)
+    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, stream, a);
+  else if (n_blk <= 2048)
+    hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(topk_kernel<0>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
