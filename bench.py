@@ -218,7 +218,7 @@ def bench_decode(cfg, steps, warmup):
     for _ in range(steps):
         timer.step(fns)
     stage = timer.collect()
-    # the whole step without events in between
+    # the whole step, eager, without events in between
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
@@ -226,10 +226,26 @@ def bench_decode(cfg, steps, warmup):
             fn()
     e1.record()
     torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / steps
+    # the step captured once in a HIP graph and replayed (how a serving loop
+    # issues it: one launch, no host gaps between the kernels)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for fn in fns:
+            fn()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
     nbytes = decode_bytes(cfg, bud)
     out = dict(step_us=step_ms * 1e3, us_per_token=step_ms * 1e3 / cfg.batch,
-               stages_us={k: v * 1e3 for k, v in stage.items()}, algo_bytes=nbytes,
+               eager_step_us=eager_ms * 1e3, timing="HIP graph replay of the whole step",
+               stages_us_eager={k: v * 1e3 for k, v in stage.items()}, algo_bytes=nbytes,
                algo_GBps=nbytes / (step_ms / 1e3) / 1e9)
     out["frac_of_hbm_peak"] = out["algo_GBps"] / PEAK_HBM_GBS
     del Q, K, V

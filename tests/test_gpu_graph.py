@@ -1,0 +1,57 @@
+"""A decode step captured in a HIP graph and replayed several times, with
+eager work and synchronisations in between, gives the eager result bit for
+bit on every replay (the library issues no memset and allocates nothing)."""
+import numpy as np
+import pytest
+import torch
+
+import trainable_block_sparse_amd as tbs
+from synth import CONFIGS, make_inputs
+
+from parity import check_rows, problems
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_step_graph_replay_matches_eager():
+    cfg = CONFIGS["decode"]
+    n_kv, batch = 5000, 4
+    print("case: decode graph replay", n_kv, batch, flush=True)
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=77)
+    lp, op = problems(cfg, n_kv=n_kv, batch=batch)
+    dev = torch.device("cuda:0")
+    Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
+    n_c1, n_blk, bud = tbs.n_kernels(lp), tbs.n_blocks(lp), tbs.budget(lp)
+    Kc1 = tbs.compress_k(lp, K)
+    S = torch.empty((batch, lp.h_kv, 1, n_blk), dtype=torch.float32, device=dev)
+    idx = torch.empty((batch, lp.h_kv, 1, bud), dtype=torch.int32, device=dev)
+    nsel = torch.empty((batch, lp.h_kv, 1), dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((batch, lp.h_q, 1), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(tbs.block_scores_workspace(lp), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(tbs.sparse_attn_workspace(lp), dtype=torch.uint8, device=dev)
+
+    def step():
+        tbs.compress_k(lp, K, Kc1, c1_begin=n_c1 - 1, c1_end=n_c1)
+        tbs.block_scores(lp, Q, Kc1, S, ws_s)
+        tbs.topk_select(lp, S, idx, nsel)
+        tbs.sparse_attn(lp, Q, K, V, idx, nsel, O, lse, ws_a)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: t.clone() for k, t in dict(idx=idx, nsel=nsel, O=O, lse=lse).items()}
+    res = dict(Kc1=Kc1.cpu(), S_cmp=S.cpu(), idx=idx.cpu(), n_sel=nsel.cpu(), O=O.cpu(),
+               lse=lse.cpu())
+    check_rows(res, x, op, n_kv - 1, {b: np.array([0]) for b in range(batch)})
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (O, lse, idx, nsel):
+            t.zero_()                     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, t in dict(idx=idx, nsel=nsel, O=O, lse=lse).items():
+            assert torch.equal(t, ref[k]), f"replay {rep}: {k} differs"

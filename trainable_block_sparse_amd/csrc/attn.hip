@@ -109,7 +109,7 @@ struct AttnArgs {
   float* lse;
   float* part_o;          // decode partials
   float2* part_ml;
-  int n_q, q_pos0, n_kv, n_blk, h_kv, budget;
+  int batch, n_q, q_pos0, n_kv, n_blk, h_kv, budget;
   int64_t kv_cap;
   float c;                // scale * log2(e)
 };
@@ -195,7 +195,12 @@ __device__ __forceinline__ void load_qfrag(const AttnArgs& a, int b, int t, int 
   for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(q + 32 * ks + 8 * (lane >> 4)));
 }
 
-// grid: x = ceil(n_q/4) token quads, y = h_kv, z = batch; 4 waves = 4 tokens.
+// 1-D grid, 16 workgroups (4 tokens each) per 64-token query block.
+// Workgroups are dispatched round-robin over the 8 XCDs; the mapping below
+// puts all 16 workgroups of one query block on the same XCD, so blocks that
+// several of its tokens select are read once into that XCD's L2 (every token
+// walks its ascending block list at about the same pace).  Late query blocks
+// (long rows) go first.
 // Loads run one block ahead: the K fragments of block i+1 are in flight
 // during the softmax and PV of block i, the V^T fragments of block i+1 during
 // the scores of block i+1.
@@ -204,10 +209,16 @@ __device__ __forceinline__ void load_qfrag(const AttnArgs& a, int b, int t, int 
 template <bool SPARSE, bool LONG>
 __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nquads = gridDim.x;
-  const int quad = nquads - 1 - (int)blockIdx.x;      // late tokens (long rows) first
-  const int t = quad * 4 + wave;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int n_qb = (a.n_q + AT_B - 1) / AT_B;
+  const int n_bg = a.batch * a.h_kv;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, r = bid >> 3;
+  const int qbg = (r >> 4) * 8 + xcd;                  // query block, global order
+  if (qbg >= n_qb * n_bg) return;
+  const int qb = n_qb - 1 - qbg / n_bg;                // late tokens (long rows) first
+  const int bg = qbg % n_bg;
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int t = qb * AT_B + (r & 15) * 4 + wave;
   if (t >= a.n_q) return;
   const int p = a.q_pos0 + t;
   const int b_p = p / AT_B;
@@ -313,13 +324,17 @@ __device__ __forceinline__ void transpose8x8_bf16(const u32x4 (&in)[8], u32x4 (&
   }
 }
 
-// V^T of one 64-key block in LDS: row d holds the 64 keys of feature d as eight
-// 16-byte slots; slot (key>>3) is stored at (key>>3) ^ (d & 7) so that both the
-// transposing writes and the fragment reads are free of bank conflicts.
-__device__ __forceinline__ int vt_slot(int d, int key8) { return key8 ^ (d & 7); }
+// One 64-key block staged in LDS for the decode kernel.  Every global load is
+// coalesced (lanes 16r..16r+15 read one 256-byte row).
+//  K: natural rows, 16-byte chunk c of row r stored at chunk c ^ (r & 15).
+//  V^T: vt2[key group kg][d'][8 keys] with d' = d ^ ((d >> 3) & 7); the 8x8
+//  register transposes write it, and the fragment reads (8 keys of one
+//  feature) read it, without bank conflicts.
+__device__ __forceinline__ int vt_row(int d) { return d ^ ((d >> 3) & 7); }
 
 __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vt[AT_D][AT_B];
+  __shared__ __attribute__((aligned(16))) uint8_t kst[AT_B * AT_D * 2];
+  __shared__ __attribute__((aligned(16))) uint16_t vt2[8][AT_D][8];
   const int lane = threadIdx.x;
   const int slot = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
   const int b = bt / a.n_q, t = bt % a.n_q;
@@ -337,24 +352,33 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
   const size_t kstride = (size_t)a.h_kv * AT_D;
   const uint16_t* kbase = a.K + (size_t)b * a.kv_cap * kstride + (size_t)g * AT_D;
   const uint16_t* vbase = a.V + (size_t)b * a.kv_cap * kstride + (size_t)g * AT_D;
-  // stage V^T: lane handles (key group kg of 8 keys, feature chunk c of 8)
-  // for c = lane>>3 and c+8; 8 row loads, an 8x8 transpose, 8 slot writes.
+  const int c = lane & 15, rq = lane >> 4;
+  // rows past the last key are clamped to it; they lie after p: masked, P = 0
+  u32x4 kv[16], vin[2][8];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int kg = lane & 7, c = (lane >> 3) + 8 * half;
-    u32x4 in[8], out[8];
+  for (int i = 0; i < 16; ++i) {
+    const int key = min(kv0 + 4 * i + rq, a.n_kv - 1);
+    kv[i] = *(const u32x4*)(kbase + (size_t)key * kstride + 8 * c);
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      // rows past the last key are clamped to it; their probabilities are 0
-      const int key = min(kv0 + 8 * kg + r, a.n_kv - 1);
-      in[r] = *(const u32x4*)(vbase + (size_t)key * kstride + 8 * c);
+      const int key = min(kv0 + 8 * (rq + 4 * hh) + r, a.n_kv - 1);
+      vin[hh][r] = *(const u32x4*)(vbase + (size_t)key * kstride + 8 * c);
     }
-    transpose8x8_bf16(in, out);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int d = 8 * c + q;
-      *(u32x4*)(&vt[d][8 * vt_slot(d, kg)]) = out[q];
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int r = 4 * i + rq;
+    *(u32x4*)(kst + r * (AT_D * 2) + ((c ^ (r & 15)) << 4)) = kv[i];
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    u32x4 out[8];
+    transpose8x8_bf16(vin[hh], out);
+    const int kg = rq + 4 * hh;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) *(u32x4*)&vt2[kg][vt_row(8 * c + q)][0] = out[q];
   }
   __syncthreads();
   bf16x8 qf[4];
@@ -367,18 +391,16 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
   bf16x8 kf[4][4], vf[8][2];
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) {
-    const int key = min(kv0 + tile_key(tt, r16), a.n_kv - 1);   // clamped rows are masked
-    const uint16_t* kr = kbase + (size_t)key * kstride + 8 * grp;
+    const int r = tile_key(tt, r16);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) kf[tt][ks] = as_bf16x8(*(const u32x4*)(kr + 32 * ks));
+    for (int ks = 0; ks < 4; ++ks)
+      kf[tt][ks] = as_bf16x8(*(const u32x4*)(kst + r * (AT_D * 2) + (((4 * ks + grp) ^ (r & 15)) << 4)));
   }
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const int d = 16 * mt + r16;
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      vf[mt][ks] = as_bf16x8(*(const u32x4*)(&vt[d][8 * vt_slot(d, 4 * ks + grp)]));
-  }
+      vf[mt][ks] = as_bf16x8(*(const u32x4*)&vt2[4 * ks + grp][vt_row(16 * mt + r16)][0]);
   bf16x8 pf[2];
   if (blk == p / AT_B)
     attn_scores<true>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
@@ -592,6 +614,7 @@ static AttnArgs fast_args(const infv2_problem& p, const void* Q, const void* K, 
   a.lse = lse;
   a.part_o = nullptr;
   a.part_ml = nullptr;
+  a.batch = p.batch;
   a.n_q = p.n_q;
   a.q_pos0 = p.q_pos0;
   a.n_kv = p.n_kv;
@@ -625,7 +648,8 @@ hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, con
     hipLaunchKernelGGL(kv_pack_kernel, dim3(a.n_blk, p.h_kv, p.batch), dim3(256), 0, stream,
                        (const uint16_t*)K, (const uint16_t*)V, (uint16_t*)a.Kp, (uint16_t*)a.Vp,
                        p.n_kv, a.n_blk, p.h_kv, kv_cap);
-    dim3 grid((p.n_q + 3) / 4, p.h_kv, p.batch);
+    const int total_qb = ((p.n_q + AT_B - 1) / AT_B) * p.batch * p.h_kv;
+    dim3 grid(((total_qb + 7) / 8) * 8 * 16);
     if (sparse && budget > 64)
       hipLaunchKernelGGL((attn_prefill_kernel<true, true>), grid, dim3(256), 0, stream, a);
     else if (sparse)

@@ -40,7 +40,7 @@ struct ScoresArgs {
   const uint16_t* Q;
   const uint16_t* Kc1;
   float* S_cmp;
-  int n_q, q_pos0, h_kv, n_c1, n_blk, tiles;
+  int batch, n_q, q_pos0, h_kv, n_c1, n_blk, tiles;
   int64_t c1_cap;
   float c;  // scale * log2(e)
 };
@@ -137,9 +137,28 @@ __global__ void __launch_bounds__(256, 2) scores_prefill_kernel(ScoresArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int tile = a.tiles - 1 - (int)(blockIdx.x % a.tiles);   // long rows first
-  const int bg = blockIdx.x / a.tiles;
-  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  // Workgroups go round-robin over the 8 XCDs.  With h_kv dividing 8, XCD x
+  // takes only group x % h_kv, so each XCD's L2 holds one group's K^C1;
+  // within a group, tiles run from the last (longest rows) to the first.
+  int tile, g, b;
+  {
+    const int bid = blockIdx.x;
+    if (8 % a.h_kv == 0) {
+      const int xcd = bid & 7, r = bid >> 3;
+      const int per = 8 / a.h_kv;                      // XCDs per group
+      g = xcd % a.h_kv;
+      const int w = r * per + xcd / a.h_kv;            // work index within the group
+      if (w >= a.tiles * a.batch) return;
+      b = w % a.batch;
+      tile = a.tiles - 1 - w / a.batch;
+    } else {
+      if (bid >= a.tiles * a.batch * a.h_kv) return;
+      tile = a.tiles - 1 - (bid % a.tiles);
+      const int bg = bid / a.tiles;
+      g = bg % a.h_kv;
+      b = bg / a.h_kv;
+    }
+  }
   const int wg_t0 = tile * SEL_TOK_WG;
   const int t0 = wg_t0 + wave * SEL_TOK_WAVE;
   const int hq = a.h_kv * SEL_G;
@@ -313,33 +332,59 @@ struct SplitArgs {
 };
 
 // grid: x = chunk, y = group, z = batch*n_q token.  4 waves x 64 kernels.
+// Each wave loads its 64 K^C1 rows (16 KB) with coalesced loads (lanes
+// 16r..16r+15 read one 256-byte row), stages them through LDS 32 rows at a
+// time and reads the MFMA fragments back XOR-swizzled, free of bank conflicts.
 __global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
   __shared__ float red_m[4][16], red_s[4][16];
+  __shared__ __attribute__((aligned(16))) uint8_t kst_all[4][32 * SEL_ROW_BYTES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
   const int b = bt / a.n_q, t = bt % a.n_q;
   const int p = a.q_pos0 + t;
   const int jmax = last_visible_kernel(p);
   const int hq = a.h_kv * SEL_G;
+  uint8_t* kst = kst_all[wave];
+  const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
+  const int jw = chunk * SPLIT_CK + wave * 64;
+  u32x4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    // kernels past the last one are clamped to it; they are never visible
+    const int j = min(jw + 4 * i + (lane >> 4), a.n_c1 - 1);
+    v[i] = *(const u32x4*)(kc1 + (size_t)j * SEL_D + 8 * (lane & 15));
+  }
   // A operand: Q rows = heads (lane & 15), k = d
   bf16x8 qf[4];
   const uint16_t* qrow = a.Q + (((size_t)b * a.n_q + t) * hq + g * SEL_G + (lane & 15)) * SEL_D;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(qrow + 32 * ks + 8 * (lane >> 4)));
-  const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
-  const int jw = chunk * SPLIT_CK + wave * 64;
   f32x4 acc[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // kernels past the last one are clamped to it; they are never visible
-    const int j = min(jw + 16 * nt + (lane & 15), a.n_c1 - 1);
-    bf16x8 kf[4];
+  for (int h = 0; h < 2; ++h) {
+    // rows 32h .. 32h+31 of the wave's 64 (row 4i + (lane>>4) came from v[i])
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = as_bf16x8(*(const u32x4*)(kc1 + (size_t)j * SEL_D + 32 * ks + 8 * (lane >> 4)));
+    for (int i = 8 * h; i < 8 * h + 8; ++i) {
+      const int row = 4 * i + (lane >> 4) - 32 * h, c16 = lane & 15;
+      *(u32x4*)(kst + row * SEL_ROW_BYTES + ((c16 ^ (row & 15)) << 4)) = v[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc[nt] = mfma16(qf[ks], kf[ks], acc[nt]);
+    for (int nt = 2 * h; nt < 2 * h + 2; ++nt) {
+      acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int row = 16 * nt + (lane & 15) - 32 * h;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c16 = 4 * ks + (lane >> 4);
+        const bf16x8 kf = as_bf16x8(*(const u32x4*)(kst + row * SEL_ROW_BYTES + ((c16 ^ (row & 15)) << 4)));
+        acc[nt] = mfma16(qf[ks], kf, acc[nt]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   // C layout: lane holds heads 4*(lane>>4)+i, kernel jw + 16*nt + (lane&15)
   float* lrow = a.logits + ((size_t)bt * a.h_kv + g) * SEL_G * a.n_c1p;
@@ -601,6 +646,7 @@ hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void
     a.Q = (const uint16_t*)Q;
     a.Kc1 = (const uint16_t*)Kc1;
     a.S_cmp = S_cmp;
+    a.batch = p.batch;
     a.n_q = p.n_q;
     a.q_pos0 = p.q_pos0;
     a.h_kv = p.h_kv;
@@ -609,7 +655,8 @@ hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void
     a.tiles = (p.n_q + SEL_TOK_WG - 1) / SEL_TOK_WG;
     a.c1_cap = c1_cap;
     a.c = scale * kLog2e;
-    dim3 grid((unsigned)a.tiles * p.h_kv * p.batch);
+    const int wgs = a.tiles * p.h_kv * p.batch;
+    dim3 grid(8 % p.h_kv == 0 ? ((wgs + 7) / 8) * 8 : wgs);
     hipLaunchKernelGGL(scores_prefill_kernel, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
