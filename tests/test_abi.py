@@ -106,6 +106,7 @@ def test_workspace_sizes_and_errors(L):
         == tbs.INFV2_E_WORKSPACE
     pre = _prob(n_q=32768, n_kv=32768)
     assert L.infv2_block_scores_workspace(ctypes.byref(pre.to_c())) == 0
-    assert L.infv2_dense_attn_workspace(ctypes.byref(pre.to_c())) == 2 * 128 * 32768 * 2
+    # packed K and V: 2 tensors x h_kv x (blocks x B) keys x d x 2 bytes
+    assert L.infv2_dense_attn_workspace(ctypes.byref(pre.to_c())) == 2 * 2 * 32768 * 128 * 2
     for s in (0, -1, -2, -3, -4, 7):
         assert L.infv2_status_string(s)
