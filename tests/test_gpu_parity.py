@@ -166,3 +166,22 @@ def test_all_equal_scores_pick_lowest_blocks():
             n = int(res["n_sel"][0, g, t])
             assert res["idx"][0, g, t, :n].tolist() == want
     check_rows(res, x, op, 0, {0: np.arange(0, n_kv, 13)})
+
+
+def test_extreme_logits_take_exact_pass():
+    # Sequence 0: head 5 of group 0 has 64x larger queries, so the other heads'
+    # sums fall far below the token-wide exponent reference (underflow risk).
+    # Sequence 1: keys of one late block are 64x larger, so later logits
+    # overflow the first chunk's reference.  Both send tiles to the exact
+    # selection pass; results must still match the oracle everywhere.
+    cfg = CONFIGS["prefill32k"]
+    n_kv, batch = 1500, 2
+    _say("case: extreme logits", n_kv, batch)
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=5)
+    x["q"][0, :, 5, :] *= 64
+    x["k"][1, 1200:1264, 1, :] *= 64
+    lp, op = problems(cfg, n_kv=n_kv, batch=batch)
+    res = run_gpu_sparse(lp, x["q"], x["k"], x["v"])
+    check_compress(res, x["k"], op)
+    rep = check_rows(res, x, op, 0, {b: np.arange(n_kv) for b in range(batch)})
+    _say(rep)

@@ -192,7 +192,8 @@ __device__ __forceinline__ void load_qfrag(const AttnArgs& a, int b, int t, int 
   const int hq = a.h_kv * AT_G;
   const uint16_t* q = a.Q + (((size_t)b * a.n_q + t) * hq + g * AT_G + (lane & 15)) * AT_D;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(q + 32 * ks + 8 * (lane >> 4)));
+  for (int ks = 0; ks < 4; ++ks)
+    qf[ks] = as_bf16x8(__builtin_nontemporal_load((const u32x4*)(q + 32 * ks + 8 * (lane >> 4))));
 }
 
 // 1-D grid, 16 workgroups (4 tokens each) per 64-token query block.
@@ -301,10 +302,11 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(AttnArgs a) {
   for (int mt = 0; mt < 8; ++mt) {
     const uint32_t w0 = pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv);
     const uint32_t w1 = pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv);
-    *(uint2*)(orow + 16 * mt + 4 * grp) = make_uint2(w0, w1);
+    __builtin_nontemporal_store(u32x2{w0, w1}, (u32x2*)(orow + 16 * mt + 4 * grp));
   }
   if (a.lse && grp == 0)
-    a.lse[((size_t)b * hq + g * AT_G + r16) * a.n_q + t] = (m_run + fast_log2(l_run)) * kLn2;
+    __builtin_nontemporal_store((m_run + fast_log2(l_run)) * kLn2,
+                                a.lse + ((size_t)b * hq + g * AT_G + r16) * a.n_q + t);
 }
 
 // ---------------------------------------------------------------------------

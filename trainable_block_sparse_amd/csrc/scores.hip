@@ -52,7 +52,9 @@ constexpr int PASS_MAX = 0;    // row maxima (only when the sum overflows)
 constexpr int PASS_SUM = 1;    // log-sum-exp sweep
 constexpr int PASS_SCORE = 2;  // normalised scores, group sum, max-pool
 
-// One chunk of 32 kernels for the wave's 64 rows (4 tokens x 16 heads).
+
+// Exact pass, one chunk of 32 kernels for the wave's 64 rows (4 tokens x 16
+// heads), with a reference per row.
 // MASKED chunks contain kernels that are not causal for some row.
 //  PASS_MAX:   M = max(M, z)
 //  PASS_SUM:   W += 2^(z*c - M); on the first chunk M is first set to the
@@ -60,7 +62,7 @@ constexpr int PASS_SCORE = 2;  // normalised scores, group sum, max-pool
 //  PASS_SCORE: S^C1 = 2^(z*c - M) * W, summed over the group's 16 heads and
 //              staged in sbuf for the max-pool
 template <int PASS, bool MASKED>
-__device__ __forceinline__ void scores_chunk(const ScoresArgs& a, const uint8_t* kb, int chunk,
+__device__ __forceinline__ void exact_chunk(const ScoresArgs& a, const uint8_t* kb, int chunk,
                                              bool first, const bf16x8 (&qf)[2][8],
                                              const int (&jm)[4], float (&M)[2][16],
                                              float (&W)[2][16], float (&sbuf)[4][SEL_CHUNK + 1],
@@ -131,33 +133,23 @@ __device__ __forceinline__ void scores_chunk(const ScoresArgs& a, const uint8_t*
   }
 }
 
-__global__ void __launch_bounds__(256, 2) scores_prefill_kernel(ScoresArgs a) {
+// The exact pass: the same two sweeps with one exponent reference per row
+// (and an extra maximum sweep when a sum overflows).  It runs only for the
+// tiles that the fast kernel marked (NaN in block 0 of the tile's first row)
+// and exits at once for all others.
+__global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][SEL_CHUNK * SEL_ROW_BYTES];
   __shared__ float sbuf_all[4][SEL_TOK_WAVE][SEL_CHUNK + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  // Workgroups go round-robin over the 8 XCDs.  With h_kv dividing 8, XCD x
-  // takes only group x % h_kv, so each XCD's L2 holds one group's K^C1;
-  // within a group, tiles run from the last (longest rows) to the first.
-  int tile, g, b;
+  const int bid = blockIdx.x;
+  const int tile = bid % a.tiles;
+  const int g = (bid / a.tiles) % a.h_kv;
+  const int b = bid / (a.tiles * a.h_kv);
   {
-    const int bid = blockIdx.x;
-    if (8 % a.h_kv == 0) {
-      const int xcd = bid & 7, r = bid >> 3;
-      const int per = 8 / a.h_kv;                      // XCDs per group
-      g = xcd % a.h_kv;
-      const int w = r * per + xcd / a.h_kv;            // work index within the group
-      if (w >= a.tiles * a.batch) return;
-      b = w % a.batch;
-      tile = a.tiles - 1 - w / a.batch;
-    } else {
-      if (bid >= a.tiles * a.batch * a.h_kv) return;
-      tile = a.tiles - 1 - (bid % a.tiles);
-      const int bg = bid / a.tiles;
-      g = bg % a.h_kv;
-      b = bg / a.h_kv;
-    }
+    const float mark = a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tile * SEL_TOK_WG) * a.n_blk];
+    if (!__builtin_isnan(mark)) return;
   }
   const int wg_t0 = tile * SEL_TOK_WG;
   const int t0 = wg_t0 + wave * SEL_TOK_WAVE;
@@ -227,9 +219,9 @@ __global__ void __launch_bounds__(256, 2) scores_prefill_kernel(ScoresArgs a) {
       const bool masked = c * SEL_CHUNK + SEL_CHUNK - 1 > jmin_wg;
       const bool first = set_ref && c == 0;
       if (masked)
-        scores_chunk<PASS, true>(a, kbuf[c & 1], c, first, qf, jm, M, W, sbuf, lane);
+        exact_chunk<PASS, true>(a, kbuf[c & 1], c, first, qf, jm, M, W, sbuf, lane);
       else
-        scores_chunk<PASS, false>(a, kbuf[c & 1], c, first, qf, jm, M, W, sbuf, lane);
+        exact_chunk<PASS, false>(a, kbuf[c & 1], c, first, qf, jm, M, W, sbuf, lane);
       if constexpr (PASS == PASS_SCORE) {
         // max-pool: block c*8+bb takes kernels c*32+4bb-1 .. c*32+4bb+3,
         // i.e. sbuf[tl][4bb .. 4bb+4] (sbuf[tl][0] carries kernel c*32-1);
@@ -310,6 +302,311 @@ __global__ void __launch_bounds__(256, 2) scores_prefill_kernel(ScoresArgs a) {
       const int b_p = (a.q_pos0 + tok) >> 6;
       float* row = a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_blk;
       for (int blk = nchunks * (SEL_CHUNK / 4) + (lane & 15); blk <= b_p; blk += 16)
+        row[blk] = kNegInf;
+    }
+  }
+}
+
+constexpr int SEL_DEPTH = 4;                                // K^C1 chunks in flight per wave
+constexpr int SEL_CHUNK_BYTES = SEL_CHUNK * SEL_ROW_BYTES;  // 8 KB
+constexpr int FAST_TOK_WAVE = 2;                            // tokens per wave
+constexpr int FAST_WAVES = SEL_TOK_WG / FAST_TOK_WAVE;      // 8 waves, 512 threads
+
+// Lane moves by the data-parallel primitives.  Every cross-lane read runs
+// with all lanes active (a read from an inactive lane yields 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_QUAD_BC0 = 0x00;    // quad_perm [0,0,0,0]
+constexpr int DPP_WAVE_SHR1 = 0x138;  // lane l <- lane l-1
+
+// Sum of four per-lane values A, B, C, D over the four 16-lane rows (lanes
+// l, l^16, l^32, l^48).  Lanes of row 0 receive A's sum, row 1 C's, row 2
+// B's, row 3 D's (two permlane32 swaps, then one permlane16 swap).
+__device__ __forceinline__ float row_sum4(float A, float B, float C, float D) {
+  const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(A), __float_as_uint(B), false, false);
+  const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(C), __float_as_uint(D), false, false);
+  const float r1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);   // rows 0,1: A; rows 2,3: B
+  const float r2 = __uint_as_float(s2[0]) + __uint_as_float(s2[1]);   // rows 0,1: C; rows 2,3: D
+  const auto s3 = __builtin_amdgcn_permlane16_swap(__float_as_uint(r1), __float_as_uint(r2), false, false);
+  return __uint_as_float(s3[0]) + __uint_as_float(s3[1]);
+}
+
+// Register state of one wave: 2 query tokens x 16 heads.  MFMA tiles are
+// 16x16x32: token tl's 16 heads are the M rows, 16 kernels the N columns;
+// acc[tl][nt] holds kernels 16nt .. 16nt+15 of the chunk.  In the C layout
+// lane l holds heads 4*(l>>4) + i (i = 0..3) of column l&15.  After the head
+// sum, lane row r = l>>4 holds token r>>1, kernels 16*(r&1) + (l&15).
+struct SelWave {
+  bf16x8 qf[2][4];   // A operand per token and k-step: head l&15, d = 32ks + 8(l>>4) ..+7
+  float Mt[2];       // exponent reference per token (times c, wave-uniform)
+  float W[2][4];     // PASS_SUM: partial sums; PASS_SCORE: 1 / row sum; [token][i]
+  float carry;       // PASS_SCORE: S^shared of kernel (chunk start - 1), rows 0 and 2
+  int jm[2];         // last visible kernel per token (wave-uniform)
+  int jm_l;          // the same for the token of this lane's row after the head sum
+  int bp_l;          // its last causal block
+  float* srow;       // its S^cmp row
+};
+
+// z = Q K^C1^T for one chunk of 32 kernels staged in LDS (16-byte piece c of
+// row r stored at piece position c ^ (r & 15)).
+__device__ __forceinline__ void chunk_mfma(const uint8_t* kb, const SelWave& w, int lane,
+                                           f32x4 (&acc)[2][2]) {
+  const int r16 = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int row = nt * 16 + r16;
+      const int piece = 4 * ks + grp;
+      const bf16x8 bfrag = as_bf16x8(*(const u32x4*)(kb + row * SEL_ROW_BYTES + ((piece ^ r16) << 4)));
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl)
+        acc[tl][nt] = mfma16(w.qf[tl][ks], bfrag, ks == 0 ? f32x4{} : acc[tl][nt]);
+    }
+  }
+}
+
+// Vector work on the logits z of chunk `chunk`.  MASKED chunks contain
+// kernels that are not causal for some token.  The exponent reference M is
+// per token (its 16 heads share it):
+//  PASS_SUM:   W += 2^(z*c - M); FIRST: M is first set to the exact maximum
+//              of the chunk's logits over the token's 16 heads (times c)
+//  PASS_SCORE: S^C1 = 2^(z*c - M) * W, summed over the group's 16 heads,
+//              max-pooled over the kernels that intersect each block and
+//              written to S^cmp
+template <int PASS, bool MASKED, bool FIRST>
+__device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][2], int chunk,
+                                           SelWave& w, int lane) {
+  static_assert(PASS == PASS_SUM || PASS == PASS_SCORE, "fast passes");
+  const int r16 = lane & 15;
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const bool out = chunk * SEL_CHUNK + nt * 16 + r16 > w.jm[tl];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (out) acc[tl][nt][i] = kNegInf;
+      }
+  }
+  if constexpr (PASS == PASS_SUM) {
+    if constexpr (FIRST) {
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl) {
+        float m = acc[tl][0][0];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, acc[tl][nt][i]);
+        m = wave_max(m);
+        m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(m)));
+        w.Mt[tl] = (m == kNegInf) ? 0.f : m * a.c;   // -inf: nothing visible
+      }
+    }
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w.W[tl][i] += fast_exp2(__builtin_fmaf(acc[tl][nt][i], a.c, -w.Mt[tl]));
+  } else {
+    float part[2][2];   // [token][nt]: this lane's 4 heads
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[tl][nt][i], a.c, -w.Mt[tl])), w.W[tl][i], s);
+        part[tl][nt] = s;
+      }
+    // rows 0..3 <- (token 0, nt 0), (token 0, nt 1), (token 1, nt 0), (token 1, nt 1)
+    float v = row_sum4(part[0][0], part[1][0], part[0][1], part[1][1]);
+    const int nt = (lane >> 4) & 1;
+    if constexpr (MASKED) v = (chunk * SEL_CHUNK + nt * 16 + r16 > w.jm_l) ? kNegInf : v;
+    // block bb = 4nt + r16/4 of the chunk takes kernels 4bb-1 .. 4bb+3: the
+    // max over its quad of lanes and the kernel before it (the previous lane;
+    // for rows 0 and 2 at column 0, the last kernel of the previous chunk)
+    float q = fmaxf(v, dpp<DPP_QUAD_XOR1>(v));
+    q = fmaxf(q, dpp<DPP_QUAD_XOR2>(q));
+    const float shr = dpp<DPP_WAVE_SHR1>(v);
+    const float prev = (r16 == 0 && nt == 0) ? w.carry : shr;
+    const float bv = fmaxf(q, dpp<DPP_QUAD_BC0>(prev));   // same in all 4 lanes of the quad
+    const int blk = chunk * (SEL_CHUNK / 4) + nt * 4 + (r16 >> 2);
+    if (!MASKED || blk <= w.bp_l) __builtin_nontemporal_store(bv, w.srow + blk);
+    // kernel 31 of this chunk: lane 31 (token 0) and lane 63 (token 1)
+    const float k31_t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+    const float k31_t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    w.carry = lane < 32 ? k31_t0 : k31_t1;
+  }
+}
+
+__global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * SEL_CHUNK_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  // Workgroups go round-robin over the 8 XCDs.  With h_kv dividing 8, XCD x
+  // takes only group x % h_kv, so each XCD's L2 holds one group's K^C1;
+  // within a group, tiles run from the last (longest rows) to the first.
+  int tile, g, b;
+  {
+    const int bid = blockIdx.x;
+    if (8 % a.h_kv == 0) {
+      const int xcd = bid & 7, r = bid >> 3;
+      const int per = 8 / a.h_kv;                      // XCDs per group
+      g = xcd % a.h_kv;
+      const int wi = r * per + xcd / a.h_kv;           // work index within the group
+      if (wi >= a.tiles * a.batch) return;
+      b = wi % a.batch;
+      tile = a.tiles - 1 - wi / a.batch;
+    } else {
+      if (bid >= a.tiles * a.batch * a.h_kv) return;
+      tile = a.tiles - 1 - (bid % a.tiles);
+      const int bg = bid / a.tiles;
+      g = bg % a.h_kv;
+      b = bg / a.h_kv;
+    }
+  }
+  const int wg_t0 = tile * SEL_TOK_WG;
+  const int t0 = wg_t0 + wave * FAST_TOK_WAVE;
+  const int hq = a.h_kv * SEL_G;
+  float* srows = a.S_cmp + ((size_t)b * a.h_kv + g) * a.n_q * a.n_blk;
+
+  // Tokens past n_q (ragged last tile) repeat the last token: they compute
+  // its values and write them to its row again.
+  SelWave w;
+#pragma unroll
+  for (int tl = 0; tl < 2; ++tl) {
+    const int tok = min(t0 + tl, a.n_q - 1);
+    const uint16_t* qrow = a.Q + (((size_t)b * a.n_q + tok) * hq + g * SEL_G + (lane & 15)) * SEL_D;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      w.qf[tl][ks] = as_bf16x8(__builtin_nontemporal_load((const u32x4*)(qrow + 32 * ks + 8 * (lane >> 4))));
+    w.jm[tl] = last_visible_kernel(a.q_pos0 + tok);
+  }
+  {
+    const int tok = min(t0 + (lane >> 5), a.n_q - 1);
+    w.jm_l = last_visible_kernel(a.q_pos0 + tok);
+    w.bp_l = (a.q_pos0 + tok) >> 6;
+    w.srow = srows + (size_t)tok * a.n_blk;
+  }
+  const int wg_last = min(wg_t0 + SEL_TOK_WG - 1, a.n_q - 1);
+  const int jmax_wg = last_visible_kernel(a.q_pos0 + wg_last);
+  const int jmin_wg = last_visible_kernel(a.q_pos0 + wg_t0);
+  const int nchunks = jmax_wg < 0 ? 0 : (jmax_wg + 2 + SEL_CHUNK - 1) / SEL_CHUNK;
+  // chunks below n_full hold only kernels that every row of the workgroup sees
+  const int n_full = jmin_wg < 0 ? 0 : (jmin_wg + 1) / SEL_CHUNK;
+
+#pragma unroll
+  for (int tl = 0; tl < 2; ++tl) {
+    w.Mt[tl] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w.W[tl][i] = 0.f;
+  }
+
+  const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
+
+  // K^C1 streams through LDS in chunks of 32 kernels (8 KB): 512 pieces of
+  // 16 bytes, one per lane of the 8 waves.  Lane L of wave w owns piece
+  // u = 64 w + L, i.e. row u/16 at piece position u%16, which holds global
+  // piece (u%16) ^ (row & 15) of that row.  Each wave keeps the pieces of
+  // the next SEL_DEPTH chunks in flight in registers (plain loads, so that
+  // the compiler tracks each register's wait); a chunk goes to LDS one step
+  // before it is used.  Chunks past the last one re-load the last kernel.
+  const int piece_u = wave * 64 + lane;
+  const int piece_row = piece_u >> 4;
+  const uint32_t piece_src = (uint32_t)((((piece_u & 15) ^ (piece_row & 15)) << 3));   // elements
+  uint8_t* const piece_dst = kbuf + piece_u * 16;
+  auto load_piece = [&](int c) -> u32x4 {
+    const int j = min(c * SEL_CHUNK + piece_row, a.n_c1 - 1);
+    return *(const u32x4*)(kc1 + (size_t)j * SEL_D + piece_src);
+  };
+  auto slot = [&](int c) -> const uint8_t* { return kbuf + (c & 1) * SEL_CHUNK_BYTES; };
+
+  // One sweep.  Step c: logits and vector work of chunk c (slot c & 1), then
+  // chunk c+1 from registers into the other slot, the register refilled with
+  // chunk c+1+SEL_DEPTH, and the barrier that publishes chunk c+1.
+  auto run_pass = [&](auto pass_tag, auto ref_tag) {
+    constexpr int PASS = decltype(pass_tag)::value;
+    constexpr bool SET_REF = decltype(ref_tag)::value;
+    if (nchunks == 0) return;
+    u32x4 st[SEL_DEPTH];
+#pragma unroll
+    for (int k = 0; k < SEL_DEPTH; ++k) st[k] = load_piece(k);
+    *(u32x4*)piece_dst = st[0];
+    st[0] = load_piece(SEL_DEPTH);
+    __syncthreads();
+    auto step = [&](int c, u32x4& next) {
+      f32x4 acc[2][2];
+      chunk_mfma(slot(c), w, lane, acc);
+      if (SET_REF && c == 0) {
+        if (n_full > 0) chunk_valu<PASS, false, SET_REF>(a, acc, c, w, lane);
+        else            chunk_valu<PASS, true, SET_REF>(a, acc, c, w, lane);
+      } else if (c < n_full) {
+        chunk_valu<PASS, false, false>(a, acc, c, w, lane);
+      } else {
+        chunk_valu<PASS, true, false>(a, acc, c, w, lane);
+      }
+      *(u32x4*)(piece_dst + ((c + 1) & 1) * SEL_CHUNK_BYTES) = next;
+      next = load_piece(c + 1 + SEL_DEPTH);
+      __syncthreads();
+    };
+    static_assert(SEL_DEPTH == 4, "unrolled below");
+    int c = 0;
+    for (; c + 4 <= nchunks; c += 4) {
+      step(c, st[1]);
+      step(c + 1, st[2]);
+      step(c + 2, st[3]);
+      step(c + 3, st[0]);
+    }
+    if (c < nchunks) step(c, st[1]);
+    if (c + 1 < nchunks) step(c + 1, st[2]);
+    if (c + 2 < nchunks) step(c + 2, st[3]);
+  };
+
+  // sweep 1 (log-sum-exp): s = sum_j 2^(z_j*c - M), M = the exact maximum
+  // over the first chunk and the token's 16 heads (every row with a visible
+  // kernel sees kernel 0)
+  run_pass(std::integral_constant<int, PASS_SUM>{}, std::true_type{});
+  // Lane partial sums -> row sums (over the 16 columns of a lane row).  A
+  // row whose sum overflowed (a later logit exceeds the reference by more
+  // than 2^127) or fell below 2^-64 (its head lies far below the token's
+  // other heads, so that terms could underflow) sends the whole tile to the
+  // exact kernel, which takes one reference per row.
+  bool bad = false;
+#pragma unroll
+  for (int tl = 0; tl < 2; ++tl)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float s = w.W[tl][i];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+      w.W[tl][i] = s > 0.f ? 1.0f / s : 0.f;
+      bad = bad || (w.jm[tl] >= 0 && !(s >= 0x1p-64f && s <= 0x1p127f));
+    }
+  if (__syncthreads_or(bad)) {
+    if (tid == 0) srows[(size_t)wg_t0 * a.n_blk] = __builtin_nanf("");
+    return;
+  }
+  // sweep 2: S^C1 = 2^(z*c - M) / s, head-group sum, max-pool, S^cmp
+  w.carry = kNegInf;
+  run_pass(std::integral_constant<int, PASS_SCORE>{}, std::false_type{});
+  // blocks with no visible kernel in the causal range
+  {
+    const int tl = lane >> 5;
+    const int tok = t0 + tl;
+    if (tok < a.n_q) {
+      const int b_p = (a.q_pos0 + tok) >> 6;
+      float* row = srows + (size_t)tok * a.n_blk;
+      for (int blk = nchunks * (SEL_CHUNK / 4) + (lane & 31); blk <= b_p; blk += 32)
         row[blk] = kNegInf;
     }
   }
@@ -657,7 +954,8 @@ hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void
     a.c = scale * kLog2e;
     const int wgs = a.tiles * p.h_kv * p.batch;
     dim3 grid(8 % p.h_kv == 0 ? ((wgs + 7) / 8) * 8 : wgs);
-    hipLaunchKernelGGL(scores_prefill_kernel, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(scores_prefill_kernel, grid, dim3(64 * FAST_WAVES), 0, stream, a);
+    hipLaunchKernelGGL(scores_exact_kernel, dim3(wgs), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   GenericScoresArgs a;
