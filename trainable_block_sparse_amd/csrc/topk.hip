@@ -5,19 +5,21 @@
 // 注意力机制", 动态上下文块选择 (initial and local blocks always attended) and
 // Top-K块共享 (one selection per (token, group)).
 //
-// One wavefront per (token, group) row.  Every candidate block gets a unique
-// 64-bit key  (order-preserving bits of S^cmp) << 32 | ~blk,  so a larger key
-// means a larger score and, at equal scores, a lower block index.  The k-th
-// largest key K* is found in two steps:
-//   1. each lane takes the maximum key of its blocks (blk = lane + 64 i); the
-//      kk-th largest of the 64 lane maxima, K0, is a lower bound of K*
-//      (kk lanes hold a key >= K0);
+// One wavefront per (token, group) row; the row's scores (up to 64 * NI
+// blocks) are read once into registers as order-preserving 32-bit keys
+// (candidates only; everything else is 0, below every candidate key).
+// s* = the kk-th largest candidate key, counted with multiplicity:
+//   1. the kk-th largest of the 64 lane maxima, K0, is a lower bound of s*;
 //   2. the keys >= K0 (usually about kk of them) are gathered, one per lane,
-//      and sorted across the wave; K* is the kk-th.  If more than 64 keys
-//      are >= K0 a bisection over the 64-bit key range finds K* instead.
-// Rows of up to 2048 blocks are read once, in one burst, into registers.
-// Membership is then  init/local, or key >= K*;  the ascending index list
-// comes from a ballot/popcount compaction over the blocks in order.
+//      and sorted across the wave; s* is the kk-th.  (If more than 64 keys
+//      are >= K0 -- massive ties -- a bisection over the key range finds s*.)
+// Selected: init/local blocks, candidates with key > s*, and, of the
+// candidates with key == s*, the lowest-index ones up to kk in total -- ties
+// go to the lower block index.  The ascending index list comes from a
+// ballot/popcount compaction over the blocks in order.
+// The sorts use lane moves of the data-parallel primitives and the permlane
+// swaps only (no LDS round trips); every cross-lane read runs with all lanes
+// active.
 #include "common.hpp"
 
 namespace infv2 {
@@ -27,30 +29,57 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
-__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-  const uint32_t lo = __shfl((uint32_t)v, src, 64);
-  const uint32_t hi = __shfl((uint32_t)(v >> 32), src, 64);
-  return ((uint64_t)hi << 32) | lo;
+
+// value of lane (lane ^ S), S = 1, 2, 4, 8, 16, 32
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
+  if constexpr (S == 1) {
+    return dpp_u<0xB1>(x);                            // quad_perm [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return dpp_u<0x4E>(x);                            // quad_perm [2,3,0,1]
+  } else if constexpr (S == 4) {
+    const uint32_t up = dpp_u<0x104>(x);              // row_shl:4  (lane + 4)
+    const uint32_t dn = dpp_u<0x114>(x);              // row_shr:4  (lane - 4)
+    return (lane & 4) ? dn : up;
+  } else if constexpr (S == 8) {
+    return dpp_u<0x128>(x);                           // row_ror:8 == lane ^ 8 within a row
+  } else if constexpr (S == 16) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? sw[0] : sw[1];
+  } else {
+    const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? sw[0] : sw[1];
+  }
+}
+
+template <int SIZE, int S>
+__device__ __forceinline__ uint32_t bitonic_step(uint32_t v, int lane) {
+  const uint32_t o = xor_lane<S>(v, lane);
+  const bool keep_max = ((lane & SIZE) == 0) == ((lane & S) == 0);
+  return keep_max ? max(v, o) : min(v, o);
 }
 
 // Bitonic sort across the 64 lanes, descending (lane 0 holds the largest).
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v, int lane) {
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane) {
+  v = bitonic_step<2, 1>(v, lane);
+  v = bitonic_step<4, 2>(v, lane);  v = bitonic_step<4, 1>(v, lane);
+  v = bitonic_step<8, 4>(v, lane);  v = bitonic_step<8, 2>(v, lane);  v = bitonic_step<8, 1>(v, lane);
+  v = bitonic_step<16, 8>(v, lane); v = bitonic_step<16, 4>(v, lane);
+  v = bitonic_step<16, 2>(v, lane); v = bitonic_step<16, 1>(v, lane);
+  v = bitonic_step<32, 16>(v, lane); v = bitonic_step<32, 8>(v, lane); v = bitonic_step<32, 4>(v, lane);
+  v = bitonic_step<32, 2>(v, lane);  v = bitonic_step<32, 1>(v, lane);
+  v = bitonic_step<64, 32>(v, lane); v = bitonic_step<64, 16>(v, lane); v = bitonic_step<64, 8>(v, lane);
+  v = bitonic_step<64, 4>(v, lane);  v = bitonic_step<64, 2>(v, lane);  v = bitonic_step<64, 1>(v, lane);
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint64_t o = shfl_xor_u64(v, stride);
-      const bool up = (lane & size) == 0;            // this run sorts descending
-      const bool lower = (lane & stride) == 0;       // this lane keeps the larger
-      const bool keep_max = (up == lower);
-      v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
-    }
-  }
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 
@@ -62,15 +91,15 @@ struct TopkArgs {
   int rows;
 };
 
-// NI > 0: the row (nb <= 64*NI blocks) is loaded once, in one burst, into
-// NI registers per lane; NI == 0: any length, scores re-read from memory.
+// NI > 0: the row (nb <= 64*NI blocks) is held in NI registers per lane;
+// NI == 0: any length, keys re-read from memory.
 template <int NI>
 __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
-  __shared__ uint64_t gather_all[4][64];
+  __shared__ uint32_t gather_all[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wave;
   if (row >= a.rows) return;                 // whole wave leaves together
-  uint64_t* gather = gather_all[wave];
+  uint32_t* gather = gather_all[wave];
   const int t = row % a.n_q;
   const int p = a.q_pos0 + t;
   const int b_p = p / a.B;
@@ -81,107 +110,122 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   const int kk = min(a.k, ncand);
   const float* srow = a.S_cmp + (size_t)row * a.n_blk;
   int32_t* out = a.idx + (size_t)row * a.budget;
+  const int niter = (nb + 63) >> 6;
   constexpr int NC = NI > 0 ? NI : 1;
-  float sc[NC];
+  uint32_t kr[NC];
+  auto key_of = [&](int blk, float v) -> uint32_t {
+    return (blk >= init_hi && blk < loc_lo) ? ordered_bits(v) : 0u;
+  };
   if constexpr (NI > 0) {
+    float sc[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) sc[i] = srow[min(lane + 64 * i, nb - 1)];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kr[i] = key_of(lane + 64 * i, sc[i]);
   }
-  const int niter = (nb + 63) >> 6;
-  auto key_at = [&](int i) -> uint64_t {     // key of block lane + 64*i
+  auto key_at = [&](int i) -> uint32_t {
+    if constexpr (NI > 0) return kr[i];
     const int blk = lane + 64 * i;
-    if (blk >= nb || blk < init_hi || blk >= loc_lo) return 0ull;   // not a candidate
-    float v;
-    if constexpr (NI > 0) v = sc[i]; else v = srow[blk];
-    return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(~(uint32_t)blk);
+    return blk < nb ? key_of(blk, srow[blk]) : 0u;
   };
-  auto count_ge = [&](uint64_t thr) -> int {
+  auto count_ge = [&](uint32_t thr) -> int {
     int c = 0;
     if constexpr (NI > 0) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) c += key_at(i) >= thr ? 1 : 0;
+      for (int i = 0; i < NI; ++i) c += kr[i] >= thr ? 1 : 0;
     } else {
       for (int i = 0; i < niter; ++i) c += key_at(i) >= thr ? 1 : 0;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-    return c;
+    return wave_sum_i(c);
   };
-  // largest X with count(key >= X) >= kk, starting from a known lower bound
-  auto bisect = [&](uint64_t lo) -> uint64_t {
-    uint64_t hi = ~0ull;
+  // largest X with count(key >= X) >= kk, from a lower bound that satisfies it
+  auto bisect = [&](uint32_t lo) -> uint32_t {
+    uint32_t hi = 0xFFFFFFFFu;
     while (lo < hi) {
-      const uint64_t mid = lo + ((hi - lo) >> 1) + 1;
+      const uint32_t mid = lo + ((hi - lo) >> 1) + 1;
       if (count_ge(mid) >= kk) lo = mid; else hi = mid - 1;
     }
     return lo;
   };
 
-  uint64_t kstar = 0ull;     // keys >= kstar are selected
+  uint32_t sstar = 0u;       // the kk-th largest candidate key
   const bool all = (kk == ncand);  // every candidate is selected
-  if (all || kk == 0) {
-    // nothing to rank
-  } else if (kk > 64) {
-    kstar = bisect(1ull);    // every candidate key is >= 1, non-candidates are 0
-  } else {
-    uint64_t lmax = 0ull;
-    if constexpr (NI > 0) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) { const uint64_t kv = key_at(i); lmax = kv > lmax ? kv : lmax; }
+  if (!all && kk > 0) {
+    if (kk > 64) {
+      sstar = bisect(1u);    // every candidate key is >= 1
     } else {
-      for (int i = 0; i < niter; ++i) { const uint64_t kv = key_at(i); lmax = kv > lmax ? kv : lmax; }
-    }
-    const uint64_t sorted = wave_sort_desc(lmax, lane);
-    const uint64_t k0 = shfl_u64(sorted, kk - 1);
-    // count and gather the keys >= k0
-    int cnt = 0;
-    if constexpr (NI > 0) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) cnt += key_at(i) >= k0 ? 1 : 0;
-    } else {
-      for (int i = 0; i < niter; ++i) cnt += key_at(i) >= k0 ? 1 : 0;
-    }
-    int total = cnt;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) total += __shfl_xor(total, o, 64);
-    if (total <= 64) {
-      int pre = cnt;                          // exclusive prefix of cnt over lanes
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(pre, o, 64);
-        if (lane >= o) pre += v;
-      }
-      pre -= cnt;
-      gather[lane] = 0ull;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint32_t lmax = 0u;
       if constexpr (NI > 0) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) { const uint64_t kv = key_at(i); if (kv >= k0) gather[pre++] = kv; }
+        for (int i = 0; i < NI; ++i) lmax = max(lmax, kr[i]);
       } else {
-        for (int i = 0; i < niter; ++i) { const uint64_t kv = key_at(i); if (kv >= k0) gather[pre++] = kv; }
+        for (int i = 0; i < niter; ++i) lmax = max(lmax, key_at(i));
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const uint64_t s2 = wave_sort_desc(gather[lane], lane);
-      kstar = shfl_u64(s2, kk - 1);
-    } else {
-      kstar = bisect(k0);                     // count(>= k0) >= kk holds
+      const uint32_t sorted = wave_sort_desc(lmax, lane);
+      const uint32_t k0 = (uint32_t)__builtin_amdgcn_readlane((int)sorted, kk - 1);
+      int cnt = 0;
+      if constexpr (NI > 0) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) cnt += kr[i] >= k0 ? 1 : 0;
+      } else {
+        for (int i = 0; i < niter; ++i) cnt += key_at(i) >= k0 ? 1 : 0;
+      }
+      const int total = wave_sum_i(cnt);
+      if (total <= 64) {
+        int pre = cnt;                        // exclusive prefix of cnt over lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int v = __shfl_up(pre, o, 64);
+          if (lane >= o) pre += v;
+        }
+        pre -= cnt;
+        gather[lane] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if constexpr (NI > 0) {
+#pragma unroll
+          for (int i = 0; i < NI; ++i) if (kr[i] >= k0) gather[pre++] = kr[i];
+        } else {
+          for (int i = 0; i < niter; ++i) { const uint32_t kv = key_at(i); if (kv >= k0) gather[pre++] = kv; }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint32_t s2 = wave_sort_desc(gather[lane], lane);
+        sstar = (uint32_t)__builtin_amdgcn_readlane((int)s2, kk - 1);
+      } else {
+        sstar = bisect(k0);                   // count(>= k0) >= kk holds
+      }
     }
+  }
+  // how many candidates equal to s* are taken (the lowest-index ones)
+  int eq_left = 0;
+  if (!all && kk > 0) {
+    int c = 0;
+    if constexpr (NI > 0) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) c += kr[i] > sstar ? 1 : 0;
+    } else {
+      for (int i = 0; i < niter; ++i) c += key_at(i) > sstar ? 1 : 0;
+    }
+    eq_left = kk - wave_sum_i(c);
   }
   // ascending compaction of the selected blocks
   int written = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
   auto emit = [&](int i) {
     const int blk = lane + 64 * i;
-    bool sel = false;
-    if (blk < nb) {
-      if (blk < init_hi || blk >= loc_lo) sel = true;
-      else sel = all || (kk > 0 && key_at(i) >= kstar);
-    }
+    const uint32_t kv = key_at(i);
+    const bool cand = blk < nb && blk >= init_hi && blk < loc_lo;
+    const bool fixed = blk < nb && !cand;
+    const bool eq = cand && !all && kv == sstar;
+    const uint64_t eq_ballot = __ballot(eq);
+    const int eq_rank = (int)__popcll(eq_ballot & below);
+    const bool sel = fixed || (cand && (all || kv > sstar || (eq && eq_rank < eq_left)));
+    eq_left -= (int)__popcll(eq_ballot);
     const uint64_t ballot = __ballot(sel);
-    const int pos = written + (int)__popcll(ballot & ((1ull << lane) - 1ull));
+    const int pos = written + (int)__popcll(ballot & below);
     if (sel) out[pos] = blk;
     written += (int)__popcll(ballot);
   };
