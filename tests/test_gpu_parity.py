@@ -70,6 +70,20 @@ def test_bf16_dense_attention(n_kv, batch):
     _say(rep)
 
 
+def test_bf16_dense_attention_unaligned_q_offset():
+    # queries 437..999: 16-token query tiles straddle 64-key blocks
+    cfg = CONFIGS["dense_switch"]
+    n_kv, q0 = 1000, 437
+    _say("case: bf16 dense, q_pos0", q0)
+    x = make_inputs(cfg, n_kv=n_kv, batch=1, seed=31)
+    xq = dict(x)
+    xq["q"] = x["q"][:, q0:].contiguous()
+    lp, op = problems(cfg, n_kv=n_kv, batch=1, n_q=n_kv - q0, q_pos0=q0)
+    res = run_gpu_dense(lp, xq["q"], x["k"], x["v"])
+    rep = check_rows(res, xq, op, q0, {0: np.arange(n_kv - q0)}, dense=True)
+    _say(rep)
+
+
 def test_fp32_dense_attention():
     cfg = CONFIGS["tiny"]
     x = make_inputs(cfg, n_kv=700, seed=3)

@@ -122,6 +122,11 @@ struct AttnArgs {
 // (log2 units): probabilities then stay below 256, and O is rescaled rarely.
 // DIAG: the block holds the query position; keys after p are masked.
 template <bool DIAG>
+__device__ __forceinline__ void attn_softmax(f32x4 (&s)[4], f32x4 (&o)[8], float& m_run,
+                                             float& l_run, int kv0, int p, float c, int lane,
+                                             bf16x8 (&pf)[2]);
+
+template <bool DIAG>
 __device__ __forceinline__ void attn_scores(const bf16x8 (&qf)[4], const bf16x8 (&kf)[4][4],
                                             f32x4 (&o)[8], float& m_run, float& l_run, int kv0,
                                             int p, float c, int lane, bf16x8 (&pf)[2]) {
@@ -132,6 +137,14 @@ __device__ __forceinline__ void attn_scores(const bf16x8 (&qf)[4], const bf16x8 
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) s[t] = mfma16(kf[t][ks], qf[ks], s[t]);
   }
+  attn_softmax<DIAG>(s, o, m_run, l_run, kv0, p, c, lane, pf);
+}
+
+// Online softmax of one 64-key block given its raw scores s (S^T tiles).
+template <bool DIAG>
+__device__ __forceinline__ void attn_softmax(f32x4 (&s)[4], f32x4 (&o)[8], float& m_run,
+                                             float& l_run, int kv0, int p, float c, int lane,
+                                             bf16x8 (&pf)[2]) {
   const int grp = lane >> 4;
   float mx = kNegInf;
 #pragma unroll
@@ -310,6 +323,145 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Dense causal attention (the dense switch): every token attends every causal
+// block, so the blocks are shared.  A workgroup takes 16 consecutive query
+// tokens of one group (8 waves x 2 tokens); each 64-key block is read once
+// from the fragment-order packs into LDS (32 KB) and serves all 16 tokens;
+// each wave reads a fragment from LDS once and applies it to both of its
+// tokens.  Blocks from the first token's block on are masked per token (one
+// block when the tile is aligned, two when q_pos0 is not a multiple of 16).
+// Blocks are prefetched one ahead in registers.
+// ---------------------------------------------------------------------------
+constexpr int DN_TOK = 16;      // tokens per workgroup
+constexpr int DN_WAVES = 8;     // 2 tokens per wave
+
+__global__ void __launch_bounds__(512, 2) attn_dense_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t kvs[2][2 * PACK_ELEMS];   // 2 x 32 KB
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n_tiles = (a.n_q + DN_TOK - 1) / DN_TOK;
+  const int n_bg = a.batch * a.h_kv;
+  // XCD x takes (b, g) pairs with bg % 8 == x when possible; tiles of a pair
+  // from the last (longest rows) to the first
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, r = bid >> 3;
+  const int wi = r * 8 + xcd;                           // global work index
+  if (wi >= n_tiles * n_bg) return;
+  const int bg = wi % n_bg;
+  const int tile = n_tiles - 1 - wi / n_bg;
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int t0 = tile * DN_TOK;
+  const int t_last = min(t0 + DN_TOK - 1, a.n_q - 1);
+  const int b_last = (a.q_pos0 + t_last) / AT_B;        // the last token's block
+  const int b_first = (a.q_pos0 + t0) / AT_B;           // the first token's block
+  // this wave's tokens (past n_q: repeat the last token, never written)
+  int tok[2], pos[2];
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    tok[u] = t0 + 2 * wave + u;
+    pos[u] = a.q_pos0 + min(tok[u], a.n_q - 1);
+    load_qfrag(a, b, min(tok[u], a.n_q - 1), g, lane, qf[u]);
+  }
+  f32x4 o[2][8];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    m_run[u] = kNegInf;
+    l_run[u] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[u][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // block staging: K pack then V pack, 2 x 16 KB, 4 pieces of 16 B per thread
+  const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS;
+  auto load_block = [&](int blk, u32x4 (&st)[4]) {
+    const uint16_t* kp = a.Kp + pack0 + (size_t)blk * PACK_ELEMS;
+    const uint16_t* vp = a.Vp + pack0 + (size_t)blk * PACK_ELEMS;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      st[i] = *(const u32x4*)(kp + (size_t)(tid + 512 * i) * 8);
+      st[2 + i] = *(const u32x4*)(vp + (size_t)(tid + 512 * i) * 8);
+    }
+  };
+  auto store_block = [&](int slot, const u32x4 (&st)[4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *(u32x4*)&kvs[slot][(tid + 512 * i) * 8] = st[i];
+      *(u32x4*)&kvs[slot][PACK_ELEMS + (tid + 512 * i) * 8] = st[2 + i];
+    }
+  };
+  u32x4 st[4];
+  load_block(0, st);
+  store_block(0, st);
+  if (b_last >= 1) load_block(1, st);
+  __syncthreads();
+  for (int blk = 0; blk <= b_last; ++blk) {
+    const uint16_t* ks_ = &kvs[blk & 1][0];
+    const uint16_t* vs_ = &kvs[blk & 1][PACK_ELEMS];
+    const int kv0 = blk * AT_B;
+    // scores S^T = K Q^T for both tokens, one K fragment read per (tile, k-step)
+    f32x4 s[2][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bf16x8 kf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[ks] = as_bf16x8(*(const u32x4*)(ks_ + (4 * t + ks) * 512 + lane * 8));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        s[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) s[u][t] = mfma16(kf[ks], qf[u][ks], s[u][t]);
+      }
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (blk >= b_first)   // blocks that hold a query position of the tile
+        attn_softmax<true>(s[u], o[u], m_run[u], l_run[u], kv0, pos[u], a.c, lane, pf[u]);
+      else
+        attn_softmax<false>(s[u], o[u], m_run[u], l_run[u], kv0, pos[u], a.c, lane, pf[u]);
+    }
+    // O^T += V^T P^T for both tokens, one V fragment read per (d-tile, k-step)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      bf16x8 vf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) vf[ks] = as_bf16x8(*(const u32x4*)(vs_ + (2 * mt + ks) * 512 + lane * 8));
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) o[u][mt] = mfma16(vf[ks], pf[u][ks], o[u][mt]);
+    }
+    // next block into the other slot (its readers finished at the last barrier)
+    if (blk + 1 <= b_last) {
+      store_block((blk + 1) & 1, st);
+      if (blk + 2 <= b_last) load_block(blk + 2, st);
+    }
+    __syncthreads();
+  }
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int hq = a.h_kv * AT_G;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (tok[u] >= a.n_q) continue;
+    float l = l_run[u];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / l;
+    uint16_t* orow = a.O + (((size_t)b * a.n_q + tok[u]) * hq + g * AT_G + r16) * AT_D;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const uint32_t w0 = pack_bf16x2(o[u][mt][0] * inv, o[u][mt][1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[u][mt][2] * inv, o[u][mt][3] * inv);
+      __builtin_nontemporal_store(u32x2{w0, w1}, (u32x2*)(orow + 16 * mt + 4 * grp));
+    }
+    if (a.lse && grp == 0)
+      __builtin_nontemporal_store((m_run[u] + fast_log2(l)) * kLn2,
+                                  a.lse + ((size_t)b * hq + g * AT_G + r16) * a.n_q + tok[u]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Decode: one workgroup (one wave) per (token, group, selected block).
 // ---------------------------------------------------------------------------
 // 8x8 transpose of bf16: in[r] holds 8 features of key r; out[q] gets feature
@@ -419,51 +571,49 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
   if (grp == 0) a.part_ml[prow * AT_G + r16] = make_float2(m_run, l_run);
 }
 
-// grid: x = h_kv, y = batch*n_q; 256 threads: head = tid/16, 8 features each.
-// Slots are folded four at a time so that their loads are in flight together.
-__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
-  const int g = blockIdx.x, bt = blockIdx.y;
+// grid: x = head within the group, y = h_kv, z = batch*n_q; 64 threads, two
+// features each.  Slots are folded eight at a time, their loads in flight
+// together; the weights rescale online when the running maximum moves.
+constexpr int MERGE_SLOTS = 8;
+__global__ void __launch_bounds__(64) attn_merge_kernel(AttnArgs a) {
+  const int h = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
   const int b = bt / a.n_q, t = bt % a.n_q;
   const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
   const int nsel = a.n_sel[row];
-  const int h = threadIdx.x >> 4, d0 = (threadIdx.x & 15) * 8;
-  float m = kNegInf, l = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsel; s0 += 4) {
-    float2 ml[4];
-    f32x4 lo[4], hi[4];
+  const int d0 = threadIdx.x * 2;
+  float m = kNegInf, l = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int s0 = 0; s0 < nsel; s0 += MERGE_SLOTS) {
+    float2 ml[MERGE_SLOTS], ov[MERGE_SLOTS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int sl = min(s0 + u, nsel - 1);
-      const size_t slot = row * a.budget + sl;
+    for (int u = 0; u < MERGE_SLOTS; ++u) {
+      const size_t slot = row * a.budget + min(s0 + u, nsel - 1);
       ml[u] = a.part_ml[slot * AT_G + h];
-      const float* po = a.part_o + (slot * AT_G + h) * AT_D + d0;
-      lo[u] = *(const f32x4*)po;
-      hi[u] = *(const f32x4*)(po + 4);
+      ov[u] = *(const float2*)(a.part_o + (slot * AT_G + h) * AT_D + d0);
     }
+    float mx = m;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < MERGE_SLOTS; ++u)
+      if (s0 + u < nsel) mx = fmaxf(mx, ml[u].x);
+    if (mx == kNegInf) continue;                 // nothing visible yet
+    const float wo = fast_exp2(m - mx);          // m == -inf gives 0
+    l *= wo;
+    acc0 *= wo;
+    acc1 *= wo;
+#pragma unroll
+    for (int u = 0; u < MERGE_SLOTS; ++u) {
       if (s0 + u >= nsel || ml[u].x == kNegInf) continue;
-      const float mn = fmaxf(m, ml[u].x);
-      const float wo = fast_exp2(m - mn), wn = fast_exp2(ml[u].x - mn);
-      l = l * wo + ml[u].y * wn;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[q] = acc[q] * wo + lo[u][q] * wn;
-        acc[4 + q] = acc[4 + q] * wo + hi[u][q] * wn;
-      }
-      m = mn;
+      const float wn = fast_exp2(ml[u].x - mx);
+      l += ml[u].y * wn;
+      acc0 += ov[u].x * wn;
+      acc1 += ov[u].y * wn;
     }
+    m = mx;
   }
   const float inv = 1.0f / l;
   const int hq = a.h_kv * AT_G;
   uint16_t* orow = a.O + (((size_t)b * a.n_q + t) * hq + g * AT_G + h) * AT_D + d0;
-  uint32_t w[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    w[q] = pack_bf16x2(acc[2 * q] * inv, acc[2 * q + 1] * inv);
-  *(u32x4*)orow = u32x4{w[0], w[1], w[2], w[3]};
-  if (a.lse && (threadIdx.x & 15) == 0)
+  *(uint32_t*)orow = pack_bf16x2(acc0 * inv, acc1 * inv);
+  if (a.lse && threadIdx.x == 0)
     a.lse[((size_t)b * hq + g * AT_G + h) * a.n_q + t] = (m + fast_log2(l)) * kLn2;
 }
 
@@ -640,8 +790,8 @@ hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, con
       a.part_ml = (float2*)((char*)ws + slots * AT_G * AT_D * sizeof(float));
       hipLaunchKernelGGL(attn_split_kernel, dim3(budget, p.h_kv, p.batch * p.n_q), dim3(64), 0,
                          stream, a);
-      hipLaunchKernelGGL(attn_merge_kernel, dim3(p.h_kv, p.batch * p.n_q), dim3(256), 0, stream,
-                         a);
+      hipLaunchKernelGGL(attn_merge_kernel, dim3(AT_G, p.h_kv, p.batch * p.n_q), dim3(64), 0,
+                         stream, a);
       return hipGetLastError();
     }
     const size_t pack = (size_t)p.batch * p.h_kv * a.n_blk * PACK_ELEMS;
@@ -652,12 +802,15 @@ hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, con
                        p.n_kv, a.n_blk, p.h_kv, kv_cap);
     const int total_qb = ((p.n_q + AT_B - 1) / AT_B) * p.batch * p.h_kv;
     dim3 grid(((total_qb + 7) / 8) * 8 * 16);
-    if (sparse && budget > 64)
+    if (sparse && budget > 64) {
       hipLaunchKernelGGL((attn_prefill_kernel<true, true>), grid, dim3(256), 0, stream, a);
-    else if (sparse)
+    } else if (sparse) {
       hipLaunchKernelGGL((attn_prefill_kernel<true, false>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_prefill_kernel<false, false>), grid, dim3(256), 0, stream, a);
+    } else {
+      const int dn_work = ((p.n_q + DN_TOK - 1) / DN_TOK) * p.batch * p.h_kv;
+      hipLaunchKernelGGL(attn_dense_kernel, dim3(((dn_work + 7) / 8) * 8), dim3(64 * DN_WAVES), 0,
+                         stream, a);
+    }
     return hipGetLastError();
   }
   GenericAttnArgs a;
