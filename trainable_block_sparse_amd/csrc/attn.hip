@@ -140,7 +140,8 @@ __device__ __forceinline__ void attn_scores(const bf16x8 (&qf)[4], const bf16x8 
   attn_softmax<DIAG>(s, o, m_run, l_run, kv0, p, c, lane, pf);
 }
 
-// Online softmax of one 64-key block given its raw scores s (S^T tiles).
+// Online softmax of one 64-key block given its raw scores s (S^T tiles); the
+// scale enters through the maximum and one fma per score in the exponent.
 template <bool DIAG>
 __device__ __forceinline__ void attn_softmax(f32x4 (&s)[4], f32x4 (&o)[8], float& m_run,
                                              float& l_run, int kv0, int p, float c, int lane,
@@ -151,7 +152,7 @@ __device__ __forceinline__ void attn_softmax(f32x4 (&s)[4], f32x4 (&o)[8], float
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float x = s[t][i] * c;
+      float x = s[t][i];
       if constexpr (DIAG) {
         const int key = kv0 + 32 * (t >> 1) + 8 * grp + 4 * (t & 1) + i;
         if (key > p) x = kNegInf;
@@ -159,6 +160,7 @@ __device__ __forceinline__ void attn_softmax(f32x4 (&s)[4], f32x4 (&o)[8], float
       s[t][i] = x;
       mx = fmaxf(mx, x);
     }
+  mx *= c;   // the maximum of the scaled scores (c > 0; -inf stays -inf)
   if (__ballot(mx > m_run + 8.0f)) {
     // (mx > m_run implies mx is finite)
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -181,8 +183,8 @@ __device__ __forceinline__ void attn_softmax(f32x4 (&s)[4], f32x4 (&o)[8], float
     for (int e = 0; e < 4; ++e) {
       const int t = 2 * ks + (e >> 1);
       const int i0 = 2 * (e & 1);
-      const float p0 = fast_exp2(s[t][i0] - mref);
-      const float p1 = fast_exp2(s[t][i0 + 1] - mref);
+      const float p0 = fast_exp2(__builtin_fmaf(s[t][i0], c, -mref));
+      const float p1 = fast_exp2(__builtin_fmaf(s[t][i0 + 1], c, -mref));
       l_run += p0 + p1;                      // fp32 sum: exact-to-fp32 LSE
       w[e] = pack_bf16x2(p0, p1);
     }
