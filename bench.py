@@ -123,7 +123,28 @@ class StageTimer:
         return {n: v / steps for n, v in self.ms.items()}
 
 
-def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None):
+def bench_pipelined(lp, Q, K, V, Kc1, O_ref, lse_ref, steps, warmup, n_chunks):
+    """The same prefill as a two-stream pipeline over query ranges (selection
+    of range i+1 beside attention of range i); checks it reproduces the serial
+    outputs bitwise."""
+    pipe = tbs.PrefillPipeline(lp, n_chunks)
+    O2, lse2 = torch.empty_like(O_ref), torch.empty_like(lse_ref)
+    for _ in range(warmup):
+        pipe.run(Q, K, V, Kc1, O2, lse2)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        pipe.run(Q, K, V, Kc1, O2, lse2)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"n_ranges": len(pipe.chunks), "ms_per_step": ms,
+            "tokens_per_s": lp.batch * lp.n_q / (ms / 1e3),
+            "same_output_as_serial": bool(torch.equal(O2, O_ref) and torch.equal(lse2, lse_ref))}
+
+
+def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None, pipeline_chunk=8192):
     log(f"[bench] {cfg.name}: generating inputs")
     x = make_inputs(cfg)
     dev = torch.device("cuda:0")
@@ -166,6 +187,9 @@ def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None):
                attn_flops=attention_flops(cfg, pos, bud))
     out["algo_tflops"] = (out["sel_flops_2pass"] + out["attn_flops"]) / (ms / 1e3) / 1e12
     out["frac_of_bf16_peak"] = out["algo_tflops"] / PEAK_BF16_TFLOPS
+    if pipeline_chunk and lp.batch == 1 and lp.n_q > pipeline_chunk:
+        out["pipelined"] = bench_pipelined(lp, Q, K, V, Kc1, O, lse, steps, warmup,
+                                           lp.n_q // pipeline_chunk)
     if with_dense:
         dsteps = dense_steps or max(1, steps // 2)
         ws_d = torch.empty(max(tbs.dense_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)

@@ -199,3 +199,30 @@ def test_extreme_logits_take_exact_pass():
     check_compress(res, x["k"], op)
     rep = check_rows(res, x, op, 0, {b: np.arange(n_kv) for b in range(batch)})
     _say(rep)
+
+
+def test_prefill_pipeline_matches_one_shot():
+    # the two-stream range pipeline computes every row exactly as the one-shot
+    # path: O and LSE bitwise equal, and both match the oracle
+    cfg = CONFIGS["prefill32k"]
+    n_kv = 2600
+    _say("case: prefill pipeline, n_kv", n_kv)
+    x = make_inputs(cfg, n_kv=n_kv, batch=1, seed=23)
+    lp, op = problems(cfg, n_kv=n_kv, batch=1)
+    ref = run_gpu_sparse(lp, x["q"], x["k"], x["v"])
+    dev = torch.device("cuda:0")
+    Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
+    Kc1 = torch.empty((1, lp.h_kv, tbs.n_kernels(lp), lp.d), dtype=Q.dtype, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((1, lp.h_q, lp.n_q), dtype=torch.float32, device=dev)
+    pipe = tbs.PrefillPipeline(lp, 3)
+    assert [c["r0"] for c in pipe.chunks] == [0, 896, 1728]
+    for _ in range(2):                  # a second run reuses every buffer
+        pipe.run(Q, K, V, Kc1, O, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(O.cpu(), ref["O"])
+    assert torch.equal(lse.cpu(), ref["lse"])
+    assert torch.equal(Kc1.cpu(), ref["Kc1"])
+    rows = sample_rows(n_kv, 40, np.random.default_rng(3), must=(0, 895, 896, 1727, 1728, 2599))
+    res = dict(ref, O=O.cpu(), lse=lse.cpu())
+    _say(check_rows(res, x, op, 0, {0: rows}))

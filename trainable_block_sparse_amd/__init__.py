@@ -263,3 +263,84 @@ def forward(prob: Problem, Q, K, V, Kc1=None, mode: str = "auto", stream=None) -
     O, lse = sparse_attn(prob, Q, K, V, idx, n_sel, stream=stream)
     out.update(Kc1=Kc1, S_cmp=S_cmp, idx=idx, n_sel=n_sel, O=O, lse=lse)
     return out
+
+
+class PrefillPipeline:
+    """Sparse prefill of one sequence as a two-stream pipeline over query chunks.
+
+    The query rows are split into ``n_chunks`` ranges on 64-token boundaries.
+    The selection of range i+1 (compressed scores and top-k: bound by the
+    matrix unit) is enqueued on one stream while the block-sparse attention of
+    range i (bound by the K/V gather) runs on another; an event per range
+    orders the two.  Each range is an ordinary call of the C ABI with
+    q_pos0/n_q/n_kv of that range, so every output row is computed exactly as
+    in the one-shot path (bitwise the same O and LSE).  Buffers and workspaces
+    are allocated once here; ``run`` allocates nothing.
+    """
+
+    def __init__(self, prob: Problem, n_chunks: int, device=None):
+        if prob.batch != 1:
+            raise ValueError("PrefillPipeline takes one sequence (batch == 1)")
+        if use_dense(prob):
+            raise ValueError("the dense switch applies: use dense_attn")
+        device = device or torch.device("cuda", torch.cuda.current_device())
+        self.prob = prob
+        n_q = prob.n_q
+        kv_cap = prob.kv_cap or prob.n_kv
+        self.n_c1 = n_kernels(prob)
+        c1_cap = prob.c1_cap or self.n_c1
+        cuts = sorted({0, n_q} | {min(n_q, round(n_q * i / n_chunks / prob.B) * prob.B)
+                                  for i in range(1, n_chunks)})
+        self.chunks = []
+        for r0, r1 in zip(cuts[:-1], cuts[1:]):
+            p = Problem(**{**prob.__dict__, "n_q": r1 - r0, "q_pos0": prob.q_pos0 + r0,
+                           "n_kv": prob.q_pos0 + r1, "kv_cap": kv_cap, "c1_cap": c1_cap})
+            self.chunks.append(dict(
+                p=p, r0=r0, r1=r1,
+                S=torch.empty((1, p.h_kv, p.n_q, n_blocks(p)), dtype=torch.float32,
+                              device=device),
+                idx=torch.empty((1, p.h_kv, p.n_q, budget(p)), dtype=torch.int32, device=device),
+                n_sel=torch.empty((1, p.h_kv, p.n_q), dtype=torch.int32, device=device),
+                lse=torch.empty((1, p.h_q, p.n_q), dtype=torch.float32, device=device),
+                ws_s=torch.empty(max(block_scores_workspace(p), 16), dtype=torch.uint8,
+                                 device=device),
+                ws_a=torch.empty(max(sparse_attn_workspace(p), 16), dtype=torch.uint8,
+                                 device=device),
+                ready=torch.cuda.Event()))
+        self.sel_stream = torch.cuda.Stream(device=device)
+        self.att_stream = torch.cuda.Stream(device=device)
+        self.done = torch.cuda.Event()
+
+    def run(self, Q, K, V, Kc1, O, lse=None, attn_events=None):
+        """Enqueue one prefill: compress, then per range selection and attention.
+        Both streams first wait for the caller's current stream; the caller's
+        stream then waits for the end.  With ``attn_events`` (a list of
+        (start, end) timing-event pairs, one per range) the attention launches
+        are bracketed on the attention stream."""
+        caller = torch.cuda.current_stream()
+        self.sel_stream.wait_stream(caller)
+        self.att_stream.wait_stream(caller)
+        prob, s_sel, s_att = self.prob, self.sel_stream, self.att_stream
+        # the previous run's attention has consumed every range's idx/n_sel
+        s_sel.wait_event(self.done)
+        compress_k(prob, K, Kc1, stream=s_sel)
+        for c in self.chunks:
+            p = c["p"]
+            block_scores(p, Q[:, c["r0"]:c["r1"]], Kc1, c["S"], c["ws_s"], stream=s_sel)
+            topk_select(p, c["S"], c["idx"], c["n_sel"], stream=s_sel)
+            c["ready"].record(s_sel)
+        for i, c in enumerate(self.chunks):
+            s_att.wait_event(c["ready"])
+            if attn_events is not None:
+                attn_events[i][0].record(s_att)
+            sparse_attn(c["p"], Q[:, c["r0"]:c["r1"]], K, V, c["idx"], c["n_sel"],
+                        O[:, c["r0"]:c["r1"]], c["lse"], c["ws_a"], stream=s_att)
+            if attn_events is not None:
+                attn_events[i][1].record(s_att)
+            if lse is not None:
+                with torch.cuda.stream(s_att):
+                    lse[:, :, c["r0"]:c["r1"]].copy_(c["lse"])
+        self.done.record(s_att)
+        caller.wait_stream(s_att)
+        caller.wait_stream(s_sel)
+        return O, lse
