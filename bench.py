@@ -334,6 +334,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the 128k and decode lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-pipeline", action="store_true",
+                    help="skip the two-stream range-pipeline record of the 128k prefill")
     ap.add_argument("--only", choices=["prefill32k", "prefill128k", "decode", "dense_switch",
                                        "copy"],
                     help="run one workload alone and print its record (profiling runs); "
@@ -363,12 +365,17 @@ def main():
         elif args.only == "dense_switch":
             rec = bench_dense_switch(c, args.steps, args.warmup)
         else:
-            rec = bench_prefill(c, args.steps, args.warmup, with_dense=not args.no_dense)
+            pipe = 0 if (args.no_pipeline or args.only == "prefill32k") else 8192
+            rec = bench_prefill(c, args.steps, args.warmup, with_dense=not args.no_dense,
+                                pipeline_chunk=pipe)
         print(json.dumps({"workload": args.only, **rec}), flush=True)
         return
 
     cfg = CONFIGS["prefill32k"]
-    main_res = bench_prefill(cfg, args.steps, args.warmup, with_dense=not args.no_dense)
+    # the headline is the one-shot path (one launch per kernel per step, as
+    # the rocprofv3 summaries see it); the 128k line adds the range pipeline
+    main_res = bench_prefill(cfg, args.steps, args.warmup, with_dense=not args.no_dense,
+                             pipeline_chunk=0)
     log(f"[bench] prefill32k: {main_res['ms_per_step']:.3f} ms/step, stages {main_res['stages_ms']}")
 
     # roofline of the dominant kernel
@@ -395,7 +402,7 @@ def main():
     if not args.no_extra:
         c3 = CONFIGS["prefill128k"]
         r3 = bench_prefill(c3, max(2, args.steps // 5), 1, with_dense=not args.no_dense,
-                           dense_steps=1)
+                           dense_steps=1, pipeline_chunk=0 if args.no_pipeline else 8192)
         extra["prefill128k"] = {k: v for k, v in r3.items()}
         log(f"[bench] prefill128k: {r3['ms_per_step']:.3f} ms/step")
         c4 = CONFIGS["decode"]
