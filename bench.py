@@ -5,7 +5,9 @@ Default workload (the headline line): MiniCPM-style GQA layer prefill at 32k
 tokens (b=1, n=32768, h_q=32, h_kv=2, d=128, bf16, B=64, l_C1=32, s_C1=16,
 l=5, s=4, N_init=1, N_local=2, k=16) on seeded synthetic inputs with planted
 needle blocks.  One step = the whole hot path: compress_k -> block_scores ->
-topk_select -> sparse_attn, inputs resident in HBM, outputs preallocated.
+topk_select -> sparse_attn (decode: compress append -> select_blocks, the
+scores with the top-k fused in -> sparse_attn), inputs resident in HBM,
+outputs preallocated.
 The same JSON line also carries the 128k prefill and the 16-sequence decode
 step (both secondary, fewer steps), the dense-attention time on the same
 input, the roofline of the dominant kernel, and the fp64 CPU oracle timed on a
@@ -224,15 +226,20 @@ def bench_decode(cfg, steps, warmup):
     nsel = torch.empty((lp.batch, lp.h_kv, 1), dtype=torch.int32, device=dev)
     O = torch.empty_like(Q)
     lse = torch.empty((lp.batch, lp.h_q, 1), dtype=torch.float32, device=dev)
-    ws_s = torch.empty(max(tbs.block_scores_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(max(tbs.select_blocks_workspace(lp), tbs.block_scores_workspace(lp), 16),
+                       dtype=torch.uint8, device=dev)
     ws_a = torch.empty(max(tbs.sparse_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    # the step: scores and top-k in one call (the top-k fused into the pooling
+    # kernel); S^cmp is not stored
     fns = [
         lambda: tbs.compress_k(lp, K, Kc1, c1_begin=n_prev, c1_end=n_c1),
-        lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s),
-        lambda: tbs.topk_select(lp, S, idx, nsel),
+        lambda: tbs.select_blocks(lp, Q, Kc1, None, idx, nsel, ws_s),
         lambda: tbs.sparse_attn(lp, Q, K, V, idx, nsel, O, lse, ws_a),
     ]
-    names = ["compress_append", "block_scores", "topk_select", "sparse_attn"]
+    names = ["compress_append", "select_blocks", "sparse_attn"]
+    # the same step with the separate score and top-k calls, for comparison
+    fns_sep = [fns[0], lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s),
+               lambda: tbs.topk_select(lp, S, idx, nsel), fns[2]]
     for _ in range(warmup):
         for fn in fns:
             fn()
@@ -266,9 +273,23 @@ def bench_decode(cfg, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
+    graph_sep = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_sep):
+        for fn in fns_sep:
+            fn()
+    for _ in range(warmup):
+        graph_sep.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        graph_sep.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    sep_ms = e0.elapsed_time(e1) / steps
     nbytes = decode_bytes(cfg, bud)
     out = dict(step_us=step_ms * 1e3, us_per_token=step_ms * 1e3 / cfg.batch,
                eager_step_us=eager_ms * 1e3, timing="HIP graph replay of the whole step",
+               separate_topk_step_us=sep_ms * 1e3,
                stages_us_eager={k: v * 1e3 for k, v in stage.items()}, algo_bytes=nbytes,
                algo_GBps=nbytes / (step_ms / 1e3) / 1e9)
     out["frac_of_hbm_peak"] = out["algo_GBps"] / PEAK_HBM_GBS

@@ -130,6 +130,25 @@ int infv2_block_scores(const infv2_problem* prob, const void* Q, const void* Kc1
 int infv2_topk_select(const infv2_problem* prob, const float* S_cmp, int32_t* idx,
                       int32_t* n_sel, void* stream);
 
+/* Stages 2-3 and the block selection in one call (the same definitions as
+ * infv2_block_scores followed by infv2_topk_select; OpenBMB blog,
+ * 高效Top-K实现, fuses the top-k into the score computation as well).  idx
+ * and n_sel are bitwise those of the two separate calls.  For decode-sized
+ * problems (few query tokens, k <= 32) the pooling kernel keeps the k best
+ * candidates of each group of 64 blocks and a small kernel merges those
+ * lists, so S^cmp need not be stored.
+ *   S_cmp : [batch][h_kv][n_q][n_blk] fp32 output as in infv2_block_scores,
+ *           or NULL when the caller does not need the scores (they then live
+ *           in the workspace where a path needs them).
+ *   idx, n_sel : outputs as in infv2_topk_select.
+ *   ws    : workspace of infv2_select_blocks_workspace(prob, S_cmp != NULL)
+ *           bytes; its contents need no initialisation and are not kept
+ *           between calls.  Calls that share a workspace must not overlap. */
+size_t infv2_select_blocks_workspace(const infv2_problem* prob, int with_scores);
+int infv2_select_blocks(const infv2_problem* prob, const void* Q, const void* Kc1,
+                        float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* Block-sparse attention (paperlayer.ai summary, A IMPLEMENTATION DETAIL):
  * for each query token and head, softmax attention over the keys
  * T(p) = {t <= p : floor(t/B) in I(p)}, returning O and the natural-log LSE.

@@ -106,9 +106,9 @@ def check_compress(res, k_cpu, op):
 
 
 def check_rows(res, x, op, q_pos0, rows_per_b, dense=False, check_scores=True,
-               Kc1_ref=None):
-    """Selection, S^cmp and outputs for the listed rows of each sequence.
-    Returns a small report dict."""
+               Kc1_ref=None, check_outputs=True):
+    """Selection, S^cmp and (unless check_outputs is false) O and LSE for the
+    listed rows of each sequence.  Returns a small report dict."""
     tol = TOL[op.io]
     n_kv = x["k"].shape[1]
     report = dict(rows=0, exempt=0, max_o=0.0, max_lse=0.0, max_scmp_rel=0.0)
@@ -144,6 +144,9 @@ def check_rows(res, x, op, q_pos0, rows_per_b, dense=False, check_scores=True,
                             rel = np.abs(s_gpu[fin] - s_ref[fin]) / np.abs(s_ref[fin])
                             report["max_scmp_rel"] = max(report["max_scmp_rel"], float(rel.max()))
                 sets.append(row_sets)
+        report["rows"] += len(rows)
+        if not check_outputs:
+            continue
         token_sets = [[orc.attended_tokens(sets[r][g], int(p), op) for g in range(op.h_kv)]
                       for r, p in enumerate(pos)]
         O64, lse = orc.attention_rows(Q[rows], K, V, token_sets, op)
@@ -156,7 +159,6 @@ def check_rows(res, x, op, q_pos0, rows_per_b, dense=False, check_scores=True,
         report["max_lse"] = max(report["max_lse"], err_l)
         assert err_o <= tol["o"], f"O max-abs {err_o:.3e} > {tol['o']}"
         assert err_l <= tol["lse"], f"LSE max-abs {err_l:.3e} > {tol['lse']}"
-        report["rows"] += len(rows)
     if check_scores and not dense:
         assert report["max_scmp_rel"] <= 1e-5, report
     return report

@@ -89,6 +89,8 @@ def test_calls_reject_null_and_misaligned_pointers_before_any_launch(L):
     assert L.infv2_compress_k(pc, 16, 32, 0, 10 ** 6, None) == tbs.INFV2_E_ARG
     assert L.infv2_topk_select(pc, None, 16, 16, None) == tbs.INFV2_E_ARG
     assert L.infv2_block_scores(pc, 16, 16, None, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_select_blocks(pc, 16, 16, None, None, 16, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_select_blocks(pc, 16, 16, 17, 16, 16, None, 0, None) == tbs.INFV2_E_ARG
     assert L.infv2_sparse_attn(pc, 16, 16, 16, 16, 16, None, None, None, 0, None) == tbs.INFV2_E_ARG
     assert L.infv2_dense_attn(pc, 16, 16, 16, 16, None, None, 0, None) == tbs.INFV2_E_ARG
     assert L.infv2_check_problem(None) == tbs.INFV2_E_ARG
@@ -104,8 +106,18 @@ def test_workspace_sizes_and_errors(L):
     assert need_a >= 16 * 2 * 19 * 16 * 128 * 4
     assert L.infv2_sparse_attn(pc, 16, 16, 16, 16, 16, 16, None, 16, 0, None) \
         == tbs.INFV2_E_WORKSPACE
+    # fused selection: the scores' workspace, then 16 candidate keys per
+    # chunk of 64 blocks and row
+    need_s = L.infv2_select_blocks_workspace(pc, 0)
+    assert need_s == L.infv2_select_blocks_workspace(pc, 1)
+    assert need_s >= need + 16 * 2 * 32 * 16 * 8
+    assert L.infv2_select_blocks(pc, 16, 16, None, 16, 16, 16, need_s - 1, None) \
+        == tbs.INFV2_E_WORKSPACE
     pre = _prob(n_q=32768, n_kv=32768)
     assert L.infv2_block_scores_workspace(ctypes.byref(pre.to_c())) == 0
+    # prefill selection keeps S^cmp in the workspace unless the caller takes it
+    assert L.infv2_select_blocks_workspace(ctypes.byref(pre.to_c()), 1) == 0
+    assert L.infv2_select_blocks_workspace(ctypes.byref(pre.to_c()), 0) == 2 * 32768 * 512 * 4
     # packed K and V: 2 tensors x h_kv x (blocks x B) keys x d x 2 bytes
     assert L.infv2_dense_attn_workspace(ctypes.byref(pre.to_c())) == 2 * 2 * 32768 * 128 * 2
     for s in (0, -1, -2, -3, -4, 7):

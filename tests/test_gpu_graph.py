@@ -55,3 +55,33 @@ def test_decode_step_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for k, t in dict(idx=idx, nsel=nsel, O=O, lse=lse).items():
             assert torch.equal(t, ref[k]), f"replay {rep}: {k} differs"
+
+
+def test_fused_selection_graph_replay_matches_eager():
+    # the fused selection's row counters are reset by a kernel of the same
+    # call, so replays need no memset between them
+    cfg = CONFIGS["decode"]
+    n_kv, batch = 20000, 3
+    print("case: fused selection graph replay", n_kv, batch, flush=True)
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=78)
+    lp, _ = problems(cfg, n_kv=n_kv, batch=batch)
+    dev = torch.device("cuda:0")
+    Q, K = x["q"].to(dev), x["k"].to(dev)
+    Kc1 = tbs.compress_k(lp, K)
+    bud = tbs.budget(lp)
+    idx = torch.empty((batch, lp.h_kv, 1, bud), dtype=torch.int32, device=dev)
+    nsel = torch.empty((batch, lp.h_kv, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(tbs.select_blocks_workspace(lp), dtype=torch.uint8, device=dev)
+    S = tbs.block_scores(lp, Q, Kc1)
+    idx_ref, nsel_ref = tbs.topk_select(lp, S)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tbs.select_blocks(lp, Q, Kc1, None, idx, nsel, ws)
+    for rep in range(4):
+        idx.zero_()
+        nsel.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx_ref), f"replay {rep}: idx differs"
+        assert torch.equal(nsel, nsel_ref), f"replay {rep}: n_sel differs"

@@ -226,3 +226,19 @@ def test_prefill_pipeline_matches_one_shot():
     rows = sample_rows(n_kv, 40, np.random.default_rng(3), must=(0, 895, 896, 1727, 1728, 2599))
     res = dict(ref, O=O.cpu(), lse=lse.cpu())
     _say(check_rows(res, x, op, 0, {0: rows}))
+
+
+def test_k_zero_selects_init_and_local_blocks_only():
+    cfg = CONFIGS["decode"]
+    n_kv, batch = 4000, 2
+    _say("case: decode k=0", n_kv, batch)
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=31)
+    lp, op = problems(cfg, n_kv=n_kv, batch=batch, k=0)
+    res = run_gpu_sparse(lp, x["q"], x["k"], x["v"])
+    b_p = (n_kv - 1) // 64
+    for b in range(batch):
+        for g in range(lp.h_kv):
+            n = int(res["n_sel"][b, g, 0])
+            assert res["idx"][b, g, 0, :n].tolist() == [0, b_p - 1, b_p]
+    rep = check_rows(res, x, op, n_kv - 1, {b: np.array([0]) for b in range(batch)})
+    _say(rep)

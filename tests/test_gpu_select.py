@@ -1,0 +1,140 @@
+"""infv2_select_blocks (scores + top-k in one call) against the two separate
+calls, bitwise, and against the fp64 oracle on decode steps.  Decode shapes
+take the fused pooling/top-k kernel; prefill shapes take the two-kernel
+fallback inside the same entry point."""
+import numpy as np
+import pytest
+import torch
+
+import trainable_block_sparse_amd as tbs
+from synth import CONFIGS, make_inputs
+
+from parity import check_compress, check_rows, problems
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _selection_inputs(cfg, n_kv, batch, n_q, seed, k=None):
+    """Keys from the config's generator; the last n_q positions query them
+    (decode configs hold one query row, extra rows are seeded normals)."""
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=seed)
+    q0 = n_kv - n_q
+    lp, op = problems(cfg, n_kv=n_kv, batch=batch, n_q=n_q, q_pos0=q0, k=k)
+    dev = torch.device("cuda:0")
+    if x["q"].shape[1] == n_q:
+        qh = x["q"]
+    elif x["q"].shape[1] == n_kv:
+        qh = x["q"][:, q0:].contiguous()
+    else:
+        gen = torch.Generator().manual_seed(seed)
+        qh = torch.randn((batch, n_q) + tuple(x["q"].shape[2:]), generator=gen)
+        qh = qh.to(x["q"].dtype)
+    Q = qh.to(dev)
+    K = x["k"].to(dev)
+    Kc1 = tbs.compress_k(lp, K)
+    return x, lp, op, Q, Kc1
+
+
+def _separate(lp, Q, Kc1):
+    S = tbs.block_scores(lp, Q, Kc1)
+    idx, n_sel = tbs.topk_select(lp, S)
+    return S, idx, n_sel
+
+
+@pytest.mark.parametrize("n_kv,batch,n_q,k", [
+    (131072, 2, 1, 16),     # 32 chunks of 64 blocks per row
+    (131072, 1, 4, 32),     # k = 32: 32 x 32 candidate keys
+    (40000, 3, 2, 16),      # ragged last chunk
+    (5000, 2, 3, 16),       # fewer chunks (2) than k: several keys per list
+    (600, 2, 1, 16),        # one chunk, 10 blocks: fewer candidates than k
+    (100, 1, 4, 16),        # early tokens with no candidate at all
+    (33, 1, 1, 16),         # one kernel
+    (20, 1, 1, 16),         # no kernel yet
+    (70000, 2, 1, 8),
+    (70000, 1, 1, 0),       # k = 0: init and local blocks only
+])
+def test_fused_selection_equals_separate_calls(n_kv, batch, n_q, k):
+    cfg = CONFIGS["decode"]
+    _say(f"case: fused selection n_kv={n_kv} batch={batch} n_q={n_q} k={k}")
+    x, lp, op, Q, Kc1 = _selection_inputs(cfg, n_kv, batch, n_q, seed=3 + n_kv + k, k=k)
+    S_ref, idx_ref, n_ref = _separate(lp, Q, Kc1)
+    idx, n_sel = tbs.select_blocks(lp, Q, Kc1)
+    S2 = torch.full_like(S_ref, float("nan"))
+    idx2, n_sel2 = tbs.select_blocks(lp, Q, Kc1, S_cmp=S2)
+    torch.cuda.synchronize()
+    assert torch.equal(n_sel, n_ref)
+    assert torch.equal(idx, idx_ref)
+    assert torch.equal(n_sel2, n_ref) and torch.equal(idx2, idx_ref)
+    b_last = (n_kv - 1) // lp.B
+    assert torch.equal(torch.nan_to_num(S2[..., :b_last + 1]),
+                       torch.nan_to_num(S_ref[..., :b_last + 1]))
+
+
+def test_fused_selection_ties_pick_lowest_blocks():
+    # Q = 0: every candidate scores the same, so the k lowest candidates win
+    cfg = CONFIGS["decode"]
+    n_kv, n_q = 20000, 2
+    _say("case: fused selection ties", n_kv)
+    x, lp, op, Q, Kc1 = _selection_inputs(cfg, n_kv, 1, n_q, seed=11)
+    Q.zero_()
+    idx, n_sel = tbs.select_blocks(lp, Q, Kc1)
+    _, idx_ref, n_ref = _separate(lp, Q, Kc1)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_ref) and torch.equal(n_sel, n_ref)
+    for t in range(n_q):
+        b_p = (n_kv - n_q + t) // lp.B
+        want = [0] + list(range(1, 1 + lp.k)) + [b_p - 1, b_p]
+        for g in range(lp.h_kv):
+            n = int(n_sel[0, g, t])
+            assert idx[0, g, t, :n].tolist() == want
+
+
+def test_fused_selection_matches_oracle_decode():
+    cfg = CONFIGS["decode"]
+    n_kv, batch = 9000, 2
+    _say("case: fused selection vs oracle", n_kv, batch)
+    x, lp, op, Q, Kc1 = _selection_inputs(cfg, n_kv, batch, 1, seed=77)
+    S = torch.full((batch, lp.h_kv, 1, tbs.n_blocks(lp)), float("nan"), device=Q.device)
+    idx, n_sel = tbs.select_blocks(lp, Q, Kc1, S_cmp=S)
+    torch.cuda.synchronize()
+    res = dict(Kc1=Kc1.cpu(), S_cmp=S.cpu(), idx=idx.cpu(), n_sel=n_sel.cpu())
+    check_compress(res, x["k"], op)
+    rep = check_rows(res, x, op, n_kv - 1, {b: np.array([0]) for b in range(batch)},
+                     check_outputs=False)
+    _say(rep)
+
+
+def test_select_blocks_prefill_shape_uses_two_kernel_path():
+    cfg = CONFIGS["prefill32k"]
+    n_kv = 2300
+    _say("case: select_blocks prefill", n_kv)
+    x, lp, op, Q, Kc1 = _selection_inputs(cfg, n_kv, 1, n_kv, seed=8)
+    S_ref, idx_ref, n_ref = _separate(lp, Q, Kc1)
+    idx, n_sel = tbs.select_blocks(lp, Q, Kc1)          # scores in the workspace
+    S2 = torch.empty_like(S_ref)
+    idx2, n_sel2 = tbs.select_blocks(lp, Q, Kc1, S_cmp=S2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_ref) and torch.equal(n_sel, n_ref)
+    assert torch.equal(idx2, idx_ref) and torch.equal(n_sel2, n_ref)
+
+
+def test_fused_selection_repeated_calls_share_workspace():
+    # the row counters live in the workspace and are reset by each call
+    cfg = CONFIGS["decode"]
+    dev = torch.device("cuda:0")
+    _say("case: fused selection workspace reuse")
+    ws = None
+    for n_kv in (30000, 12000, 30000):
+        x, lp, op, Q, Kc1 = _selection_inputs(cfg, n_kv, 2, 1, seed=n_kv)
+        need = tbs.select_blocks_workspace(lp)
+        if ws is None:
+            ws = torch.full((need,), 0xAB, dtype=torch.uint8, device=dev)
+        assert need <= ws.numel()
+        _, idx_ref, n_ref = _separate(lp, Q, Kc1)
+        idx, n_sel = tbs.select_blocks(lp, Q, Kc1, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, idx_ref) and torch.equal(n_sel, n_ref)

@@ -193,6 +193,17 @@ def test_topk_brute_force_subsets():
         assert got == (init & set(range(b_p + 1))) | local | wins[0]
 
 
+def test_topk_k_zero_keeps_init_and_local_only():
+    # k = 0 leaves the union of the initial and local blocks, whatever the scores
+    prob = Problem(G=1, h_kv=1, d=4, k=0)
+    rng = np.random.default_rng(9)
+    for p in (0, 64, 130, 5000):
+        b_p = p // 64
+        got = select_blocks(rng.random(b_p + 1), p, prob)
+        want = sorted({0} | set(range(max(0, b_p - 1), b_p + 1)))
+        np.testing.assert_array_equal(got, want)
+
+
 def test_topk_planted_block_and_init_local_always_in():
     rng = np.random.default_rng(8)
     prob = Problem(G=1, h_kv=1, d=4, k=16)

@@ -21,7 +21,8 @@ INFV2_BF16, INFV2_F32 = 0, 1
 EXPORTED = (
     "infv2_n_kernels", "infv2_n_blocks", "infv2_budget", "infv2_use_dense",
     "infv2_check_problem", "infv2_compress_k", "infv2_block_scores_workspace",
-    "infv2_block_scores", "infv2_topk_select", "infv2_sparse_attn_workspace",
+    "infv2_block_scores", "infv2_topk_select", "infv2_select_blocks_workspace",
+    "infv2_select_blocks", "infv2_sparse_attn_workspace",
     "infv2_sparse_attn", "infv2_dense_attn_workspace", "infv2_dense_attn",
     "infv2_status_string", "infv2_last_error",
 )
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "infv2_block_scores_workspace": (sz, [P]),
             "infv2_block_scores": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
             "infv2_topk_select": (ctypes.c_int, [P, vp, vp, vp, vp]),
+            "infv2_select_blocks_workspace": (sz, [P, ctypes.c_int]),
+            "infv2_select_blocks": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_sparse_attn_workspace": (sz, [P]),
             "infv2_sparse_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_dense_attn_workspace": (sz, [P]),
@@ -204,6 +207,31 @@ def topk_select(prob: Problem, S_cmp: torch.Tensor, idx: torch.Tensor | None = N
                             device=S_cmp.device)
     _check(lib().infv2_topk_select(ctypes.byref(prob.to_c()), _ptr(S_cmp), _ptr(idx), _ptr(n_sel),
                                    _stream(stream)))
+    return idx, n_sel
+
+
+def select_blocks_workspace(prob: Problem, with_scores: bool = False) -> int:
+    return lib().infv2_select_blocks_workspace(ctypes.byref(prob.to_c()), int(bool(with_scores)))
+
+
+def select_blocks(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
+                  S_cmp: torch.Tensor | None = None, idx: torch.Tensor | None = None,
+                  n_sel: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                  stream=None):
+    """Q, K^C1 -> (idx, n_sel) as block_scores + topk_select; S^cmp is written
+    only when a tensor is passed for it."""
+    if idx is None:
+        idx = torch.empty((prob.batch, prob.h_kv, prob.n_q, budget(prob)), dtype=torch.int32,
+                          device=Q.device)
+    if n_sel is None:
+        n_sel = torch.empty((prob.batch, prob.h_kv, prob.n_q), dtype=torch.int32,
+                            device=Q.device)
+    need = select_blocks_workspace(prob, S_cmp is not None)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    _check(lib().infv2_select_blocks(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1), _ptr(S_cmp),
+                                     _ptr(idx), _ptr(n_sel), _ptr(ws),
+                                     ws.numel() if ws is not None else 0, _stream(stream)))
     return idx, n_sel
 
 

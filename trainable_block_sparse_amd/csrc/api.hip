@@ -20,6 +20,12 @@ hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void
                                float scale, hipStream_t stream);
 hipError_t launch_topk(const infv2_problem& p, const float* S_cmp, int32_t* idx, int32_t* n_sel,
                        int n_blk, int budget, hipStream_t stream);
+bool select_fused_shape(const infv2_problem& p, int n_c1);
+size_t select_fused_workspace(const infv2_problem& p, int n_c1);
+hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const void* Kc1,
+                               float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, int n_c1,
+                               int n_blk, int64_t c1_cap, float scale, int budget,
+                               hipStream_t stream);
 bool attn_fast_shape(const infv2_problem& p);
 size_t attn_workspace(const infv2_problem& p, int budget, bool sparse);
 hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, const void* V,
@@ -43,6 +49,8 @@ int fail(int status, const char* fmt, ...) {
   g_last_error = buf;
   return status;
 }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int ok() {
   g_last_error.clear();
@@ -187,6 +195,46 @@ int infv2_topk_select(const infv2_problem* p, const float* S_cmp, int32_t* idx, 
   return hip_status(
       launch_topk(*p, S_cmp, idx, n_sel, n_blk_of(*p), budget_of(*p), (hipStream_t)stream),
       "infv2_topk_select");
+}
+
+size_t infv2_select_blocks_workspace(const infv2_problem* p, int with_scores) {
+  if (check(p) != INFV2_OK) return 0;
+  const int n_c1 = n_c1_of(*p);
+  const size_t base = scores_workspace(*p, n_c1);
+  if (select_fused_shape(*p, n_c1)) return align256(base) + select_fused_workspace(*p, n_c1);
+  if (with_scores) return base;
+  const size_t rows = (size_t)p->batch * p->n_q * p->h_kv;
+  return align256(base) + rows * (size_t)n_blk_of(*p) * sizeof(float);
+}
+
+int infv2_select_blocks(const infv2_problem* p, const void* Q, const void* Kc1, float* S_cmp,
+                        int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(Q);
+  CHECK_PTR(idx);
+  CHECK_PTR(n_sel);
+  if (S_cmp && !aligned16(S_cmp)) return fail(INFV2_E_ARG, "S_cmp is not 16-byte aligned");
+  const int n_c1 = n_c1_of(*p);
+  if (n_c1 > 0) CHECK_PTR(Kc1);
+  const size_t need = infv2_select_blocks_workspace(p, S_cmp != nullptr);
+  if (need) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need)
+      return fail(INFV2_E_WORKSPACE, "select_blocks workspace %zu < %zu bytes", ws_bytes, need);
+  }
+  const hipStream_t s = (hipStream_t)stream;
+  if (select_fused_shape(*p, n_c1)) {
+    return hip_status(launch_select_fused(*p, Q, Kc1, S_cmp, idx, n_sel, ws, n_c1, n_blk_of(*p),
+                                          c1_cap_of(*p), scale_of(*p), budget_of(*p), s),
+                      "infv2_select_blocks");
+  }
+  float* S = S_cmp ? S_cmp
+                   : (float*)((char*)ws + align256(scores_workspace(*p, n_c1)));
+  hipError_t e = launch_block_scores(*p, Q, Kc1, S, ws, n_c1, n_blk_of(*p), c1_cap_of(*p),
+                                     scale_of(*p), s);
+  if (e == hipSuccess) e = launch_topk(*p, S, idx, n_sel, n_blk_of(*p), budget_of(*p), s);
+  return hip_status(e, "infv2_select_blocks");
 }
 
 size_t infv2_sparse_attn_workspace(const infv2_problem* p) {

@@ -623,6 +623,12 @@ struct SplitArgs {
   float* S_cmp;
   float* logits;    // [batch*n_q][h_kv][16][n_c1p]  (z*c, -inf when invisible)
   float2* part;     // [batch*n_q][h_kv][nch][16]    (chunk max, chunk sum)
+  // fused top-k (select_blocks), row = (b*h_kv + g)*n_q + t: per-chunk
+  // candidate lists ([rows][nch][kc], null when not fused) and the outputs
+  uint64_t* cand;
+  int32_t* idx;
+  int32_t* n_sel;
+  int k, N_init, N_local, budget, kc;
   int n_q, q_pos0, h_kv, n_c1, n_c1p, n_blk, nch;
   int64_t c1_cap;
   float c;
@@ -648,8 +654,10 @@ __global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     // kernels past the last one are clamped to it; they are never visible
+    // (with no kernel at all nothing is read: every logit is -inf)
     const int j = min(jw + 4 * i + (lane >> 4), a.n_c1 - 1);
-    v[i] = *(const u32x4*)(kc1 + (size_t)j * SEL_D + 8 * (lane & 15));
+    v[i] = a.n_c1 > 0 ? *(const u32x4*)(kc1 + (size_t)j * SEL_D + 8 * (lane & 15))
+                      : u32x4{0u, 0u, 0u, 0u};
   }
   // A operand: Q rows = heads (lane & 15), k = d
   bf16x8 qf[4];
@@ -732,39 +740,50 @@ __global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
   }
 }
 
-// grid as above; 256 threads = 256 kernels of the chunk (+ the carry kernel).
-__global__ void __launch_bounds__(256) scores_split_pool_kernel(SplitArgs a) {
-  __shared__ float Mh[SEL_G], Wh[SEL_G];
-  __shared__ float sh[SPLIT_CK + 1];
-  const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+// Each head's softmax reference and weight from the per-chunk (max, sum)
+// partials of a row: Mh[h] = the running maximum, Wh[h] = 1 / sum of
+// exp2(z - Mh[h]).  Threads 0..255: 16 per head, each folding every 16th
+// chunk, then a 16-lane merge.  Every product-sum is an explicit fma, so
+// all kernels that call this round identically.
+__device__ __forceinline__ void head_lse_weights(const SplitArgs& a, int g, int bt, int tid,
+                                                 float* Mh, float* Wh) {
+  const int h = tid >> 4, q = tid & 15;
+  const float2* pr = a.part + ((size_t)bt * a.h_kv + g) * a.nch * SEL_G + h;
+  float m = kNegInf, s = 0.f;
+  for (int c = q; c < a.nch; c += 16) {
+    const float2 v = pr[(size_t)c * SEL_G];
+    if (v.x == kNegInf) continue;
+    if (v.x > m) { s = __builtin_fmaf(s, fast_exp2(m - v.x), v.y); m = v.x; }
+    else s = __builtin_fmaf(v.y, fast_exp2(v.x - m), s);
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const float mo = __shfl_xor(m, o, 64), so = __shfl_xor(s, o, 64);
+    const float mn = fmaxf(m, mo);
+    if (mn != kNegInf) {
+      const float e = __builtin_fmaf(s, fast_exp2(m - mn), 0.f);
+      s = __builtin_fmaf(so, fast_exp2(mo - mn), e);
+    }
+    m = mn;
+  }
+  if (q == 0) {
+    Mh[h] = (m == kNegInf) ? 0.f : m;
+    Wh[h] = s > 0.f ? 1.0f / s : 0.f;
+  }
+}
+
+// The pool step for one chunk: merges the per-chunk (max, sum) partials of
+// every head into the exact log-sum-exp, forms S^shared for the chunk's 256
+// kernels (+ the carry kernel) and max-pools them into its 64 blocks; thread
+// bb < 64 returns block chunk*64 + bb's score (-inf when not causal).  S^cmp
+// is written when S_cmp is not null.  256 threads.
+__device__ __forceinline__ float split_pool_chunk(const SplitArgs& a, int chunk, int g, int bt,
+                                                  float* Mh, float* Wh, float* sh) {
   const int b = bt / a.n_q, t = bt % a.n_q;
   const int p = a.q_pos0 + t;
   const int jmax = last_visible_kernel(p);
   const int b_p = p >> 6;
-  {
-    // merge the per-chunk (max, sum) partials of every head: 16 threads per
-    // head, each folding every 16th chunk, then a 16-lane reduction
-    const int h = threadIdx.x >> 4, q = threadIdx.x & 15;
-    const float2* pr = a.part + ((size_t)bt * a.h_kv + g) * a.nch * SEL_G + h;
-    float m = kNegInf, s = 0.f;
-    for (int c = q; c < a.nch; c += 16) {
-      const float2 v = pr[(size_t)c * SEL_G];
-      if (v.x == kNegInf) continue;
-      if (v.x > m) { s = s * fast_exp2(m - v.x) + v.y; m = v.x; }
-      else s += v.y * fast_exp2(v.x - m);
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float mo = __shfl_xor(m, o, 64), so = __shfl_xor(s, o, 64);
-      const float mn = fmaxf(m, mo);
-      if (mn != kNegInf) s = s * fast_exp2(m - mn) + so * fast_exp2(mo - mn);
-      m = mn;
-    }
-    if (q == 0) {
-      Mh[h] = (m == kNegInf) ? 0.f : m;
-      Wh[h] = s > 0.f ? 1.0f / s : 0.f;
-    }
-  }
+  head_lse_weights(a, g, bt, threadIdx.x, Mh, Wh);
   __syncthreads();
   const float* lrow = a.logits + ((size_t)bt * a.h_kv + g) * SEL_G * a.n_c1p;
   const int j0 = chunk * SPLIT_CK;
@@ -780,19 +799,157 @@ __global__ void __launch_bounds__(256) scores_split_pool_kernel(SplitArgs a) {
     sh[x] = v;
   }
   __syncthreads();
-  float* row = a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_blk;
+  float* row = a.S_cmp ? a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_blk : nullptr;
   const int nblk_chunk = SPLIT_CK / 4;
+  float out = kNegInf;
   if (threadIdx.x < nblk_chunk) {
     const int bb = threadIdx.x;
     const int blk = chunk * nblk_chunk + bb;
     float v = sh[4 * bb];
 #pragma unroll
     for (int q = 1; q < 5; ++q) v = fmaxf(v, sh[4 * bb + q]);
-    if (blk <= b_p) row[blk] = v;
+    if (row && blk <= b_p) row[blk] = v;
+    out = v;
   }
-  if (chunk == a.nch - 1)
+  if (row && chunk == a.nch - 1)
     for (int blk = a.nch * nblk_chunk + threadIdx.x; blk <= b_p; blk += blockDim.x)
       row[blk] = kNegInf;
+  return out;
+}
+
+// grid as above; 256 threads = 256 kernels of the chunk (+ the carry kernel).
+// With the top-k fused in (a.cand set), wave 0 also writes the chunk's kc
+// best candidate blocks, sorted, as 64-bit keys: order-preserving score bits
+// << 32 | ~blk, unique, and at equal scores the lower block ranks higher;
+// 0 marks "no candidate".
+__global__ void __launch_bounds__(256) scores_split_pool_kernel(SplitArgs a) {
+  __shared__ float Mh[SEL_G], Wh[SEL_G];
+  __shared__ float sh[SPLIT_CK + 1];
+  const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+  const float v = split_pool_chunk(a, chunk, g, bt, Mh, Wh, sh);
+  if (a.cand == nullptr || threadIdx.x >= 64) return;     // whole waves leave
+  const int lane = threadIdx.x;
+  const int b = bt / a.n_q, t = bt % a.n_q;
+  const int b_p = (a.q_pos0 + t) >> 6;
+  const int init_hi = min(a.N_init, b_p + 1);
+  const int loc_lo = max(0, b_p - a.N_local + 1);
+  const int blk = chunk * 64 + lane;
+  const bool cand = blk >= init_hi && blk < loc_lo;
+  const uint64_t key = cand ? ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(~(uint32_t)blk) : 0ull;
+  const uint64_t sorted = wave_sort_desc<uint64_t>(key, lane);
+  const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+  if (lane < a.kc) a.cand[(row * a.nch + chunk) * a.kc + lane] = sorted;
+}
+
+// The top-k of the fused selection, one workgroup per row (token, group),
+// from the sorted per-chunk candidate lists of the pool kernel:
+//   * the kk-th best key K* is bounded from below by the kk-th best of the
+//     first r = ceil(kk / nch) keys of every list (those nch*r >= kk keys are
+//     distinct, so at least kk keys reach the bound); the keys at or above the
+//     bound (usually a few more than kk) are sorted by one wave;
+//   * the selection is init/local plus the candidates with key >= K*, written
+//     in ascending block order with -1 padding.
+constexpr int MERGE_THREADS = 256;
+constexpr int MERGE_WAVES = MERGE_THREADS / 64;
+constexpr int SELECT_MAX_CHUNKS = 64;      // rows of up to 64 * 256 kernels
+constexpr int SELECT_MAX_KC = 32;          // k <= 32
+constexpr int SELECT_MAX_KEYS = 1024;      // chunks * k <= 1024
+__global__ void __launch_bounds__(MERGE_THREADS) scores_select_merge_kernel(SplitArgs a) {
+  __shared__ uint64_t keys[SELECT_MAX_KEYS];
+  __shared__ uint64_t pick[64];
+  __shared__ uint32_t selbits[SELECT_MAX_CHUNKS * 2 + 2];   // blocks 0 .. 64 * nch
+  __shared__ uint32_t count_s;
+  __shared__ uint64_t kstar_s, bound_s;
+  __shared__ int wave_cnt[MERGE_WAVES];
+  const int g = blockIdx.x, bt = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = bt / a.n_q, t = bt % a.n_q;
+  const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+  const int b_p = (a.q_pos0 + t) >> 6;
+  const int nb = b_p + 1;
+  const int init_hi = min(a.N_init, nb);
+  const int loc_lo = max(0, b_p - a.N_local + 1);
+  const int ncand = max(0, loc_lo - init_hi);
+  const int kk = min(a.k, ncand);
+  const int nch = a.nch;
+  const int nkeys = nch * a.kc;
+  const uint64_t* rlist = a.cand + row * nkeys;
+  for (int i = tid; i < nkeys; i += MERGE_THREADS) keys[i] = rlist[i];
+  for (int i = tid; i < SELECT_MAX_CHUNKS * 2 + 2; i += MERGE_THREADS) selbits[i] = 0u;
+  if (tid < 64) pick[tid] = 0ull;
+  if (tid == 0) count_s = 0u;
+  __syncthreads();
+  uint64_t kstar = 1ull;   // keys >= kstar are selected; every candidate key is >= 1
+  if (kk > 0 && kk < ncand) {
+    const int r = (kk + nch - 1) / nch;   // nch * r <= 64 as kk <= 32, nch <= 64
+    if (wave == 0) {
+      const uint64_t e = lane < nch * r ? keys[(lane / r) * a.kc + lane % r] : 0ull;
+      const uint64_t sorted = wave_sort_desc<uint64_t>(e, lane);
+      if (lane == kk - 1) bound_s = sorted > 1ull ? sorted : 1ull;
+    }
+    __syncthreads();
+    const uint64_t bound = bound_s;
+    for (int i = tid; i < nkeys; i += MERGE_THREADS) {
+      const uint64_t kv = keys[i];
+      if (kv >= bound) {
+        const uint32_t pos = atomicAdd(&count_s, 1u);
+        if (pos < 64) pick[pos] = kv;
+      }
+    }
+    __syncthreads();
+    if (count_s <= 64) {
+      if (wave == 0) {
+        const uint64_t sorted = wave_sort_desc<uint64_t>(pick[lane], lane);
+        if (lane == kk - 1) kstar_s = sorted;
+      }
+    } else {
+      // many keys at or above the bound: rank each against every key
+      for (int i = tid; i < nkeys; i += MERGE_THREADS) {
+        const uint64_t kv = keys[i];
+        if (kv < bound) continue;
+        int above = 0;
+        for (int j = 0; j < nkeys; ++j) above += keys[j] > kv ? 1 : 0;
+        if (above == kk - 1) kstar_s = kv;
+      }
+    }
+    __syncthreads();
+    kstar = kstar_s;
+  }
+  // selection bitmap: init/local blocks and the candidates with key >= K*
+  for (int blk = tid; blk < nb; blk += MERGE_THREADS)
+    if (blk < init_hi || blk >= loc_lo) atomicOr(&selbits[blk >> 5], 1u << (blk & 31));
+  if (kk > 0)
+    for (int i = tid; i < nkeys; i += MERGE_THREADS) {
+      const uint64_t kv = keys[i];
+      if (kv != 0ull && kv >= kstar) {
+        const uint32_t blk = ~(uint32_t)kv;
+        atomicOr(&selbits[blk >> 5], 1u << (blk & 31));
+      }
+    }
+  __syncthreads();
+  // ascending compaction: thread i takes bitmap word i (blocks 32i..32i+31)
+  const int nwords = (nb + 31) >> 5;
+  const uint32_t word = tid < nwords ? selbits[tid] : 0u;
+  const int cnt = __popc(word);
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wave_cnt[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < MERGE_WAVES; ++w) {
+    base += w < wave ? wave_cnt[w] : 0;
+    total += wave_cnt[w];
+  }
+  int pos = base + incl - cnt;
+  int32_t* out = a.idx + row * a.budget;
+  for (uint32_t wv = word; wv; wv &= wv - 1) out[pos++] = tid * 32 + __builtin_ctz(wv);
+  for (int i = total + tid; i < a.budget; i += MERGE_THREADS) out[i] = -1;
+  if (tid == 0) a.n_sel[row] = total;
 }
 
 // ---------------------------------------------------------------------------
@@ -913,26 +1070,68 @@ size_t scores_generic_lds(const infv2_problem& p, int n_c1) {
   return (size_t)(n_c1 + p.G + 1) * sizeof(double);
 }
 
+static SplitArgs split_args(const infv2_problem& p, const void* Q, const void* Kc1, float* S_cmp,
+                            void* ws, int n_c1, int n_blk, int64_t c1_cap, float scale) {
+  SplitArgs a = {};
+  a.Q = (const uint16_t*)Q;
+  a.Kc1 = (const uint16_t*)Kc1;
+  a.S_cmp = S_cmp;
+  a.n_q = p.n_q;
+  a.q_pos0 = p.q_pos0;
+  a.h_kv = p.h_kv;
+  a.n_c1 = n_c1;
+  a.n_c1p = (n_c1 + 63) & ~63;
+  a.n_blk = n_blk;
+  a.nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
+  a.c1_cap = c1_cap;
+  a.c = scale * kLog2e;
+  const size_t rows = (size_t)p.batch * p.n_q * p.h_kv;
+  a.logits = (float*)ws;
+  a.part = (float2*)((char*)ws + rows * SEL_G * (size_t)a.n_c1p * sizeof(float));
+  return a;
+}
+
+// The fused selection (candidate lists from the pool kernel, then a per-row
+// merge) serves the split shapes with k <= 32 and at most 1024 candidate keys
+// per row.
+bool select_fused_shape(const infv2_problem& p, int n_c1) {
+  if (!scores_use_split(p)) return false;
+  const int nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
+  return p.k <= SELECT_MAX_KC && nch <= SELECT_MAX_CHUNKS && nch * p.k <= SELECT_MAX_KEYS;
+}
+
+// workspace beyond scores_workspace() rounded up to 256 bytes: the lists
+size_t select_fused_workspace(const infv2_problem& p, int n_c1) {
+  const int nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
+  return (size_t)p.batch * p.n_q * p.h_kv * nch * p.k * sizeof(uint64_t);
+}
+
+hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const void* Kc1,
+                               float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, int n_c1,
+                               int n_blk, int64_t c1_cap, float scale, int budget,
+                               hipStream_t stream) {
+  SplitArgs a = split_args(p, Q, Kc1, S_cmp, ws, n_c1, n_blk, c1_cap, scale);
+  a.cand = (uint64_t*)((char*)ws + ((scores_workspace(p, n_c1) + 255) & ~(size_t)255));
+  a.idx = idx;
+  a.n_sel = n_sel;
+  a.k = p.k;
+  a.kc = p.k;
+  a.N_init = p.N_init;
+  a.N_local = p.N_local;
+  a.budget = budget;
+  const dim3 grid(a.nch, p.h_kv, p.batch * p.n_q);
+  hipLaunchKernelGGL(scores_split_logits_kernel, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(scores_split_pool_kernel, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(scores_select_merge_kernel, dim3(p.h_kv, p.batch * p.n_q),
+                     dim3(MERGE_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void* Kc1,
                                float* S_cmp, void* ws, int n_c1, int n_blk, int64_t c1_cap,
                                float scale, hipStream_t stream) {
   if (scores_use_split(p)) {
-    SplitArgs a;
-    a.Q = (const uint16_t*)Q;
-    a.Kc1 = (const uint16_t*)Kc1;
-    a.S_cmp = S_cmp;
-    a.n_q = p.n_q;
-    a.q_pos0 = p.q_pos0;
-    a.h_kv = p.h_kv;
-    a.n_c1 = n_c1;
-    a.n_c1p = (n_c1 + 63) & ~63;
-    a.n_blk = n_blk;
-    a.nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
-    a.c1_cap = c1_cap;
-    a.c = scale * kLog2e;
-    const size_t rows = (size_t)p.batch * p.n_q * p.h_kv;
-    a.logits = (float*)ws;
-    a.part = (float2*)((char*)ws + rows * SEL_G * (size_t)a.n_c1p * sizeof(float));
+    SplitArgs a = split_args(p, Q, Kc1, S_cmp, ws, n_c1, n_blk, c1_cap, scale);
     dim3 grid(a.nch, p.h_kv, p.batch * p.n_q);
     hipLaunchKernelGGL(scores_split_logits_kernel, grid, dim3(256), 0, stream, a);
     hipLaunchKernelGGL(scores_split_pool_kernel, grid, dim3(256), 0, stream, a);

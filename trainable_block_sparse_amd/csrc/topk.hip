@@ -24,65 +24,6 @@
 
 namespace infv2 {
 
-__device__ __forceinline__ uint32_t ordered_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
-}
-
-// value of lane (lane ^ S), S = 1, 2, 4, 8, 16, 32
-template <int S>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
-  if constexpr (S == 1) {
-    return dpp_u<0xB1>(x);                            // quad_perm [1,0,3,2]
-  } else if constexpr (S == 2) {
-    return dpp_u<0x4E>(x);                            // quad_perm [2,3,0,1]
-  } else if constexpr (S == 4) {
-    const uint32_t up = dpp_u<0x104>(x);              // row_shl:4  (lane + 4)
-    const uint32_t dn = dpp_u<0x114>(x);              // row_shr:4  (lane - 4)
-    return (lane & 4) ? dn : up;
-  } else if constexpr (S == 8) {
-    return dpp_u<0x128>(x);                           // row_ror:8 == lane ^ 8 within a row
-  } else if constexpr (S == 16) {
-    const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane & 16) ? sw[0] : sw[1];
-  } else {
-    const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane & 32) ? sw[0] : sw[1];
-  }
-}
-
-template <int SIZE, int S>
-__device__ __forceinline__ uint32_t bitonic_step(uint32_t v, int lane) {
-  const uint32_t o = xor_lane<S>(v, lane);
-  const bool keep_max = ((lane & SIZE) == 0) == ((lane & S) == 0);
-  return keep_max ? max(v, o) : min(v, o);
-}
-
-// Bitonic sort across the 64 lanes, descending (lane 0 holds the largest).
-__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v, int lane) {
-  v = bitonic_step<2, 1>(v, lane);
-  v = bitonic_step<4, 2>(v, lane);  v = bitonic_step<4, 1>(v, lane);
-  v = bitonic_step<8, 4>(v, lane);  v = bitonic_step<8, 2>(v, lane);  v = bitonic_step<8, 1>(v, lane);
-  v = bitonic_step<16, 8>(v, lane); v = bitonic_step<16, 4>(v, lane);
-  v = bitonic_step<16, 2>(v, lane); v = bitonic_step<16, 1>(v, lane);
-  v = bitonic_step<32, 16>(v, lane); v = bitonic_step<32, 8>(v, lane); v = bitonic_step<32, 4>(v, lane);
-  v = bitonic_step<32, 2>(v, lane);  v = bitonic_step<32, 1>(v, lane);
-  v = bitonic_step<64, 32>(v, lane); v = bitonic_step<64, 16>(v, lane); v = bitonic_step<64, 8>(v, lane);
-  v = bitonic_step<64, 4>(v, lane);  v = bitonic_step<64, 2>(v, lane);  v = bitonic_step<64, 1>(v, lane);
-  return v;
-}
-
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 struct TopkArgs {
   const float* S_cmp;
   int32_t* idx;
@@ -161,7 +102,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
       } else {
         for (int i = 0; i < niter; ++i) lmax = max(lmax, key_at(i));
       }
-      const uint32_t sorted = wave_sort_desc(lmax, lane);
+      const uint32_t sorted = wave_sort_desc<uint32_t>(lmax, lane);
       const uint32_t k0 = (uint32_t)__builtin_amdgcn_readlane((int)sorted, kk - 1);
       int cnt = 0;
       if constexpr (NI > 0) {
@@ -172,27 +113,29 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
       }
       const int total = wave_sum_i(cnt);
       if (total <= 64) {
-        int pre = cnt;                        // exclusive prefix of cnt over lanes
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int v = __shfl_up(pre, o, 64);
-          if (lane >= o) pre += v;
-        }
-        pre -= cnt;
+        // gather the keys >= k0, one per lane: positions by ballot and
+        // count of set bits below this lane
         gather[lane] = 0u;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        int base = 0;
+        auto put = [&](uint32_t kv) {
+          const bool hit = kv >= k0;
+          const uint64_t bal = __ballot(hit);
+          if (hit) gather[base + (int)__popcll(bal & ((1ull << lane) - 1ull))] = kv;
+          base += (int)__popcll(bal);
+        };
         if constexpr (NI > 0) {
 #pragma unroll
-          for (int i = 0; i < NI; ++i) if (kr[i] >= k0) gather[pre++] = kr[i];
+          for (int i = 0; i < NI; ++i) put(kr[i]);
         } else {
-          for (int i = 0; i < niter; ++i) { const uint32_t kv = key_at(i); if (kv >= k0) gather[pre++] = kv; }
+          for (int i = 0; i < niter; ++i) put(key_at(i));
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint32_t s2 = wave_sort_desc(gather[lane], lane);
+        const uint32_t s2 = wave_sort_desc<uint32_t>(gather[lane], lane);
         sstar = (uint32_t)__builtin_amdgcn_readlane((int)s2, kk - 1);
       } else {
         sstar = bisect(k0);                   // count(>= k0) >= kk holds
@@ -222,7 +165,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
     const bool eq = cand && !all && kv == sstar;
     const uint64_t eq_ballot = __ballot(eq);
     const int eq_rank = (int)__popcll(eq_ballot & below);
-    const bool sel = fixed || (cand && (all || kv > sstar || (eq && eq_rank < eq_left)));
+    const bool sel = fixed || (cand && kk > 0 && (all || kv > sstar || (eq && eq_rank < eq_left)));
     eq_left -= (int)__popcll(eq_ballot);
     const uint64_t ballot = __ballot(sel);
     const int pos = written + (int)__popcll(ballot & below);
