@@ -67,11 +67,16 @@ typedef struct infv2_problem {
   float scale;               /* softmax scale; 0 selects 1/sqrt(d)             */
   int64_t kv_cap;            /* token rows allocated in K and V; 0 -> n_kv     */
   int64_t c1_cap;            /* kernel rows allocated in K^C1; 0 -> n_C1       */
+  int64_t c2_cap;            /* coarse kernel rows in K^C2; 0 -> n_C2          */
+  int32_t lse_approx;        /* 1: estimate the stage-1 softmax normaliser from
+                                coarse kernels (see infv2_compress_k2); 0: exact */
 } infv2_problem;
 
 /* Derived sizes.  n_C1 = floor((n_kv - l_C1)/s_C1) + 1 complete kernels
- * (0 if n_kv < l_C1); n_blk = ceil(n_kv / B); budget = N_init + N_local + k. */
+ * (0 if n_kv < l_C1); n_C2 the same for the coarse kernels (l_C2 = 4 l_C1,
+ * s_C2 = 4 s_C1); n_blk = ceil(n_kv / B); budget = N_init + N_local + k. */
 int32_t infv2_n_kernels(const infv2_problem* prob);
+int32_t infv2_n_coarse_kernels(const infv2_problem* prob);
 int32_t infv2_n_blocks(const infv2_problem* prob);
 int32_t infv2_budget(const infv2_problem* prob);
 
@@ -98,6 +103,16 @@ int infv2_check_problem(const infv2_problem* prob);
 int infv2_compress_k(const infv2_problem* prob, const void* K, void* Kc1,
                      int32_t c1_begin, int32_t c1_end, void* stream);
 
+/* Coarse keys for the LSE approximation (papernotes note, 关键设计 4; OpenBMB
+ * blog, 高效Top-K实现): K^C2[b][g][j][:] = (1/l_C2) * sum_{u<l_C2}
+ * K[b][j*s_C2+u][g][:] with l_C2 = 4 l_C1 and s_C2 = 4 s_C1, for coarse
+ * kernels j in [c2_begin, c2_end); exact sum, one rounding, as for K^C1.
+ *   K   : [batch][kv_cap][h_kv][d]   (input)
+ *   Kc2 : [batch][h_kv][c2_cap][d]   (output rows c2_begin..c2_end-1 only)
+ * Requires 0 <= c2_begin <= c2_end <= n_C2 <= c2_cap. */
+int infv2_compress_k2(const infv2_problem* prob, const void* K, void* Kc2,
+                      int32_t c2_begin, int32_t c2_end, void* stream);
+
 /* Stages 2-3 with the exact two-pass log-sum-exp (papernotes note, 关键设计 3
  * and 4; OpenBMB blog, 高效Top-K实现).  For query token t (position p), group g:
  *   z[h][j]     = scale * Q[b][t][h][:] . K^C1[b][g][j][:]   for visible j,
@@ -107,8 +122,15 @@ int infv2_compress_k(const infv2_problem* prob, const void* K, void* Kc1,
  *   S^shared[j] = sum over the G heads of g of S^C1[h][j]   (kept on chip);
  *   S^cmp[blk]  = max of S^shared over the visible kernels that intersect
  *                 block blk (-inf when there is none).
+ * With prob->lse_approx the normaliser is the coarse estimate instead (the
+ * same pages, LSE approximation): lse[h] = log sum over the visible coarse
+ * kernels j2 (j2*s_C2 + l_C2 - 1 <= p) of exp(scale * Q . K^C2[j2])
+ * + ln(s_C2/s_C1); a token that sees no coarse kernel keeps the exact lse.
+ * S^C1 is then exp(z - lse) in fp32 (+inf beyond the fp32 range).
  *   Q     : [batch][n_q][h_q][d]
  *   Kc1   : [batch][h_kv][c1_cap][d]  (rows 0..n_C1-1 valid)
+ *   Kc2   : [batch][h_kv][c2_cap][d]  (rows 0..n_C2-1 valid) with
+ *           lse_approx, else ignored (may be NULL)
  *   S_cmp : [batch][h_kv][n_q][n_blk] fp32 (output).  Entries for blocks
  *           0..floor(p/B) are written; entries after the query's own block are
  *           left untouched.
@@ -116,7 +138,8 @@ int infv2_compress_k(const infv2_problem* prob, const void* K, void* Kc1,
  *           NULL when that size is 0). */
 size_t infv2_block_scores_workspace(const infv2_problem* prob);
 int infv2_block_scores(const infv2_problem* prob, const void* Q, const void* Kc1,
-                       float* S_cmp, void* ws, size_t ws_bytes, void* stream);
+                       const void* Kc2, float* S_cmp, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Block selection (papernotes note, 关键设计 2; OpenBMB blog, Top-K块共享):
  *   I(p) = I_init  u  I_local(p)  u  top-k(p),
@@ -137,6 +160,7 @@ int infv2_topk_select(const infv2_problem* prob, const float* S_cmp, int32_t* id
  * problems (few query tokens, k <= 32) the pooling kernel keeps the k best
  * candidates of each group of 64 blocks and a small kernel merges those
  * lists, so S^cmp need not be stored.
+ *   Kc2   : as in infv2_block_scores (with lse_approx).
  *   S_cmp : [batch][h_kv][n_q][n_blk] fp32 output as in infv2_block_scores,
  *           or NULL when the caller does not need the scores (they then live
  *           in the workspace where a path needs them).
@@ -146,8 +170,8 @@ int infv2_topk_select(const infv2_problem* prob, const float* S_cmp, int32_t* id
  *           between calls.  Calls that share a workspace must not overlap. */
 size_t infv2_select_blocks_workspace(const infv2_problem* prob, int with_scores);
 int infv2_select_blocks(const infv2_problem* prob, const void* Q, const void* Kc1,
-                        float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws,
-                        size_t ws_bytes, void* stream);
+                        const void* Kc2, float* S_cmp, int32_t* idx, int32_t* n_sel,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Block-sparse attention (paperlayer.ai summary, A IMPLEMENTATION DETAIL):
  * for each query token and head, softmax attention over the keys

@@ -24,7 +24,7 @@ TOL = {"bf16": dict(o=2e-2, lse=1e-3), "f32": dict(o=1e-4, lse=1e-5)}
 EXEMPT_REL = 1e-6
 
 
-def problems(cfg, n_kv=None, batch=None, n_q=None, q_pos0=None, k=None):
+def problems(cfg, n_kv=None, batch=None, n_q=None, q_pos0=None, k=None, lse_approx=False):
     """(library Problem, oracle Problem) for a config variant."""
     n_kv = cfg.n_kv if n_kv is None else n_kv
     batch = cfg.batch if batch is None else batch
@@ -35,9 +35,11 @@ def problems(cfg, n_kv=None, batch=None, n_q=None, q_pos0=None, k=None):
     k = cfg.k if k is None else k
     lp = tbs.Problem(batch=batch, n_q=n_q, n_kv=n_kv, h_kv=cfg.h_kv, G=cfg.G, d=cfg.d,
                      q_pos0=q_pos0, B=cfg.B, l_C1=cfg.l_C1, s_C1=cfg.s_C1, l=cfg.l, s=cfg.s,
-                     k=k, N_init=cfg.N_init, N_local=cfg.N_local, dtype=cfg.io)
+                     k=k, N_init=cfg.N_init, N_local=cfg.N_local, dtype=cfg.io,
+                     lse_approx=lse_approx)
     op = orc.Problem(G=cfg.G, h_kv=cfg.h_kv, d=cfg.d, B=cfg.B, l_C1=cfg.l_C1, s_C1=cfg.s_C1,
-                     l=cfg.l, s=cfg.s, k=k, N_init=cfg.N_init, N_local=cfg.N_local, io=cfg.io)
+                     l=cfg.l, s=cfg.s, k=k, N_init=cfg.N_init, N_local=cfg.N_local, io=cfg.io,
+                     lse_approx=lse_approx)
     return lp, op
 
 
@@ -46,16 +48,21 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def run_gpu_sparse(lp, q, k, v):
-    """The sparse path through the C ABI, every intermediate kept."""
+    """The sparse path through the C ABI, every intermediate kept (with the
+    LSE approximation, the coarse keys too)."""
     dev = torch.device("cuda:0")
     Q, K, V = q.to(dev), k.to(dev), v.to(dev)
     Kc1 = tbs.compress_k(lp, K)
-    S = tbs.block_scores(lp, Q, Kc1)
+    Kc2 = tbs.compress_k2(lp, K) if lp.lse_approx else None
+    S = tbs.block_scores(lp, Q, Kc1, Kc2=Kc2)
     idx, n_sel = tbs.topk_select(lp, S)
     O, lse = tbs.sparse_attn(lp, Q, K, V, idx, n_sel)
     torch.cuda.synchronize()
-    return dict(Kc1=Kc1.cpu(), S_cmp=S.cpu(), idx=idx.cpu(), n_sel=n_sel.cpu(), O=O.cpu(),
-                lse=lse.cpu())
+    out = dict(Kc1=Kc1.cpu(), S_cmp=S.cpu(), idx=idx.cpu(), n_sel=n_sel.cpu(), O=O.cpu(),
+               lse=lse.cpu())
+    if Kc2 is not None:
+        out["Kc2"] = Kc2.cpu()
+    return out
 
 
 def run_gpu_dense(lp, q, k, v):
@@ -96,12 +103,16 @@ def compare_sets(gpu, ref, S_cmp_ref, p, op):
 
 
 def check_compress(res, k_cpu, op):
-    """K^C1 bit-exact against the oracle; returns the oracle's K^C1 per
-    sequence ({b: [h_kv, n_C1, d]}) for the selection checks."""
+    """K^C1 (and K^C2 when the result holds it) bit-exact against the oracle;
+    returns the oracle's K^C1 per sequence ({b: [h_kv, n_C1, d]})."""
     n_c1 = orc.n_kernels(k_cpu.shape[1], op.l_C1, op.s_C1)
     ref = orc.compress_k(to_f64(k_cpu), op)
     got = to_f64(res["Kc1"][:, :, :n_c1])
     np.testing.assert_array_equal(got, ref)
+    if "Kc2" in res:
+        n_c2 = orc.n_coarse_kernels(k_cpu.shape[1], op)
+        ref2 = orc.compress_k2(to_f64(k_cpu), op)
+        np.testing.assert_array_equal(to_f64(res["Kc2"][:, :, :n_c2]), ref2)
     return {b: ref[b] for b in range(ref.shape[0])}
 
 
@@ -122,7 +133,8 @@ def check_rows(res, x, op, q_pos0, rows_per_b, dense=False, check_scores=True,
             sets = [[np.arange(p // op.B + 1) for _ in range(op.h_kv)] for p in pos]
         else:
             Kc1 = orc.compress_k(K[None], op)[0] if Kc1_ref is None else Kc1_ref[b]
-            _, _, S_ref = orc.selection_scores(Q[rows], Kc1, pos, n_kv, op)
+            Kc2 = orc.compress_k2(K[None], op)[0] if op.lse_approx else None
+            _, _, S_ref = orc.selection_scores(Q[rows], Kc1, pos, n_kv, op, Kc2=Kc2)
             sets = []
             for r, (t, p) in enumerate(zip(rows, pos)):
                 row_sets = []

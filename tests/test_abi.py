@@ -51,6 +51,9 @@ def test_derived_sizes(L):
     assert tbs.budget(p) == 19
     assert tbs.n_kernels(_prob(n_kv=31, n_q=31)) == 0
     assert tbs.n_kernels(_prob(n_kv=32, n_q=32)) == 1
+    assert tbs.n_coarse_kernels(_prob(n_kv=127, n_q=127)) == 0
+    assert tbs.n_coarse_kernels(_prob(n_kv=128, n_q=128)) == 1
+    assert tbs.n_coarse_kernels(_prob(n_kv=131072, n_q=1, q_pos0=131071)) == 2047
 
 
 def test_dense_switch_rule(L):
@@ -70,6 +73,8 @@ def test_dense_switch_rule(L):
     (dict(N_local=0), tbs.INFV2_E_ARG),
     (dict(scale=-1.0), tbs.INFV2_E_ARG),
     (dict(kv_cap=100), tbs.INFV2_E_ARG),
+    (dict(lse_approx=True), 0),
+    (dict(lse_approx=True, c2_cap=10), tbs.INFV2_E_ARG),                 # < n_C2 = 63
     (dict(l_C1=24, l=5, s=4), tbs.INFV2_E_UNSUPPORTED),  # not a power of two
     (dict(d=260), tbs.INFV2_E_UNSUPPORTED),
     (dict(dtype="f32", G=4, d=64), 0),
@@ -88,9 +93,18 @@ def test_calls_reject_null_and_misaligned_pointers_before_any_launch(L):
     assert b"aligned" in L.infv2_last_error()
     assert L.infv2_compress_k(pc, 16, 32, 0, 10 ** 6, None) == tbs.INFV2_E_ARG
     assert L.infv2_topk_select(pc, None, 16, 16, None) == tbs.INFV2_E_ARG
-    assert L.infv2_block_scores(pc, 16, 16, None, None, 0, None) == tbs.INFV2_E_ARG
-    assert L.infv2_select_blocks(pc, 16, 16, None, None, 16, None, 0, None) == tbs.INFV2_E_ARG
-    assert L.infv2_select_blocks(pc, 16, 16, 17, 16, 16, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_block_scores(pc, 16, 16, None, None, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_select_blocks(pc, 16, 16, None, None, None, 16, None, 0, None) \
+        == tbs.INFV2_E_ARG
+    assert L.infv2_select_blocks(pc, 16, 16, None, 17, 16, 16, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_compress_k2(pc, 16, None, 0, 1, None) == tbs.INFV2_E_ARG
+    # the LSE approximation needs the coarse keys
+    pa = _prob(lse_approx=True)
+    pac = ctypes.byref(pa.to_c())
+    assert L.infv2_block_scores(pac, 16, 16, None, 16, None, 0, None) == tbs.INFV2_E_ARG
+    assert b"Kc2" in L.infv2_last_error()
+    assert L.infv2_compress_k2(pac, 16, 32, 0, tbs.n_coarse_kernels(pa) + 1, None) \
+        == tbs.INFV2_E_ARG
     assert L.infv2_sparse_attn(pc, 16, 16, 16, 16, 16, None, None, None, 0, None) == tbs.INFV2_E_ARG
     assert L.infv2_dense_attn(pc, 16, 16, 16, 16, None, None, 0, None) == tbs.INFV2_E_ARG
     assert L.infv2_check_problem(None) == tbs.INFV2_E_ARG
@@ -101,7 +115,7 @@ def test_workspace_sizes_and_errors(L):
     pc = ctypes.byref(dec.to_c())
     need = L.infv2_block_scores_workspace(pc)
     assert need >= 16 * 2 * 16 * 8191 * 4
-    assert L.infv2_block_scores(pc, 16, 16, 16, 16, need - 1, None) == tbs.INFV2_E_WORKSPACE
+    assert L.infv2_block_scores(pc, 16, 16, None, 16, 16, need - 1, None) == tbs.INFV2_E_WORKSPACE
     need_a = L.infv2_sparse_attn_workspace(pc)
     assert need_a >= 16 * 2 * 19 * 16 * 128 * 4
     assert L.infv2_sparse_attn(pc, 16, 16, 16, 16, 16, 16, None, 16, 0, None) \
@@ -111,8 +125,13 @@ def test_workspace_sizes_and_errors(L):
     need_s = L.infv2_select_blocks_workspace(pc, 0)
     assert need_s == L.infv2_select_blocks_workspace(pc, 1)
     assert need_s >= need + 16 * 2 * 32 * 16 * 8
-    assert L.infv2_select_blocks(pc, 16, 16, None, 16, 16, 16, need_s - 1, None) \
+    assert L.infv2_select_blocks(pc, 16, 16, None, None, 16, 16, 16, need_s - 1, None) \
         == tbs.INFV2_E_WORKSPACE
+    # the approximation's split path keeps only the coarse partials: 8 chunks
+    # of 256 coarse kernels x 16 heads x (max, sum) per row
+    dec_a = _prob(batch=16, n_q=1, q_pos0=131071, n_kv=131072, lse_approx=True)
+    assert tbs.n_coarse_kernels(dec_a) == 2047
+    assert L.infv2_block_scores_workspace(ctypes.byref(dec_a.to_c())) == 16 * 2 * 8 * 16 * 8
     pre = _prob(n_q=32768, n_kv=32768)
     assert L.infv2_block_scores_workspace(ctypes.byref(pre.to_c())) == 0
     # prefill selection keeps S^cmp in the workspace unless the caller takes it

@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_PKG, "libinfv2.so")
 INFV2_OK, INFV2_E_ARG, INFV2_E_UNSUPPORTED, INFV2_E_WORKSPACE, INFV2_E_HIP = 0, -1, -2, -3, -4
 INFV2_BF16, INFV2_F32 = 0, 1
 EXPORTED = (
-    "infv2_n_kernels", "infv2_n_blocks", "infv2_budget", "infv2_use_dense",
-    "infv2_check_problem", "infv2_compress_k", "infv2_block_scores_workspace",
+    "infv2_n_kernels", "infv2_n_coarse_kernels", "infv2_n_blocks", "infv2_budget",
+    "infv2_use_dense", "infv2_check_problem", "infv2_compress_k", "infv2_compress_k2",
+    "infv2_block_scores_workspace",
     "infv2_block_scores", "infv2_topk_select", "infv2_select_blocks_workspace",
     "infv2_select_blocks", "infv2_sparse_attn_workspace",
     "infv2_sparse_attn", "infv2_dense_attn_workspace", "infv2_dense_attn",
@@ -36,7 +37,7 @@ class _Problem(ctypes.Structure):
         ("s_C1", ctypes.c_int32), ("l", ctypes.c_int32), ("s", ctypes.c_int32),
         ("k", ctypes.c_int32), ("N_init", ctypes.c_int32), ("N_local", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("kv_cap", ctypes.c_int64),
-        ("c1_cap", ctypes.c_int64),
+        ("c1_cap", ctypes.c_int64), ("c2_cap", ctypes.c_int64), ("lse_approx", ctypes.c_int32),
     ]
 
 
@@ -62,6 +63,8 @@ class Problem:
     scale: float = 0.0
     kv_cap: int = 0
     c1_cap: int = 0
+    c2_cap: int = 0
+    lse_approx: bool = False
 
     @property
     def h_q(self) -> int:
@@ -71,7 +74,7 @@ class Problem:
         return _Problem(self.batch, self.n_q, self.q_pos0, self.n_kv, self.h_kv, self.G, self.d,
                         self.B, self.l_C1, self.s_C1, self.l, self.s, self.k, self.N_init,
                         self.N_local, INFV2_BF16 if self.dtype == "bf16" else INFV2_F32,
-                        self.scale, self.kv_cap, self.c1_cap)
+                        self.scale, self.kv_cap, self.c1_cap, self.c2_cap, int(self.lse_approx))
 
 
 class Infv2Error(RuntimeError):
@@ -94,15 +97,17 @@ def lib() -> ctypes.CDLL:
         P = ctypes.POINTER(_Problem)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         sig = {
-            "infv2_n_kernels": (i32, [P]), "infv2_n_blocks": (i32, [P]),
+            "infv2_n_kernels": (i32, [P]), "infv2_n_coarse_kernels": (i32, [P]),
+            "infv2_n_blocks": (i32, [P]),
             "infv2_budget": (i32, [P]), "infv2_use_dense": (ctypes.c_int, [P]),
             "infv2_check_problem": (ctypes.c_int, [P]),
             "infv2_compress_k": (ctypes.c_int, [P, vp, vp, i32, i32, vp]),
+            "infv2_compress_k2": (ctypes.c_int, [P, vp, vp, i32, i32, vp]),
             "infv2_block_scores_workspace": (sz, [P]),
-            "infv2_block_scores": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
+            "infv2_block_scores": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_topk_select": (ctypes.c_int, [P, vp, vp, vp, vp]),
             "infv2_select_blocks_workspace": (sz, [P, ctypes.c_int]),
-            "infv2_select_blocks": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "infv2_select_blocks": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_sparse_attn_workspace": (sz, [P]),
             "infv2_sparse_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_dense_attn_workspace": (sz, [P]),
@@ -135,6 +140,10 @@ def _stream(stream=None) -> int:
 
 def n_kernels(prob: Problem) -> int:
     return lib().infv2_n_kernels(ctypes.byref(prob.to_c()))
+
+
+def n_coarse_kernels(prob: Problem) -> int:
+    return lib().infv2_n_coarse_kernels(ctypes.byref(prob.to_c()))
 
 
 def n_blocks(prob: Problem) -> int:
@@ -176,22 +185,38 @@ def compress_k(prob: Problem, K: torch.Tensor, Kc1: torch.Tensor | None = None,
     return Kc1
 
 
+def compress_k2(prob: Problem, K: torch.Tensor, Kc2: torch.Tensor | None = None,
+                c2_begin: int = 0, c2_end: int | None = None, stream=None) -> torch.Tensor:
+    """K [b, kv_cap, h_kv, d] -> K^C2 [b, h_kv, c2_cap, d] (rows c2_begin..c2_end-1),
+    the coarse keys of the LSE approximation."""
+    n_c2 = n_coarse_kernels(prob)
+    if Kc2 is None:
+        cap = prob.c2_cap or n_c2
+        Kc2 = torch.empty((prob.batch, prob.h_kv, max(cap, 1), prob.d), dtype=K.dtype,
+                          device=K.device)
+    c2_end = n_c2 if c2_end is None else c2_end
+    _check(lib().infv2_compress_k2(ctypes.byref(prob.to_c()), _ptr(K), _ptr(Kc2), c2_begin,
+                                   c2_end, _stream(stream)))
+    return Kc2
+
+
 def block_scores_workspace(prob: Problem) -> int:
     return lib().infv2_block_scores_workspace(ctypes.byref(prob.to_c()))
 
 
 def block_scores(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
                  S_cmp: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-                 stream=None) -> torch.Tensor:
-    """Q, K^C1 -> S^cmp [b, h_kv, n_q, n_blk] fp32 (blocks after floor(p/B) untouched)."""
+                 stream=None, Kc2: torch.Tensor | None = None) -> torch.Tensor:
+    """Q, K^C1 (and K^C2 with prob.lse_approx) -> S^cmp [b, h_kv, n_q, n_blk]
+    fp32 (blocks after floor(p/B) untouched)."""
     if S_cmp is None:
         S_cmp = torch.full((prob.batch, prob.h_kv, prob.n_q, n_blocks(prob)), float("nan"),
                            dtype=torch.float32, device=Q.device)
     need = block_scores_workspace(prob)
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _check(lib().infv2_block_scores(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1), _ptr(S_cmp),
-                                    _ptr(ws), ws.numel() if ws is not None else 0,
+    _check(lib().infv2_block_scores(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1), _ptr(Kc2),
+                                    _ptr(S_cmp), _ptr(ws), ws.numel() if ws is not None else 0,
                                     _stream(stream)))
     return S_cmp
 
@@ -217,9 +242,9 @@ def select_blocks_workspace(prob: Problem, with_scores: bool = False) -> int:
 def select_blocks(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
                   S_cmp: torch.Tensor | None = None, idx: torch.Tensor | None = None,
                   n_sel: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-                  stream=None):
-    """Q, K^C1 -> (idx, n_sel) as block_scores + topk_select; S^cmp is written
-    only when a tensor is passed for it."""
+                  stream=None, Kc2: torch.Tensor | None = None):
+    """Q, K^C1 (and K^C2 with prob.lse_approx) -> (idx, n_sel) as block_scores
+    + topk_select; S^cmp is written only when a tensor is passed for it."""
     if idx is None:
         idx = torch.empty((prob.batch, prob.h_kv, prob.n_q, budget(prob)), dtype=torch.int32,
                           device=Q.device)
@@ -229,8 +254,8 @@ def select_blocks(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
     need = select_blocks_workspace(prob, S_cmp is not None)
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _check(lib().infv2_select_blocks(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1), _ptr(S_cmp),
-                                     _ptr(idx), _ptr(n_sel), _ptr(ws),
+    _check(lib().infv2_select_blocks(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1), _ptr(Kc2),
+                                     _ptr(S_cmp), _ptr(idx), _ptr(n_sel), _ptr(ws),
                                      ws.numel() if ws is not None else 0, _stream(stream)))
     return idx, n_sel
 
@@ -275,9 +300,11 @@ def dense_attn(prob: Problem, Q, K, V, O=None, lse=None, ws=None, want_lse: bool
     return O, lse
 
 
-def forward(prob: Problem, Q, K, V, Kc1=None, mode: str = "auto", stream=None) -> dict:
+def forward(prob: Problem, Q, K, V, Kc1=None, mode: str = "auto", stream=None,
+            Kc2=None) -> dict:
     """Whole forward path: the dense switch, else compress -> scores -> top-k ->
-    sparse attention.  Returns a dict of the intermediate and final tensors."""
+    sparse attention (with prob.lse_approx the coarse keys are compressed too).
+    Returns a dict of the intermediate and final tensors."""
     if mode == "auto":
         mode = "dense" if use_dense(prob) else "sparse"
     out = {"mode": mode}
@@ -286,10 +313,12 @@ def forward(prob: Problem, Q, K, V, Kc1=None, mode: str = "auto", stream=None) -
         return out
     if Kc1 is None:
         Kc1 = compress_k(prob, K, stream=stream)
-    S_cmp = block_scores(prob, Q, Kc1, stream=stream)
+    if prob.lse_approx and Kc2 is None:
+        Kc2 = compress_k2(prob, K, stream=stream)
+    S_cmp = block_scores(prob, Q, Kc1, stream=stream, Kc2=Kc2)
     idx, n_sel = topk_select(prob, S_cmp, stream=stream)
     O, lse = sparse_attn(prob, Q, K, V, idx, n_sel, stream=stream)
-    out.update(Kc1=Kc1, S_cmp=S_cmp, idx=idx, n_sel=n_sel, O=O, lse=lse)
+    out.update(Kc1=Kc1, Kc2=Kc2, S_cmp=S_cmp, idx=idx, n_sel=n_sel, O=O, lse=lse)
     return out
 
 

@@ -11,21 +11,21 @@
 
 namespace infv2 {
 hipError_t launch_compress_k(const infv2_problem& p, const void* K, void* Kc1, int c1_begin,
-                             int c1_end, int64_t kv_cap, int64_t c1_cap, hipStream_t stream);
+                             int c1_end, int64_t kv_cap, int64_t c1_cap, int l_len, int s_len,
+                             hipStream_t stream);
 bool scores_fast_shape(const infv2_problem& p);
-size_t scores_workspace(const infv2_problem& p, int n_c1);
+size_t scores_workspace(const infv2_problem& p, const KeySet& ks);
 size_t scores_generic_lds(const infv2_problem& p, int n_c1);
-hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void* Kc1,
-                               float* S_cmp, void* ws, int n_c1, int n_blk, int64_t c1_cap,
-                               float scale, hipStream_t stream);
+hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const KeySet& ks,
+                               float* S_cmp, void* ws, int n_blk, float scale,
+                               hipStream_t stream);
 hipError_t launch_topk(const infv2_problem& p, const float* S_cmp, int32_t* idx, int32_t* n_sel,
                        int n_blk, int budget, hipStream_t stream);
 bool select_fused_shape(const infv2_problem& p, int n_c1);
 size_t select_fused_workspace(const infv2_problem& p, int n_c1);
-hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const void* Kc1,
-                               float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, int n_c1,
-                               int n_blk, int64_t c1_cap, float scale, int budget,
-                               hipStream_t stream);
+hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeySet& ks,
+                               float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, int n_blk,
+                               float scale, int budget, hipStream_t stream);
 bool attn_fast_shape(const infv2_problem& p);
 size_t attn_workspace(const infv2_problem& p, int budget, bool sparse);
 hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, const void* V,
@@ -68,10 +68,27 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 int n_c1_of(const infv2_problem& p) {
   return p.n_kv < p.l_C1 ? 0 : (p.n_kv - p.l_C1) / p.s_C1 + 1;
 }
+// coarse kernels of the LSE approximation: l_C2 = 4 l_C1, s_C2 = 4 s_C1
+int l_c2_of(const infv2_problem& p) { return 4 * p.l_C1; }
+int s_c2_of(const infv2_problem& p) { return 4 * p.s_C1; }
+int n_c2_of(const infv2_problem& p) {
+  return p.n_kv < l_c2_of(p) ? 0 : (p.n_kv - l_c2_of(p)) / s_c2_of(p) + 1;
+}
 int n_blk_of(const infv2_problem& p) { return (p.n_kv + p.B - 1) / p.B; }
 int budget_of(const infv2_problem& p) { return p.N_init + p.N_local + p.k; }
 int64_t kv_cap_of(const infv2_problem& p) { return p.kv_cap ? p.kv_cap : p.n_kv; }
 int64_t c1_cap_of(const infv2_problem& p) { return p.c1_cap ? p.c1_cap : n_c1_of(p); }
+int64_t c2_cap_of(const infv2_problem& p) { return p.c2_cap ? p.c2_cap : n_c2_of(p); }
+KeySet keys_of(const infv2_problem& p, const void* Kc1, const void* Kc2) {
+  KeySet ks;
+  ks.Kc1 = Kc1;
+  ks.Kc2 = p.lse_approx ? Kc2 : nullptr;
+  ks.n_c1 = n_c1_of(p);
+  ks.n_c2 = n_c2_of(p);
+  ks.c1_cap = c1_cap_of(p);
+  ks.c2_cap = c2_cap_of(p);
+  return ks;
+}
 float scale_of(const infv2_problem& p) {
   return p.scale != 0.0f ? p.scale : 1.0f / sqrtf((float)p.d);
 }
@@ -106,6 +123,9 @@ int check(const infv2_problem* pp) {
     return fail(INFV2_E_ARG, "kv_cap (%lld) < n_kv (%d)", (long long)p.kv_cap, p.n_kv);
   if (p.c1_cap != 0 && p.c1_cap < n_c1_of(p))
     return fail(INFV2_E_ARG, "c1_cap (%lld) < n_C1 (%d)", (long long)p.c1_cap, n_c1_of(p));
+  if (p.c2_cap != 0 && p.c2_cap < n_c2_of(p))
+    return fail(INFV2_E_ARG, "c2_cap (%lld) < n_C2 (%d)", (long long)p.c2_cap, n_c2_of(p));
+  if (p.lse_approx != 0 && p.lse_approx != 1) return fail(INFV2_E_ARG, "lse_approx must be 0 or 1");
   if (budget_of(p) < 1) return fail(INFV2_E_ARG, "N_init + N_local + k must be >= 1");
   if ((int64_t)p.G * p.h_kv > 4096) return fail(INFV2_E_ARG, "h_q too large");
   // kernel instances
@@ -133,6 +153,7 @@ int check(const infv2_problem* pp) {
 extern "C" {
 
 int32_t infv2_n_kernels(const infv2_problem* p) { return p ? n_c1_of(*p) : -1; }
+int32_t infv2_n_coarse_kernels(const infv2_problem* p) { return p ? n_c2_of(*p) : -1; }
 int32_t infv2_n_blocks(const infv2_problem* p) { return p ? n_blk_of(*p) : -1; }
 int32_t infv2_budget(const infv2_problem* p) { return p ? budget_of(*p) : -1; }
 
@@ -157,31 +178,54 @@ int infv2_compress_k(const infv2_problem* p, const void* K, void* Kc1, int32_t c
     return fail(INFV2_E_ARG, "need 0 <= c1_begin <= c1_end <= n_C1 (%d..%d, n_C1=%d)",
                 c1_begin, c1_end, n_c1);
   return hip_status(launch_compress_k(*p, K, Kc1, c1_begin, c1_end, kv_cap_of(*p), c1_cap_of(*p),
-                                      (hipStream_t)stream),
+                                      p->l_C1, p->s_C1, (hipStream_t)stream),
                     "infv2_compress_k");
+}
+
+int infv2_compress_k2(const infv2_problem* p, const void* K, void* Kc2, int32_t c2_begin,
+                      int32_t c2_end, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(K);
+  CHECK_PTR(Kc2);
+  const int n_c2 = n_c2_of(*p);
+  if (c2_begin < 0 || c2_begin > c2_end || c2_end > n_c2)
+    return fail(INFV2_E_ARG, "need 0 <= c2_begin <= c2_end <= n_C2 (%d..%d, n_C2=%d)",
+                c2_begin, c2_end, n_c2);
+  return hip_status(launch_compress_k(*p, K, Kc2, c2_begin, c2_end, kv_cap_of(*p), c2_cap_of(*p),
+                                      l_c2_of(*p), s_c2_of(*p), (hipStream_t)stream),
+                    "infv2_compress_k2");
 }
 
 size_t infv2_block_scores_workspace(const infv2_problem* p) {
   if (check(p) != INFV2_OK) return 0;
-  return scores_workspace(*p, n_c1_of(*p));
+  return scores_workspace(*p, keys_of(*p, nullptr, nullptr));
 }
 
-int infv2_block_scores(const infv2_problem* p, const void* Q, const void* Kc1, float* S_cmp,
-                       void* ws, size_t ws_bytes, void* stream) {
+// The key pointers a selection call needs: K^C1 when a kernel exists, K^C2
+// with the LSE approximation when a coarse kernel exists.
+static int check_keys(const infv2_problem& p, const void* Kc1, const void* Kc2) {
+  if (n_c1_of(p) > 0) CHECK_PTR(Kc1);
+  if (p.lse_approx && n_c2_of(p) > 0) CHECK_PTR(Kc2);
+  return INFV2_OK;
+}
+
+int infv2_block_scores(const infv2_problem* p, const void* Q, const void* Kc1, const void* Kc2,
+                       float* S_cmp, void* ws, size_t ws_bytes, void* stream) {
   int st = check(p);
   if (st) return st;
   CHECK_PTR(Q);
   CHECK_PTR(S_cmp);
-  const int n_c1 = n_c1_of(*p);
-  if (n_c1 > 0) CHECK_PTR(Kc1);
-  const size_t need = scores_workspace(*p, n_c1);
+  if ((st = check_keys(*p, Kc1, Kc2))) return st;
+  const KeySet ks = keys_of(*p, Kc1, Kc2);
+  const size_t need = scores_workspace(*p, ks);
   if (need) {
     CHECK_PTR(ws);
     if (ws_bytes < need)
       return fail(INFV2_E_WORKSPACE, "block_scores workspace %zu < %zu bytes", ws_bytes, need);
   }
-  return hip_status(launch_block_scores(*p, Q, Kc1, S_cmp, ws, n_c1, n_blk_of(*p), c1_cap_of(*p),
-                                        scale_of(*p), (hipStream_t)stream),
+  return hip_status(launch_block_scores(*p, Q, ks, S_cmp, ws, n_blk_of(*p), scale_of(*p),
+                                        (hipStream_t)stream),
                     "infv2_block_scores");
 }
 
@@ -199,24 +243,25 @@ int infv2_topk_select(const infv2_problem* p, const float* S_cmp, int32_t* idx, 
 
 size_t infv2_select_blocks_workspace(const infv2_problem* p, int with_scores) {
   if (check(p) != INFV2_OK) return 0;
-  const int n_c1 = n_c1_of(*p);
-  const size_t base = scores_workspace(*p, n_c1);
-  if (select_fused_shape(*p, n_c1)) return align256(base) + select_fused_workspace(*p, n_c1);
+  const KeySet ks = keys_of(*p, nullptr, nullptr);
+  const size_t base = scores_workspace(*p, ks);
+  if (select_fused_shape(*p, ks.n_c1)) return align256(base) + select_fused_workspace(*p, ks.n_c1);
   if (with_scores) return base;
   const size_t rows = (size_t)p->batch * p->n_q * p->h_kv;
   return align256(base) + rows * (size_t)n_blk_of(*p) * sizeof(float);
 }
 
-int infv2_select_blocks(const infv2_problem* p, const void* Q, const void* Kc1, float* S_cmp,
-                        int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+int infv2_select_blocks(const infv2_problem* p, const void* Q, const void* Kc1, const void* Kc2,
+                        float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes,
+                        void* stream) {
   int st = check(p);
   if (st) return st;
   CHECK_PTR(Q);
   CHECK_PTR(idx);
   CHECK_PTR(n_sel);
   if (S_cmp && !aligned16(S_cmp)) return fail(INFV2_E_ARG, "S_cmp is not 16-byte aligned");
-  const int n_c1 = n_c1_of(*p);
-  if (n_c1 > 0) CHECK_PTR(Kc1);
+  if ((st = check_keys(*p, Kc1, Kc2))) return st;
+  const KeySet ks = keys_of(*p, Kc1, Kc2);
   const size_t need = infv2_select_blocks_workspace(p, S_cmp != nullptr);
   if (need) {
     CHECK_PTR(ws);
@@ -224,15 +269,13 @@ int infv2_select_blocks(const infv2_problem* p, const void* Q, const void* Kc1, 
       return fail(INFV2_E_WORKSPACE, "select_blocks workspace %zu < %zu bytes", ws_bytes, need);
   }
   const hipStream_t s = (hipStream_t)stream;
-  if (select_fused_shape(*p, n_c1)) {
-    return hip_status(launch_select_fused(*p, Q, Kc1, S_cmp, idx, n_sel, ws, n_c1, n_blk_of(*p),
-                                          c1_cap_of(*p), scale_of(*p), budget_of(*p), s),
+  if (select_fused_shape(*p, ks.n_c1)) {
+    return hip_status(launch_select_fused(*p, Q, ks, S_cmp, idx, n_sel, ws, n_blk_of(*p),
+                                          scale_of(*p), budget_of(*p), s),
                       "infv2_select_blocks");
   }
-  float* S = S_cmp ? S_cmp
-                   : (float*)((char*)ws + align256(scores_workspace(*p, n_c1)));
-  hipError_t e = launch_block_scores(*p, Q, Kc1, S, ws, n_c1, n_blk_of(*p), c1_cap_of(*p),
-                                     scale_of(*p), s);
+  float* S = S_cmp ? S_cmp : (float*)((char*)ws + align256(scores_workspace(*p, ks)));
+  hipError_t e = launch_block_scores(*p, Q, ks, S, ws, n_blk_of(*p), scale_of(*p), s);
   if (e == hipSuccess) e = launch_topk(*p, S, idx, n_sel, n_blk_of(*p), budget_of(*p), s);
   return hip_status(e, "infv2_select_blocks");
 }

@@ -8,6 +8,15 @@
 
 namespace infv2 {
 
+// The compressed keys a selection call reads: K^C1 and, for the LSE
+// approximation, K^C2 (else null), with their valid and allocated row counts.
+struct KeySet {
+  const void* Kc1;
+  const void* Kc2;
+  int n_c1, n_c2;
+  int64_t c1_cap, c2_cap;
+};
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -91,22 +91,24 @@ __global__ void __launch_bounds__(256) compress_k_kernel(
   store_rounded<T>(dst, t * inv_l, e * inv_l);
 }
 
+// Kernels of length l_len at stride s_len (K^C1: l_C1, s_C1; K^C2: 4 l_C1, 4 s_C1).
 hipError_t launch_compress_k(const infv2_problem& p, const void* K, void* Kc1, int c1_begin,
-                             int c1_end, int64_t kv_cap, int64_t c1_cap, hipStream_t stream) {
+                             int c1_end, int64_t kv_cap, int64_t c1_cap, int l_len, int s_len,
+                             hipStream_t stream) {
   if (c1_end <= c1_begin) return hipSuccess;
   const int per_blk = 256 / p.d;
   const int n = c1_end - c1_begin;
   dim3 grid((n + per_blk - 1) / per_blk, p.h_kv, p.batch);
   dim3 block(per_blk * p.d);
-  const double inv_l = 1.0 / (double)p.l_C1;
+  const double inv_l = 1.0 / (double)l_len;
   if (p.dtype == INFV2_BF16) {
     hipLaunchKernelGGL(compress_k_kernel<uint16_t>, grid, block, 0, stream,
                        (const uint16_t*)K, (uint16_t*)Kc1, c1_begin, c1_end, p.h_kv, p.d, kv_cap,
-                       c1_cap, p.l_C1, p.s_C1, inv_l);
+                       c1_cap, l_len, s_len, inv_l);
   } else {
     hipLaunchKernelGGL(compress_k_kernel<float>, grid, block, 0, stream, (const float*)K,
-                       (float*)Kc1, c1_begin, c1_end, p.h_kv, p.d, kv_cap, c1_cap, p.l_C1,
-                       p.s_C1, inv_l);
+                       (float*)Kc1, c1_begin, c1_end, p.h_kv, p.d, kv_cap, c1_cap, l_len,
+                       s_len, inv_l);
   }
   return hipGetLastError();
 }

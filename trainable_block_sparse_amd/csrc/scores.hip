@@ -39,14 +39,19 @@ constexpr int SEL_TOK_WG = 16;                // tokens per workgroup
 struct ScoresArgs {
   const uint16_t* Q;
   const uint16_t* Kc1;
+  const uint16_t* Kc2;   // coarse keys (LSE approximation), else null
   float* S_cmp;
-  int batch, n_q, q_pos0, h_kv, n_c1, n_blk, tiles;
-  int64_t c1_cap;
+  int batch, n_q, q_pos0, h_kv, n_c1, n_c2, n_blk, tiles;
+  int64_t c1_cap, c2_cap;
   float c;  // scale * log2(e)
 };
 
 // kernel j is causal for position p when its last token j*16+31 <= p
 __device__ __forceinline__ int last_visible_kernel(int p) { return p >= 31 ? (p - 31) >> 4 : -1; }
+// coarse kernel j (tokens 64j .. 64j+127) is causal when 64j+127 <= p
+__device__ __forceinline__ int last_visible_coarse(int p) { return p >= 127 ? (p - 127) >> 6 : -1; }
+// log2(s_C2 / s_C1): the count correction of the coarse estimate
+constexpr float kLog2CoarseRatio = 2.0f;
 
 constexpr int PASS_MAX = 0;    // row maxima (only when the sum overflows)
 constexpr int PASS_SUM = 1;    // log-sum-exp sweep
@@ -136,10 +141,15 @@ __device__ __forceinline__ void exact_chunk(const ScoresArgs& a, const uint8_t* 
 // The exact pass: the same two sweeps with one exponent reference per row
 // (and an extra maximum sweep when a sum overflows).  It runs only for the
 // tiles that the fast kernel marked (NaN in block 0 of the tile's first row)
-// and exits at once for all others.
+// and exits at once for all others.  APPROX: rows whose token sees a coarse
+// kernel take the coarse estimate (a sum sweep over K^C2 with the same
+// machinery), the others the exact LSE; the score sweep then uses
+// 2^(z*c - L) with L = log2 of the row's normaliser.
+template <bool APPROX>
 __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][SEL_CHUNK * SEL_ROW_BYTES];
   __shared__ float sbuf_all[4][SEL_TOK_WAVE][SEL_CHUNK + 1];
+  __shared__ float lfine_all[4][2][32];   // APPROX: exact log2-normaliser per row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -185,16 +195,19 @@ __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
     for (int i = 0; i < 16; ++i) { M[rb][i] = kNegInf; W[rb][i] = 0.f; }
 
   const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
+  // the sweep's key rows: K^C1, or K^C2 for the approximate LSE sweep
+  const uint16_t* src = kc1;
+  int n_src = a.n_c1;
 
-  // stage one chunk of 32 K^C1 rows (8 KB): 2 x 16 B per thread, XOR-swizzled
+  // stage one chunk of 32 key rows (8 KB): 2 x 16 B per thread, XOR-swizzled
   auto stage_load = [&](int chunk, u32x4 (&st)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int u = tid + 256 * i;
       const int row = u >> 4, c16 = u & 15;
       // rows past the last kernel are clamped to it; they are never visible
-      const int j = min(chunk * SEL_CHUNK + row, a.n_c1 - 1);
-      st[i] = *(const u32x4*)(kc1 + (size_t)j * SEL_D + c16 * 8);
+      const int j = min(chunk * SEL_CHUNK + row, n_src - 1);
+      st[i] = *(const u32x4*)(src + (size_t)j * SEL_D + c16 * 8);
     }
   };
   auto stage_store = [&](uint8_t* kb, const u32x4 (&st)[2]) {
@@ -206,7 +219,7 @@ __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
     }
   };
 
-  auto run_pass = [&](auto pass_tag, bool set_ref) {
+  auto run_pass = [&](auto pass_tag, bool set_ref, int nchunks, int jmin_wg) {
     constexpr int PASS = decltype(pass_tag)::value;
     if (nchunks == 0) return;
     u32x4 st[2];
@@ -265,35 +278,90 @@ __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
 
   // sweep 1 (log-sum-exp): s = sum_j 2^(z_j*c - M), M = the exact row maximum
   // over the first chunk (every row with a visible kernel sees kernel 0)
-  run_pass(std::integral_constant<int, PASS_SUM>{}, true);
-  const bool finite = merge_sums();
-  if (__syncthreads_or(!finite)) {
-    // a later logit exceeded the reference by more than 2^127: take the exact
-    // row maximum (one extra sweep) and sum again
+  auto lse_sweep = [&](int nch, int jmin) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) { M[rb][i] = kNegInf; W[rb][i] = 0.f; }
-    run_pass(std::integral_constant<int, PASS_MAX>{}, false);
+    run_pass(std::integral_constant<int, PASS_SUM>{}, true, nch, jmin);
+    const bool finite = merge_sums();
+    if (__syncthreads_or(!finite)) {
+      // a later logit exceeded the reference by more than 2^127: take the
+      // exact row maximum (one extra sweep) and sum again
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { M[rb][i] = kNegInf; W[rb][i] = 0.f; }
+      run_pass(std::integral_constant<int, PASS_MAX>{}, false, nch, jmin);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float m = M[rb][i];
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+          M[rb][i] = (m == kNegInf) ? 0.f : m * a.c;
+        }
+      run_pass(std::integral_constant<int, PASS_SUM>{}, false, nch, jmin);
+      merge_sums();
+    }
+  };
+  if constexpr (!APPROX) {
+    lse_sweep(nchunks, jmin_wg);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) W[rb][i] = W[rb][i] > 0.f ? 1.0f / W[rb][i] : 0.f;
+  } else {
+    // Row (rb, i) of this lane is token 2rb + (row >> 4), head row & 15, with
+    // row = 8(i/4) + 4(lane/32) + i%4 (32x32 C layout); after merge_sums its
+    // M and W are the same in the 32 lanes of the lane's half.
+    auto row_of = [&](int i) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); };
+    const int p_first = a.q_pos0 + wg_t0, p_last = a.q_pos0 + wg_last;
+    const bool need_fine = p_first < 127 && p_last >= 31;
+    if (need_fine) {
+      // exact normaliser of the tokens that see no coarse kernel
+      lse_sweep(nchunks, jmin_wg);
+      if ((lane & 31) == 0)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            lfine_all[wave][rb][row_of(i)] = M[rb][i] + fast_log2(W[rb][i]);
+    }
+    int jm2[4];
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl) jm2[tl] = t0 + tl < a.n_q ? last_visible_coarse(a.q_pos0 + t0 + tl) : -1;
+    const int jmax2 = last_visible_coarse(p_last), jmin2 = last_visible_coarse(p_first);
+    if (jmax2 >= 0) {
+      // coarse sweep (masks from the coarse visibility)
+      int jm_fine[4];
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) { jm_fine[tl] = jm[tl]; jm[tl] = jm2[tl]; }
+      src = a.Kc2 + ((size_t)b * a.h_kv + g) * a.c2_cap * SEL_D;
+      n_src = a.n_c2;
+      lse_sweep((jmax2 + SEL_CHUNK) / SEL_CHUNK, jmin2);
+      src = kc1;
+      n_src = a.n_c1;
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) jm[tl] = jm_fine[tl];
+    }
+    __syncthreads();
+    // per row: L = coarse estimate where the token sees a coarse kernel,
+    // else the exact one; the score sweep runs with M = L and W = 1
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float m = M[rb][i];
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-        M[rb][i] = (m == kNegInf) ? 0.f : m * a.c;
+        const int tl = 2 * rb + (row_of(i) >> 4);
+        const float l2 = M[rb][i] + (fast_log2(W[rb][i]) + kLog2CoarseRatio);
+        M[rb][i] = jm2[tl] >= 0 ? l2 : (need_fine ? lfine_all[wave][rb][row_of(i)] : 0.f);
+        W[rb][i] = 1.0f;
       }
-    run_pass(std::integral_constant<int, PASS_SUM>{}, false);
-    merge_sums();
   }
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) W[rb][i] = W[rb][i] > 0.f ? 1.0f / W[rb][i] : 0.f;
   // sweep 2: S^C1 = 2^(z*c - M) / s, head-group sum, max-pool, S^cmp
   if (lane < 4) sbuf[lane][0] = kNegInf;
-  run_pass(std::integral_constant<int, PASS_SCORE>{}, false);
+  run_pass(std::integral_constant<int, PASS_SCORE>{}, false, nchunks, jmin_wg);
   // blocks with no visible kernel in the causal range
   {
     const int tl = lane >> 4;
@@ -375,10 +443,11 @@ __device__ __forceinline__ void chunk_mfma(const uint8_t* kb, const SelWave& w, 
 // per token (its 16 heads share it):
 //  PASS_SUM:   W += 2^(z*c - M); FIRST: M is first set to the exact maximum
 //              of the chunk's logits over the token's 16 heads (times c)
-//  PASS_SCORE: S^C1 = 2^(z*c - M) * W, summed over the group's 16 heads,
+//  PASS_SCORE: S^C1 = 2^(z*c - M) * W (LFORM: 2^(z*c - W), W holding each
+//              head's log2-normaliser), summed over the group's 16 heads,
 //              max-pooled over the kernels that intersect each block and
 //              written to S^cmp
-template <int PASS, bool MASKED, bool FIRST>
+template <int PASS, bool MASKED, bool FIRST, bool LFORM = false>
 __device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][2], int chunk,
                                            SelWave& w, int lane) {
   static_assert(PASS == PASS_SUM || PASS == PASS_SCORE, "fast passes");
@@ -423,8 +492,13 @@ __device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][
       for (int nt = 0; nt < 2; ++nt) {
         float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[tl][nt][i], a.c, -w.Mt[tl])), w.W[tl][i], s);
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (LFORM)
+            s += fast_exp2(__builtin_fmaf(acc[tl][nt][i], a.c, -w.W[tl][i]));
+          else
+            s = __builtin_fmaf(fast_exp2(__builtin_fmaf(acc[tl][nt][i], a.c, -w.Mt[tl])),
+                               w.W[tl][i], s);
+        }
         part[tl][nt] = s;
       }
     // rows 0..3 <- (token 0, nt 0), (token 0, nt 1), (token 1, nt 0), (token 1, nt 1)
@@ -448,6 +522,7 @@ __device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][
   }
 }
 
+template <bool APPROX>
 __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * SEL_CHUNK_BYTES];
 
@@ -514,6 +589,16 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
 
   const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
 
+  // The LSE approximation takes the normaliser from the coarse kernels.  A
+  // tile holding a token that sees fine kernels but no coarse kernel (it
+  // keeps the exact LSE) goes to the exact kernel.
+  if constexpr (APPROX) {
+    if (a.q_pos0 + wg_t0 < 127 && a.q_pos0 + wg_last >= 31) {
+      if (tid == 0) srows[(size_t)wg_t0 * a.n_blk] = __builtin_nanf("");
+      return;
+    }
+  }
+
   // K^C1 streams through LDS in chunks of 32 kernels (8 KB): 512 pieces of
   // 16 bytes, one per lane of the 8 waves.  Lane L of wave w owns piece
   // u = 64 w + L, i.e. row u/16 at piece position u%16, which holds global
@@ -525,16 +610,19 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
   const int piece_row = piece_u >> 4;
   const uint32_t piece_src = (uint32_t)((((piece_u & 15) ^ (piece_row & 15)) << 3));   // elements
   uint8_t* const piece_dst = kbuf + piece_u * 16;
+  // the sweep's key rows: K^C1, or K^C2 for the approximate LSE sweep
+  const uint16_t* src = kc1;
+  int n_src = a.n_c1;
   auto load_piece = [&](int c) -> u32x4 {
-    const int j = min(c * SEL_CHUNK + piece_row, a.n_c1 - 1);
-    return *(const u32x4*)(kc1 + (size_t)j * SEL_D + piece_src);
+    const int j = min(c * SEL_CHUNK + piece_row, n_src - 1);
+    return *(const u32x4*)(src + (size_t)j * SEL_D + piece_src);
   };
   auto slot = [&](int c) -> const uint8_t* { return kbuf + (c & 1) * SEL_CHUNK_BYTES; };
 
   // One sweep.  Step c: logits and vector work of chunk c (slot c & 1), then
   // chunk c+1 from registers into the other slot, the register refilled with
   // chunk c+1+SEL_DEPTH, and the barrier that publishes chunk c+1.
-  auto run_pass = [&](auto pass_tag, auto ref_tag) {
+  auto run_pass = [&](auto pass_tag, auto ref_tag, int nchunks, int n_full) {
     constexpr int PASS = decltype(pass_tag)::value;
     constexpr bool SET_REF = decltype(ref_tag)::value;
     if (nchunks == 0) return;
@@ -547,13 +635,14 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
     auto step = [&](int c, u32x4& next) {
       f32x4 acc[2][2];
       chunk_mfma(slot(c), w, lane, acc);
+      constexpr bool LF = APPROX && PASS == PASS_SCORE;
       if (SET_REF && c == 0) {
-        if (n_full > 0) chunk_valu<PASS, false, SET_REF>(a, acc, c, w, lane);
-        else            chunk_valu<PASS, true, SET_REF>(a, acc, c, w, lane);
+        if (n_full > 0) chunk_valu<PASS, false, SET_REF, LF>(a, acc, c, w, lane);
+        else            chunk_valu<PASS, true, SET_REF, LF>(a, acc, c, w, lane);
       } else if (c < n_full) {
-        chunk_valu<PASS, false, false>(a, acc, c, w, lane);
+        chunk_valu<PASS, false, false, LF>(a, acc, c, w, lane);
       } else {
-        chunk_valu<PASS, true, false>(a, acc, c, w, lane);
+        chunk_valu<PASS, true, false, LF>(a, acc, c, w, lane);
       }
       *(u32x4*)(piece_dst + ((c + 1) & 1) * SEL_CHUNK_BYTES) = next;
       next = load_piece(c + 1 + SEL_DEPTH);
@@ -574,8 +663,28 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
 
   // sweep 1 (log-sum-exp): s = sum_j 2^(z_j*c - M), M = the exact maximum
   // over the first chunk and the token's 16 heads (every row with a visible
-  // kernel sees kernel 0)
-  run_pass(std::integral_constant<int, PASS_SUM>{}, std::true_type{});
+  // kernel sees kernel 0).  APPROX: the same over the coarse kernels.
+  if constexpr (APPROX) {
+    src = a.Kc2 + ((size_t)b * a.h_kv + g) * a.c2_cap * SEL_D;
+    n_src = a.n_c2;
+    int jm_fine[2];
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl) {
+      jm_fine[tl] = w.jm[tl];
+      w.jm[tl] = last_visible_coarse(a.q_pos0 + min(t0 + tl, a.n_q - 1));
+    }
+    const int jmax2 = last_visible_coarse(a.q_pos0 + wg_last);
+    const int jmin2 = last_visible_coarse(a.q_pos0 + wg_t0);
+    run_pass(std::integral_constant<int, PASS_SUM>{}, std::true_type{},
+             jmax2 < 0 ? 0 : (jmax2 + SEL_CHUNK) / SEL_CHUNK,
+             jmin2 < 0 ? 0 : (jmin2 + 1) / SEL_CHUNK);
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl) w.jm[tl] = jm_fine[tl];
+    src = kc1;
+    n_src = a.n_c1;
+  } else {
+    run_pass(std::integral_constant<int, PASS_SUM>{}, std::true_type{}, nchunks, n_full);
+  }
   // Lane partial sums -> row sums (over the 16 columns of a lane row).  A
   // row whose sum overflowed (a later logit exceeds the reference by more
   // than 2^127) or fell below 2^-64 (its head lies far below the token's
@@ -589,16 +698,20 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
       float s = w.W[tl][i];
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
-      w.W[tl][i] = s > 0.f ? 1.0f / s : 0.f;
+      if constexpr (APPROX)   // log2 of the normaliser: M + log2(s) + log2(s_C2/s_C1)
+        w.W[tl][i] = w.Mt[tl] + (fast_log2(s) + kLog2CoarseRatio);
+      else
+        w.W[tl][i] = s > 0.f ? 1.0f / s : 0.f;
       bad = bad || (w.jm[tl] >= 0 && !(s >= 0x1p-64f && s <= 0x1p127f));
     }
   if (__syncthreads_or(bad)) {
     if (tid == 0) srows[(size_t)wg_t0 * a.n_blk] = __builtin_nanf("");
     return;
   }
-  // sweep 2: S^C1 = 2^(z*c - M) / s, head-group sum, max-pool, S^cmp
+  // sweep 2: S^C1 = 2^(z*c - M) / s (APPROX: 2^(z*c - L)), head-group sum,
+  // max-pool, S^cmp
   w.carry = kNegInf;
-  run_pass(std::integral_constant<int, PASS_SCORE>{}, std::false_type{});
+  run_pass(std::integral_constant<int, PASS_SCORE>{}, std::false_type{}, nchunks, n_full);
   // blocks with no visible kernel in the causal range
   {
     const int tl = lane >> 5;
@@ -620,51 +733,44 @@ constexpr int SPLIT_CK = 256;   // kernels per workgroup
 struct SplitArgs {
   const uint16_t* Q;
   const uint16_t* Kc1;
+  const uint16_t* Kc2;  // coarse keys (LSE approximation), else null
   float* S_cmp;
   float* logits;    // [batch*n_q][h_kv][16][n_c1p]  (z*c, -inf when invisible)
   float2* part;     // [batch*n_q][h_kv][nch][16]    (chunk max, chunk sum)
+  float2* part2;    // [batch*n_q][h_kv][nch2][16]   the same over the coarse kernels
   // fused top-k (select_blocks), row = (b*h_kv + g)*n_q + t: per-chunk
   // candidate lists ([rows][nch][kc], null when not fused) and the outputs
   uint64_t* cand;
   int32_t* idx;
   int32_t* n_sel;
   int k, N_init, N_local, budget, kc;
-  int n_q, q_pos0, h_kv, n_c1, n_c1p, n_blk, nch;
-  int64_t c1_cap;
+  int n_q, q_pos0, h_kv, n_c1, n_c1p, n_c2, n_blk, nch, nch2;
+  int64_t c1_cap, c2_cap;
   float c;
 };
 
-// grid: x = chunk, y = group, z = batch*n_q token.  4 waves x 64 kernels.
-// Each wave loads its 64 K^C1 rows (16 KB) with coalesced loads (lanes
-// 16r..16r+15 read one 256-byte row), stages them through LDS 32 rows at a
-// time and reads the MFMA fragments back XOR-swizzled, free of bank conflicts.
-__global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
-  __shared__ float red_m[4][16], red_s[4][16];
-  __shared__ __attribute__((aligned(16))) uint8_t kst_all[4][32 * SEL_ROW_BYTES];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
-  const int b = bt / a.n_q, t = bt % a.n_q;
-  const int p = a.q_pos0 + t;
-  const int jmax = last_visible_kernel(p);
-  const int hq = a.h_kv * SEL_G;
-  uint8_t* kst = kst_all[wave];
-  const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
-  const int jw = chunk * SPLIT_CK + wave * 64;
+// z = Q K^T (raw dot products) for the 64 key rows jw .. jw+63 of one wave:
+// the rows are loaded with coalesced loads (lanes 16r..16r+15 read one
+// 256-byte row), staged through the wave's LDS 32 rows at a time and read
+// back XOR-swizzled as MFMA fragments, free of bank conflicts.  Rows past
+// n_rows-1 are clamped to it (the caller masks them); with no row at all
+// nothing is read.  C layout: acc[nt][i] is head 4*(lane>>4)+i, row
+// jw + 16*nt + (lane&15).
+__device__ __forceinline__ void split_logits_mfma(const uint16_t* keys, int n_rows, int jw,
+                                                  const uint16_t* qrow_base, int lane,
+                                                  uint8_t* kst, f32x4 (&acc)[4]) {
   u32x4 v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    // kernels past the last one are clamped to it; they are never visible
-    // (with no kernel at all nothing is read: every logit is -inf)
-    const int j = min(jw + 4 * i + (lane >> 4), a.n_c1 - 1);
-    v[i] = a.n_c1 > 0 ? *(const u32x4*)(kc1 + (size_t)j * SEL_D + 8 * (lane & 15))
+    const int j = min(jw + 4 * i + (lane >> 4), n_rows - 1);
+    v[i] = n_rows > 0 ? *(const u32x4*)(keys + (size_t)j * SEL_D + 8 * (lane & 15))
                       : u32x4{0u, 0u, 0u, 0u};
   }
   // A operand: Q rows = heads (lane & 15), k = d
   bf16x8 qf[4];
-  const uint16_t* qrow = a.Q + (((size_t)b * a.n_q + t) * hq + g * SEL_G + (lane & 15)) * SEL_D;
+  const uint16_t* qrow = qrow_base + (size_t)(lane & 15) * SEL_D;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(qrow + 32 * ks + 8 * (lane >> 4)));
-  f32x4 acc[4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     // rows 32h .. 32h+31 of the wave's 64 (row 4i + (lane>>4) came from v[i])
@@ -691,21 +797,21 @@ __global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  // C layout: lane holds heads 4*(lane>>4)+i, kernel jw + 16*nt + (lane&15)
-  float* lrow = a.logits + ((size_t)bt * a.h_kv + g) * SEL_G * a.n_c1p;
-  float mloc[4], sloc[4];
+}
+
+// Per-head (max, sum) of a workgroup's 256 masked logits zc (times c, -inf
+// when not visible), acc as left by split_logits_mfma after scaling: mc =
+// the chunk maximum, s = sum of 2^(zc - mc).  Every thread gets the values of
+// the heads it holds (4*(lane>>4)+i).
+__device__ __forceinline__ void split_chunk_partials(const f32x4 (&acc)[4], int lane, int wave,
+                                                     float (&red_m)[4][16], float (&red_s)[4][16],
+                                                     float (&mc_out)[4], float (&s_out)[4]) {
+  float mloc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = 4 * (lane >> 4) + i;
     float m = kNegInf;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int j = jw + 16 * nt + (lane & 15);
-      const float zc = (j <= jmax) ? acc[nt][i] * a.c : kNegInf;
-      acc[nt][i] = zc;
-      if (j < a.n_c1p) lrow[(size_t)h * a.n_c1p + j] = zc;
-      m = fmaxf(m, zc);
-    }
+    for (int nt = 0; nt < 4; ++nt) m = fmaxf(m, acc[nt][i]);
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     mloc[i] = m;
@@ -725,32 +831,71 @@ __global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
     }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
-    sloc[i] = s;
-    mloc[i] = mc;
+    if ((lane & 15) == 0) red_s[wave][h] = s;
+    mc_out[i] = mc;
   }
-  if ((lane & 15) == 0)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red_s[wave][4 * (lane >> 4) + i] = sloc[i];
   __syncthreads();
-  if (threadIdx.x < 16) {
-    const int h = threadIdx.x;
-    const float mc = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
-    const float s = red_s[0][h] + red_s[1][h] + red_s[2][h] + red_s[3][h];
-    a.part[(((size_t)bt * a.h_kv + g) * a.nch + chunk) * SEL_G + h] = make_float2(mc, s);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * (lane >> 4) + i;
+    s_out[i] = red_s[0][h] + red_s[1][h] + red_s[2][h] + red_s[3][h];
   }
 }
 
-// Each head's softmax reference and weight from the per-chunk (max, sum)
-// partials of a row: Mh[h] = the running maximum, Wh[h] = 1 / sum of
-// exp2(z - Mh[h]).  Threads 0..255: 16 per head, each folding every 16th
-// chunk, then a 16-lane merge.  Every product-sum is an explicit fma, so
-// all kernels that call this round identically.
-__device__ __forceinline__ void head_lse_weights(const SplitArgs& a, int g, int bt, int tid,
-                                                 float* Mh, float* Wh) {
+// grid: x = chunk, y = group, z = batch*n_q token.  4 waves x 64 kernels.
+// Fine: writes z*c (-inf when not visible) to the logits buffer and the
+// chunk's per-head (max, sum).  COARSE: the same sweep over the coarse
+// kernels for the LSE approximation, partials only.
+template <bool COARSE>
+__global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
+  __shared__ float red_m[4][16], red_s[4][16];
+  __shared__ __attribute__((aligned(16))) uint8_t kst_all[4][32 * SEL_ROW_BYTES];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+  const int b = bt / a.n_q, t = bt % a.n_q;
+  const int p = a.q_pos0 + t;
+  const int jmax = COARSE ? last_visible_coarse(p) : last_visible_kernel(p);
+  const int hq = a.h_kv * SEL_G;
+  const uint16_t* keys = COARSE ? a.Kc2 + ((size_t)b * a.h_kv + g) * a.c2_cap * SEL_D
+                                : a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
+  const int n_rows = COARSE ? a.n_c2 : a.n_c1;
+  const int jw = chunk * SPLIT_CK + wave * 64;
+  f32x4 acc[4];
+  split_logits_mfma(keys, n_rows, jw, a.Q + (((size_t)b * a.n_q + t) * hq + g * SEL_G) * SEL_D,
+                    lane, kst_all[wave], acc);
+  float* lrow = a.logits + ((size_t)bt * a.h_kv + g) * SEL_G * a.n_c1p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * (lane >> 4) + i;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int j = jw + 16 * nt + (lane & 15);
+      const float zc = (j <= jmax) ? acc[nt][i] * a.c : kNegInf;
+      acc[nt][i] = zc;
+      if (!COARSE && j < a.n_c1p) lrow[(size_t)h * a.n_c1p + j] = zc;
+    }
+  }
+  float mc[4], sc[4];
+  split_chunk_partials(acc, lane, wave, red_m, red_s, mc, sc);
+  if (wave == 0 && (lane & 15) == 0) {
+    float2* part = COARSE ? a.part2 + (((size_t)bt * a.h_kv + g) * a.nch2 + chunk) * SEL_G
+                          : a.part + (((size_t)bt * a.h_kv + g) * a.nch + chunk) * SEL_G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[4 * (lane >> 4) + i] = make_float2(mc[i], sc[i]);
+  }
+}
+
+// Each head's softmax reference and sum from per-chunk (max, sum) partials
+// [.][nch][16] of a row: threads 0..255, 16 per head, each folding every
+// 16th chunk, then a 16-lane merge; thread 16h returns head h's (m, s).
+// Every product-sum is an explicit fma, so all kernels that call this round
+// identically.
+__device__ __forceinline__ float2 head_lse_merge(const float2* part, int nch, int h_kv, int g,
+                                                 int bt, int tid) {
   const int h = tid >> 4, q = tid & 15;
-  const float2* pr = a.part + ((size_t)bt * a.h_kv + g) * a.nch * SEL_G + h;
+  const float2* pr = part + ((size_t)bt * h_kv + g) * nch * SEL_G + h;
   float m = kNegInf, s = 0.f;
-  for (int c = q; c < a.nch; c += 16) {
+  for (int c = q; c < nch; c += 16) {
     const float2 v = pr[(size_t)c * SEL_G];
     if (v.x == kNegInf) continue;
     if (v.x > m) { s = __builtin_fmaf(s, fast_exp2(m - v.x), v.y); m = v.x; }
@@ -766,9 +911,18 @@ __device__ __forceinline__ void head_lse_weights(const SplitArgs& a, int g, int 
     }
     m = mn;
   }
-  if (q == 0) {
-    Mh[h] = (m == kNegInf) ? 0.f : m;
-    Wh[h] = s > 0.f ? 1.0f / s : 0.f;
+  return make_float2(m, s);
+}
+
+// Mh[h] = the running maximum (0 when nothing is visible), Wh[h] = 1 / sum of
+// exp2(z - Mh[h]) over the row's fine kernels.
+__device__ __forceinline__ void head_lse_weights(const SplitArgs& a, int g, int bt, int tid,
+                                                 float* Mh, float* Wh) {
+  const float2 ms = head_lse_merge(a.part, a.nch, a.h_kv, g, bt, tid);
+  if ((tid & 15) == 0) {
+    const int h = tid >> 4;
+    Mh[h] = (ms.x == kNegInf) ? 0.f : ms.x;
+    Wh[h] = ms.y > 0.f ? 1.0f / ms.y : 0.f;
   }
 }
 
@@ -839,6 +993,121 @@ __global__ void __launch_bounds__(256) scores_split_pool_kernel(SplitArgs a) {
   const uint64_t sorted = wave_sort_desc<uint64_t>(key, lane);
   const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
   if (lane < a.kc) a.cand[(row * a.nch + chunk) * a.kc + lane] = sorted;
+}
+
+// The LSE approximation for few query tokens, in one sweep over K^C1: a
+// workgroup takes 256 kernels of a row (grid as the logits kernel), takes
+// each head's log2-normaliser L[h] from the coarse partials (a token that
+// sees no coarse kernel has all its visible kernels in chunk 0, whose
+// workgroup takes the exact LSE from its own logits), forms
+// S^shared = sum_h 2^(z*c - L[h]) for its kernels and the kernel before them
+// (a plain dot product), max-pools its 64 blocks and writes S^cmp (when
+// S_cmp is set) and, with LISTS, the chunk's sorted candidate list as the
+// pool kernel does.
+template <bool LISTS>
+__global__ void __launch_bounds__(256) scores_split_fused_kernel(SplitArgs a) {
+  __shared__ float red_m[4][16], red_s[4][16];
+  __shared__ __attribute__((aligned(16))) uint8_t kst_all[4][32 * SEL_ROW_BYTES];
+  __shared__ float Lh[SEL_G];
+  __shared__ float sh[SPLIT_CK + 1];    // sh[x] = S^shared of kernel j0 - 1 + x
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+  const int b = bt / a.n_q, t = bt % a.n_q;
+  const int p = a.q_pos0 + t;
+  const int jmax = last_visible_kernel(p);
+  const bool coarse = last_visible_coarse(p) >= 0;      // row-uniform
+  const int hq = a.h_kv * SEL_G;
+  const int j0 = chunk * SPLIT_CK;
+  const uint16_t* qbase = a.Q + (((size_t)b * a.n_q + t) * hq + g * SEL_G) * SEL_D;
+  const uint16_t* kc1 = a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
+  if (coarse) {
+    // L = M + log2(s) + log2(s_C2/s_C1) from the coarse partials
+    const float2 ms = head_lse_merge(a.part2, a.nch2, a.h_kv, g, bt, tid);
+    if ((tid & 15) == 0) Lh[tid >> 4] = ms.x + (fast_log2(ms.y) + kLog2CoarseRatio);
+  }
+  const int jw = j0 + wave * 64;
+  f32x4 acc[4];
+  split_logits_mfma(kc1, a.n_c1, jw, qbase, lane, kst_all[wave], acc);
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int j = jw + 16 * nt + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[nt][i] = (j <= jmax) ? acc[nt][i] * a.c : kNegInf;
+  }
+  if (!coarse) {
+    // no coarse kernel: the exact LSE (every visible kernel is in chunk 0;
+    // later chunks see none and only write -inf)
+    float mc[4], sc[4];
+    split_chunk_partials(acc, lane, wave, red_m, red_s, mc, sc);
+    if (wave == 0 && (lane & 15) == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Lh[4 * (lane >> 4) + i] = mc[i] + fast_log2(sc[i]);
+  }
+  // the kernel before the chunk (block 64*chunk takes kernels j0-1 .. j0+3):
+  // wave 3, lane = 4 * head + quarter of d
+  float carry_part = 0.f;
+  const int jc = j0 - 1;
+  const bool carry_vis = chunk > 0 && jc <= jmax;
+  if (wave == 3 && carry_vis) {
+    const int h = lane >> 2, qd = lane & 3;
+    const uint16_t* qrow = qbase + (size_t)h * SEL_D + 32 * qd;
+    const uint16_t* krow = kc1 + (size_t)jc * SEL_D + 32 * qd;
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < 32; e += 8) {
+      const u32x4 qv = *(const u32x4*)(qrow + e), kv = *(const u32x4*)(krow + e);
+      const uint32_t qw[4] = {qv[0], qv[1], qv[2], qv[3]}, kw[4] = {kv[0], kv[1], kv[2], kv[3]};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        z = __builtin_fmaf(__uint_as_float(qw[u] << 16), __uint_as_float(kw[u] << 16), z);
+        z = __builtin_fmaf(__uint_as_float(qw[u] & 0xFFFF0000u), __uint_as_float(kw[u] & 0xFFFF0000u), z);
+      }
+    }
+    z += __shfl_xor(z, 1, 64);
+    z += __shfl_xor(z, 2, 64);
+    carry_part = z;   // every lane of the head's quad holds the dot product
+  }
+  __syncthreads();    // Lh ready
+  // S^shared of the wave's 64 kernels: the lane's 4 heads, then the 4 lane rows
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v += fast_exp2(acc[nt][i] - Lh[4 * (lane >> 4) + i]);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    const int j = jw + 16 * nt + (lane & 15);
+    if ((lane >> 4) == nt) sh[1 + wave * 64 + 16 * nt + (lane & 15)] = (j <= jmax) ? v : kNegInf;
+  }
+  if (wave == 3) {
+    float v = 0.f;
+    if (carry_vis) {
+      v = (lane & 3) == 0 ? fast_exp2(__builtin_fmaf(carry_part, a.c, -Lh[lane >> 2])) : 0.f;
+#pragma unroll
+      for (int o = 4; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+    }
+    if (lane == 0) sh[0] = carry_vis ? v : kNegInf;
+  }
+  __syncthreads();
+  const int b_p = p >> 6;
+  float* srow = a.S_cmp ? a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_blk : nullptr;
+  if (srow && chunk == a.nch - 1)
+    for (int blk = a.nch * 64 + tid; blk <= b_p; blk += 256) srow[blk] = kNegInf;
+  if (wave != 0) return;
+  const int blk = chunk * 64 + lane;
+  float v = sh[4 * lane];
+#pragma unroll
+  for (int q = 1; q < 5; ++q) v = fmaxf(v, sh[4 * lane + q]);
+  if (srow && blk <= b_p) srow[blk] = v;
+  if constexpr (LISTS) {
+    const int init_hi = min(a.N_init, b_p + 1);
+    const int loc_lo = max(0, b_p - a.N_local + 1);
+    const bool cand = blk >= init_hi && blk < loc_lo;
+    const uint64_t key = cand ? ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(~(uint32_t)blk) : 0ull;
+    const uint64_t sorted = wave_sort_desc<uint64_t>(key, lane);
+    const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+    if (lane < a.kc) a.cand[(row * a.nch + chunk) * a.kc + lane] = sorted;
+  }
 }
 
 // The top-k of the fused selection, one workgroup per row (token, group),
@@ -960,9 +1229,11 @@ __global__ void __launch_bounds__(MERGE_THREADS) scores_select_merge_kernel(Spli
 struct GenericScoresArgs {
   const void* Q;
   const void* Kc1;
+  const void* Kc2;   // coarse keys (LSE approximation), else null
   float* S_cmp;
-  int dtype, n_q, q_pos0, h_kv, G, d, n_c1, n_blk, B, l_C1, s_C1;
-  int64_t c1_cap;
+  int dtype, n_q, q_pos0, h_kv, G, d, n_c1, n_c2, n_blk, B, l_C1, s_C1;
+  int approx;
+  int64_t c1_cap, c2_cap;
   double scale;
 };
 
@@ -1007,8 +1278,31 @@ __global__ void __launch_bounds__(256) scores_generic_kernel(GenericScoresArgs a
   const T* K = (const T*)a.Kc1;
   const int hq = a.h_kv * a.G;
   const T* kbase = K + ((size_t)b * a.h_kv + g) * a.c1_cap * a.d;
+  // LSE approximation: coarse kernels of length 4 l_C1 and stride 4 s_C1
+  const int l2 = 4 * a.l_C1, s2 = 4 * a.s_C1;
+  const int nv2 = a.approx ? min(p >= l2 - 1 ? (p - l2 + 1) / s2 + 1 : 0, a.n_c2) : 0;
+  const T* k2base = nv2 > 0 ? (const T*)a.Kc2 + ((size_t)b * a.h_kv + g) * a.c2_cap * a.d : nullptr;
   for (int h = 0; h < a.G; ++h) {
     const T* q = Q + (((size_t)b * a.n_q + t) * hq + g * a.G + h) * a.d;
+    if (nv2 > 0) {
+      // lse~ = log sum over the visible coarse kernels of exp(z2) + ln(s_C2/s_C1)
+      double m = -__builtin_huge_val();
+      for (int j = threadIdx.x; j < nv2; j += blockDim.x) {
+        double z = 0.0;
+        for (int i = 0; i < a.d; ++i) z += ld<T>(q, i) * ld<T>(k2base, (size_t)j * a.d + i);
+        m = fmax(m, z * a.scale);
+      }
+      m = block_reduce_max(m, red);
+      double s = 0.0;
+      for (int j = threadIdx.x; j < nv2; j += blockDim.x) {
+        double z = 0.0;
+        for (int i = 0; i < a.d; ++i) z += ld<T>(q, i) * ld<T>(k2base, (size_t)j * a.d + i);
+        s += exp(z * a.scale - m);
+      }
+      s = block_reduce_sum(s, red);
+      if (threadIdx.x == 0) lse[h] = m + log(s) + log((double)s2 / (double)a.s_C1);
+      continue;
+    }
     double m = -__builtin_huge_val();
     for (int j = threadIdx.x; j < nv; j += blockDim.x) {
       double z = 0.0;
@@ -1058,37 +1352,71 @@ bool scores_fast_shape(const infv2_problem& p) {
 }
 bool scores_use_split(const infv2_problem& p) { return scores_fast_shape(p) && p.n_q <= 4; }
 
-size_t scores_workspace(const infv2_problem& p, int n_c1) {
+static int split_nch(int n_c1) { return (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK; }
+static int split_nch2(int n_c2) { return (n_c2 + SPLIT_CK - 1) / SPLIT_CK; }
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Split path workspace: exact LSE: the logits and the fine partials; LSE
+// approximation: the coarse partials only (one sweep, no logits).
+size_t scores_workspace(const infv2_problem& p, const KeySet& ks) {
   if (!scores_use_split(p)) return 0;
-  const int n_c1p = (n_c1 + 63) & ~63;
-  const int nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
   const size_t rows = (size_t)p.batch * p.n_q * p.h_kv;
-  return rows * SEL_G * (size_t)n_c1p * sizeof(float) + rows * nch * SEL_G * sizeof(float2);
+  if (p.lse_approx) return rows * split_nch2(ks.n_c2) * SEL_G * sizeof(float2);
+  const int n_c1p = (ks.n_c1 + 63) & ~63;
+  return rows * SEL_G * (size_t)n_c1p * sizeof(float) +
+         rows * split_nch(ks.n_c1) * SEL_G * sizeof(float2);
 }
 
 size_t scores_generic_lds(const infv2_problem& p, int n_c1) {
   return (size_t)(n_c1 + p.G + 1) * sizeof(double);
 }
 
-static SplitArgs split_args(const infv2_problem& p, const void* Q, const void* Kc1, float* S_cmp,
-                            void* ws, int n_c1, int n_blk, int64_t c1_cap, float scale) {
+static SplitArgs split_args(const infv2_problem& p, const void* Q, const KeySet& ks,
+                            float* S_cmp, void* ws, int n_blk, float scale) {
   SplitArgs a = {};
   a.Q = (const uint16_t*)Q;
-  a.Kc1 = (const uint16_t*)Kc1;
+  a.Kc1 = (const uint16_t*)ks.Kc1;
+  a.Kc2 = (const uint16_t*)ks.Kc2;
   a.S_cmp = S_cmp;
   a.n_q = p.n_q;
   a.q_pos0 = p.q_pos0;
   a.h_kv = p.h_kv;
-  a.n_c1 = n_c1;
-  a.n_c1p = (n_c1 + 63) & ~63;
+  a.n_c1 = ks.n_c1;
+  a.n_c1p = (ks.n_c1 + 63) & ~63;
+  a.n_c2 = ks.n_c2;
   a.n_blk = n_blk;
-  a.nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
-  a.c1_cap = c1_cap;
+  a.nch = split_nch(ks.n_c1);
+  a.nch2 = split_nch2(ks.n_c2);
+  a.c1_cap = ks.c1_cap;
+  a.c2_cap = ks.c2_cap;
   a.c = scale * kLog2e;
   const size_t rows = (size_t)p.batch * p.n_q * p.h_kv;
-  a.logits = (float*)ws;
-  a.part = (float2*)((char*)ws + rows * SEL_G * (size_t)a.n_c1p * sizeof(float));
+  if (p.lse_approx) {
+    a.part2 = (float2*)ws;
+  } else {
+    a.logits = (float*)ws;
+    a.part = (float2*)((char*)ws + rows * SEL_G * (size_t)a.n_c1p * sizeof(float));
+  }
   return a;
+}
+
+// The selection scores of the split path: exact LSE: logits (fine partials)
+// then pool; approximation: coarse partials, then one fused sweep over K^C1.
+// With a.cand set the pool / fused kernel also writes the candidate lists.
+static void launch_split_scores(const infv2_problem& p, const SplitArgs& a, hipStream_t stream) {
+  const dim3 grid(a.nch, p.h_kv, p.batch * p.n_q);
+  if (p.lse_approx) {
+    if (a.nch2 > 0)
+      hipLaunchKernelGGL(scores_split_logits_kernel<true>, dim3(a.nch2, p.h_kv, p.batch * p.n_q),
+                         dim3(256), 0, stream, a);
+    if (a.cand)
+      hipLaunchKernelGGL(scores_split_fused_kernel<true>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(scores_split_fused_kernel<false>, grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(scores_split_logits_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(scores_split_pool_kernel, grid, dim3(256), 0, stream, a);
+  }
 }
 
 // The fused selection (candidate lists from the pool kernel, then a per-row
@@ -1096,22 +1424,20 @@ static SplitArgs split_args(const infv2_problem& p, const void* Q, const void* K
 // per row.
 bool select_fused_shape(const infv2_problem& p, int n_c1) {
   if (!scores_use_split(p)) return false;
-  const int nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
+  const int nch = split_nch(n_c1);
   return p.k <= SELECT_MAX_KC && nch <= SELECT_MAX_CHUNKS && nch * p.k <= SELECT_MAX_KEYS;
 }
 
 // workspace beyond scores_workspace() rounded up to 256 bytes: the lists
 size_t select_fused_workspace(const infv2_problem& p, int n_c1) {
-  const int nch = (n_c1 + 1 + SPLIT_CK - 1) / SPLIT_CK;
-  return (size_t)p.batch * p.n_q * p.h_kv * nch * p.k * sizeof(uint64_t);
+  return (size_t)p.batch * p.n_q * p.h_kv * split_nch(n_c1) * p.k * sizeof(uint64_t);
 }
 
-hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const void* Kc1,
-                               float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, int n_c1,
-                               int n_blk, int64_t c1_cap, float scale, int budget,
-                               hipStream_t stream) {
-  SplitArgs a = split_args(p, Q, Kc1, S_cmp, ws, n_c1, n_blk, c1_cap, scale);
-  a.cand = (uint64_t*)((char*)ws + ((scores_workspace(p, n_c1) + 255) & ~(size_t)255));
+hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeySet& ks,
+                               float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, int n_blk,
+                               float scale, int budget, hipStream_t stream) {
+  SplitArgs a = split_args(p, Q, ks, S_cmp, ws, n_blk, scale);
+  a.cand = (uint64_t*)((char*)ws + align256(scores_workspace(p, ks)));
   a.idx = idx;
   a.n_sel = n_sel;
   a.k = p.k;
@@ -1119,47 +1445,51 @@ hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const void
   a.N_init = p.N_init;
   a.N_local = p.N_local;
   a.budget = budget;
-  const dim3 grid(a.nch, p.h_kv, p.batch * p.n_q);
-  hipLaunchKernelGGL(scores_split_logits_kernel, grid, dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(scores_split_pool_kernel, grid, dim3(256), 0, stream, a);
+  launch_split_scores(p, a, stream);
   hipLaunchKernelGGL(scores_select_merge_kernel, dim3(p.h_kv, p.batch * p.n_q),
                      dim3(MERGE_THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void* Kc1,
-                               float* S_cmp, void* ws, int n_c1, int n_blk, int64_t c1_cap,
-                               float scale, hipStream_t stream) {
+hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const KeySet& ks,
+                               float* S_cmp, void* ws, int n_blk, float scale,
+                               hipStream_t stream) {
   if (scores_use_split(p)) {
-    SplitArgs a = split_args(p, Q, Kc1, S_cmp, ws, n_c1, n_blk, c1_cap, scale);
-    dim3 grid(a.nch, p.h_kv, p.batch * p.n_q);
-    hipLaunchKernelGGL(scores_split_logits_kernel, grid, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(scores_split_pool_kernel, grid, dim3(256), 0, stream, a);
+    launch_split_scores(p, split_args(p, Q, ks, S_cmp, ws, n_blk, scale), stream);
     return hipGetLastError();
   }
   if (scores_fast_shape(p)) {
-    ScoresArgs a;
+    ScoresArgs a = {};
     a.Q = (const uint16_t*)Q;
-    a.Kc1 = (const uint16_t*)Kc1;
+    a.Kc1 = (const uint16_t*)ks.Kc1;
+    a.Kc2 = (const uint16_t*)ks.Kc2;
     a.S_cmp = S_cmp;
     a.batch = p.batch;
     a.n_q = p.n_q;
     a.q_pos0 = p.q_pos0;
     a.h_kv = p.h_kv;
-    a.n_c1 = n_c1;
+    a.n_c1 = ks.n_c1;
+    a.n_c2 = ks.n_c2;
     a.n_blk = n_blk;
     a.tiles = (p.n_q + SEL_TOK_WG - 1) / SEL_TOK_WG;
-    a.c1_cap = c1_cap;
+    a.c1_cap = ks.c1_cap;
+    a.c2_cap = ks.c2_cap;
     a.c = scale * kLog2e;
     const int wgs = a.tiles * p.h_kv * p.batch;
     dim3 grid(8 % p.h_kv == 0 ? ((wgs + 7) / 8) * 8 : wgs);
-    hipLaunchKernelGGL(scores_prefill_kernel, grid, dim3(64 * FAST_WAVES), 0, stream, a);
-    hipLaunchKernelGGL(scores_exact_kernel, dim3(wgs), dim3(256), 0, stream, a);
+    if (p.lse_approx) {
+      hipLaunchKernelGGL(scores_prefill_kernel<true>, grid, dim3(64 * FAST_WAVES), 0, stream, a);
+      hipLaunchKernelGGL(scores_exact_kernel<true>, dim3(wgs), dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL(scores_prefill_kernel<false>, grid, dim3(64 * FAST_WAVES), 0, stream, a);
+      hipLaunchKernelGGL(scores_exact_kernel<false>, dim3(wgs), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
   }
-  GenericScoresArgs a;
+  GenericScoresArgs a = {};
   a.Q = Q;
-  a.Kc1 = Kc1;
+  a.Kc1 = ks.Kc1;
+  a.Kc2 = ks.Kc2;
   a.S_cmp = S_cmp;
   a.dtype = p.dtype;
   a.n_q = p.n_q;
@@ -1167,15 +1497,18 @@ hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const void
   a.h_kv = p.h_kv;
   a.G = p.G;
   a.d = p.d;
-  a.n_c1 = n_c1;
+  a.n_c1 = ks.n_c1;
+  a.n_c2 = ks.n_c2;
   a.n_blk = n_blk;
   a.B = p.B;
   a.l_C1 = p.l_C1;
   a.s_C1 = p.s_C1;
-  a.c1_cap = c1_cap;
+  a.approx = p.lse_approx;
+  a.c1_cap = ks.c1_cap;
+  a.c2_cap = ks.c2_cap;
   a.scale = scale;
   dim3 grid(p.n_q, p.h_kv, p.batch);
-  const size_t lds = scores_generic_lds(p, n_c1);
+  const size_t lds = scores_generic_lds(p, ks.n_c1);
   if (p.dtype == INFV2_F32)
     hipLaunchKernelGGL(scores_generic_kernel<float>, grid, dim3(256), lds, stream, a);
   else
