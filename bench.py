@@ -61,9 +61,20 @@ def visible_kernels(p, l_C1=32, s_C1=16):
     return np.where(p >= l_C1 - 1, (p - l_C1 + 1) // s_C1 + 1, 0)
 
 
-def selection_flops_per_pass(cfg, positions):
-    """b * h_q * 2d * sum_p |V(p)|  (one pass over the visible kernels)."""
-    return float(cfg.batch * cfg.h_q * 2 * cfg.d * visible_kernels(positions).sum())
+def selection_flops_per_pass(cfg, positions, l_len=None, s_len=None):
+    """b * h_q * 2d * sum_p |V(p)|  (one pass over the visible kernels of
+    length l_len and stride s_len: K^C1's by default)."""
+    vis = visible_kernels(positions, l_len or cfg.l_C1, s_len or cfg.s_C1)
+    return float(cfg.batch * cfg.h_q * 2 * cfg.d * vis.sum())
+
+
+def selection_flops_approx(cfg, positions):
+    """The LSE approximation: the coarse sweep (kernels of 4 l_C1 at stride
+    4 s_C1), one sweep over K^C1, and a second fine sweep for the positions
+    that see no coarse kernel (they keep the exact LSE)."""
+    early = positions[positions < 4 * cfg.l_C1 - 1]
+    return (selection_flops_per_pass(cfg, positions, 4 * cfg.l_C1, 4 * cfg.s_C1) +
+            selection_flops_per_pass(cfg, positions) + selection_flops_per_pass(cfg, early))
 
 
 def attention_flops(cfg, positions, budget):
@@ -74,16 +85,18 @@ def attention_flops(cfg, positions, budget):
     return float(cfg.batch * cfg.h_q * 4 * cfg.d * keys.sum())
 
 
-def decode_bytes(cfg, budget):
-    """Algorithmic HBM bytes of one decode step: K^C1 of every visible kernel,
-    the selected K and V blocks, Q and O."""
+def decode_bytes(cfg, budget, lse_approx=False):
+    """Algorithmic HBM bytes of one decode step: K^C1 of every visible kernel
+    (and K^C2 of every visible coarse kernel with the LSE approximation), the
+    selected K and V blocks, Q and O."""
     L = cfg.n_kv
     n_c1 = (L - cfg.l_C1) // cfg.s_C1 + 1
+    n_c2 = (L - 4 * cfg.l_C1) // (4 * cfg.s_C1) + 1 if lse_approx else 0
     nsel = min((L - 1) // cfg.B + 1, budget)
-    kc1 = n_c1 * cfg.d * 2
+    kc = (n_c1 + n_c2) * cfg.d * 2
     kv = nsel * cfg.B * cfg.d * 2 * 2
     qo = 2 * cfg.G * cfg.d * 2
-    return float(cfg.batch * cfg.h_kv * (kc1 + kv + qo))
+    return float(cfg.batch * cfg.h_kv * (kc + kv + qo))
 
 
 def kernel_source_hash():
@@ -125,19 +138,19 @@ class StageTimer:
         return {n: v / steps for n, v in self.ms.items()}
 
 
-def bench_pipelined(lp, Q, K, V, Kc1, O_ref, lse_ref, steps, warmup, n_chunks):
+def bench_pipelined(lp, Q, K, V, Kc1, O_ref, lse_ref, steps, warmup, n_chunks, Kc2=None):
     """The same prefill as a two-stream pipeline over query ranges (selection
     of range i+1 beside attention of range i); checks it reproduces the serial
     outputs bitwise."""
     pipe = tbs.PrefillPipeline(lp, n_chunks)
     O2, lse2 = torch.empty_like(O_ref), torch.empty_like(lse_ref)
     for _ in range(warmup):
-        pipe.run(Q, K, V, Kc1, O2, lse2)
+        pipe.run(Q, K, V, Kc1, O2, lse2, Kc2=Kc2)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        pipe.run(Q, K, V, Kc1, O2, lse2)
+        pipe.run(Q, K, V, Kc1, O2, lse2, Kc2=Kc2)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
@@ -146,15 +159,19 @@ def bench_pipelined(lp, Q, K, V, Kc1, O_ref, lse_ref, steps, warmup, n_chunks):
             "same_output_as_serial": bool(torch.equal(O2, O_ref) and torch.equal(lse2, lse_ref))}
 
 
-def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None, pipeline_chunk=8192):
-    log(f"[bench] {cfg.name}: generating inputs")
+def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None, pipeline_chunk=8192,
+                  lse_approx=False):
+    log(f"[bench] {cfg.name}{' (LSE approximation)' if lse_approx else ''}: generating inputs")
     x = make_inputs(cfg)
     dev = torch.device("cuda:0")
     Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
     del x
-    lp = problem_of(cfg)
+    lp = problem_of(cfg, lse_approx=lse_approx)
     n_blk, bud, n_c1 = tbs.n_blocks(lp), tbs.budget(lp), tbs.n_kernels(lp)
     Kc1 = torch.empty((lp.batch, lp.h_kv, n_c1, lp.d), dtype=Q.dtype, device=dev)
+    n_c2 = tbs.n_coarse_kernels(lp)
+    Kc2 = (torch.empty((lp.batch, lp.h_kv, n_c2, lp.d), dtype=Q.dtype, device=dev)
+           if lse_approx else None)
     S = torch.empty((lp.batch, lp.h_kv, lp.n_q, n_blk), dtype=torch.float32, device=dev)
     idx = torch.empty((lp.batch, lp.h_kv, lp.n_q, bud), dtype=torch.int32, device=dev)
     nsel = torch.empty((lp.batch, lp.h_kv, lp.n_q), dtype=torch.int32, device=dev)
@@ -164,11 +181,14 @@ def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None, pipelin
     ws_a = torch.empty(max(tbs.sparse_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
     fns = [
         lambda: tbs.compress_k(lp, K, Kc1),
-        lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s),
+        lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s, Kc2=Kc2),
         lambda: tbs.topk_select(lp, S, idx, nsel),
         lambda: tbs.sparse_attn(lp, Q, K, V, idx, nsel, O, lse, ws_a),
     ]
     names = ["compress_k", "block_scores", "topk_select", "sparse_attn"]
+    if lse_approx:
+        fns.insert(1, lambda: tbs.compress_k2(lp, K, Kc2))
+        names.insert(1, "compress_k2")
     log(f"[bench] {cfg.name}: warmup {warmup}")
     for _ in range(warmup):
         for fn in fns:
@@ -185,13 +205,18 @@ def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None, pipelin
     pos = np.arange(cfg.n_kv)
     out = dict(ms_per_step=ms, wall_ms_per_step=wall, stages_ms=stage,
                tokens_per_s=cfg.batch * cfg.n_q / (ms / 1e3),
-               sel_flops_2pass=2 * selection_flops_per_pass(cfg, pos),
                attn_flops=attention_flops(cfg, pos, bud))
-    out["algo_tflops"] = (out["sel_flops_2pass"] + out["attn_flops"]) / (ms / 1e3) / 1e12
+    if lse_approx:
+        # one sweep over K^C1 plus the coarse sweep over K^C2 (1/4 the kernels)
+        out["lse_approx"] = True
+        out["sel_flops"] = selection_flops_approx(cfg, pos)
+    else:
+        out["sel_flops"] = out["sel_flops_2pass"] = 2 * selection_flops_per_pass(cfg, pos)
+    out["algo_tflops"] = (out["sel_flops"] + out["attn_flops"]) / (ms / 1e3) / 1e12
     out["frac_of_bf16_peak"] = out["algo_tflops"] / PEAK_BF16_TFLOPS
     if pipeline_chunk and lp.batch == 1 and lp.n_q > pipeline_chunk:
         out["pipelined"] = bench_pipelined(lp, Q, K, V, Kc1, O, lse, steps, warmup,
-                                           lp.n_q // pipeline_chunk)
+                                           lp.n_q // pipeline_chunk, Kc2=Kc2)
     if with_dense:
         dsteps = dense_steps or max(1, steps // 2)
         ws_d = torch.empty(max(tbs.dense_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
@@ -208,19 +233,26 @@ def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None, pipelin
     return out
 
 
-def bench_decode(cfg, steps, warmup):
-    log(f"[bench] {cfg.name}: generating the KV cache")
+def bench_decode(cfg, steps, warmup, lse_approx=False):
+    log(f"[bench] {cfg.name}{' (LSE approximation)' if lse_approx else ''}: "
+        "generating the KV cache")
     x = make_inputs(cfg)
     dev = torch.device("cuda:0")
     Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
     del x
-    lp = problem_of(cfg)
-    prev = problem_of(cfg, n_kv=cfg.n_kv - 1, q_pos0=cfg.n_kv - 2, kv_cap=cfg.n_kv)
+    lp = problem_of(cfg, lse_approx=lse_approx)
+    prev = problem_of(cfg, n_kv=cfg.n_kv - 1, q_pos0=cfg.n_kv - 2, kv_cap=cfg.n_kv,
+                      lse_approx=lse_approx)
     n_blk, bud, n_c1 = tbs.n_blocks(lp), tbs.budget(lp), tbs.n_kernels(lp)
     n_prev = tbs.n_kernels(prev)
     lp.c1_cap = prev.c1_cap = n_c1
     Kc1 = torch.empty((lp.batch, lp.h_kv, n_c1, lp.d), dtype=Q.dtype, device=dev)
     tbs.compress_k(prev, K, Kc1)           # the cache before this step
+    Kc2, n_c2, n_prev2 = None, tbs.n_coarse_kernels(lp), tbs.n_coarse_kernels(prev)
+    if lse_approx:
+        lp.c2_cap = prev.c2_cap = n_c2
+        Kc2 = torch.empty((lp.batch, lp.h_kv, n_c2, lp.d), dtype=Q.dtype, device=dev)
+        tbs.compress_k2(prev, K, Kc2)
     S = torch.empty((lp.batch, lp.h_kv, 1, n_blk), dtype=torch.float32, device=dev)
     idx = torch.empty((lp.batch, lp.h_kv, 1, bud), dtype=torch.int32, device=dev)
     nsel = torch.empty((lp.batch, lp.h_kv, 1), dtype=torch.int32, device=dev)
@@ -233,13 +265,17 @@ def bench_decode(cfg, steps, warmup):
     # kernel); S^cmp is not stored
     fns = [
         lambda: tbs.compress_k(lp, K, Kc1, c1_begin=n_prev, c1_end=n_c1),
-        lambda: tbs.select_blocks(lp, Q, Kc1, None, idx, nsel, ws_s),
+        lambda: tbs.select_blocks(lp, Q, Kc1, None, idx, nsel, ws_s, Kc2=Kc2),
         lambda: tbs.sparse_attn(lp, Q, K, V, idx, nsel, O, lse, ws_a),
     ]
     names = ["compress_append", "select_blocks", "sparse_attn"]
+    if lse_approx and n_c2 > n_prev2:
+        # this step also completes a coarse kernel (every 64th token)
+        fns.insert(1, lambda: tbs.compress_k2(lp, K, Kc2, c2_begin=n_prev2, c2_end=n_c2))
+        names.insert(1, "compress2_append")
     # the same step with the separate score and top-k calls, for comparison
-    fns_sep = [fns[0], lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s),
-               lambda: tbs.topk_select(lp, S, idx, nsel), fns[2]]
+    fns_sep = fns[:-2] + [lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s, Kc2=Kc2),
+                          lambda: tbs.topk_select(lp, S, idx, nsel), fns[-1]]
     for _ in range(warmup):
         for fn in fns:
             fn()
@@ -286,7 +322,7 @@ def bench_decode(cfg, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     sep_ms = e0.elapsed_time(e1) / steps
-    nbytes = decode_bytes(cfg, bud)
+    nbytes = decode_bytes(cfg, bud, lse_approx)
     out = dict(step_us=step_ms * 1e3, us_per_token=step_ms * 1e3 / cfg.batch,
                eager_step_us=eager_ms * 1e3, timing="HIP graph replay of the whole step",
                separate_topk_step_us=sep_ms * 1e3,
@@ -362,6 +398,10 @@ def main():
                     help="run one workload alone and print its record (profiling runs); "
                          "'copy' is a plain 256 MiB device copy used to calibrate the "
                          "FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--lse-approx", action="store_true",
+                    help="with --only: the LSE approximation instead of the exact LSE")
+    ap.add_argument("--no-approx", action="store_true",
+                    help="skip the LSE-approximation records")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -382,14 +422,15 @@ def main():
             return
         c = CONFIGS[args.only]
         if args.only == "decode":
-            rec = bench_decode(c, args.steps, args.warmup)
+            rec = bench_decode(c, args.steps, args.warmup, lse_approx=args.lse_approx)
         elif args.only == "dense_switch":
             rec = bench_dense_switch(c, args.steps, args.warmup)
         else:
             pipe = 0 if (args.no_pipeline or args.only == "prefill32k") else 8192
             rec = bench_prefill(c, args.steps, args.warmup, with_dense=not args.no_dense,
-                                pipeline_chunk=pipe)
-        print(json.dumps({"workload": args.only, **rec}), flush=True)
+                                pipeline_chunk=pipe, lse_approx=args.lse_approx)
+        name = args.only + ("_lse_approx" if args.lse_approx else "")
+        print(json.dumps({"workload": name, **rec}), flush=True)
         return
 
     cfg = CONFIGS["prefill32k"]
@@ -433,6 +474,20 @@ def main():
         c5 = CONFIGS["dense_switch"]
         r5 = bench_dense_switch(c5, args.steps, args.warmup)
         extra["dense_switch"] = r5
+        if not args.no_approx:
+            # the pages' default selection: the LSE approximation (its own
+            # oracle mode and parity tests)
+            ra = bench_prefill(cfg, args.steps, args.warmup, with_dense=False, pipeline_chunk=0,
+                               lse_approx=True)
+            extra["prefill32k_lse_approx"] = ra
+            log(f"[bench] prefill32k (LSE approx): {ra['ms_per_step']:.3f} ms/step")
+            rb = bench_prefill(c3, max(2, args.steps // 5), 1, with_dense=False,
+                               pipeline_chunk=0 if args.no_pipeline else 8192, lse_approx=True)
+            extra["prefill128k_lse_approx"] = rb
+            log(f"[bench] prefill128k (LSE approx): {rb['ms_per_step']:.3f} ms/step")
+            rc = bench_decode(c4, max(20, args.steps * 5), args.warmup, lse_approx=True)
+            extra["decode_lse_approx"] = rc
+            log(f"[bench] decode (LSE approx): {rc['step_us']:.1f} us/step")
 
     cpu = None
     if not args.no_cpu:

@@ -346,12 +346,14 @@ class PrefillPipeline:
         kv_cap = prob.kv_cap or prob.n_kv
         self.n_c1 = n_kernels(prob)
         c1_cap = prob.c1_cap or self.n_c1
+        c2_cap = prob.c2_cap or n_coarse_kernels(prob)
         cuts = sorted({0, n_q} | {min(n_q, round(n_q * i / n_chunks / prob.B) * prob.B)
                                   for i in range(1, n_chunks)})
         self.chunks = []
         for r0, r1 in zip(cuts[:-1], cuts[1:]):
             p = Problem(**{**prob.__dict__, "n_q": r1 - r0, "q_pos0": prob.q_pos0 + r0,
-                           "n_kv": prob.q_pos0 + r1, "kv_cap": kv_cap, "c1_cap": c1_cap})
+                           "n_kv": prob.q_pos0 + r1, "kv_cap": kv_cap, "c1_cap": c1_cap,
+                           "c2_cap": c2_cap})
             self.chunks.append(dict(
                 p=p, r0=r0, r1=r1,
                 S=torch.empty((1, p.h_kv, p.n_q, n_blocks(p)), dtype=torch.float32,
@@ -368,8 +370,9 @@ class PrefillPipeline:
         self.att_stream = torch.cuda.Stream(device=device)
         self.done = torch.cuda.Event()
 
-    def run(self, Q, K, V, Kc1, O, lse=None, attn_events=None):
-        """Enqueue one prefill: compress, then per range selection and attention.
+    def run(self, Q, K, V, Kc1, O, lse=None, attn_events=None, Kc2=None):
+        """Enqueue one prefill: compress (K^C1, and K^C2 into ``Kc2`` with the
+        LSE approximation), then per range selection and attention.
         Both streams first wait for the caller's current stream; the caller's
         stream then waits for the end.  With ``attn_events`` (a list of
         (start, end) timing-event pairs, one per range) the attention launches
@@ -381,9 +384,13 @@ class PrefillPipeline:
         # the previous run's attention has consumed every range's idx/n_sel
         s_sel.wait_event(self.done)
         compress_k(prob, K, Kc1, stream=s_sel)
+        if prob.lse_approx:
+            if Kc2 is None:
+                raise ValueError("the LSE approximation needs a K^C2 buffer (Kc2)")
+            compress_k2(prob, K, Kc2, stream=s_sel)
         for c in self.chunks:
             p = c["p"]
-            block_scores(p, Q[:, c["r0"]:c["r1"]], Kc1, c["S"], c["ws_s"], stream=s_sel)
+            block_scores(p, Q[:, c["r0"]:c["r1"]], Kc1, c["S"], c["ws_s"], stream=s_sel, Kc2=Kc2)
             topk_select(p, c["S"], c["idx"], c["n_sel"], stream=s_sel)
             c["ready"].record(s_sel)
         for i, c in enumerate(self.chunks):
