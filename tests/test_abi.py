@@ -134,9 +134,13 @@ def test_workspace_sizes_and_errors(L):
     assert L.infv2_block_scores_workspace(ctypes.byref(dec_a.to_c())) == 16 * 2 * 8 * 16 * 8
     pre = _prob(n_q=32768, n_kv=32768)
     assert L.infv2_block_scores_workspace(ctypes.byref(pre.to_c())) == 0
-    # prefill selection keeps S^cmp in the workspace unless the caller takes it
-    assert L.infv2_select_blocks_workspace(ctypes.byref(pre.to_c()), 1) == 0
-    assert L.infv2_select_blocks_workspace(ctypes.byref(pre.to_c()), 0) == 2 * 32768 * 512 * 4
+    # prefill selection streams the top-k: one mark per 16-token tile
+    assert L.infv2_select_blocks_workspace(ctypes.byref(pre.to_c()), 0) == 2 * 2048 * 4
+    assert L.infv2_select_blocks_workspace(ctypes.byref(pre.to_c()), 1) == 2 * 2048 * 4
+    # shapes without a fused path keep S^cmp in the workspace
+    pre64 = _prob(n_q=32768, n_kv=32768, k=64)
+    assert L.infv2_select_blocks_workspace(ctypes.byref(pre64.to_c()), 1) == 0
+    assert L.infv2_select_blocks_workspace(ctypes.byref(pre64.to_c()), 0) == 2 * 32768 * 512 * 4
     # packed K and V: 2 tensors x h_kv x (blocks x B) keys x d x 2 bytes
     assert L.infv2_dense_attn_workspace(ctypes.byref(pre.to_c())) == 2 * 2 * 32768 * 128 * 2
     for s in (0, -1, -2, -3, -4, 7):

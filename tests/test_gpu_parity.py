@@ -201,12 +201,14 @@ def test_extreme_logits_take_exact_pass():
     _say(rep)
 
 
-def test_prefill_pipeline_matches_one_shot():
+@pytest.mark.parametrize("lean", [False, True])
+def test_prefill_pipeline_matches_one_shot(lean):
     # the two-stream range pipeline computes every row exactly as the one-shot
-    # path: O and LSE bitwise equal, and both match the oracle
+    # path: O and LSE bitwise equal, and both match the oracle (lean: the
+    # streamed top-k selection, no S^cmp buffers)
     cfg = CONFIGS["prefill32k"]
     n_kv = 2600
-    _say("case: prefill pipeline, n_kv", n_kv)
+    _say("case: prefill pipeline, n_kv", n_kv, "lean", lean)
     x = make_inputs(cfg, n_kv=n_kv, batch=1, seed=23)
     lp, op = problems(cfg, n_kv=n_kv, batch=1)
     ref = run_gpu_sparse(lp, x["q"], x["k"], x["v"])
@@ -215,7 +217,7 @@ def test_prefill_pipeline_matches_one_shot():
     Kc1 = torch.empty((1, lp.h_kv, tbs.n_kernels(lp), lp.d), dtype=Q.dtype, device=dev)
     O = torch.empty_like(Q)
     lse = torch.empty((1, lp.h_q, lp.n_q), dtype=torch.float32, device=dev)
-    pipe = tbs.PrefillPipeline(lp, 3)
+    pipe = tbs.PrefillPipeline(lp, 3, lean=lean)
     assert [c["r0"] for c in pipe.chunks] == [0, 896, 1728]
     for _ in range(2):                  # a second run reuses every buffer
         pipe.run(Q, K, V, Kc1, O, lse)

@@ -108,18 +108,82 @@ def test_fused_selection_matches_oracle_decode():
     _say(rep)
 
 
-def test_select_blocks_prefill_shape_uses_two_kernel_path():
+@pytest.mark.parametrize("n_kv,batch,n_q,k,approx", [
+    (2300, 1, 2300, 16, False),    # ragged last tile
+    (3000, 2, 3000, 32, False),
+    (2100, 1, 1333, 8, False),     # query offset 767, ragged
+    (1500, 1, 1500, 0, False),     # init and local only
+    (700, 1, 700, 16, False),      # fewer candidates than k for most rows
+    (2300, 2, 2300, 16, True),     # LSE approximation (early tiles: exact kernel)
+    (1800, 1, 1700, 16, True),
+])
+def test_prefill_streamed_topk_equals_separate_calls(n_kv, batch, n_q, k, approx):
+    # the prefill selection streams the top-k through the score sweep; idx,
+    # n_sel and (when asked for) S^cmp equal the two-call path bit for bit
     cfg = CONFIGS["prefill32k"]
-    n_kv = 2300
-    _say("case: select_blocks prefill", n_kv)
-    x, lp, op, Q, Kc1 = _selection_inputs(cfg, n_kv, 1, n_kv, seed=8)
-    S_ref, idx_ref, n_ref = _separate(lp, Q, Kc1)
-    idx, n_sel = tbs.select_blocks(lp, Q, Kc1)          # scores in the workspace
-    S2 = torch.empty_like(S_ref)
-    idx2, n_sel2 = tbs.select_blocks(lp, Q, Kc1, S_cmp=S2)
+    _say(f"case: prefill select_blocks n_kv={n_kv} batch={batch} n_q={n_q} k={k} approx={approx}")
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=8 + n_kv + k)
+    q0 = n_kv - n_q
+    lp, _ = problems(cfg, n_kv=n_kv, batch=batch, n_q=n_q, q_pos0=q0, k=k, lse_approx=approx)
+    dev = torch.device("cuda:0")
+    Q = x["q"][:, q0:].contiguous().to(dev)
+    K = x["k"].to(dev)
+    Kc1 = tbs.compress_k(lp, K)
+    Kc2 = tbs.compress_k2(lp, K) if approx else None
+    S_ref = tbs.block_scores(lp, Q, Kc1, Kc2=Kc2)
+    idx_ref, n_ref = tbs.topk_select(lp, S_ref)
+    idx, n_sel = tbs.select_blocks(lp, Q, Kc1, Kc2=Kc2)
+    S2 = torch.full_like(S_ref, float("nan"))
+    idx2, n_sel2 = tbs.select_blocks(lp, Q, Kc1, S_cmp=S2, Kc2=Kc2)
+    torch.cuda.synchronize()
+    assert torch.equal(n_sel, n_ref)
+    assert torch.equal(idx, idx_ref)
+    assert torch.equal(idx2, idx_ref) and torch.equal(n_sel2, n_ref)
+    for t in (0, n_q // 2, n_q - 1):
+        b_p = (q0 + t) // 64
+        assert torch.equal(torch.nan_to_num(S2[:, :, t, :b_p + 1]),
+                           torch.nan_to_num(S_ref[:, :, t, :b_p + 1]))
+
+
+def test_prefill_streamed_topk_extreme_logits_take_exact_kernel():
+    cfg = CONFIGS["prefill32k"]
+    n_kv, batch = 1500, 2
+    _say("case: prefill select_blocks extreme logits")
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=5)
+    x["q"][0, :, 5, :] *= 64
+    x["k"][1, 1200:1264, 1, :] *= 64
+    lp, op = problems(cfg, n_kv=n_kv, batch=batch)
+    dev = torch.device("cuda:0")
+    Q, K = x["q"].to(dev), x["k"].to(dev)
+    Kc1 = tbs.compress_k(lp, K)
+    S_ref = tbs.block_scores(lp, Q, Kc1)
+    idx_ref, n_ref = tbs.topk_select(lp, S_ref)
+    idx, n_sel = tbs.select_blocks(lp, Q, Kc1)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx_ref) and torch.equal(n_sel, n_ref)
-    assert torch.equal(idx2, idx_ref) and torch.equal(n_sel2, n_ref)
+
+
+def test_prefill_streamed_topk_all_ties():
+    # Q = 0: every candidate ties; the lowest k candidates win
+    cfg = CONFIGS["prefill32k"]
+    n_kv = 1600
+    x = make_inputs(cfg, n_kv=n_kv, batch=1, seed=1)
+    x["q"].zero_()
+    lp, _ = problems(cfg, n_kv=n_kv, batch=1)
+    dev = torch.device("cuda:0")
+    Q, K = x["q"].to(dev), x["k"].to(dev)
+    Kc1 = tbs.compress_k(lp, K)
+    idx, n_sel = tbs.select_blocks(lp, Q, Kc1)
+    torch.cuda.synchronize()
+    for t in (0, 63, 64, 500, 1200, 1599):
+        b_p = t // 64
+        local = set(range(max(0, b_p - 1), b_p + 1))
+        cand = [c for c in range(1, b_p + 1) if c not in local]
+        want = sorted({0} | local | set(cand[:16]))
+        for g in range(lp.h_kv):
+            n = int(n_sel[0, g, t])
+            assert idx[0, g, t, :n].tolist() == want
+            assert (idx[0, g, t, n:] == -1).all()
 
 
 def test_fused_selection_repeated_calls_share_workspace():

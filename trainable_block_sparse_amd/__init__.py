@@ -332,16 +332,20 @@ class PrefillPipeline:
     orders the two.  Each range is an ordinary call of the C ABI with
     q_pos0/n_q/n_kv of that range, so every output row is computed exactly as
     in the one-shot path (bitwise the same O and LSE).  Buffers and workspaces
-    are allocated once here; ``run`` allocates nothing.
+    are allocated once here; ``run`` allocates nothing.  With ``lean`` the
+    selection streams the top-k through the score sweep (select_blocks), so
+    no S^cmp buffer is held (2.1 GB at 128k); the two-call selection is
+    faster on MI355X and is the default.
     """
 
-    def __init__(self, prob: Problem, n_chunks: int, device=None):
+    def __init__(self, prob: Problem, n_chunks: int, device=None, lean: bool = False):
         if prob.batch != 1:
             raise ValueError("PrefillPipeline takes one sequence (batch == 1)")
         if use_dense(prob):
             raise ValueError("the dense switch applies: use dense_attn")
         device = device or torch.device("cuda", torch.cuda.current_device())
         self.prob = prob
+        self.lean = lean
         n_q = prob.n_q
         kv_cap = prob.kv_cap or prob.n_kv
         self.n_c1 = n_kernels(prob)
@@ -354,15 +358,15 @@ class PrefillPipeline:
             p = Problem(**{**prob.__dict__, "n_q": r1 - r0, "q_pos0": prob.q_pos0 + r0,
                            "n_kv": prob.q_pos0 + r1, "kv_cap": kv_cap, "c1_cap": c1_cap,
                            "c2_cap": c2_cap})
+            ws_bytes = select_blocks_workspace(p) if lean else block_scores_workspace(p)
             self.chunks.append(dict(
                 p=p, r0=r0, r1=r1,
-                S=torch.empty((1, p.h_kv, p.n_q, n_blocks(p)), dtype=torch.float32,
-                              device=device),
+                S=None if lean else torch.empty((1, p.h_kv, p.n_q, n_blocks(p)),
+                                                dtype=torch.float32, device=device),
                 idx=torch.empty((1, p.h_kv, p.n_q, budget(p)), dtype=torch.int32, device=device),
                 n_sel=torch.empty((1, p.h_kv, p.n_q), dtype=torch.int32, device=device),
                 lse=torch.empty((1, p.h_q, p.n_q), dtype=torch.float32, device=device),
-                ws_s=torch.empty(max(block_scores_workspace(p), 16), dtype=torch.uint8,
-                                 device=device),
+                ws_s=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device),
                 ws_a=torch.empty(max(sparse_attn_workspace(p), 16), dtype=torch.uint8,
                                  device=device),
                 ready=torch.cuda.Event()))
@@ -390,8 +394,13 @@ class PrefillPipeline:
             compress_k2(prob, K, Kc2, stream=s_sel)
         for c in self.chunks:
             p = c["p"]
-            block_scores(p, Q[:, c["r0"]:c["r1"]], Kc1, c["S"], c["ws_s"], stream=s_sel, Kc2=Kc2)
-            topk_select(p, c["S"], c["idx"], c["n_sel"], stream=s_sel)
+            q = Q[:, c["r0"]:c["r1"]]
+            if self.lean:
+                select_blocks(p, q, Kc1, None, c["idx"], c["n_sel"], c["ws_s"], stream=s_sel,
+                              Kc2=Kc2)
+            else:
+                block_scores(p, q, Kc1, c["S"], c["ws_s"], stream=s_sel, Kc2=Kc2)
+                topk_select(p, c["S"], c["idx"], c["n_sel"], stream=s_sel)
             c["ready"].record(s_sel)
         for i, c in enumerate(self.chunks):
             s_att.wait_event(c["ready"])

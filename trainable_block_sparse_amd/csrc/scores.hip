@@ -40,11 +40,124 @@ struct ScoresArgs {
   const uint16_t* Q;
   const uint16_t* Kc1;
   const uint16_t* Kc2;   // coarse keys (LSE approximation), else null
-  float* S_cmp;
+  float* S_cmp;          // null in the selection mode unless the caller wants it
+  // selection mode (top-k streamed inside the score sweep): outputs, and one
+  // mark per tile for the exact kernel (1: recompute this tile)
+  int32_t* idx;
+  int32_t* n_sel;
+  int32_t* marks;        // [batch][h_kv][tiles]
+  int k, N_init, N_local, budget;
   int batch, n_q, q_pos0, h_kv, n_c1, n_c2, n_blk, tiles;
   int64_t c1_cap, c2_cap;
   float c;  // scale * log2(e)
 };
+
+// ---------------------------------------------------------------------------
+// Streaming top-k inside a wave, for NT query tokens.  Candidate blocks enter
+// as 64-bit keys: order-preserving score bits << 32 | ~blk (unique; at equal
+// scores the lower block ranks higher; 0 = no key).  A key that beats the
+// token's threshold is appended to the token's 64-entry LDS buffer; when the
+// buffer could overflow on the next push it is sorted by one wave and cut to
+// its k best, whose k-th key becomes the threshold (keys are unique, so a key
+// below it can never reach the final top k).  Buffer entries at and past the
+// count are kept at 0.
+// ---------------------------------------------------------------------------
+template <int NT>
+struct TopkStream {
+  uint64_t tau[NT];   // keys <= tau are out (0 until k keys have been kept)
+  int cnt[NT];        // keys in the token's buffer
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int NT>
+__device__ __forceinline__ void topk_init(TopkStream<NT>& st, uint64_t* buf, int lane) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    st.tau[t] = 0ull;
+    st.cnt[t] = 0;
+    buf[t * 64 + lane] = 0ull;
+  }
+  wave_lds_sync();
+}
+
+// sort token t's buffer and keep its k best (all lanes active).  The pushes
+// write the buffer without waiting; the waits are here, where it is read and
+// rewritten (rarely: a few times per token).
+template <int NT>
+__device__ __forceinline__ void topk_compact(TopkStream<NT>& st, uint64_t* buf, int t, int lane,
+                                             int k) {
+  wave_lds_sync();
+  const uint64_t sorted = wave_sort_desc<uint64_t>(buf[t * 64 + lane], lane);
+  const int keep = min(st.cnt[t], k);
+  wave_lds_sync();
+  buf[t * 64 + lane] = lane < keep ? sorted : 0ull;
+  st.cnt[t] = keep;
+  if (keep > 0 && keep == k) st.tau[t] = readlane_u64(sorted, k - 1);
+  wave_lds_sync();
+}
+
+// each lane offers at most one key (0: none) for its token tl; at most
+// max_new keys per token per call (all lanes active)
+template <int NT>
+__device__ __forceinline__ void topk_push(TopkStream<NT>& st, uint64_t* buf, int tl, uint64_t key,
+                                          int lane, int k, int max_new) {
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const bool hit = tl == t && key > st.tau[t];
+    const uint64_t m = __ballot(hit);
+    if (hit) buf[t * 64 + st.cnt[t] + (int)__popcll(m & below)] = key;
+    st.cnt[t] += (int)__popcll(m);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (st.cnt[t] > 64 - max_new) topk_compact(st, buf, t, lane, k);
+}
+
+// Final selection of token t (after its last push): I(p) = init u local u
+// the kept keys, ascending and -1 padded, to out[0..budget) (budget <= 64),
+// and |I(p)| to *n_out.  Candidates lie strictly between the init and the
+// local blocks, so the ascending set is init, then the kept blocks in
+// ascending order, then local.
+template <int NT>
+__device__ __forceinline__ void topk_emit(TopkStream<NT>& st, uint64_t* buf, int t, int lane,
+                                          int k, int p, int N_init, int N_local, int budget,
+                                          int32_t* out, int32_t* n_out, bool write) {
+  topk_compact(st, buf, t, lane, k);
+  const int kk = st.cnt[t];
+  const uint64_t key = buf[t * 64 + lane];
+  const uint32_t nb_key = lane < kk ? (uint32_t)key : 0u;   // ~blk: larger = lower block
+  const uint32_t asc = wave_sort_desc<uint32_t>(nb_key, lane);  // lanes 0..kk-1: ascending blocks
+  const int b_p = p >> 6, nb = b_p + 1;
+  const int init_hi = min(N_init, nb);
+  const int loc_lo = max(0, b_p - N_local + 1);
+  int v = -1, n;
+  if (loc_lo <= init_hi) {             // init and local cover every causal block
+    n = nb;
+    v = lane < nb ? lane : -1;
+  } else {
+    n = init_hi + kk + (nb - loc_lo);
+    const int blk_j = (int)~__shfl(asc, max(0, min(lane - init_hi, 63)), 64);
+    if (lane < init_hi) v = lane;
+    else if (lane < init_hi + kk) v = blk_j;
+    else if (lane < n) v = loc_lo + (lane - init_hi - kk);
+  }
+  if (write) {
+    if (lane < budget) out[lane] = v;
+    if (lane == 0) *n_out = n;
+  }
+}
 
 // kernel j is causal for position p when its last token j*16+31 <= p
 __device__ __forceinline__ int last_visible_kernel(int p) { return p >= 31 ? (p - 31) >> 4 : -1; }
@@ -145,11 +258,14 @@ __device__ __forceinline__ void exact_chunk(const ScoresArgs& a, const uint8_t* 
 // kernel take the coarse estimate (a sum sweep over K^C2 with the same
 // machinery), the others the exact LSE; the score sweep then uses
 // 2^(z*c - L) with L = log2 of the row's normaliser.
-template <bool APPROX>
+// SELECT: the selection mode of the fast kernel (marks instead of the NaN
+// marker; idx / n_sel from a streaming top-k; S^cmp only when a.S_cmp is set).
+template <bool APPROX, bool SELECT>
 __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][SEL_CHUNK * SEL_ROW_BYTES];
   __shared__ float sbuf_all[4][SEL_TOK_WAVE][SEL_CHUNK + 1];
   __shared__ float lfine_all[4][2][32];   // APPROX: exact log2-normaliser per row
+  __shared__ uint64_t tkbuf_all[SELECT ? 4 : 1][SEL_TOK_WAVE][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -157,10 +273,15 @@ __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
   const int tile = bid % a.tiles;
   const int g = (bid / a.tiles) % a.h_kv;
   const int b = bid / (a.tiles * a.h_kv);
-  {
+  if constexpr (SELECT) {
+    if (a.marks[((size_t)b * a.h_kv + g) * a.tiles + tile] == 0) return;
+  } else {
     const float mark = a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tile * SEL_TOK_WG) * a.n_blk];
     if (!__builtin_isnan(mark)) return;
   }
+  TopkStream<SEL_TOK_WAVE> tk;
+  uint64_t* tkbuf = &tkbuf_all[SELECT ? wave : 0][0][0];
+  if constexpr (SELECT) topk_init<SEL_TOK_WAVE>(tk, tkbuf, lane);
   const int wg_t0 = tile * SEL_TOK_WG;
   const int t0 = wg_t0 + wave * SEL_TOK_WAVE;
   const int hq = a.h_kv * SEL_G;
@@ -242,15 +363,21 @@ __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < 32) {
-          const int tl = lane >> 3, bb = lane & 7;
-          float v = sbuf[tl][4 * bb];
+        const int tl = (lane >> 3) & 3, bb = lane & 7;
+        float v = sbuf[tl][4 * bb];
 #pragma unroll
-          for (int q = 1; q < 5; ++q) v = fmaxf(v, sbuf[tl][4 * bb + q]);
-          const int tok = t0 + tl;
-          const int blk = c * (SEL_CHUNK / 4) + bb;
-          if (tok < a.n_q && blk <= (a.q_pos0 + tok) >> 6)
-            a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_blk + blk] = v;
+        for (int q = 1; q < 5; ++q) v = fmaxf(v, sbuf[tl][4 * bb + q]);
+        const int tok = t0 + tl;
+        const int blk = c * (SEL_CHUNK / 4) + bb;
+        const int b_p = (a.q_pos0 + tok) >> 6;
+        if (lane < 32 && a.S_cmp && tok < a.n_q && blk <= b_p)
+          a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_blk + blk] = v;
+        if constexpr (SELECT) {
+          const bool cand = lane < 32 && tok < a.n_q && blk >= min(a.N_init, b_p + 1) &&
+                            blk < max(0, b_p - a.N_local + 1);
+          const uint64_t key = cand ? ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(~(uint32_t)blk)
+                                    : 0ull;
+          topk_push<SEL_TOK_WAVE>(tk, tkbuf, tl, key, lane, a.k, SEL_CHUNK / 4);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -363,7 +490,7 @@ __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
   if (lane < 4) sbuf[lane][0] = kNegInf;
   run_pass(std::integral_constant<int, PASS_SCORE>{}, false, nchunks, jmin_wg);
   // blocks with no visible kernel in the causal range
-  {
+  if (a.S_cmp) {
     const int tl = lane >> 4;
     const int tok = t0 + tl;
     if (tok < a.n_q) {
@@ -371,6 +498,16 @@ __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
       float* row = a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_blk;
       for (int blk = nchunks * (SEL_CHUNK / 4) + (lane & 15); blk <= b_p; blk += 16)
         row[blk] = kNegInf;
+    }
+  }
+  if constexpr (SELECT) {
+#pragma unroll
+    for (int tl = 0; tl < SEL_TOK_WAVE; ++tl) {
+      const int tok = t0 + tl;
+      const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + min(tok, a.n_q - 1);
+      topk_emit<SEL_TOK_WAVE>(tk, tkbuf, tl, lane, a.k, a.q_pos0 + min(tok, a.n_q - 1),
+                              a.N_init, a.N_local, a.budget, a.idx + row * a.budget,
+                              a.n_sel + row, tok < a.n_q);
     }
   }
 }
@@ -416,7 +553,9 @@ struct SelWave {
   int jm[2];         // last visible kernel per token (wave-uniform)
   int jm_l;          // the same for the token of this lane's row after the head sum
   int bp_l;          // its last causal block
-  float* srow;       // its S^cmp row
+  float* srow;       // its S^cmp row (null: not written)
+  TopkStream<2> tk;  // selection mode: streaming top-k of the wave's 2 tokens
+  uint64_t* tkbuf;   // their LDS buffers [2][64]
 };
 
 // z = Q K^C1^T for one chunk of 32 kernels staged in LDS (16-byte piece c of
@@ -447,7 +586,7 @@ __device__ __forceinline__ void chunk_mfma(const uint8_t* kb, const SelWave& w, 
 //              head's log2-normaliser), summed over the group's 16 heads,
 //              max-pooled over the kernels that intersect each block and
 //              written to S^cmp
-template <int PASS, bool MASKED, bool FIRST, bool LFORM = false>
+template <int PASS, bool MASKED, bool FIRST, bool LFORM = false, bool TOPK = false>
 __device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][2], int chunk,
                                            SelWave& w, int lane) {
   static_assert(PASS == PASS_SUM || PASS == PASS_SCORE, "fast passes");
@@ -514,7 +653,16 @@ __device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][
     const float prev = (r16 == 0 && nt == 0) ? w.carry : shr;
     const float bv = fmaxf(q, dpp<DPP_QUAD_BC0>(prev));   // same in all 4 lanes of the quad
     const int blk = chunk * (SEL_CHUNK / 4) + nt * 4 + (r16 >> 2);
-    if (!MASKED || blk <= w.bp_l) __builtin_nontemporal_store(bv, w.srow + blk);
+    if (w.srow && (!MASKED || blk <= w.bp_l)) __builtin_nontemporal_store(bv, w.srow + blk);
+    if constexpr (TOPK) {
+      // one lane of each quad offers the block when it is a candidate
+      const int init_hi = min(a.N_init, w.bp_l + 1);
+      const int loc_lo = max(0, w.bp_l - a.N_local + 1);
+      const bool cand = (r16 & 3) == 0 && blk >= init_hi && blk < loc_lo;
+      const uint64_t key = cand ? ((uint64_t)ordered_bits(bv) << 32) | (uint64_t)(~(uint32_t)blk)
+                                : 0ull;
+      topk_push<2>(w.tk, w.tkbuf, lane >> 5, key, lane, a.k, SEL_CHUNK / 4);
+    }
     // kernel 31 of this chunk: lane 31 (token 0) and lane 63 (token 1)
     const float k31_t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
     const float k31_t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
@@ -522,9 +670,14 @@ __device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][
   }
 }
 
-template <bool APPROX>
+// SELECT: the selection mode.  Each wave streams the top-k of its two tokens
+// through the score sweep (no S^cmp round trip; S^cmp is still written when
+// a.S_cmp is set) and writes idx / n_sel; the tile's mark tells the exact
+// kernel whether to redo it.
+template <bool APPROX, bool SELECT>
 __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * SEL_CHUNK_BYTES];
+  __shared__ uint64_t tkbuf_all[SELECT ? FAST_WAVES : 1][2][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -553,7 +706,15 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
   const int wg_t0 = tile * SEL_TOK_WG;
   const int t0 = wg_t0 + wave * FAST_TOK_WAVE;
   const int hq = a.h_kv * SEL_G;
-  float* srows = a.S_cmp + ((size_t)b * a.h_kv + g) * a.n_q * a.n_blk;
+  float* srows = a.S_cmp ? a.S_cmp + ((size_t)b * a.h_kv + g) * a.n_q * a.n_blk : nullptr;
+  const size_t tile_id = ((size_t)b * a.h_kv + g) * a.tiles + tile;
+  // hands the tile to the exact kernel
+  auto mark_tile = [&]() {
+    if (tid == 0) {
+      if constexpr (SELECT) a.marks[tile_id] = 1;
+      else srows[(size_t)wg_t0 * a.n_blk] = __builtin_nanf("");
+    }
+  };
 
   // Tokens past n_q (ragged last tile) repeat the last token: they compute
   // its values and write them to its row again.
@@ -571,7 +732,11 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
     const int tok = min(t0 + (lane >> 5), a.n_q - 1);
     w.jm_l = last_visible_kernel(a.q_pos0 + tok);
     w.bp_l = (a.q_pos0 + tok) >> 6;
-    w.srow = srows + (size_t)tok * a.n_blk;
+    w.srow = srows ? srows + (size_t)tok * a.n_blk : nullptr;
+  }
+  if constexpr (SELECT) {
+    w.tkbuf = &tkbuf_all[wave][0][0];
+    topk_init<2>(w.tk, w.tkbuf, lane);
   }
   const int wg_last = min(wg_t0 + SEL_TOK_WG - 1, a.n_q - 1);
   const int jmax_wg = last_visible_kernel(a.q_pos0 + wg_last);
@@ -594,7 +759,7 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
   // keeps the exact LSE) goes to the exact kernel.
   if constexpr (APPROX) {
     if (a.q_pos0 + wg_t0 < 127 && a.q_pos0 + wg_last >= 31) {
-      if (tid == 0) srows[(size_t)wg_t0 * a.n_blk] = __builtin_nanf("");
+      mark_tile();
       return;
     }
   }
@@ -636,13 +801,14 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
       f32x4 acc[2][2];
       chunk_mfma(slot(c), w, lane, acc);
       constexpr bool LF = APPROX && PASS == PASS_SCORE;
+      constexpr bool TK = SELECT && PASS == PASS_SCORE;
       if (SET_REF && c == 0) {
-        if (n_full > 0) chunk_valu<PASS, false, SET_REF, LF>(a, acc, c, w, lane);
-        else            chunk_valu<PASS, true, SET_REF, LF>(a, acc, c, w, lane);
+        if (n_full > 0) chunk_valu<PASS, false, SET_REF, LF, TK>(a, acc, c, w, lane);
+        else            chunk_valu<PASS, true, SET_REF, LF, TK>(a, acc, c, w, lane);
       } else if (c < n_full) {
-        chunk_valu<PASS, false, false, LF>(a, acc, c, w, lane);
+        chunk_valu<PASS, false, false, LF, TK>(a, acc, c, w, lane);
       } else {
-        chunk_valu<PASS, true, false, LF>(a, acc, c, w, lane);
+        chunk_valu<PASS, true, false, LF, TK>(a, acc, c, w, lane);
       }
       *(u32x4*)(piece_dst + ((c + 1) & 1) * SEL_CHUNK_BYTES) = next;
       next = load_piece(c + 1 + SEL_DEPTH);
@@ -705,15 +871,16 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
       bad = bad || (w.jm[tl] >= 0 && !(s >= 0x1p-64f && s <= 0x1p127f));
     }
   if (__syncthreads_or(bad)) {
-    if (tid == 0) srows[(size_t)wg_t0 * a.n_blk] = __builtin_nanf("");
+    mark_tile();
     return;
   }
   // sweep 2: S^C1 = 2^(z*c - M) / s (APPROX: 2^(z*c - L)), head-group sum,
   // max-pool, S^cmp
   w.carry = kNegInf;
   run_pass(std::integral_constant<int, PASS_SCORE>{}, std::false_type{}, nchunks, n_full);
-  // blocks with no visible kernel in the causal range
-  {
+  // blocks with no visible kernel in the causal range (never candidates: the
+  // chunks reach every block below the local ones)
+  if (srows) {
     const int tl = lane >> 5;
     const int tok = t0 + tl;
     if (tok < a.n_q) {
@@ -721,6 +888,16 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
       float* row = srows + (size_t)tok * a.n_blk;
       for (int blk = nchunks * (SEL_CHUNK / 4) + (lane & 31); blk <= b_p; blk += 32)
         row[blk] = kNegInf;
+    }
+  }
+  if constexpr (SELECT) {
+    if (tid == 0) a.marks[tile_id] = 0;
+#pragma unroll
+    for (int tl = 0; tl < 2; ++tl) {
+      const int tok = t0 + tl;
+      const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + min(tok, a.n_q - 1);
+      topk_emit<2>(w.tk, w.tkbuf, tl, lane, a.k, a.q_pos0 + min(tok, a.n_q - 1), a.N_init,
+                   a.N_local, a.budget, a.idx + row * a.budget, a.n_sel + row, tok < a.n_q);
     }
   }
 }
@@ -1419,23 +1596,79 @@ static void launch_split_scores(const infv2_problem& p, const SplitArgs& a, hipS
   }
 }
 
-// The fused selection (candidate lists from the pool kernel, then a per-row
-// merge) serves the split shapes with k <= 32 and at most 1024 candidate keys
-// per row.
-bool select_fused_shape(const infv2_problem& p, int n_c1) {
-  if (!scores_use_split(p)) return false;
-  const int nch = split_nch(n_c1);
-  return p.k <= SELECT_MAX_KC && nch <= SELECT_MAX_CHUNKS && nch * p.k <= SELECT_MAX_KEYS;
+static ScoresArgs prefill_args(const infv2_problem& p, const void* Q, const KeySet& ks,
+                               float* S_cmp, int n_blk, float scale) {
+  ScoresArgs a = {};
+  a.Q = (const uint16_t*)Q;
+  a.Kc1 = (const uint16_t*)ks.Kc1;
+  a.Kc2 = (const uint16_t*)ks.Kc2;
+  a.S_cmp = S_cmp;
+  a.batch = p.batch;
+  a.n_q = p.n_q;
+  a.q_pos0 = p.q_pos0;
+  a.h_kv = p.h_kv;
+  a.n_c1 = ks.n_c1;
+  a.n_c2 = ks.n_c2;
+  a.n_blk = n_blk;
+  a.tiles = (p.n_q + SEL_TOK_WG - 1) / SEL_TOK_WG;
+  a.c1_cap = ks.c1_cap;
+  a.c2_cap = ks.c2_cap;
+  a.c = scale * kLog2e;
+  return a;
 }
 
-// workspace beyond scores_workspace() rounded up to 256 bytes: the lists
+template <bool SELECT>
+static void launch_prefill_scores(const infv2_problem& p, const ScoresArgs& a,
+                                  hipStream_t stream) {
+  const int wgs = a.tiles * p.h_kv * p.batch;
+  dim3 grid(8 % p.h_kv == 0 ? ((wgs + 7) / 8) * 8 : wgs);
+  if (p.lse_approx) {
+    hipLaunchKernelGGL((scores_prefill_kernel<true, SELECT>), grid, dim3(64 * FAST_WAVES), 0,
+                       stream, a);
+    hipLaunchKernelGGL((scores_exact_kernel<true, SELECT>), dim3(wgs), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((scores_prefill_kernel<false, SELECT>), grid, dim3(64 * FAST_WAVES), 0,
+                       stream, a);
+    hipLaunchKernelGGL((scores_exact_kernel<false, SELECT>), dim3(wgs), dim3(256), 0, stream, a);
+  }
+}
+
+// The fused selection serves the split shapes (candidate lists from the pool
+// kernel, then a per-row merge; at most 1024 candidate keys per row) and the
+// fast prefill shapes (a streaming top-k inside the score sweep), with
+// k <= 32 and a budget of at most 64 blocks.
+bool select_fused_shape(const infv2_problem& p, int n_c1) {
+  if (p.k > SELECT_MAX_KC || p.N_init + p.N_local + p.k > 64) return false;
+  if (scores_use_split(p)) {
+    const int nch = split_nch(n_c1);
+    return nch <= SELECT_MAX_CHUNKS && nch * p.k <= SELECT_MAX_KEYS;
+  }
+  return scores_fast_shape(p);
+}
+
+// workspace beyond scores_workspace() rounded up to 256 bytes: the candidate
+// lists (split shapes) or one mark per tile (prefill shapes)
 size_t select_fused_workspace(const infv2_problem& p, int n_c1) {
-  return (size_t)p.batch * p.n_q * p.h_kv * split_nch(n_c1) * p.k * sizeof(uint64_t);
+  if (scores_use_split(p))
+    return (size_t)p.batch * p.n_q * p.h_kv * split_nch(n_c1) * p.k * sizeof(uint64_t);
+  return (size_t)p.batch * p.h_kv * ((p.n_q + SEL_TOK_WG - 1) / SEL_TOK_WG) * sizeof(int32_t);
 }
 
 hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeySet& ks,
                                float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, int n_blk,
                                float scale, int budget, hipStream_t stream) {
+  if (!scores_use_split(p)) {
+    ScoresArgs a = prefill_args(p, Q, ks, S_cmp, n_blk, scale);
+    a.idx = idx;
+    a.n_sel = n_sel;
+    a.marks = (int32_t*)((char*)ws + align256(scores_workspace(p, ks)));
+    a.k = p.k;
+    a.N_init = p.N_init;
+    a.N_local = p.N_local;
+    a.budget = budget;
+    launch_prefill_scores<true>(p, a, stream);
+    return hipGetLastError();
+  }
   SplitArgs a = split_args(p, Q, ks, S_cmp, ws, n_blk, scale);
   a.cand = (uint64_t*)((char*)ws + align256(scores_workspace(p, ks)));
   a.idx = idx;
@@ -1459,31 +1692,7 @@ hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const KeyS
     return hipGetLastError();
   }
   if (scores_fast_shape(p)) {
-    ScoresArgs a = {};
-    a.Q = (const uint16_t*)Q;
-    a.Kc1 = (const uint16_t*)ks.Kc1;
-    a.Kc2 = (const uint16_t*)ks.Kc2;
-    a.S_cmp = S_cmp;
-    a.batch = p.batch;
-    a.n_q = p.n_q;
-    a.q_pos0 = p.q_pos0;
-    a.h_kv = p.h_kv;
-    a.n_c1 = ks.n_c1;
-    a.n_c2 = ks.n_c2;
-    a.n_blk = n_blk;
-    a.tiles = (p.n_q + SEL_TOK_WG - 1) / SEL_TOK_WG;
-    a.c1_cap = ks.c1_cap;
-    a.c2_cap = ks.c2_cap;
-    a.c = scale * kLog2e;
-    const int wgs = a.tiles * p.h_kv * p.batch;
-    dim3 grid(8 % p.h_kv == 0 ? ((wgs + 7) / 8) * 8 : wgs);
-    if (p.lse_approx) {
-      hipLaunchKernelGGL(scores_prefill_kernel<true>, grid, dim3(64 * FAST_WAVES), 0, stream, a);
-      hipLaunchKernelGGL(scores_exact_kernel<true>, dim3(wgs), dim3(256), 0, stream, a);
-    } else {
-      hipLaunchKernelGGL(scores_prefill_kernel<false>, grid, dim3(64 * FAST_WAVES), 0, stream, a);
-      hipLaunchKernelGGL(scores_exact_kernel<false>, dim3(wgs), dim3(256), 0, stream, a);
-    }
+    launch_prefill_scores<false>(p, prefill_args(p, Q, ks, S_cmp, n_blk, scale), stream);
     return hipGetLastError();
   }
   GenericScoresArgs a = {};
