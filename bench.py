@@ -369,18 +369,31 @@ def cpu_baseline(cfg, budget_s=15.0):
                        f"{t_rows:.1f} s), extrapolated to {cfg.batch * cfg.n_q} rows")}
 
 
-def traffic_for(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources."""
+# the kernels one call of each prefill stage launches (rocprofv3 names)
+STAGE_KERNELS = {
+    "compress_k": ["compress_k_kernel"],
+    "block_scores": ["scores_prefill_kernel", "scores_exact_kernel"],
+    "topk_select": ["topk_kernel"],
+    "sparse_attn": ["kv_pack_kernel", "attn_prefill_kernel"],
+}
+
+
+def traffic_for(stage, workload):
+    """HBM bytes of one call of a stage (the sum over the kernels it
+    launches) from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = tr.get(f"{workload}/{kernel}")
-    if not ent or ent.get("source_hash") != kernel_source_hash():
-        return None
-    return ent.get("bytes_per_launch")
+    total = 0.0
+    for kernel in STAGE_KERNELS.get(stage, [stage]):
+        ent = tr.get(f"{workload}/{kernel}")
+        if not ent or ent.get("source_hash") != kernel_source_hash():
+            return None
+        total += ent.get("bytes_per_launch", 0.0)
+    return total
 
 
 def main():
@@ -452,7 +465,8 @@ def main():
         flops = None
     if flops is not None:
         ach = flops / (stages[dom] / 1e3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+        roof = {"kernel": dom, "launches": STAGE_KERNELS.get(dom, [dom]), "bound": "mfma",
+                "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
                 "traffic": traffic_for(dom, "prefill32k"),
                 "per_launch_algorithmic": flops, "avg_launch_ms": stages[dom]}

@@ -260,8 +260,10 @@ __device__ __forceinline__ void exact_chunk(const ScoresArgs& a, const uint8_t* 
 // 2^(z*c - L) with L = log2 of the row's normaliser.
 // SELECT: the selection mode of the fast kernel (marks instead of the NaN
 // marker; idx / n_sel from a streaming top-k; S^cmp only when a.S_cmp is set).
+// The body is a separate (not inlined) function: most workgroups leave at
+// the mark test, before the body's stack frame exists.
 template <bool APPROX, bool SELECT>
-__global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
+__device__ __noinline__ void scores_exact_body(const ScoresArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][SEL_CHUNK * SEL_ROW_BYTES];
   __shared__ float sbuf_all[4][SEL_TOK_WAVE][SEL_CHUNK + 1];
   __shared__ float lfine_all[4][2][32];   // APPROX: exact log2-normaliser per row
@@ -273,12 +275,6 @@ __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
   const int tile = bid % a.tiles;
   const int g = (bid / a.tiles) % a.h_kv;
   const int b = bid / (a.tiles * a.h_kv);
-  if constexpr (SELECT) {
-    if (a.marks[((size_t)b * a.h_kv + g) * a.tiles + tile] == 0) return;
-  } else {
-    const float mark = a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tile * SEL_TOK_WG) * a.n_blk];
-    if (!__builtin_isnan(mark)) return;
-  }
   TopkStream<SEL_TOK_WAVE> tk;
   uint64_t* tkbuf = &tkbuf_all[SELECT ? wave : 0][0][0];
   if constexpr (SELECT) topk_init<SEL_TOK_WAVE>(tk, tkbuf, lane);
@@ -510,6 +506,21 @@ __global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
                               a.n_sel + row, tok < a.n_q);
     }
   }
+}
+
+template <bool APPROX, bool SELECT>
+__global__ void __launch_bounds__(256, 2) scores_exact_kernel(ScoresArgs a) {
+  const int bid = blockIdx.x;
+  const int tile = bid % a.tiles;
+  const int g = (bid / a.tiles) % a.h_kv;
+  const int b = bid / (a.tiles * a.h_kv);
+  if constexpr (SELECT) {
+    if (a.marks[((size_t)b * a.h_kv + g) * a.tiles + tile] == 0) return;
+  } else {
+    const float mark = a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tile * SEL_TOK_WG) * a.n_blk];
+    if (!__builtin_isnan(mark)) return;
+  }
+  scores_exact_body<APPROX, SELECT>(a);
 }
 
 constexpr int SEL_DEPTH = 4;                                // K^C1 chunks in flight per wave
