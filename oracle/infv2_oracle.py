@@ -40,6 +40,11 @@ Sources (cited by tag in the docstrings below):
        degrade to dense attention.
 [BLOG-SHARE] same blog, Top-K块共享 (top-k sharing): the heads of one group
        share one block selection.
+[BLOG-TRAIN] same blog, 可训练稀疏注意力的设计原则 (design principles of trainable
+       sparse attention): the top-k selection is not differentiable; the kernels
+       are parameter-free mean-pools, optimised only through the token-level
+       keys, so training differentiates the block-sparse attention with the
+       selected sets held fixed.
 [BLOG-TOPK] same blog, 高效Top-K实现 (efficient top-k): softmax per kernel,
        aggregate over the head group, then top-k per query token.
 
@@ -56,6 +61,8 @@ design notes list them all:
                                                    estimate is log sum over visible coarse
                                                    kernels of exp(z2) + ln(s_C2/s_C1); with
                                                    no visible coarse kernel the exact LSE
+                                                17 backward: the sets I(p) are constants;
+                                                   gradients of the sparse attention only
 
 Parity: every function below is pinned by ``tests/test_oracle_*.py`` against
 closed forms, invariants, library special cases (torch SDPA, torch's bf16
@@ -74,7 +81,7 @@ __all__ = [
     "Problem", "round_to_bf16", "round_to_io", "n_kernels", "kernel_visible",
     "kernels_of_block", "compress_k", "selection_scores", "max_pool_blocks", "select_blocks",
     "attention_rows", "dense_switch", "forward_rows", "attended_tokens", "compress_k2",
-    "n_coarse_kernels", "coarse_visible", "coarse_lse",
+    "n_coarse_kernels", "coarse_visible", "coarse_lse", "attention_rows_backward",
 ]
 
 # --------------------------------------------------------------------------
@@ -430,6 +437,48 @@ def attention_rows(Qrows, K, V, token_sets, prob: Problem):
             O[r, g * G:(g + 1) * G] = (e / ssum) @ V[T, g]
             lse[r, g * G:(g + 1) * G] = (mx + np.log(ssum))[:, 0]
     return O, lse
+
+def attention_rows_backward(Qrows, K, V, token_sets, dO, prob: Problem, q_index=None):
+    """Gradients of the block-sparse attention with the selected sets held
+    fixed ([BLOG-TRAIN], READING-17), for the rows of one sequence.
+
+    Qrows, dO: [R, h_q, d]; K, V: [n_kv, h_kv, d]; token_sets[r][g] as for
+    attention_rows.  For each row and head, with z_t = scale * q . k_t over
+    t in T(p), P = softmax(z) and O = sum_t P_t v_t:
+        dP_t = dO . v_t,   D = sum_t P_t dP_t (= dO . O),   dZ_t = P_t (dP_t - D)
+        dq   = scale * sum_t dZ_t k_t
+        dk_t += scale * dZ_t q,   dv_t += P_t dO
+    dK and dV sum over every row given (rows of other queries add nothing).
+    Returns (dQ [R, h_q, d], dK [n_kv, h_kv, d], dV [n_kv, h_kv, d]) in fp64.
+    """
+    Qrows = np.asarray(Qrows, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    dO = np.asarray(dO, np.float64)
+    R = Qrows.shape[0]
+    G = prob.G
+    sc = prob.sm_scale
+    dQ = np.zeros_like(Qrows)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for r in range(R):
+        for g in range(prob.h_kv):
+            T = np.asarray(token_sets[r][g], dtype=np.int64)
+            if T.size == 0:
+                continue
+            q = Qrows[r, g * G:(g + 1) * G]                  # [G, d]
+            do = dO[r, g * G:(g + 1) * G]                    # [G, d]
+            Kt, Vt = K[T, g], V[T, g]                        # [|T|, d]
+            z = (q @ Kt.T) * sc                              # [G, |T|]
+            e = np.exp(z - z.max(axis=1, keepdims=True))
+            P = e / e.sum(axis=1, keepdims=True)
+            dP = do @ Vt.T                                   # [G, |T|]
+            Dr = (P * dP).sum(axis=1, keepdims=True)
+            dZ = P * (dP - Dr)
+            dQ[r, g * G:(g + 1) * G] = sc * (dZ @ Kt)
+            np.add.at(dK[:, g], T, sc * (dZ.T @ q))
+            np.add.at(dV[:, g], T, P.T @ do)
+    return dQ, dK, dV
 
 
 # --------------------------------------------------------------------------
