@@ -195,6 +195,37 @@ int infv2_dense_attn(const infv2_problem* prob, const void* Q, const void* K,
                      const void* V, void* O, float* lse, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* Backward of the block-sparse attention for training (OpenBMB blog,
+ * 可训练稀疏注意力的设计原则: the top-k selection is not differentiable and the
+ * kernels are parameter-free means trained through the token keys, so the
+ * gradients are those of the attention with the sets I(p) held fixed).  Per
+ * query token and head, over T(p) = {t <= p : floor(t/B) in I(p)}:
+ *   P_t = exp(scale q.k_t - lse),  dP_t = dO.v_t,  D = dO.O,
+ *   dZ_t = P_t (dP_t - D),  dQ = scale sum_t dZ_t k_t,
+ *   dK_t += scale dZ_t q,  dV_t += P_t dO  (summed over the query tokens).
+ *   Q, K, V, idx, n_sel : as given to infv2_sparse_attn
+ *   O, lse : its outputs (lse required)
+ *   dO    : [batch][n_q][h_q][d] I/O dtype, the gradient of O
+ *   dQ    : [batch][n_q][h_q][d] fp32 (output)
+ *   dK, dV: [batch][kv_cap][h_kv][d] fp32 (output; rows 0..n_kv-1 are
+ *           written, zero where no query attends)
+ *   ws    : workspace of infv2_sparse_attn_bwd_workspace(prob) bytes.
+ * dQ is deterministic; the bf16 kernels add the partial dK / dV of different
+ * query windows with atomics, so their last bits may differ between runs. */
+size_t infv2_sparse_attn_bwd_workspace(const infv2_problem* prob);
+int infv2_sparse_attn_bwd(const infv2_problem* prob, const void* Q, const void* K,
+                          const void* V, const int32_t* idx, const int32_t* n_sel,
+                          const void* O, const float* lse, const void* dO, float* dQ,
+                          float* dK, float* dV, void* ws, size_t ws_bytes, void* stream);
+
+/* The same for dense causal attention (T(p) = {0..p}), the backward of
+ * infv2_dense_attn; ws: infv2_dense_attn_bwd_workspace(prob) bytes. */
+size_t infv2_dense_attn_bwd_workspace(const infv2_problem* prob);
+int infv2_dense_attn_bwd(const infv2_problem* prob, const void* Q, const void* K,
+                         const void* V, const void* O, const float* lse, const void* dO,
+                         float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
+                         void* stream);
+
 const char* infv2_status_string(int status);
 const char* infv2_last_error(void);
 

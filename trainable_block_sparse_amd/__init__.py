@@ -25,6 +25,8 @@ EXPORTED = (
     "infv2_block_scores", "infv2_topk_select", "infv2_select_blocks_workspace",
     "infv2_select_blocks", "infv2_sparse_attn_workspace",
     "infv2_sparse_attn", "infv2_dense_attn_workspace", "infv2_dense_attn",
+    "infv2_sparse_attn_bwd_workspace", "infv2_sparse_attn_bwd",
+    "infv2_dense_attn_bwd_workspace", "infv2_dense_attn_bwd",
     "infv2_status_string", "infv2_last_error",
 )
 
@@ -112,6 +114,10 @@ def lib() -> ctypes.CDLL:
             "infv2_sparse_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_dense_attn_workspace": (sz, [P]),
             "infv2_dense_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "infv2_sparse_attn_bwd_workspace": (sz, [P]),
+            "infv2_sparse_attn_bwd": (ctypes.c_int, [P] + [vp] * 12 + [sz, vp]),
+            "infv2_dense_attn_bwd_workspace": (sz, [P]),
+            "infv2_dense_attn_bwd": (ctypes.c_int, [P] + [vp] * 10 + [sz, vp]),
             "infv2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "infv2_last_error": (ctypes.c_char_p, []),
         }
@@ -298,6 +304,55 @@ def dense_attn(prob: Problem, Q, K, V, O=None, lse=None, ws=None, want_lse: bool
                                   _ptr(lse), _ptr(ws), ws.numel() if ws is not None else 0,
                                   _stream(stream)))
     return O, lse
+
+
+def _bwd_outputs(prob: Problem, Q, K, dQ, dK, dV):
+    kv_rows = prob.kv_cap or prob.n_kv
+    if dQ is None:
+        dQ = torch.empty(Q.shape, dtype=torch.float32, device=Q.device)
+    if dK is None:
+        dK = torch.empty((prob.batch, kv_rows, prob.h_kv, prob.d), dtype=torch.float32,
+                         device=K.device)
+    if dV is None:
+        dV = torch.empty_like(dK)
+    return dQ, dK, dV
+
+
+def sparse_attn_bwd_workspace(prob: Problem) -> int:
+    return lib().infv2_sparse_attn_bwd_workspace(ctypes.byref(prob.to_c()))
+
+
+def sparse_attn_bwd(prob: Problem, Q, K, V, idx, n_sel, O, lse, dO, dQ=None, dK=None,
+                    dV=None, ws=None, stream=None):
+    """Gradients (dQ, dK, dV) in fp32 of the block-sparse attention with the
+    selected sets held fixed."""
+    dQ, dK, dV = _bwd_outputs(prob, Q, K, dQ, dK, dV)
+    need = sparse_attn_bwd_workspace(prob)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    _check(lib().infv2_sparse_attn_bwd(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(K), _ptr(V),
+                                       _ptr(idx), _ptr(n_sel), _ptr(O), _ptr(lse), _ptr(dO),
+                                       _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
+                                       ws.numel() if ws is not None else 0, _stream(stream)))
+    return dQ, dK, dV
+
+
+def dense_attn_bwd_workspace(prob: Problem) -> int:
+    return lib().infv2_dense_attn_bwd_workspace(ctypes.byref(prob.to_c()))
+
+
+def dense_attn_bwd(prob: Problem, Q, K, V, O, lse, dO, dQ=None, dK=None, dV=None, ws=None,
+                   stream=None):
+    """Gradients (dQ, dK, dV) in fp32 of dense causal attention."""
+    dQ, dK, dV = _bwd_outputs(prob, Q, K, dQ, dK, dV)
+    need = dense_attn_bwd_workspace(prob)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    _check(lib().infv2_dense_attn_bwd(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(K), _ptr(V),
+                                      _ptr(O), _ptr(lse), _ptr(dO), _ptr(dQ), _ptr(dK),
+                                      _ptr(dV), _ptr(ws), ws.numel() if ws is not None else 0,
+                                      _stream(stream)))
+    return dQ, dK, dV
 
 
 def forward(prob: Problem, Q, K, V, Kc1=None, mode: str = "auto", stream=None,

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libinfv2.so")
-SOURCES = ["api.hip", "compress.hip", "scores.hip", "topk.hip", "attn.hip"]
+SOURCES = ["api.hip", "compress.hip", "scores.hip", "topk.hip", "attn.hip", "attn_bwd.hip"]
 
 # Packed-fp32 instructions are disabled for all device code; the host pass
 # reports the feature as unknown, which is harmless.

@@ -31,6 +31,13 @@ size_t attn_workspace(const infv2_problem& p, int budget, bool sparse);
 hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, const void* V,
                        const int32_t* idx, const int32_t* n_sel, void* O, float* lse, void* ws,
                        int budget, int64_t kv_cap, float scale, hipStream_t stream);
+size_t attn_bwd_workspace(const infv2_problem& p, bool sparse);
+size_t attn_bwd_generic_lds(const infv2_problem& p, int budget, bool sparse);
+hipError_t launch_attn_bwd(const infv2_problem& p, const void* Q, const void* K, const void* V,
+                           const int32_t* idx, const int32_t* n_sel, const void* O,
+                           const float* lse, const void* dO, float* dQ, float* dK, float* dV,
+                           void* ws, int budget, int64_t kv_cap, float scale,
+                           hipStream_t stream);
 }  // namespace infv2
 
 using namespace infv2;
@@ -331,6 +338,64 @@ int infv2_dense_attn(const infv2_problem* p, const void* Q, const void* K, const
   return hip_status(launch_attn(*p, Q, K, V, nullptr, nullptr, O, lse, ws, budget_of(*p),
                                 kv_cap_of(*p), scale_of(*p), (hipStream_t)stream),
                     "infv2_dense_attn");
+}
+
+size_t infv2_sparse_attn_bwd_workspace(const infv2_problem* p) {
+  if (check(p) != INFV2_OK) return 0;
+  return attn_bwd_workspace(*p, true);
+}
+
+size_t infv2_dense_attn_bwd_workspace(const infv2_problem* p) {
+  if (check(p) != INFV2_OK) return 0;
+  return attn_bwd_workspace(*p, false);
+}
+
+static int attn_bwd_common(const infv2_problem* p, const void* Q, const void* K, const void* V,
+                           const int32_t* idx, const int32_t* n_sel, const void* O,
+                           const float* lse, const void* dO, float* dQ, float* dK, float* dV,
+                           void* ws, size_t ws_bytes, void* stream, const char* what) {
+  int st = check(p);
+  if (st) return st;
+  const bool sparse = idx != nullptr;
+  CHECK_PTR(Q);
+  CHECK_PTR(K);
+  CHECK_PTR(V);
+  CHECK_PTR(O);
+  CHECK_PTR(lse);
+  CHECK_PTR(dO);
+  CHECK_PTR(dQ);
+  CHECK_PTR(dK);
+  CHECK_PTR(dV);
+  if (sparse) CHECK_PTR(n_sel);
+  if (!attn_fast_shape(*p) && attn_bwd_generic_lds(*p, budget_of(*p), sparse) > 64 * 1024)
+    return fail(INFV2_E_UNSUPPORTED,
+                "%s: %s for the generic backward kernel (shape G=%d d=%d dtype=%d)", what,
+                sparse ? "budget * B too large" : "n_kv too large", p->G, p->d, p->dtype);
+  const size_t need = attn_bwd_workspace(*p, sparse);
+  if (need) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need) return fail(INFV2_E_WORKSPACE, "%s workspace %zu < %zu bytes", what, ws_bytes, need);
+  }
+  return hip_status(launch_attn_bwd(*p, Q, K, V, idx, n_sel, O, lse, dO, dQ, dK, dV, ws,
+                                    budget_of(*p), kv_cap_of(*p), scale_of(*p),
+                                    (hipStream_t)stream),
+                    what);
+}
+
+int infv2_sparse_attn_bwd(const infv2_problem* p, const void* Q, const void* K, const void* V,
+                          const int32_t* idx, const int32_t* n_sel, const void* O,
+                          const float* lse, const void* dO, float* dQ, float* dK, float* dV,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (!idx) return fail(INFV2_E_ARG, "idx is NULL");
+  return attn_bwd_common(p, Q, K, V, idx, n_sel, O, lse, dO, dQ, dK, dV, ws, ws_bytes, stream,
+                         "infv2_sparse_attn_bwd");
+}
+
+int infv2_dense_attn_bwd(const infv2_problem* p, const void* Q, const void* K, const void* V,
+                         const void* O, const float* lse, const void* dO, float* dQ, float* dK,
+                         float* dV, void* ws, size_t ws_bytes, void* stream) {
+  return attn_bwd_common(p, Q, K, V, nullptr, nullptr, O, lse, dO, dQ, dK, dV, ws, ws_bytes,
+                         stream, "infv2_dense_attn_bwd");
 }
 
 const char* infv2_status_string(int status) {

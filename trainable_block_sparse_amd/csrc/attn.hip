@@ -22,20 +22,10 @@
 //  * decode splits the selected blocks over workgroups (one block each) and
 //    merges the partial (max, sum, O) afterwards.
 // A generic fp64 kernel serves fp32 I/O and other shapes.
-#include "common.hpp"
+#include "attn_layout.hpp"
 
 namespace infv2 {
 
-constexpr int AT_D = 128;
-constexpr int AT_G = 16;
-constexpr int AT_B = 64;
-
-// Key held by row r (0..15) of score tile t (0..3) of a 64-key block: the
-// permutation makes a lane's 8 P^T elements of k-step ks the 8 consecutive
-// keys 32*ks + 8*(lane>>4) .. +7.
-__device__ __forceinline__ int tile_key(int t, int r) {
-  return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
-}
 
 // ---------------------------------------------------------------------------
 // K, V [b][kv_cap][h_kv][d] -> packs [b][h_kv][n_blk][16 fragments][64 lanes][8]
@@ -48,7 +38,6 @@ __device__ __forceinline__ int tile_key(int t, int r) {
 // rows on consecutive lanes and cost one address request per lane.)
 // grid: x = blocks, y = h_kv, z = batch.  256 threads.
 // ---------------------------------------------------------------------------
-constexpr int PACK_ELEMS = AT_B * AT_D;   // 8192 bf16 = 16 KB per block
 
 __global__ void __launch_bounds__(256) kv_pack_kernel(const uint16_t* __restrict__ K,
                                                       const uint16_t* __restrict__ V,
@@ -75,25 +64,13 @@ __global__ void __launch_bounds__(256) kv_pack_kernel(const uint16_t* __restrict
   }
   __syncthreads();
   const size_t base = (((size_t)b * h_kv + g) * n_blk + blk) * PACK_ELEMS;
-  // 16 fragments x 64 lanes = 1024 pieces of 16 B per pack, 4 per thread
+  // 16 fragments x 64 lanes = 1024 pieces of 16 B per pack, 4 per thread;
+  // K in the key layout, V in the feature layout
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int u = tid + 256 * i;
-    const int f = u >> 6, l = u & 63;
-    {  // K: f = 4t + ks
-      const int t = f >> 2, ks = f & 3;
-      *(u32x4*)(Kp + base + (size_t)u * 8) =
-          *(const u32x4*)&kt[tile_key(t, l & 15)][32 * ks + 8 * (l >> 4)];
-    }
-    {  // V: f = 2mt + ks
-      const int mt = f >> 1, ks = f & 1;
-      const int d = 16 * mt + (l & 15), k0 = 32 * ks + 8 * (l >> 4);
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = (uint32_t)vt[k0 + 2 * e][d] | ((uint32_t)vt[k0 + 2 * e + 1][d] << 16);
-      *(u32x4*)(Vp + base + (size_t)u * 8) = u32x4{w[0], w[1], w[2], w[3]};
-    }
+    *(u32x4*)(Kp + base + (size_t)u * 8) = pack_piece_keys(&kt[0][0], AT_D + 8, u);
+    *(u32x4*)(Vp + base + (size_t)u * 8) = pack_piece_features(&vt[0][0], AT_D + 8, u);
   }
 }
 

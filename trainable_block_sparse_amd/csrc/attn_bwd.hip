@@ -1,0 +1,666 @@
+// Backward of the block-sparse attention (and of dense causal attention).
+//
+// OpenBMB blog "技术Blog-4 | 新一代InfLLM：可训练的稀疏注意力机制", 可训练稀疏注意力的
+// 设计原则: the top-k selection is not differentiable and the kernels are
+// parameter-free mean-pools, trained only through the token-level keys; so the
+// gradients are those of the attention over the selected blocks, with the
+// sets I(p) held fixed.  Per query row and head, with P the softmax of
+// z = scale q.k over T(p):
+//   dP_t = dO.v_t,  D = dO.O,  dZ_t = P_t (dP_t - D),
+//   dq = scale sum_t dZ_t k_t,  dk_t += scale dZ_t q,  dv_t += P_t dO.
+// P is recomputed from the forward's log-sum-exp.
+//
+// bf16 kernels (G = 16, d = 128, B = 64), fp32 gradients:
+//  * bwd_pack_kernel writes, once per call, K in the key layout (the forward's
+//    K pack), V in the key layout and K in the feature layout (attn_layout.hpp):
+//    every MFMA operand below is one coalesced 1 KB fragment load.
+//  * attn_bwd_dq_kernel: one wavefront per (token, group), as the forward:
+//    S^T = K Q^T and dP^T = V dO^T (keys on the M axis, the 16 heads on N), so
+//    that dZ^T lands in the B-operand layout of dQ^T = K^T dZ^T.  It also
+//    writes D = dO.O per (token, head) for the second kernel.
+//  * attn_bwd_dkdv_kernel: one workgroup per (key block, group, window of 1024
+//    query tokens), 4 waves x 16 keys.  The tokens of the window that
+//    selected the block come from a bitmap (bwd_bitmap_kernel) in ascending
+//    order and are taken two at a time: S = Q K^T and dP = dO V^T with the 16
+//    heads of both tokens on M; two permlane swaps turn P and dZ into the
+//    A operand of dV = P^T dO and dK = dZ^T Q (keys on M, the 32 (token, head)
+//    pairs on K), whose B operands are dO and Q transposed through LDS.  The
+//    window's partial dK / dV are added to the fp32 outputs with atomics
+//    (their order between windows is not fixed: the last bits of dK / dV can
+//    vary between runs; dQ is deterministic).
+// A generic fp64 kernel serves fp32 I/O and other shapes.
+#include "attn_layout.hpp"
+
+namespace infv2 {
+
+struct BwdArgs {
+  const uint16_t* Q;
+  const uint16_t* dO;
+  const uint16_t* O;
+  const float* lse;       // [b][h_q][n_q], natural log (the forward's output)
+  const uint16_t* Kp;     // K, key layout
+  const uint16_t* Vk;     // V, key layout
+  const uint16_t* Kv;     // K, feature layout
+  const int32_t* idx;     // null: dense
+  const int32_t* n_sel;
+  const uint32_t* bitmap; // [b][h_kv][n_blk][nw]: bit t: query token t selected the block
+  float* dQ;              // [b][n_q][h_q][d]
+  float* dK;              // [b][kv_cap][h_kv][d]
+  float* dV;
+  float* Dsum;            // [b][h_q][n_q]
+  int batch, n_q, q_pos0, n_kv, n_blk, h_kv, budget, nw;
+  int64_t kv_cap;
+  float c;                // scale * log2(e)
+  float scale;
+};
+
+// ---------------------------------------------------------------------------
+// grid: x = blocks, y = h_kv, z = batch.  256 threads.
+__global__ void __launch_bounds__(256) bwd_pack_kernel(const uint16_t* __restrict__ K,
+                                                       const uint16_t* __restrict__ V,
+                                                       uint16_t* __restrict__ Kp,
+                                                       uint16_t* __restrict__ Vk,
+                                                       uint16_t* __restrict__ Kv, int n_kv,
+                                                       int n_blk, int h_kv, int64_t kv_cap) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt[AT_B][AT_D + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[AT_B][AT_D + 8];
+  const int blk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + 256 * i;
+    const int r = u >> 4, c8 = (u & 15) * 8;
+    const int tok = blk * AT_B + r;
+    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (tok < n_kv) {
+      const size_t off = (((size_t)b * kv_cap + tok) * h_kv + g) * AT_D + c8;
+      kv = *(const u32x4*)(K + off);
+      vv = *(const u32x4*)(V + off);
+    }
+    *(u32x4*)&kt[r][c8] = kv;
+    *(u32x4*)&vt[r][c8] = vv;
+  }
+  __syncthreads();
+  const size_t base = (((size_t)b * h_kv + g) * n_blk + blk) * PACK_ELEMS;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int u = tid + 256 * i;
+    *(u32x4*)(Kp + base + (size_t)u * 8) = pack_piece_keys(&kt[0][0], AT_D + 8, u);
+    *(u32x4*)(Vk + base + (size_t)u * 8) = pack_piece_keys(&vt[0][0], AT_D + 8, u);
+    *(u32x4*)(Kv + base + (size_t)u * 8) = pack_piece_features(&kt[0][0], AT_D + 8, u);
+  }
+}
+
+// n 32-bit words of zeros (dK, dV, the bitmap); grid-stride.
+__global__ void __launch_bounds__(256) bwd_zero_kernel(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+// dK / dV rows 0..n_kv-1 of [b][kv_cap][row_elems] to zero.
+__global__ void __launch_bounds__(256) bwd_zero_kv_kernel(float* __restrict__ dK,
+                                                          float* __restrict__ dV, int n_kv,
+                                                          int row_elems, int64_t kv_cap) {
+  const size_t per_seq = (size_t)n_kv * row_elems;
+  const int b = blockIdx.y;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < per_seq;
+       i += (size_t)gridDim.x * 256) {
+    const size_t off = (size_t)b * kv_cap * row_elems + i;
+    dK[off] = 0.f;
+    dV[off] = 0.f;
+  }
+}
+
+// One thread per (sequence, group, query token): sets the token's bit in the
+// row of every causal block it selected.
+__global__ void __launch_bounds__(256) bwd_bitmap_kernel(BwdArgs a) {
+  const size_t row = (size_t)blockIdx.x * 256 + threadIdx.x;   // (b*h_kv + g)*n_q + t
+  const size_t rows = (size_t)a.batch * a.h_kv * a.n_q;
+  if (row >= rows) return;
+  const int t = (int)(row % a.n_q);
+  const size_t bg = row / a.n_q;
+  const int b_p = (a.q_pos0 + t) / AT_B;
+  const int n = a.n_sel[row];
+  const int32_t* sel = a.idx + row * a.budget;
+  uint32_t* base = const_cast<uint32_t*>(a.bitmap) + bg * a.n_blk * a.nw + (t >> 5);
+  for (int i = 0; i < n; ++i) {
+    const int blk = sel[i];
+    if (blk < 0 || blk > b_p) continue;
+    atomicOr(base + (size_t)blk * a.nw, 1u << (t & 31));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  Grid and token mapping as the forward prefill kernel (16 workgroups of
+// 4 tokens per 64-token query block, all on one XCD).
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_qb = (a.n_q + AT_B - 1) / AT_B;
+  const int n_bg = a.batch * a.h_kv;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, r = bid >> 3;
+  const int qbg = (r >> 4) * 8 + xcd;
+  if (qbg >= n_qb * n_bg) return;
+  const int qb = n_qb - 1 - qbg / n_bg;
+  const int bg = qbg % n_bg;
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int t = qb * AT_B + (r & 15) * 4 + wave;
+  if (t >= a.n_q) return;
+  const int p = a.q_pos0 + t;
+  const int b_p = p / AT_B;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int hq = a.h_kv * AT_G;
+  const int head = g * AT_G + r16;
+  // B operands: Q and dO of head r16, d = 32ks + 8grp .. +7
+  const size_t qoff = (((size_t)b * a.n_q + t) * hq + head) * AT_D + 8 * grp;
+  bf16x8 qf[4], dof[4];
+  float dsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4 qv = *(const u32x4*)(a.Q + qoff + 32 * ks);
+    const u32x4 dv = *(const u32x4*)(a.dO + qoff + 32 * ks);
+    const u32x4 ov = *(const u32x4*)(a.O + qoff + 32 * ks);
+    qf[ks] = as_bf16x8(qv);
+    dof[ks] = as_bf16x8(dv);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dsum = __builtin_fmaf(bf16_bits_to_f32(dv[e] & 0xFFFFu), bf16_bits_to_f32(ov[e] & 0xFFFFu), dsum);
+      dsum = __builtin_fmaf(bf16_bits_to_f32(dv[e] >> 16), bf16_bits_to_f32(ov[e] >> 16), dsum);
+    }
+  }
+  dsum += __shfl_xor(dsum, 16, 64);
+  dsum += __shfl_xor(dsum, 32, 64);
+  const float L2 = a.lse[((size_t)b * hq + head) * a.n_q + t] * kLog2e;
+  if (grp == 0) a.Dsum[((size_t)b * hq + head) * a.n_q + t] = dsum;
+  f32x4 acc[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+  const bool sparse = a.idx != nullptr;
+  const int nblocks = sparse ? a.n_sel[row] : b_p + 1;
+  const int32_t* sel = sparse ? a.idx + row * a.budget : nullptr;
+  const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS + lane * 8;
+  for (int bi = 0; bi < nblocks; ++bi) {
+    const int blk = sparse ? sel[bi] : bi;
+    if (blk < 0 || blk > b_p) continue;
+    const size_t boff = pack0 + (size_t)blk * PACK_ELEMS;
+    bf16x8 kf[4][4], vkf[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kf[tt][ks] = as_bf16x8(*(const u32x4*)(a.Kp + boff + (4 * tt + ks) * 512));
+        vkf[tt][ks] = as_bf16x8(*(const u32x4*)(a.Vk + boff + (4 * tt + ks) * 512));
+      }
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s[tt] = mfma16(kf[tt][ks], qf[ks], s[tt]);
+        dp[tt] = mfma16(vkf[tt][ks], dof[ks], dp[tt]);
+      }
+    }
+    bf16x8 kvf[8][2];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        kvf[mt][ks] = as_bf16x8(*(const u32x4*)(a.Kv + boff + (2 * mt + ks) * 512));
+    // dZ^T = P^T (dP^T - D), keys past p masked; packed as the B operand
+    // (k-step ks = keys 32ks + 8grp .. +7)
+    const int kv0 = blk * AT_B;
+    const bool diag = blk == b_p;
+    bf16x8 dzf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tt = 2 * ks + (e >> 1);
+        const int i0 = 2 * (e & 1);
+        float z2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = i0 + u;
+          const int key = kv0 + tile_key(tt, 4 * grp + i);
+          const float pr = (diag && key > p) ? 0.f
+                                             : fast_exp2(__builtin_fmaf(s[tt][i], a.c, -L2));
+          z2[u] = pr * (dp[tt][i] - dsum);
+        }
+        w[e] = pack_bf16x2(z2[0], z2[1]);
+      }
+      dzf[ks] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma16(kvf[mt][ks], dzf[ks], acc[mt]);
+  }
+  // dQ^T tile mt: rows d = 16mt + 4grp + i, column = head r16
+  float* drow = a.dQ + (((size_t)b * a.n_q + t) * hq + head) * AT_D;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const f32x4 v = acc[mt] * a.scale;
+    *(f32x4*)(drow + 16 * mt + 4 * grp) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  grid: x = window of BW_WIN query tokens, y = key block, z = b*h_kv.
+constexpr int BW_WIN = 1024;
+constexpr int BW_TROW = AT_G + 8;   // LDS row of a transposed token: 16 heads + pad (48 B)
+
+__global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ int toks[BW_WIN];
+  __shared__ int wcnt[64];
+  __shared__ __attribute__((aligned(16))) uint16_t qT[2][AT_D][BW_TROW];
+  __shared__ __attribute__((aligned(16))) uint16_t doT[2][AT_D][BW_TROW];
+  __shared__ float Ls[2][AT_G], Ds[2][AT_G];
+  __shared__ int ntok_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int win = blockIdx.x, blk = blockIdx.y, bg = blockIdx.z;
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int t_lo = win * BW_WIN;
+  const int t_hi = min(t_lo + BW_WIN, a.n_q);
+  // query tokens that can see a key of the block: p >= 64 * blk
+  const int t_first = max(t_lo, blk * AT_B - a.q_pos0);
+  if (t_first >= t_hi) return;
+  const bool sparse = a.idx != nullptr;
+  // the window's tokens that selected the block, ascending
+  if (sparse) {
+    const int w0 = t_lo >> 5;
+    const int nwin = (t_hi - t_lo + 31) >> 5;                 // <= 32 words
+    const uint32_t* bm = a.bitmap + ((size_t)bg * a.n_blk + blk) * a.nw + w0;
+    uint32_t word = 0u;
+    if (tid < nwin) word = bm[tid];
+    if (wave == 0) {
+      const int c = __popc(word);
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      int pos = incl - c;
+      for (uint32_t wv = word; wv; wv &= wv - 1) toks[pos++] = t_lo + 32 * tid + __builtin_ctz(wv);
+      if (lane == 63) ntok_s = incl;
+    }
+  } else {
+    for (int i = tid; i < t_hi - t_first; i += 256) toks[i] = t_first + i;
+    if (tid == 0) ntok_s = t_hi - t_first;
+  }
+  __syncthreads();
+  const int ntok = ntok_s;
+  if (ntok == 0) return;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int hq = a.h_kv * AT_G;
+  // this wave's 16 keys: tile `wave` of the block (row r16 holds key
+  // tile_key(wave, r16)); B operands of S = Q K^T and dP = dO V^T
+  const size_t boff = (((size_t)b * a.h_kv + g) * a.n_blk + blk) * PACK_ELEMS + lane * 8;
+  bf16x8 kf[4], vkf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    kf[ks] = as_bf16x8(*(const u32x4*)(a.Kp + boff + (4 * wave + ks) * 512));
+    vkf[ks] = as_bf16x8(*(const u32x4*)(a.Vk + boff + (4 * wave + ks) * 512));
+  }
+  const int key_l = blk * AT_B + tile_key(wave, r16);    // key of this lane's column
+  f32x4 accV[8], accK[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    accV[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accK[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int i = 0; i < ntok; i += 2) {
+    const int tA = toks[i];
+    const int tB = i + 1 < ntok ? toks[i + 1] : -1;
+    __syncthreads();   // the previous pair's LDS reads are done
+    // Q^T and dO^T of the pair into LDS: thread = (token, head, 16-feature chunk)
+    {
+      const int tk = tid >> 7, hh = (tid >> 3) & 15, dc = (tid & 7) * 16;
+      const int tt = tk == 0 ? tA : tB;
+      u32x4 q0 = {0u, 0u, 0u, 0u}, q1 = q0, d0 = q0, d1 = q0;
+      if (tt >= 0) {
+        const size_t off = (((size_t)b * a.n_q + tt) * hq + g * AT_G + hh) * AT_D + dc;
+        q0 = *(const u32x4*)(a.Q + off);
+        q1 = *(const u32x4*)(a.Q + off + 8);
+        d0 = *(const u32x4*)(a.dO + off);
+        d1 = *(const u32x4*)(a.dO + off + 8);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qT[tk][dc + 2 * e][hh] = (uint16_t)(q0[e] & 0xFFFFu);
+        qT[tk][dc + 2 * e + 1][hh] = (uint16_t)(q0[e] >> 16);
+        qT[tk][dc + 8 + 2 * e][hh] = (uint16_t)(q1[e] & 0xFFFFu);
+        qT[tk][dc + 8 + 2 * e + 1][hh] = (uint16_t)(q1[e] >> 16);
+        doT[tk][dc + 2 * e][hh] = (uint16_t)(d0[e] & 0xFFFFu);
+        doT[tk][dc + 2 * e + 1][hh] = (uint16_t)(d0[e] >> 16);
+        doT[tk][dc + 8 + 2 * e][hh] = (uint16_t)(d1[e] & 0xFFFFu);
+        doT[tk][dc + 8 + 2 * e + 1][hh] = (uint16_t)(d1[e] >> 16);
+      }
+      if (tid < 2 * AT_G) {
+        const int k2 = tid >> 4, h2 = tid & 15;
+        const int t2 = k2 == 0 ? tA : tB;
+        float L = 0.f, D = 0.f;
+        if (t2 >= 0) {
+          const size_t o2 = ((size_t)b * hq + g * AT_G + h2) * a.n_q + t2;
+          L = a.lse[o2] * kLog2e;
+          D = a.Dsum[o2];
+        }
+        Ls[k2][h2] = L;
+        Ds[k2][h2] = D;
+      }
+    }
+    __syncthreads();
+    // S and dP for both tokens: rows = heads 4grp + j, column = key key_l
+    f32x4 sc[2], dpv[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int tt = k2 == 0 ? tA : tB;
+      const int tq = tt >= 0 ? tt : tA;
+      const size_t qoff = (((size_t)b * a.n_q + tq) * hq + g * AT_G + r16) * AT_D + 8 * grp;
+      sc[k2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dpv[k2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 qa = as_bf16x8(*(const u32x4*)(a.Q + qoff + 32 * ks));
+        const bf16x8 da = as_bf16x8(*(const u32x4*)(a.dO + qoff + 32 * ks));
+        sc[k2] = mfma16(qa, kf[ks], sc[k2]);
+        dpv[k2] = mfma16(da, vkf[ks], dpv[k2]);
+      }
+    }
+    // P and dZ (0 for masked keys and for a missing second token)
+    f32x4 pv[2], zv[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int tt = k2 == 0 ? tA : tB;
+      const bool live = tt >= 0 && key_l <= a.q_pos0 + tt;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int h = 4 * grp + j;
+        const float pr = live ? fast_exp2(__builtin_fmaf(sc[k2][j], a.c, -Ls[k2][h])) : 0.f;
+        pv[k2][j] = pr;
+        zv[k2][j] = pr * (dpv[k2][j] - Ds[k2][h]);
+      }
+    }
+    // to A operands: lane row r16 = key, k = 8*grp + e = the 32 (token, head)
+    // pairs (grp 0, 1: token A heads 0-7, 8-15; grp 2, 3: token B)
+    bf16x8 pa, za;
+    {
+      uint32_t wp[4], wz[4];
+      float xp[4], yp[4], xz[4], yz[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pv[0][j]),
+                                                         __float_as_uint(pv[1][j]), false, false);
+        const auto s2 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+        xp[j] = __uint_as_float(s2[0]);
+        yp[j] = __uint_as_float(s2[1]);
+        const auto z1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(zv[0][j]),
+                                                         __float_as_uint(zv[1][j]), false, false);
+        const auto z2 = __builtin_amdgcn_permlane16_swap(z1[0], z1[1], false, false);
+        xz[j] = __uint_as_float(z2[0]);
+        yz[j] = __uint_as_float(z2[1]);
+      }
+      wp[0] = pack_bf16x2(xp[0], xp[1]);
+      wp[1] = pack_bf16x2(xp[2], xp[3]);
+      wp[2] = pack_bf16x2(yp[0], yp[1]);
+      wp[3] = pack_bf16x2(yp[2], yp[3]);
+      wz[0] = pack_bf16x2(xz[0], xz[1]);
+      wz[1] = pack_bf16x2(xz[2], xz[3]);
+      wz[2] = pack_bf16x2(yz[0], yz[1]);
+      wz[3] = pack_bf16x2(yz[2], yz[3]);
+      pa = as_bf16x8(u32x4{wp[0], wp[1], wp[2], wp[3]});
+      za = as_bf16x8(u32x4{wz[0], wz[1], wz[2], wz[3]});
+    }
+    // dV += P^T dO, dK += dZ^T Q: B operand lane = feature 16nt + r16,
+    // k = the 8 heads 8(grp&1) .. of token grp>>1
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int d = 16 * nt + r16;
+      const bf16x8 bd = as_bf16x8(*(const u32x4*)&doT[grp >> 1][d][8 * (grp & 1)]);
+      const bf16x8 bq = as_bf16x8(*(const u32x4*)&qT[grp >> 1][d][8 * (grp & 1)]);
+      accV[nt] = mfma16(pa, bd, accV[nt]);
+      accK[nt] = mfma16(za, bq, accK[nt]);
+    }
+  }
+  // C layout: rows = keys tile_key(wave, 4grp + j), column = feature 16nt + r16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int key = blk * AT_B + tile_key(wave, 4 * grp + j);
+    if (key >= a.n_kv) continue;
+    const size_t off = (((size_t)b * a.kv_cap + key) * a.h_kv + g) * AT_D + r16;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      atomicAdd(a.dV + off + 16 * nt, accV[nt][j]);
+      atomicAdd(a.dK + off + 16 * nt, accK[nt][j] * a.scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic shapes (fp32 I/O, other G, d, B): one workgroup per (token, group),
+// fp64 math; dK / dV by fp32 atomics.  Dynamic LDS: 2 * max keys doubles.
+struct GenericBwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* lse;
+  const int32_t* idx;
+  const int32_t* n_sel;
+  float* dQ;
+  float* dK;
+  float* dV;
+  int n_q, q_pos0, n_kv, h_kv, G, d, B, budget, max_keys;
+  int64_t kv_cap;
+  double scale;
+};
+
+template <typename T> __device__ __forceinline__ double bld(const T* p, size_t i);
+template <> __device__ __forceinline__ double bld<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ double bld<uint16_t>(const uint16_t* p, size_t i) {
+  return (double)bf16_bits_to_f32(p[i]);
+}
+
+__device__ double bwd_block_sum(double v, double* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  double r = 0.0;
+  for (int i = 0; i < nw; ++i) r += red[i];
+  return r;
+}
+
+template <typename T, bool SPARSE>
+__global__ void __launch_bounds__(256) attn_bwd_generic_kernel(GenericBwdArgs a) {
+  extern __shared__ double gdyn[];
+  __shared__ double red[8];
+  __shared__ int keys_s[1];
+  double* pz = gdyn;                 // [max_keys]: P_t, then dZ_t
+  double* pp = gdyn + a.max_keys;    // [max_keys]: P_t
+  int* klist = (int*)(gdyn + 2 * (size_t)a.max_keys);   // [max_keys] key positions
+  const int t = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int p = a.q_pos0 + t;
+  const int b_p = p / a.B;
+  const int hq = a.h_kv * a.G;
+  const T* Q = (const T*)a.Q;
+  const T* K = (const T*)a.K;
+  const T* V = (const T*)a.V;
+  const T* O = (const T*)a.O;
+  const T* dO = (const T*)a.dO;
+  // the attended keys T(p), ascending
+  if (threadIdx.x == 0) {
+    int n = 0;
+    const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+    const int nb = SPARSE ? a.n_sel[row] : b_p + 1;
+    for (int i = 0; i < nb; ++i) {
+      const int blk = SPARSE ? a.idx[row * a.budget + i] : i;
+      if (blk < 0 || blk > b_p) continue;
+      for (int key = blk * a.B; key < min(blk * a.B + a.B, p + 1); ++key) klist[n++] = key;
+    }
+    keys_s[0] = n;
+  }
+  __syncthreads();
+  const int nk = keys_s[0];
+  for (int hh = 0; hh < a.G; ++hh) {
+    const int h = g * a.G + hh;
+    const size_t qo = (((size_t)b * a.n_q + t) * hq + h) * a.d;
+    const double L = (double)a.lse[((size_t)b * hq + h) * a.n_q + t];
+    // D = dO . O
+    double dpart = 0.0;
+    for (int i = threadIdx.x; i < a.d; i += blockDim.x) dpart += bld<T>(dO, qo + i) * bld<T>(O, qo + i);
+    const double D = bwd_block_sum(dpart, red);
+    for (int j = threadIdx.x; j < nk; j += blockDim.x) {
+      const size_t ko = (((size_t)b * a.kv_cap + klist[j]) * a.h_kv + g) * a.d;
+      double z = 0.0, dp = 0.0;
+      for (int i = 0; i < a.d; ++i) {
+        z += bld<T>(Q, qo + i) * bld<T>(K, ko + i);
+        dp += bld<T>(dO, qo + i) * bld<T>(V, ko + i);
+      }
+      const double pr = exp(z * a.scale - L);
+      pp[j] = pr;
+      pz[j] = pr * (dp - D);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.d; i += blockDim.x) {
+      double acc = 0.0;
+      for (int j = 0; j < nk; ++j)
+        acc += pz[j] * bld<T>(K, (((size_t)b * a.kv_cap + klist[j]) * a.h_kv + g) * a.d + i);
+      a.dQ[qo + i] = (float)(acc * a.scale);
+    }
+    for (size_t u = threadIdx.x; u < (size_t)nk * a.d; u += blockDim.x) {
+      const int j = (int)(u / a.d), i = (int)(u % a.d);
+      const size_t ko = (((size_t)b * a.kv_cap + klist[j]) * a.h_kv + g) * a.d + i;
+      atomicAdd(a.dK + ko, (float)(pz[j] * a.scale * bld<T>(Q, qo + i)));
+      atomicAdd(a.dV + ko, (float)(pp[j] * bld<T>(dO, qo + i)));
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+bool attn_fast_shape(const infv2_problem& p);
+
+static size_t bwd_nw(const infv2_problem& p) { return ((size_t)p.n_q + 31) / 32; }
+
+size_t attn_bwd_workspace(const infv2_problem& p, bool sparse) {
+  if (!attn_fast_shape(p)) return 0;
+  const size_t n_blk = ((size_t)p.n_kv + AT_B - 1) / AT_B;
+  const size_t packs = 3 * (size_t)p.batch * p.h_kv * n_blk * PACK_ELEMS * sizeof(uint16_t);
+  const size_t dsum = (size_t)p.batch * p.h_kv * AT_G * p.n_q * sizeof(float);
+  const size_t bitmap = sparse ? (size_t)p.batch * p.h_kv * n_blk * bwd_nw(p) * sizeof(uint32_t) : 0;
+  return packs + ((dsum + 255) & ~(size_t)255) + bitmap;
+}
+
+size_t attn_bwd_generic_lds(const infv2_problem& p, int budget, bool sparse) {
+  const size_t max_keys = sparse ? (size_t)budget * p.B : (size_t)p.n_kv;
+  return max_keys * (2 * sizeof(double) + sizeof(int));
+}
+
+hipError_t launch_attn_bwd(const infv2_problem& p, const void* Q, const void* K, const void* V,
+                           const int32_t* idx, const int32_t* n_sel, const void* O,
+                           const float* lse, const void* dO, float* dQ, float* dK, float* dV,
+                           void* ws, int budget, int64_t kv_cap, float scale,
+                           hipStream_t stream) {
+  const bool sparse = idx != nullptr;
+  const int n_blk = (p.n_kv + AT_B - 1) / AT_B;
+  {  // dK, dV rows 0..n_kv-1 start at zero
+    const size_t per_seq = (size_t)p.n_kv * p.h_kv * p.d;
+    const size_t blocks = (per_seq + 255) / 256;
+    const int gx = (int)(blocks < 4096 ? blocks : 4096);
+    hipLaunchKernelGGL(bwd_zero_kv_kernel, dim3(gx, p.batch), dim3(256), 0, stream, dK, dV,
+                       p.n_kv, p.h_kv * p.d, kv_cap);
+  }
+  if (attn_fast_shape(p)) {
+    BwdArgs a = {};
+    a.Q = (const uint16_t*)Q;
+    a.dO = (const uint16_t*)dO;
+    a.O = (const uint16_t*)O;
+    a.lse = lse;
+    const size_t pack = (size_t)p.batch * p.h_kv * n_blk * PACK_ELEMS;
+    a.Kp = (const uint16_t*)ws;
+    a.Vk = (const uint16_t*)ws + pack;
+    a.Kv = (const uint16_t*)ws + 2 * pack;
+    char* tail = (char*)ws + 3 * pack * sizeof(uint16_t);
+    a.Dsum = (float*)tail;
+    const size_t dsum = (size_t)p.batch * p.h_kv * AT_G * p.n_q * sizeof(float);
+    a.bitmap = sparse ? (const uint32_t*)(tail + ((dsum + 255) & ~(size_t)255)) : nullptr;
+    a.idx = idx;
+    a.n_sel = n_sel;
+    a.dQ = dQ;
+    a.dK = dK;
+    a.dV = dV;
+    a.batch = p.batch;
+    a.n_q = p.n_q;
+    a.q_pos0 = p.q_pos0;
+    a.n_kv = p.n_kv;
+    a.n_blk = n_blk;
+    a.h_kv = p.h_kv;
+    a.budget = budget;
+    a.nw = (int)bwd_nw(p);
+    a.kv_cap = kv_cap;
+    a.c = scale * kLog2e;
+    a.scale = scale;
+    hipLaunchKernelGGL(bwd_pack_kernel, dim3(n_blk, p.h_kv, p.batch), dim3(256), 0, stream,
+                       (const uint16_t*)K, (const uint16_t*)V, (uint16_t*)a.Kp, (uint16_t*)a.Vk,
+                       (uint16_t*)a.Kv, p.n_kv, n_blk, p.h_kv, kv_cap);
+    if (sparse) {
+      const size_t words = (size_t)p.batch * p.h_kv * n_blk * a.nw;
+      const size_t zblocks = (words + 255) / 256;
+      const int gz = (int)(zblocks < 4096 ? zblocks : 4096);
+      hipLaunchKernelGGL(bwd_zero_kernel, dim3(gz), dim3(256), 0, stream,
+                         const_cast<uint32_t*>(a.bitmap), words);
+      const size_t rows = (size_t)p.batch * p.h_kv * p.n_q;
+      hipLaunchKernelGGL(bwd_bitmap_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                         stream, a);
+    }
+    const int total_qb = ((p.n_q + AT_B - 1) / AT_B) * p.batch * p.h_kv;
+    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(((total_qb + 7) / 8) * 8 * 16), dim3(256), 0,
+                       stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel,
+                       dim3((p.n_q + BW_WIN - 1) / BW_WIN, n_blk, p.batch * p.h_kv), dim3(256),
+                       0, stream, a);
+    return hipGetLastError();
+  }
+  GenericBwdArgs a = {};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.dO = dO;
+  a.lse = lse;
+  a.idx = idx;
+  a.n_sel = n_sel;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.n_q = p.n_q;
+  a.q_pos0 = p.q_pos0;
+  a.n_kv = p.n_kv;
+  a.h_kv = p.h_kv;
+  a.G = p.G;
+  a.d = p.d;
+  a.B = p.B;
+  a.budget = budget;
+  a.max_keys = sparse ? budget * p.B : p.n_kv;
+  a.kv_cap = kv_cap;
+  a.scale = scale;
+  const size_t lds = attn_bwd_generic_lds(p, budget, sparse);
+  dim3 grid(p.n_q, p.h_kv, p.batch);
+  if (p.dtype == INFV2_F32) {
+    if (sparse) hipLaunchKernelGGL((attn_bwd_generic_kernel<float, true>), grid, dim3(256), lds, stream, a);
+    else hipLaunchKernelGGL((attn_bwd_generic_kernel<float, false>), grid, dim3(256), lds, stream, a);
+  } else {
+    if (sparse) hipLaunchKernelGGL((attn_bwd_generic_kernel<uint16_t, true>), grid, dim3(256), lds, stream, a);
+    else hipLaunchKernelGGL((attn_bwd_generic_kernel<uint16_t, false>), grid, dim3(256), lds, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace infv2
