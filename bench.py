@@ -233,6 +233,55 @@ def bench_prefill(cfg, steps, warmup, with_dense=True, dense_steps=None, pipelin
     return out
 
 
+def bench_backward(cfg, steps, warmup, with_dense=True):
+    """Training-side record: the backward of the block-sparse attention (dQ,
+    dK, dV with the selected sets fixed) after one forward on the same
+    inputs; algorithmic work = 2.5x the forward attention flops (recomputed
+    scores and dP: 2d each, dV, dK, dQ: 2d each per (token, head, key))."""
+    log(f"[bench] {cfg.name}: backward")
+    x = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
+    del x
+    lp = problem_of(cfg)
+    bud = tbs.budget(lp)
+    gen = torch.Generator().manual_seed(cfg.seed)
+    dO = torch.randn(Q.shape, generator=gen).to(Q.dtype).to(dev)
+    Kc1 = tbs.compress_k(lp, K)
+    idx, nsel = tbs.topk_select(lp, tbs.block_scores(lp, Q, Kc1))
+    O, lse = tbs.sparse_attn(lp, Q, K, V, idx, nsel)
+    dQ = torch.empty(Q.shape, dtype=torch.float32, device=dev)
+    dK = torch.empty((lp.batch, lp.n_kv, lp.h_kv, lp.d), dtype=torch.float32, device=dev)
+    dV = torch.empty_like(dK)
+    ws = torch.empty(max(tbs.sparse_attn_bwd_workspace(lp), tbs.dense_attn_bwd_workspace(lp), 16),
+                     dtype=torch.uint8, device=dev)
+    fn = lambda: tbs.sparse_attn_bwd(lp, Q, K, V, idx, nsel, O, lse, dO, dQ, dK, dV, ws)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t = StageTimer(["sparse_attn_bwd"])
+    for _ in range(steps):
+        t.step([fn])
+    ms = t.collect()["sparse_attn_bwd"]
+    pos = np.arange(cfg.n_kv)
+    flops = 2.5 * attention_flops(cfg, pos, bud)
+    out = dict(ms=ms, tokens_per_s=cfg.batch * cfg.n_q / (ms / 1e3), algo_flops=flops,
+               algo_tflops=flops / (ms / 1e3) / 1e12)
+    out["frac_of_bf16_peak"] = out["algo_tflops"] / PEAK_BF16_TFLOPS
+    if with_dense:
+        Od, lsed = tbs.dense_attn(lp, Q, K, V)
+        fd = lambda: tbs.dense_attn_bwd(lp, Q, K, V, Od, lsed, dO, dQ, dK, dV, ws)
+        fd()
+        td = StageTimer(["dense_attn_bwd"])
+        for _ in range(max(1, steps // 2)):
+            td.step([fd])
+        out["dense_bwd_ms"] = td.collect()["dense_attn_bwd"]
+        out["speedup_vs_dense_bwd"] = out["dense_bwd_ms"] / ms
+    del Q, K, V, O, dO, dQ, dK, dV, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(cfg, steps, warmup, lse_approx=False):
     log(f"[bench] {cfg.name}{' (LSE approximation)' if lse_approx else ''}: "
         "generating the KV cache")
@@ -407,7 +456,7 @@ def main():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the two-stream range-pipeline record of the 128k prefill")
     ap.add_argument("--only", choices=["prefill32k", "prefill128k", "decode", "dense_switch",
-                                       "copy"],
+                                       "copy", "backward32k", "backward128k"],
                     help="run one workload alone and print its record (profiling runs); "
                          "'copy' is a plain 256 MiB device copy used to calibrate the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -432,6 +481,11 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
             print(json.dumps({"workload": "copy", "bytes_read": n, "bytes_written": n}), flush=True)
+            return
+        if args.only.startswith("backward"):
+            c = CONFIGS["prefill" + args.only[len("backward"):]]
+            rec = bench_backward(c, args.steps, args.warmup, with_dense=not args.no_dense)
+            print(json.dumps({"workload": args.only, **rec}), flush=True)
             return
         c = CONFIGS[args.only]
         if args.only == "decode":
@@ -488,6 +542,9 @@ def main():
         c5 = CONFIGS["dense_switch"]
         r5 = bench_dense_switch(c5, args.steps, args.warmup)
         extra["dense_switch"] = r5
+        rbw = bench_backward(cfg, args.steps, args.warmup, with_dense=not args.no_dense)
+        extra["prefill32k_backward"] = rbw
+        log(f"[bench] prefill32k backward: {rbw['ms']:.3f} ms")
         if not args.no_approx:
             # the pages' default selection: the LSE approximation (its own
             # oracle mode and parity tests)

@@ -22,7 +22,7 @@
 //    query tokens), 4 waves x 16 keys.  The tokens of the window that
 //    selected the block come from a bitmap (bwd_bitmap_kernel) in ascending
 //    order and are taken two at a time: S = Q K^T and dP = dO V^T with the 16
-//    heads of both tokens on M; two permlane swaps turn P and dZ into the
+//    heads of a token on M; two permlane swaps turn P and dZ into the
 //    A operand of dV = P^T dO and dK = dZ^T Q (keys on M, the 32 (token, head)
 //    pairs on K), whose B operands are dO and Q transposed through LDS.  The
 //    window's partial dK / dV are added to the fp32 outputs with atomics
@@ -226,9 +226,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
         for (int u = 0; u < 2; ++u) {
           const int i = i0 + u;
           const int key = kv0 + tile_key(tt, 4 * grp + i);
-          const float pr = (diag && key > p) ? 0.f
-                                             : fast_exp2(__builtin_fmaf(s[tt][i], a.c, -L2));
-          z2[u] = pr * (dp[tt][i] - dsum);
+          // masked keys take exp2(-inf) = 0: a select, no branch
+          const float arg = (diag && key > p) ? kNegInf : __builtin_fmaf(s[tt][i], a.c, -L2);
+          z2[u] = fast_exp2(arg) * (dp[tt][i] - dsum);
         }
         w[e] = pack_bf16x2(z2[0], z2[1]);
       }
@@ -250,15 +250,36 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dK, dV.  grid: x = window of BW_WIN query tokens, y = key block, z = b*h_kv.
+// Tokens go two at a time (a pair) through LDS, as row-major Q and dO (the
+// A operands of S = Q K^T and dP = dO V^T) and as transposed Q^T, dO^T (the
+// B operands of dV = P^T dO and dK = dZ^T Q).  Wave w stages token w>>1's Q
+// (w even) or dO (w odd): lane (hq = lane>>4, fo = lane&15) loads heads
+// 4hq .. 4hq+3 at features 8fo .. 8fo+7 (consecutive lanes read one head's
+// row), writes the four rows as they are and the transposed 8 x 4 tile as
+// eight 8-byte words.  Transposed rows are 16 bytes (8 heads; two halves of
+// the 16 heads) and row d sits in slot 16(d>>4) + ((d&15) ^ (d>>4)): the
+// stores (rows 8 apart across lanes) and the operand reads (16 consecutive
+// rows) both fall on distinct banks.  LDS holds two pairs; the registers of
+// two more are in flight, so a load has two pairs of compute to land.
 constexpr int BW_WIN = 1024;
-constexpr int BW_TROW = AT_G + 8;   // LDS row of a transposed token: 16 heads + pad (48 B)
+constexpr int BW_RROW = AT_D + 8;   // row-major LDS row (bf16): 272 B, conflict-free reads
+
+struct BwdTok {                      // one staged token (16 896 B)
+  uint16_t R[2][AT_G][BW_RROW];      // [Q, dO][head][feature]
+  uint16_t T[2][2][AT_D][8];         // [Q, dO][head half][slot of feature][8 heads]
+};
+
+__device__ __forceinline__ int bwd_tslot(int d) { return (d & ~15) | ((d & 15) ^ (d >> 4)); }
+
+struct BwdStage {                    // one thread's share of a staged pair
+  u32x4 r[4];                        // heads 4hq + j, features 8fo .. +7
+  float ld;                          // L (Q waves) or D (dO waves) of head lane&15
+};
 
 __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ int toks[BW_WIN];
-  __shared__ int wcnt[64];
-  __shared__ __attribute__((aligned(16))) uint16_t qT[2][AT_D][BW_TROW];
-  __shared__ __attribute__((aligned(16))) uint16_t doT[2][AT_D][BW_TROW];
-  __shared__ float Ls[2][AT_G], Ds[2][AT_G];
+  __shared__ __attribute__((aligned(16))) BwdTok stg[2][2];   // [buffer][token of the pair]
+  __shared__ float LD[2][2][2][AT_G];                         // [buffer][token][L, D][head]
   __shared__ int ntok_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int win = blockIdx.x, blk = blockIdx.y, bg = blockIdx.z;
@@ -269,10 +290,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   const int t_first = max(t_lo, blk * AT_B - a.q_pos0);
   if (t_first >= t_hi) return;
   const bool sparse = a.idx != nullptr;
-  // the window's tokens that selected the block, ascending
   if (sparse) {
+    // tokens of the window that selected the block, ascending
     const int w0 = t_lo >> 5;
-    const int nwin = (t_hi - t_lo + 31) >> 5;                 // <= 32 words
+    const int nwin = (t_hi - t_lo + 31) >> 5;
     const uint32_t* bm = a.bitmap + ((size_t)bg * a.n_blk + blk) * a.nw + w0;
     uint32_t word = 0u;
     if (tid < nwin) word = bm[tid];
@@ -295,6 +316,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   __syncthreads();
   const int ntok = ntok_s;
   if (ntok == 0) return;
+  const int npairs = (ntok + 1) >> 1;
   const int grp = lane >> 4, r16 = lane & 15;
   const int hq = a.h_kv * AT_G;
   // this wave's 16 keys: tile `wave` of the block (row r16 holds key
@@ -307,66 +329,72 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     vkf[ks] = as_bf16x8(*(const u32x4*)(a.Vk + boff + (4 * wave + ks) * 512));
   }
   const int key_l = blk * AT_B + tile_key(wave, r16);    // key of this lane's column
+  // staging role: token st_k of the pair, tensor st_x (0: Q, 1: dO)
+  const int st_k = wave >> 1, st_x = wave & 1;
+  const int s_hq = lane >> 4, s_fo = lane & 15;
+  const uint16_t* st_src = st_x ? a.dO : a.Q;
+  const float* st_ld = st_x ? a.Dsum : a.lse;
+  const float st_mul = st_x ? 1.f : kLog2e;
+  // Branch-free loads (a branch around them would make the compiler wait for
+  // them at its end): a missing second token of the last pair stages the
+  // window's first token instead, whose finite values its masked P and dZ
+  // (exact zeros) then cancel.
+  auto stage_load = [&](int pair, BwdStage& s) {
+    const int k = 2 * pair + st_k;
+    const int tt = toks[k < ntok ? k : 0];
+    const size_t off = (((size_t)b * a.n_q + tt) * hq + g * AT_G + 4 * s_hq) * AT_D + 8 * s_fo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.r[j] = *(const u32x4*)(st_src + off + j * AT_D);
+    s.ld = st_ld[((size_t)b * hq + g * AT_G + (lane & 15)) * a.n_q + tt];
+  };
+  auto stage_store = [&](int buf, const BwdStage& s) {
+    BwdTok& T = stg[buf][st_k];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *(u32x4*)&T.R[st_x][4 * s_hq + j][8 * s_fo] = s.r[j];
+    uint16_t* th = &T.T[st_x][s_hq >> 1][0][4 * (s_hq & 1)];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // features 8fo + 2m (low halves) and 8fo + 2m + 1 (high halves), heads 4hq .. +3
+      const u32x2 lo = {(s.r[0][m] & 0xFFFFu) | (s.r[1][m] << 16),
+                        (s.r[2][m] & 0xFFFFu) | (s.r[3][m] << 16)};
+      const u32x2 hi = {(s.r[0][m] >> 16) | (s.r[1][m] & 0xFFFF0000u),
+                        (s.r[2][m] >> 16) | (s.r[3][m] & 0xFFFF0000u)};
+      *(u32x2*)(th + 8 * bwd_tslot(8 * s_fo + 2 * m)) = lo;
+      *(u32x2*)(th + 8 * bwd_tslot(8 * s_fo + 2 * m + 1)) = hi;
+    }
+    // lanes l, l+16, l+32, l+48 hold the same value: all write it, with no
+    // branch (a branch would wait for every load in flight)
+    LD[buf][st_k][st_x][lane & 15] = s.ld * st_mul;
+  };
   f32x4 accV[8], accK[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     accV[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     accK[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  for (int i = 0; i < ntok; i += 2) {
-    const int tA = toks[i];
-    const int tB = i + 1 < ntok ? toks[i + 1] : -1;
-    __syncthreads();   // the previous pair's LDS reads are done
-    // Q^T and dO^T of the pair into LDS: thread = (token, head, 16-feature chunk)
-    {
-      const int tk = tid >> 7, hh = (tid >> 3) & 15, dc = (tid & 7) * 16;
-      const int tt = tk == 0 ? tA : tB;
-      u32x4 q0 = {0u, 0u, 0u, 0u}, q1 = q0, d0 = q0, d1 = q0;
-      if (tt >= 0) {
-        const size_t off = (((size_t)b * a.n_q + tt) * hq + g * AT_G + hh) * AT_D + dc;
-        q0 = *(const u32x4*)(a.Q + off);
-        q1 = *(const u32x4*)(a.Q + off + 8);
-        d0 = *(const u32x4*)(a.dO + off);
-        d1 = *(const u32x4*)(a.dO + off + 8);
-      }
+  auto compute = [&](int buf, int pair) {
+    const int tA = toks[2 * pair];
+    const int tB = 2 * pair + 1 < ntok ? toks[2 * pair + 1] : -1;
+    // the (token, head) normalisers and D of this lane's rows
+    float Lr[2][4], Dr[2][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qT[tk][dc + 2 * e][hh] = (uint16_t)(q0[e] & 0xFFFFu);
-        qT[tk][dc + 2 * e + 1][hh] = (uint16_t)(q0[e] >> 16);
-        qT[tk][dc + 8 + 2 * e][hh] = (uint16_t)(q1[e] & 0xFFFFu);
-        qT[tk][dc + 8 + 2 * e + 1][hh] = (uint16_t)(q1[e] >> 16);
-        doT[tk][dc + 2 * e][hh] = (uint16_t)(d0[e] & 0xFFFFu);
-        doT[tk][dc + 2 * e + 1][hh] = (uint16_t)(d0[e] >> 16);
-        doT[tk][dc + 8 + 2 * e][hh] = (uint16_t)(d1[e] & 0xFFFFu);
-        doT[tk][dc + 8 + 2 * e + 1][hh] = (uint16_t)(d1[e] >> 16);
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Lr[k2][j] = LD[buf][k2][0][4 * grp + j];
+        Dr[k2][j] = LD[buf][k2][1][4 * grp + j];
       }
-      if (tid < 2 * AT_G) {
-        const int k2 = tid >> 4, h2 = tid & 15;
-        const int t2 = k2 == 0 ? tA : tB;
-        float L = 0.f, D = 0.f;
-        if (t2 >= 0) {
-          const size_t o2 = ((size_t)b * hq + g * AT_G + h2) * a.n_q + t2;
-          L = a.lse[o2] * kLog2e;
-          D = a.Dsum[o2];
-        }
-        Ls[k2][h2] = L;
-        Ds[k2][h2] = D;
-      }
-    }
-    __syncthreads();
     // S and dP for both tokens: rows = heads 4grp + j, column = key key_l
     f32x4 sc[2], dpv[2];
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
-      const int tt = k2 == 0 ? tA : tB;
-      const int tq = tt >= 0 ? tt : tA;
-      const size_t qoff = (((size_t)b * a.n_q + tq) * hq + g * AT_G + r16) * AT_D + 8 * grp;
       sc[k2] = f32x4{0.f, 0.f, 0.f, 0.f};
       dpv[k2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const BwdTok& T = stg[buf][k2];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 qa = as_bf16x8(*(const u32x4*)(a.Q + qoff + 32 * ks));
-        const bf16x8 da = as_bf16x8(*(const u32x4*)(a.dO + qoff + 32 * ks));
+        const bf16x8 qa = as_bf16x8(*(const u32x4*)&T.R[0][r16][32 * ks + 8 * grp]);
+        const bf16x8 da = as_bf16x8(*(const u32x4*)&T.R[1][r16][32 * ks + 8 * grp]);
         sc[k2] = mfma16(qa, kf[ks], sc[k2]);
         dpv[k2] = mfma16(da, vkf[ks], dpv[k2]);
       }
@@ -379,17 +407,17 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
       const bool live = tt >= 0 && key_l <= a.q_pos0 + tt;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int h = 4 * grp + j;
-        const float pr = live ? fast_exp2(__builtin_fmaf(sc[k2][j], a.c, -Ls[k2][h])) : 0.f;
+        // masked entries take exp2(-inf) = 0: a select, no branch
+        const float arg = live ? __builtin_fmaf(sc[k2][j], a.c, -Lr[k2][j]) : kNegInf;
+        const float pr = fast_exp2(arg);
         pv[k2][j] = pr;
-        zv[k2][j] = pr * (dpv[k2][j] - Ds[k2][h]);
+        zv[k2][j] = pr * (dpv[k2][j] - Dr[k2][j]);
       }
     }
     // to A operands: lane row r16 = key, k = 8*grp + e = the 32 (token, head)
     // pairs (grp 0, 1: token A heads 0-7, 8-15; grp 2, 3: token B)
     bf16x8 pa, za;
     {
-      uint32_t wp[4], wz[4];
       float xp[4], yp[4], xz[4], yz[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -404,27 +432,45 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
         xz[j] = __uint_as_float(z2[0]);
         yz[j] = __uint_as_float(z2[1]);
       }
-      wp[0] = pack_bf16x2(xp[0], xp[1]);
-      wp[1] = pack_bf16x2(xp[2], xp[3]);
-      wp[2] = pack_bf16x2(yp[0], yp[1]);
-      wp[3] = pack_bf16x2(yp[2], yp[3]);
-      wz[0] = pack_bf16x2(xz[0], xz[1]);
-      wz[1] = pack_bf16x2(xz[2], xz[3]);
-      wz[2] = pack_bf16x2(yz[0], yz[1]);
-      wz[3] = pack_bf16x2(yz[2], yz[3]);
-      pa = as_bf16x8(u32x4{wp[0], wp[1], wp[2], wp[3]});
-      za = as_bf16x8(u32x4{wz[0], wz[1], wz[2], wz[3]});
+      pa = as_bf16x8(u32x4{pack_bf16x2(xp[0], xp[1]), pack_bf16x2(xp[2], xp[3]),
+                           pack_bf16x2(yp[0], yp[1]), pack_bf16x2(yp[2], yp[3])});
+      za = as_bf16x8(u32x4{pack_bf16x2(xz[0], xz[1]), pack_bf16x2(xz[2], xz[3]),
+                           pack_bf16x2(yz[0], yz[1]), pack_bf16x2(yz[2], yz[3])});
     }
     // dV += P^T dO, dK += dZ^T Q: B operand lane = feature 16nt + r16,
     // k = the 8 heads 8(grp&1) .. of token grp>>1
+    const BwdTok& T = stg[buf][grp >> 1];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const int d = 16 * nt + r16;
-      const bf16x8 bd = as_bf16x8(*(const u32x4*)&doT[grp >> 1][d][8 * (grp & 1)]);
-      const bf16x8 bq = as_bf16x8(*(const u32x4*)&qT[grp >> 1][d][8 * (grp & 1)]);
+      const int slot = 16 * nt + (r16 ^ nt);
+      const bf16x8 bq = as_bf16x8(*(const u32x4*)&T.T[0][grp & 1][slot][0]);
+      const bf16x8 bd = as_bf16x8(*(const u32x4*)&T.T[1][grp & 1][slot][0]);
       accV[nt] = mfma16(pa, bd, accV[nt]);
       accK[nt] = mfma16(za, bq, accK[nt]);
     }
+  };
+  // pipeline: pair i is read from buffer i&1; set A holds the registers of
+  // even pairs, set B of odd pairs, loaded two pairs ahead.  Loads and stores
+  // are unconditional (pair indices past the end are clamped to the last
+  // pair, whose copies are never read): a load under a branch would make the
+  // compiler wait for all loads in flight where the branch joins.
+  const int last = npairs - 1;
+  BwdStage sa, sb;
+  stage_load(0, sa);
+  stage_load(min(1, last), sb);
+  stage_store(0, sa);
+  stage_load(min(2, last), sa);
+  __syncthreads();
+  for (int i = 0; i < npairs; i += 2) {
+    compute(0, i);
+    stage_store(1, sb);
+    stage_load(min(i + 3, last), sb);
+    __syncthreads();
+    if (i + 1 >= npairs) break;
+    compute(1, i + 1);
+    stage_store(0, sa);
+    stage_load(min(i + 4, last), sa);
+    __syncthreads();
   }
   // C layout: rows = keys tile_key(wave, 4grp + j), column = feature 16nt + r16
 #pragma unroll
