@@ -226,6 +226,59 @@ int infv2_dense_attn_bwd(const infv2_problem* prob, const void* Q, const void* K
                          float* dQ, float* dK, float* dV, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* Varlen batches and a paged K/V cache, for serving decode (OpenBMB blog,
+ * 查询和键值词元的不同粒度: token-level queries are what makes the sparse
+ * decode step fast; the paged layout is this library's own serving format).
+ * The definitions are those of the calls above, applied to each sequence
+ * with its own length:
+ *  - seq_lens : [batch] int32 (device): sequence i's cache holds seq_lens[i]
+ *    tokens, the new ones included; its n_q query tokens are its last n_q,
+ *    at positions seq_lens[i]-n_q .. seq_lens[i]-1.  Entries must lie in
+ *    [n_q, n_kv]; values outside are clamped into that range on the device.
+ *    prob->n_kv is the longest length any sequence may have (it sizes the
+ *    grids and workspaces); prob->q_pos0 is not used (pass 0).
+ *  - Paged cache: K and V are pools of n_pages pages [B][h_kv][d] (bf16);
+ *    block_table [batch][max_blocks] int32 (device) gives the page of block j
+ *    of sequence i, for j < ceil(seq_lens[i]/B) (max_blocks >= ceil(n_kv/B)).
+ *    A page holds one KV block, so a selected block is read from one page.
+ *    Entries outside [0, n_pages) are clamped into it (that sequence's
+ *    result is then meaningless, but nothing is read out of the pool).
+ *    block_table == NULL: contiguous K, V [batch][kv_cap][h_kv][d].
+ *  - K^C1 (and K^C2) stay contiguous per sequence, [batch][h_kv][c1_cap][d].
+ * Decode shapes only: bf16, G = 16, d = 128, B = 64, l_C1 = 32, s_C1 = 16,
+ * n_q <= 4, k <= 32, budget <= 64 (others: INFV2_E_UNSUPPORTED).
+ *
+ * infv2_compress_k_varlen: stage 1 (coarse = 0: K^C1 into Kc [batch][h_kv]
+ * [c1_cap][d]) or the coarse keys of the LSE approximation (coarse = 1: K^C2
+ * into [batch][h_kv][c2_cap][d]) for each sequence's last `last_n` complete
+ * kernels (all of them when last_n <= 0), with the definitions of
+ * infv2_compress_k / infv2_compress_k2.  A decode step passes last_n = 1
+ * (rewriting a kernel that exists already is harmless). */
+int infv2_compress_k_varlen(const infv2_problem* prob, const void* K,
+                            const int32_t* block_table, int32_t max_blocks, int32_t n_pages,
+                            const int32_t* seq_lens, void* Kc, int32_t coarse,
+                            int32_t last_n, void* stream);
+
+/* infv2_select_blocks for a varlen batch: idx [batch][h_kv][n_q][budget],
+ * n_sel [batch][h_kv][n_q] as in infv2_topk_select, each row with its own
+ * sequence's positions and kernels (S^cmp is not produced).  Kc2 with
+ * prob->lse_approx.  ws: infv2_select_blocks_varlen_workspace(prob) bytes,
+ * not kept between calls. */
+size_t infv2_select_blocks_varlen_workspace(const infv2_problem* prob);
+int infv2_select_blocks_varlen(const infv2_problem* prob, const void* Q, const void* Kc1,
+                               const void* Kc2, const int32_t* seq_lens, int32_t* idx,
+                               int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
+
+/* infv2_sparse_attn for a varlen batch, from a paged (block_table set) or
+ * contiguous cache: O [batch][n_q][h_q][d], lse [batch][h_q][n_q] (may be
+ * NULL).  ws: infv2_sparse_attn_varlen_workspace(prob) bytes. */
+size_t infv2_sparse_attn_varlen_workspace(const infv2_problem* prob);
+int infv2_sparse_attn_varlen(const infv2_problem* prob, const void* Q, const void* K,
+                             const void* V, const int32_t* block_table, int32_t max_blocks,
+                             int32_t n_pages, const int32_t* seq_lens, const int32_t* idx,
+                             const int32_t* n_sel, void* O, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
+
 const char* infv2_status_string(int status);
 const char* infv2_last_error(void);
 

@@ -47,6 +47,9 @@ Sources (cited by tag in the docstrings below):
        selected sets held fixed.
 [BLOG-TOPK] same blog, 高效Top-K实现 (efficient top-k): softmax per kernel,
        aggregate over the head group, then top-k per query token.
+[BLOG-GRAN] same blog, 查询和键值词元的不同粒度 (query and key-value tokens at
+       different granularity): selection is made per query token, which is
+       what lets decoding (one new token per sequence) use the sparse path.
 
 Readings where the pages are silent or ambiguous are tagged READING-<n>; the
 design notes list them all:
@@ -63,6 +66,10 @@ design notes list them all:
                                                    no visible coarse kernel the exact LSE
                                                 17 backward: the sets I(p) are constants;
                                                    gradients of the sparse attention only
+                                                18 varlen batch / paged cache: each sequence
+                                                   is its own problem of its own length;
+                                                   a page table only says where its key
+                                                   rows are stored
 
 Parity: every function below is pinned by ``tests/test_oracle_*.py`` against
 closed forms, invariants, library special cases (torch SDPA, torch's bf16
@@ -82,6 +89,7 @@ __all__ = [
     "kernels_of_block", "compress_k", "selection_scores", "max_pool_blocks", "select_blocks",
     "attention_rows", "dense_switch", "forward_rows", "attended_tokens", "compress_k2",
     "n_coarse_kernels", "coarse_visible", "coarse_lse", "attention_rows_backward",
+    "gather_paged", "decode_varlen",
 ]
 
 # --------------------------------------------------------------------------
@@ -519,4 +527,41 @@ def forward_rows(Q, K, V, rows, prob: Problem, q_pos0: int = 0, Kc1=None,
                   for r, p in enumerate(q_pos)]
     O64, lse = attention_rows(Qrows, K, V, token_sets, prob)
     out.update(sets=sets, O64=O64, O=round_to_io(O64, prob.io), lse=lse)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Varlen batches and paged caches (serving decode)
+# --------------------------------------------------------------------------
+
+
+def gather_paged(pool, table_row, n_tokens: int, B: int) -> np.ndarray:
+    """The first n_tokens token rows of one sequence kept in a paged cache
+    (READING-18): token u lives in page table_row[u // B], row u % B.  Pure
+    indexing, no arithmetic.  pool: [n_pages, B, ...]."""
+    pool = np.asarray(pool)
+    u = np.arange(n_tokens)
+    pages = np.asarray(table_row)[u // B]
+    return pool[pages, u % B]
+
+
+def decode_varlen(Q, K, V, seq_lens, prob: Problem, block_table=None, mode: str = "auto"):
+    """A varlen batch ([BLOG-GRAN], READING-18): sequence i holds seq_lens[i]
+    tokens and its n_q = Q.shape[1] query tokens are its last ones; each
+    sequence is the problem of forward_rows on its own keys, with
+    q_pos0 = seq_lens[i] - n_q.
+
+    Q: [b, n_q, h_q, d].  K, V: [b, kv_cap, h_kv, d] (contiguous) or, with
+    block_table [b, max_blocks], page pools [n_pages, B, h_kv, d].
+    Returns one forward_rows dict per sequence."""
+    Q = np.asarray(Q)
+    n_q = Q.shape[1]
+    out = []
+    for i, L in enumerate(int(x) for x in seq_lens):
+        if block_table is None:
+            Ki, Vi = np.asarray(K)[i, :L], np.asarray(V)[i, :L]
+        else:
+            Ki = gather_paged(K, block_table[i], L, prob.B)
+            Vi = gather_paged(V, block_table[i], L, prob.B)
+        out.append(forward_rows(Q[i], Ki, Vi, np.arange(n_q), prob, q_pos0=L - n_q, mode=mode))
     return out

@@ -4,4 +4,4 @@ Holds none of the method's arithmetic: only shapes, hyper-parameters,
 random numbers, needle planting and dtype casts.
 """
 from .configs import CONFIGS, Config  # noqa: F401
-from .inputs import make_inputs, needle_blocks  # noqa: F401
+from .inputs import make_inputs, needle_blocks, paged_cache, varlen_lengths  # noqa: F401

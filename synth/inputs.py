@@ -76,3 +76,36 @@ def make_inputs(cfg: Config, seed: int | None = None, n_kv: int | None = None,
 def _with_nkv(cfg: Config, n_kv: int) -> Config:
     from dataclasses import replace
     return replace(cfg, n_kv=n_kv, n_q=(1 if cfg.decode else n_kv))
+
+
+def varlen_lengths(batch: int, max_len: int, seed: int, must=()) -> np.ndarray:
+    """Seeded cache lengths of a varlen decode batch: the listed lengths first,
+    the rest uniform on [1, max_len]; int32 [batch]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = list(must)[:batch]
+    lens += rng.integers(1, max_len + 1, size=batch - len(lens)).tolist()
+    return np.asarray(lens, dtype=np.int32)
+
+
+def paged_cache(k: torch.Tensor, v: torch.Tensor, lengths, B: int, seed: int,
+                extra_pages: int = 3):
+    """The same tokens in a paged layout: pools [n_pages, B, h_kv, d] and a
+    page table [batch, max_blocks] int32 with the pages of all sequences in a
+    seeded random order (pages past a sequence's length hold its zero-padded
+    rows; the pool also has `extra_pages` random pages no table points to).
+    k, v: contiguous [batch, kv_cap, h_kv, d] CPU tensors.  Layout only."""
+    b, cap, h_kv, d = k.shape
+    max_blocks = (cap + B - 1) // B
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n_pages = b * max_blocks + extra_pages
+    order = rng.permutation(n_pages)
+    table = order[: b * max_blocks].reshape(b, max_blocks).astype(np.int32)
+    kp = torch.from_numpy(rng.standard_normal((n_pages, B, h_kv, d), dtype=np.float32)).to(k.dtype)
+    vp = torch.from_numpy(rng.standard_normal((n_pages, B, h_kv, d), dtype=np.float32)).to(v.dtype)
+    pad = max_blocks * B - cap
+    kf = torch.nn.functional.pad(k, (0, 0, 0, 0, 0, pad)) if pad else k
+    vf = torch.nn.functional.pad(v, (0, 0, 0, 0, 0, pad)) if pad else v
+    idx = torch.from_numpy(table.reshape(-1).astype(np.int64))
+    kp[idx] = kf.reshape(b * max_blocks, B, h_kv, d)
+    vp[idx] = vf.reshape(b * max_blocks, B, h_kv, d)
+    return kp.contiguous(), vp.contiguous(), torch.from_numpy(table)

@@ -145,3 +145,31 @@ def test_workspace_sizes_and_errors(L):
     assert L.infv2_dense_attn_workspace(ctypes.byref(pre.to_c())) == 2 * 2 * 32768 * 128 * 2
     for s in (0, -1, -2, -3, -4, 7):
         assert L.infv2_status_string(s)
+
+
+def test_varlen_calls_validate_before_any_launch(L):
+    dec = _prob(batch=4, n_q=1, q_pos0=0, n_kv=131072)
+    pc = ctypes.byref(dec.to_c())
+    # workspaces: the fused decode selection's and the split attention's
+    assert L.infv2_select_blocks_varlen_workspace(pc) == L.infv2_select_blocks_workspace(pc, 0)
+    assert L.infv2_sparse_attn_varlen_workspace(pc) == L.infv2_sparse_attn_workspace(pc)
+    ws = L.infv2_select_blocks_varlen_workspace(pc)
+    # seq_lens is required
+    assert L.infv2_select_blocks_varlen(pc, 16, 16, None, None, 16, 16, 16, ws, None) \
+        == tbs.INFV2_E_ARG
+    assert b"seq_lens" in L.infv2_last_error()
+    assert L.infv2_select_blocks_varlen(pc, 16, 16, None, 16, 16, 16, 16, ws - 1, None) \
+        == tbs.INFV2_E_WORKSPACE
+    # a page table must cover ceil(n_kv / B) = 2048 blocks
+    assert L.infv2_sparse_attn_varlen(pc, 16, 16, 16, 16, 2047, 10, 16, 16, 16, 16, None, 16,
+                                      1 << 30, None) == tbs.INFV2_E_ARG
+    assert b"max_blocks" in L.infv2_last_error()
+    assert L.infv2_compress_k_varlen(pc, 16, 16, 2048, 0, 16, 16, 0, 1, None) == tbs.INFV2_E_ARG
+    assert L.infv2_compress_k_varlen(pc, 16, None, 0, 0, 16, 16, 2, 1, None) == tbs.INFV2_E_ARG
+    # prefill shapes and other dtypes have no varlen kernels
+    pre = ctypes.byref(_prob(n_q=4096, n_kv=4096).to_c())
+    assert L.infv2_select_blocks_varlen(pre, 16, 16, None, 16, 16, 16, 16, 1 << 30, None) \
+        == tbs.INFV2_E_UNSUPPORTED
+    f32 = ctypes.byref(_prob(dtype="f32", G=4, d=64, n_q=1, n_kv=4096).to_c())
+    assert L.infv2_sparse_attn_varlen(f32, 16, 16, 16, None, 0, 0, 16, 16, 16, 16, None, 16,
+                                      1 << 30, None) == tbs.INFV2_E_UNSUPPORTED

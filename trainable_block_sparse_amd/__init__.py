@@ -27,6 +27,9 @@ EXPORTED = (
     "infv2_sparse_attn", "infv2_dense_attn_workspace", "infv2_dense_attn",
     "infv2_sparse_attn_bwd_workspace", "infv2_sparse_attn_bwd",
     "infv2_dense_attn_bwd_workspace", "infv2_dense_attn_bwd",
+    "infv2_compress_k_varlen", "infv2_select_blocks_varlen_workspace",
+    "infv2_select_blocks_varlen", "infv2_sparse_attn_varlen_workspace",
+    "infv2_sparse_attn_varlen",
     "infv2_status_string", "infv2_last_error",
 )
 
@@ -118,6 +121,12 @@ def lib() -> ctypes.CDLL:
             "infv2_sparse_attn_bwd": (ctypes.c_int, [P] + [vp] * 12 + [sz, vp]),
             "infv2_dense_attn_bwd_workspace": (sz, [P]),
             "infv2_dense_attn_bwd": (ctypes.c_int, [P] + [vp] * 10 + [sz, vp]),
+            "infv2_compress_k_varlen": (ctypes.c_int, [P, vp, vp, i32, i32, vp, vp, i32, i32, vp]),
+            "infv2_select_blocks_varlen_workspace": (sz, [P]),
+            "infv2_select_blocks_varlen": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "infv2_sparse_attn_varlen_workspace": (sz, [P]),
+            "infv2_sparse_attn_varlen": (ctypes.c_int, [P, vp, vp, vp, vp, i32, i32] + [vp] * 6
+                                         + [sz, vp]),
             "infv2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "infv2_last_error": (ctypes.c_char_p, []),
         }
@@ -303,6 +312,73 @@ def dense_attn(prob: Problem, Q, K, V, O=None, lse=None, ws=None, want_lse: bool
     _check(lib().infv2_dense_attn(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
                                   _ptr(lse), _ptr(ws), ws.numel() if ws is not None else 0,
                                   _stream(stream)))
+    return O, lse
+
+
+# --- varlen batches / paged cache (decode shapes) ---------------------------
+
+def _pages(block_table, K):
+    """(pointer, max_blocks, n_pages) of a page table over the pool K."""
+    if block_table is None:
+        return None, 0, 0
+    return _ptr(block_table), block_table.shape[1], K.shape[0]
+
+
+def compress_k_varlen(prob: Problem, K: torch.Tensor, seq_lens: torch.Tensor, Kc: torch.Tensor,
+                      block_table: torch.Tensor | None = None, coarse: bool = False,
+                      last_n: int = 0, stream=None) -> torch.Tensor:
+    """Each sequence's last `last_n` complete kernels (all when last_n <= 0)
+    of K^C1 (coarse=False) or K^C2 (coarse=True) into Kc [b, h_kv, cap, d];
+    K is a page pool [n_pages, B, h_kv, d] when block_table is given."""
+    bt, mb, npg = _pages(block_table, K)
+    _check(lib().infv2_compress_k_varlen(ctypes.byref(prob.to_c()), _ptr(K), bt, mb, npg,
+                                         _ptr(seq_lens), _ptr(Kc), int(bool(coarse)), last_n,
+                                         _stream(stream)))
+    return Kc
+
+
+def select_blocks_varlen_workspace(prob: Problem) -> int:
+    return lib().infv2_select_blocks_varlen_workspace(ctypes.byref(prob.to_c()))
+
+
+def select_blocks_varlen(prob: Problem, Q, Kc1, seq_lens, idx=None, n_sel=None, ws=None,
+                         stream=None, Kc2=None):
+    """(idx, n_sel) of a varlen decode batch (sequence i: seq_lens[i] keys)."""
+    if idx is None:
+        idx = torch.empty((prob.batch, prob.h_kv, prob.n_q, budget(prob)), dtype=torch.int32,
+                          device=Q.device)
+    if n_sel is None:
+        n_sel = torch.empty((prob.batch, prob.h_kv, prob.n_q), dtype=torch.int32,
+                            device=Q.device)
+    if ws is None:
+        ws = torch.empty(max(select_blocks_varlen_workspace(prob), 16), dtype=torch.uint8,
+                         device=Q.device)
+    _check(lib().infv2_select_blocks_varlen(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1),
+                                            _ptr(Kc2), _ptr(seq_lens), _ptr(idx), _ptr(n_sel),
+                                            _ptr(ws), ws.numel(), _stream(stream)))
+    return idx, n_sel
+
+
+def sparse_attn_varlen_workspace(prob: Problem) -> int:
+    return lib().infv2_sparse_attn_varlen_workspace(ctypes.byref(prob.to_c()))
+
+
+def sparse_attn_varlen(prob: Problem, Q, K, V, seq_lens, idx, n_sel, block_table=None, O=None,
+                       lse=None, ws=None, want_lse: bool = True, stream=None):
+    """Sparse attention of a varlen decode batch -> (O, lse); K, V are page
+    pools [n_pages, B, h_kv, d] when block_table [b, max_blocks] is given."""
+    if O is None:
+        O = torch.empty_like(Q)
+    if lse is None and want_lse:
+        lse = torch.empty((prob.batch, prob.h_q, prob.n_q), dtype=torch.float32, device=Q.device)
+    if ws is None:
+        ws = torch.empty(max(sparse_attn_varlen_workspace(prob), 16), dtype=torch.uint8,
+                         device=Q.device)
+    bt, mb, npg = _pages(block_table, K)
+    _check(lib().infv2_sparse_attn_varlen(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(K), _ptr(V),
+                                          bt, mb, npg, _ptr(seq_lens), _ptr(idx), _ptr(n_sel),
+                                          _ptr(O), _ptr(lse), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
     return O, lse
 
 

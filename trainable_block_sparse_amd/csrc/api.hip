@@ -13,6 +13,21 @@ namespace infv2 {
 hipError_t launch_compress_k(const infv2_problem& p, const void* K, void* Kc1, int c1_begin,
                              int c1_end, int64_t kv_cap, int64_t c1_cap, int l_len, int s_len,
                              hipStream_t stream);
+hipError_t launch_compress_k_varlen(const infv2_problem& p, const void* K,
+                                    const int32_t* block_table, int max_blocks, int n_pages,
+                                    const int32_t* seq_lens, void* Kc, int64_t kv_cap,
+                                    int64_t c_cap, int l_len, int s_len, int last_n,
+                                    hipStream_t stream);
+hipError_t launch_select_varlen(const infv2_problem& p, const void* Q, const KeySet& ks,
+                                const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, void* ws,
+                                int n_blk, float scale, int budget, hipStream_t stream);
+hipError_t launch_attn_varlen(const infv2_problem& p, const void* Q, const void* K,
+                              const void* V, const int32_t* block_table, int max_blocks,
+                              int n_pages, const int32_t* seq_lens, const int32_t* idx,
+                              const int32_t* n_sel, void* O, float* lse, void* ws, int budget,
+                              int64_t kv_cap, float scale, hipStream_t stream);
+bool scores_use_split(const infv2_problem& p);
+bool attn_use_split(const infv2_problem& p);
 bool scores_fast_shape(const infv2_problem& p);
 size_t scores_workspace(const infv2_problem& p, const KeySet& ks);
 size_t scores_generic_lds(const infv2_problem& p, int n_c1);
@@ -396,6 +411,104 @@ int infv2_dense_attn_bwd(const infv2_problem* p, const void* Q, const void* K, c
                          float* dV, void* ws, size_t ws_bytes, void* stream) {
   return attn_bwd_common(p, Q, K, V, nullptr, nullptr, O, lse, dO, dQ, dK, dV, ws, ws_bytes,
                          stream, "infv2_dense_attn_bwd");
+}
+
+// ---- varlen batches / paged cache (decode shapes)
+static int check_varlen(const infv2_problem* p, const char* what) {
+  int st = check(p);
+  if (st) return st;
+  if (!scores_use_split(*p) || !attn_use_split(*p))
+    return fail(INFV2_E_UNSUPPORTED,
+                "%s: decode shapes only (bf16, G=16, d=128, B=64, l_C1=32, s_C1=16, n_q<=4)",
+                what);
+  if (!select_fused_shape(*p, n_c1_of(*p)))
+    return fail(INFV2_E_UNSUPPORTED, "%s: needs k <= 32, budget <= 64 and n_kv <= 262144", what);
+  return INFV2_OK;
+}
+
+static int check_pages(const infv2_problem& p, const int32_t* block_table, int32_t max_blocks,
+                       int32_t n_pages) {
+  if (!block_table) return INFV2_OK;
+  CHECK_PTR(block_table);
+  if (max_blocks < n_blk_of(p))
+    return fail(INFV2_E_ARG, "max_blocks (%d) < ceil(n_kv/B) (%d)", max_blocks, n_blk_of(p));
+  if (n_pages < 1) return fail(INFV2_E_ARG, "n_pages must be >= 1");
+  return INFV2_OK;
+}
+
+int infv2_compress_k_varlen(const infv2_problem* p, const void* K, const int32_t* block_table,
+                            int32_t max_blocks, int32_t n_pages, const int32_t* seq_lens,
+                            void* Kc, int32_t coarse, int32_t last_n, void* stream) {
+  int st = check_varlen(p, "infv2_compress_k_varlen");
+  if (st) return st;
+  CHECK_PTR(K);
+  CHECK_PTR(seq_lens);
+  CHECK_PTR(Kc);
+  if (coarse != 0 && coarse != 1) return fail(INFV2_E_ARG, "coarse must be 0 or 1");
+  if ((st = check_pages(*p, block_table, max_blocks, n_pages))) return st;
+  const int l_len = coarse ? l_c2_of(*p) : p->l_C1;
+  const int s_len = coarse ? s_c2_of(*p) : p->s_C1;
+  return hip_status(launch_compress_k_varlen(*p, K, block_table, max_blocks, n_pages, seq_lens,
+                                             Kc, kv_cap_of(*p), coarse ? c2_cap_of(*p) : c1_cap_of(*p),
+                                             l_len, s_len, last_n, (hipStream_t)stream),
+                    "infv2_compress_k_varlen");
+}
+
+size_t infv2_select_blocks_varlen_workspace(const infv2_problem* p) {
+  if (check(p) != INFV2_OK || !scores_use_split(*p)) return 0;
+  const KeySet ks = keys_of(*p, nullptr, nullptr);
+  return align256(scores_workspace(*p, ks)) + select_fused_workspace(*p, ks.n_c1);
+}
+
+int infv2_select_blocks_varlen(const infv2_problem* p, const void* Q, const void* Kc1,
+                               const void* Kc2, const int32_t* seq_lens, int32_t* idx,
+                               int32_t* n_sel, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_varlen(p, "infv2_select_blocks_varlen");
+  if (st) return st;
+  CHECK_PTR(Q);
+  CHECK_PTR(seq_lens);
+  CHECK_PTR(idx);
+  CHECK_PTR(n_sel);
+  if ((st = check_keys(*p, Kc1, Kc2))) return st;
+  const KeySet ks = keys_of(*p, Kc1, Kc2);
+  const size_t need = infv2_select_blocks_varlen_workspace(p);
+  CHECK_PTR(ws);
+  if (ws_bytes < need)
+    return fail(INFV2_E_WORKSPACE, "select_blocks_varlen workspace %zu < %zu bytes", ws_bytes,
+                need);
+  return hip_status(launch_select_varlen(*p, Q, ks, seq_lens, idx, n_sel, ws, n_blk_of(*p),
+                                         scale_of(*p), budget_of(*p), (hipStream_t)stream),
+                    "infv2_select_blocks_varlen");
+}
+
+size_t infv2_sparse_attn_varlen_workspace(const infv2_problem* p) {
+  if (check(p) != INFV2_OK || !attn_use_split(*p)) return 0;
+  return attn_workspace(*p, budget_of(*p), true);
+}
+
+int infv2_sparse_attn_varlen(const infv2_problem* p, const void* Q, const void* K, const void* V,
+                             const int32_t* block_table, int32_t max_blocks, int32_t n_pages,
+                             const int32_t* seq_lens, const int32_t* idx, const int32_t* n_sel,
+                             void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_varlen(p, "infv2_sparse_attn_varlen");
+  if (st) return st;
+  CHECK_PTR(Q);
+  CHECK_PTR(K);
+  CHECK_PTR(V);
+  CHECK_PTR(seq_lens);
+  CHECK_PTR(idx);
+  CHECK_PTR(n_sel);
+  CHECK_PTR(O);
+  if (lse && !aligned16(lse)) return fail(INFV2_E_ARG, "lse is not 16-byte aligned");
+  if ((st = check_pages(*p, block_table, max_blocks, n_pages))) return st;
+  const size_t need = infv2_sparse_attn_varlen_workspace(p);
+  CHECK_PTR(ws);
+  if (ws_bytes < need)
+    return fail(INFV2_E_WORKSPACE, "sparse_attn_varlen workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(launch_attn_varlen(*p, Q, K, V, block_table, max_blocks, n_pages, seq_lens,
+                                       idx, n_sel, O, lse, ws, budget_of(*p), kv_cap_of(*p),
+                                       scale_of(*p), (hipStream_t)stream),
+                    "infv2_sparse_attn_varlen");
 }
 
 const char* infv2_status_string(int status) {

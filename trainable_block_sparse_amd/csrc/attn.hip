@@ -89,6 +89,14 @@ struct AttnArgs {
   int batch, n_q, q_pos0, n_kv, n_blk, h_kv, budget;
   int64_t kv_cap;
   float c;                // scale * log2(e)
+  // decode of a varlen batch (null: every sequence has n_kv keys, queries
+  // from q_pos0): sequence b holds seq_lens[b] keys, its queries are the last
+  // n_q.  Paged cache (null: K, V [b][kv_cap][h_kv][d]): K, V are pools of
+  // n_pages pages [B][h_kv][d]; block j of sequence b is page
+  // block_table[b * max_blocks + j].
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int max_blocks, n_pages;
 };
 
 // Scores and online softmax of one 64-key block for one token's 16 heads.
@@ -475,7 +483,8 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
   const size_t prow = row * a.budget + slot;
   const int nsel = a.n_sel[row];
   if (slot >= nsel) return;
-  const int p = a.q_pos0 + t;
+  const int n_kv = a.seq_lens ? seq_len_of(a.seq_lens, b, a.n_q, a.n_kv) : a.n_kv;
+  const int p = (a.seq_lens ? n_kv - a.n_q : a.q_pos0) + t;
   const int blk = a.idx[row * a.budget + slot];
   if (blk < 0 || blk > p / AT_B) {                  // only causal blocks
     if (lane < AT_G) a.part_ml[prow * AT_G + lane] = make_float2(kNegInf, 0.f);
@@ -483,22 +492,29 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
   }
   const int kv0 = blk * AT_B;
   const size_t kstride = (size_t)a.h_kv * AT_D;
-  const uint16_t* kbase = a.K + (size_t)b * a.kv_cap * kstride + (size_t)g * AT_D;
-  const uint16_t* vbase = a.V + (size_t)b * a.kv_cap * kstride + (size_t)g * AT_D;
+  // the block's first key row (a page of the pool, or rows of the sequence);
+  // a page index out of the pool is clamped into it
+  size_t row0 = (size_t)b * a.kv_cap + kv0;
+  if (a.block_table)
+    row0 = (size_t)min(max(a.block_table[(size_t)b * a.max_blocks + blk], 0), a.n_pages - 1) * AT_B;
+  const uint16_t* kbase = a.K + row0 * kstride + (size_t)g * AT_D;
+  const uint16_t* vbase = a.V + row0 * kstride + (size_t)g * AT_D;
   const int c = lane & 15, rq = lane >> 4;
-  // rows past the last key are clamped to it; they lie after p: masked, P = 0
+  // rows past the last key are clamped to it (still in this block, as
+  // kv0 <= p < n_kv); they lie after p: masked, P = 0
+  const int r_last = n_kv - 1 - kv0;
   u32x4 kv[16], vin[2][8];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int key = min(kv0 + 4 * i + rq, a.n_kv - 1);
-    kv[i] = *(const u32x4*)(kbase + (size_t)key * kstride + 8 * c);
+    const int r = min(4 * i + rq, r_last);
+    kv[i] = *(const u32x4*)(kbase + (size_t)r * kstride + 8 * c);
   }
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int key = min(kv0 + 8 * (rq + 4 * hh) + r, a.n_kv - 1);
-      vin[hh][r] = *(const u32x4*)(vbase + (size_t)key * kstride + 8 * c);
+    for (int r8 = 0; r8 < 8; ++r8) {
+      const int r = min(8 * (rq + 4 * hh) + r8, r_last);
+      vin[hh][r8] = *(const u32x4*)(vbase + (size_t)r * kstride + 8 * c);
     }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -754,7 +770,34 @@ static AttnArgs fast_args(const infv2_problem& p, const void* Q, const void* K, 
   a.budget = budget;
   a.kv_cap = kv_cap;
   a.c = scale * kLog2e;
+  a.seq_lens = nullptr;
+  a.block_table = nullptr;
+  a.max_blocks = 0;
+  a.n_pages = 0;
   return a;
+}
+
+// Decode of a varlen batch, optionally from a paged cache: the split kernel
+// (one selected block per workgroup) and the merge; requires
+// attn_use_split(p).  Workspace as attn_workspace(p, budget, true).
+hipError_t launch_attn_varlen(const infv2_problem& p, const void* Q, const void* K,
+                              const void* V, const int32_t* block_table, int max_blocks,
+                              int n_pages, const int32_t* seq_lens, const int32_t* idx,
+                              const int32_t* n_sel, void* O, float* lse, void* ws, int budget,
+                              int64_t kv_cap, float scale, hipStream_t stream) {
+  AttnArgs a = fast_args(p, Q, K, V, idx, n_sel, O, lse, budget, kv_cap, scale);
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.n_pages = n_pages;
+  const size_t slots = (size_t)p.batch * p.h_kv * p.n_q * budget;
+  a.part_o = (float*)ws;
+  a.part_ml = (float2*)((char*)ws + slots * AT_G * AT_D * sizeof(float));
+  hipLaunchKernelGGL(attn_split_kernel, dim3(budget, p.h_kv, p.batch * p.n_q), dim3(64), 0,
+                     stream, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(AT_G, p.h_kv, p.batch * p.n_q), dim3(64), 0, stream,
+                     a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, const void* V,

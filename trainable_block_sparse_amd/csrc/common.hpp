@@ -149,6 +149,12 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   return (int)(s32[0] + s32[1]);
 }
 
+// Varlen batches: sequence b's cache length, clamped to [n_q, n_kv] so that a
+// bad entry can never move a read past the buffers sized for n_kv.
+__device__ __forceinline__ int seq_len_of(const int32_t* seq_lens, int b, int n_q, int n_kv) {
+  return min(max(seq_lens[b], n_q), n_kv);
+}
+
 // order-preserving bits of a float (larger float -> larger unsigned)
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
   const uint32_t u = __float_as_uint(f);

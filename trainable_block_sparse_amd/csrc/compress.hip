@@ -51,34 +51,63 @@ template <> __device__ __forceinline__ void store_rounded<float>(float* p, doubl
   *p = (float)round_pair<24>(hi, lo);                 // exact conversion
 }
 
+// Where the keys come from.  Contiguous: K [b][kv_cap][h_kv][d], kernels
+// [c1_begin, c1_end) of every sequence.  Varlen (seq_lens set): sequence b
+// holds seq_lens[b] keys (clamped to [n_q, n_kv]) and gets its last `last_n`
+// complete kernels (all of them when last_n <= 0), c1_begin/c1_end unused.
+// Paged (block_table set): K is a pool of n_pages pages [B][h_kv][d], token
+// u of sequence b in page block_table[b * max_blocks + u / B] (clamped into
+// the pool).
+struct CompressSrc {
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int max_blocks, n_pages, B, n_q, n_kv, last_n;
+};
+
 // grid: x = kernel groups of (blockDim / d) kernels, y = h_kv, z = batch.
 template <typename T>
 __global__ void __launch_bounds__(256) compress_k_kernel(
     const T* __restrict__ K, T* __restrict__ Kc1, int c1_begin, int c1_end, int h_kv, int d,
-    int64_t kv_cap, int64_t c1_cap, int l_C1, int s_C1, double inv_l) {
+    int64_t kv_cap, int64_t c1_cap, int l_C1, int s_C1, double inv_l, CompressSrc src_of) {
   const int per_blk = blockDim.x / d;
   const int local = threadIdx.x / d;
   const int di = threadIdx.x % d;
   if (local >= per_blk) return;
-  const int j = c1_begin + blockIdx.x * per_blk + local;
-  if (j >= c1_end) return;
   const int g = blockIdx.y, b = blockIdx.z;
+  int j_lo = c1_begin, j_hi = c1_end;
+  if (src_of.seq_lens) {
+    const int len = seq_len_of(src_of.seq_lens, b, src_of.n_q, src_of.n_kv);
+    j_hi = len < l_C1 ? 0 : (len - l_C1) / s_C1 + 1;
+    j_lo = src_of.last_n > 0 ? max(0, j_hi - src_of.last_n) : 0;
+  }
+  const int j = j_lo + blockIdx.x * per_blk + local;
+  if (j >= j_hi) return;
   const size_t row_stride = (size_t)h_kv * d;
-  const T* src = K + ((size_t)b * kv_cap + (size_t)j * s_C1) * row_stride + (size_t)g * d + di;
+  const size_t col = (size_t)g * d + di;
+  const T* seq_base = K + (size_t)b * kv_cap * row_stride + col;
+  const int32_t* table = src_of.block_table ? src_of.block_table + (size_t)b * src_of.max_blocks
+                                            : nullptr;
   double hi = 0.0, lo = 0.0;
   // 32 keys per step, all loaded before the (serial) compensated sum
   for (int u0 = 0; u0 < l_C1; u0 += 32) {
     const int cnt = min(32, l_C1 - u0);
     double x[32];
 #pragma unroll
-    for (int u = 0; u < 32; ++u)
-      x[u] = load_f64<T>(src + (size_t)(u0 + min(u, cnt - 1)) * row_stride);
+    for (int u = 0; u < 32; ++u) {
+      const int tok = j * s_C1 + u0 + min(u, cnt - 1);
+      size_t row = tok;   // token row of the sequence, or of its page in the pool
+      if (table)
+        row = (size_t)min(max(table[tok / src_of.B], 0), src_of.n_pages - 1) * src_of.B +
+              tok % src_of.B;
+      x[u] = load_f64<T>((table ? K + col : seq_base) + row * row_stride);
+    }
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
-      if (u >= cnt) break;
-      const double t = hi + x[u];
+      // (a predicate, not a break: the unrolled loop keeps x in registers)
+      const double xu = u < cnt ? x[u] : -0.0;   // -0 is the exact identity of +
+      const double t = hi + xu;
       const double bp = t - hi;
-      lo += (hi - (t - bp)) + (x[u] - bp);  // TwoSum error, accumulated exactly
+      lo += (hi - (t - bp)) + (xu - bp);    // TwoSum error, accumulated exactly
       hi = t;                               // for the magnitudes of one kernel
     }
   }
@@ -101,14 +130,41 @@ hipError_t launch_compress_k(const infv2_problem& p, const void* K, void* Kc1, i
   dim3 grid((n + per_blk - 1) / per_blk, p.h_kv, p.batch);
   dim3 block(per_blk * p.d);
   const double inv_l = 1.0 / (double)l_len;
+  const CompressSrc src = {nullptr, nullptr, 0, 0, p.B, p.n_q, p.n_kv, 0};
   if (p.dtype == INFV2_BF16) {
     hipLaunchKernelGGL(compress_k_kernel<uint16_t>, grid, block, 0, stream,
                        (const uint16_t*)K, (uint16_t*)Kc1, c1_begin, c1_end, p.h_kv, p.d, kv_cap,
-                       c1_cap, l_len, s_len, inv_l);
+                       c1_cap, l_len, s_len, inv_l, src);
   } else {
     hipLaunchKernelGGL(compress_k_kernel<float>, grid, block, 0, stream, (const float*)K,
                        (float*)Kc1, c1_begin, c1_end, p.h_kv, p.d, kv_cap, c1_cap, l_len,
-                       s_len, inv_l);
+                       s_len, inv_l, src);
+  }
+  return hipGetLastError();
+}
+
+// Varlen / paged: each sequence's last `last_n` complete kernels (all when
+// last_n <= 0); the grid covers the most any sequence can have.
+hipError_t launch_compress_k_varlen(const infv2_problem& p, const void* K,
+                                    const int32_t* block_table, int max_blocks, int n_pages,
+                                    const int32_t* seq_lens, void* Kc, int64_t kv_cap,
+                                    int64_t c_cap, int l_len, int s_len, int last_n,
+                                    hipStream_t stream) {
+  const int n_max = p.n_kv < l_len ? 0 : (p.n_kv - l_len) / s_len + 1;
+  const int n = last_n > 0 ? min(last_n, n_max) : n_max;
+  if (n <= 0) return hipSuccess;
+  const int per_blk = 256 / p.d;
+  dim3 grid((n + per_blk - 1) / per_blk, p.h_kv, p.batch);
+  dim3 block(per_blk * p.d);
+  const double inv_l = 1.0 / (double)l_len;
+  const CompressSrc src = {seq_lens, block_table, max_blocks, n_pages, p.B, p.n_q, p.n_kv, last_n};
+  if (p.dtype == INFV2_BF16) {
+    hipLaunchKernelGGL(compress_k_kernel<uint16_t>, grid, block, 0, stream,
+                       (const uint16_t*)K, (uint16_t*)Kc, 0, 0, p.h_kv, p.d, kv_cap, c_cap,
+                       l_len, s_len, inv_l, src);
+  } else {
+    hipLaunchKernelGGL(compress_k_kernel<float>, grid, block, 0, stream, (const float*)K,
+                       (float*)Kc, 0, 0, p.h_kv, p.d, kv_cap, c_cap, l_len, s_len, inv_l, src);
   }
   return hipGetLastError();
 }

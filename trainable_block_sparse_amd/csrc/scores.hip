@@ -935,7 +935,23 @@ struct SplitArgs {
   int n_q, q_pos0, h_kv, n_c1, n_c1p, n_c2, n_blk, nch, nch2;
   int64_t c1_cap, c2_cap;
   float c;
+  // varlen batches (null: every sequence has n_kv keys and its queries start
+  // at q_pos0): sequence b holds seq_lens[b] keys, its queries are the last
+  // n_q; n_c1, n_c2, nch, nch2 are then those of the longest, n_kv
+  const int32_t* seq_lens;
+  int n_kv;
 };
+
+// position of sequence b's first query token
+__device__ __forceinline__ int split_pos0(const SplitArgs& a, int b) {
+  return a.seq_lens ? seq_len_of(a.seq_lens, b, a.n_q, a.n_kv) - a.n_q : a.q_pos0;
+}
+// complete (coarse) kernels of sequence b
+__device__ __forceinline__ int split_rows(const SplitArgs& a, int b, bool coarse) {
+  if (!a.seq_lens) return coarse ? a.n_c2 : a.n_c1;
+  const int last = seq_len_of(a.seq_lens, b, a.n_q, a.n_kv) - 1;
+  return (coarse ? last_visible_coarse(last) : last_visible_kernel(last)) + 1;
+}
 
 // z = Q K^T (raw dot products) for the 64 key rows jw .. jw+63 of one wave:
 // the rows are loaded with coalesced loads (lanes 16r..16r+15 read one
@@ -1041,12 +1057,12 @@ __global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
   const int b = bt / a.n_q, t = bt % a.n_q;
-  const int p = a.q_pos0 + t;
+  const int p = split_pos0(a, b) + t;
   const int jmax = COARSE ? last_visible_coarse(p) : last_visible_kernel(p);
   const int hq = a.h_kv * SEL_G;
   const uint16_t* keys = COARSE ? a.Kc2 + ((size_t)b * a.h_kv + g) * a.c2_cap * SEL_D
                                 : a.Kc1 + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D;
-  const int n_rows = COARSE ? a.n_c2 : a.n_c1;
+  const int n_rows = split_rows(a, b, COARSE);
   const int jw = chunk * SPLIT_CK + wave * 64;
   f32x4 acc[4];
   split_logits_mfma(keys, n_rows, jw, a.Q + (((size_t)b * a.n_q + t) * hq + g * SEL_G) * SEL_D,
@@ -1122,7 +1138,7 @@ __device__ __forceinline__ void head_lse_weights(const SplitArgs& a, int g, int 
 __device__ __forceinline__ float split_pool_chunk(const SplitArgs& a, int chunk, int g, int bt,
                                                   float* Mh, float* Wh, float* sh) {
   const int b = bt / a.n_q, t = bt % a.n_q;
-  const int p = a.q_pos0 + t;
+  const int p = split_pos0(a, b) + t;
   const int jmax = last_visible_kernel(p);
   const int b_p = p >> 6;
   head_lse_weights(a, g, bt, threadIdx.x, Mh, Wh);
@@ -1172,7 +1188,7 @@ __global__ void __launch_bounds__(256) scores_split_pool_kernel(SplitArgs a) {
   if (a.cand == nullptr || threadIdx.x >= 64) return;     // whole waves leave
   const int lane = threadIdx.x;
   const int b = bt / a.n_q, t = bt % a.n_q;
-  const int b_p = (a.q_pos0 + t) >> 6;
+  const int b_p = (split_pos0(a, b) + t) >> 6;
   const int init_hi = min(a.N_init, b_p + 1);
   const int loc_lo = max(0, b_p - a.N_local + 1);
   const int blk = chunk * 64 + lane;
@@ -1201,7 +1217,7 @@ __global__ void __launch_bounds__(256) scores_split_fused_kernel(SplitArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
   const int b = bt / a.n_q, t = bt % a.n_q;
-  const int p = a.q_pos0 + t;
+  const int p = split_pos0(a, b) + t;
   const int jmax = last_visible_kernel(p);
   const bool coarse = last_visible_coarse(p) >= 0;      // row-uniform
   const int hq = a.h_kv * SEL_G;
@@ -1215,7 +1231,7 @@ __global__ void __launch_bounds__(256) scores_split_fused_kernel(SplitArgs a) {
   }
   const int jw = j0 + wave * 64;
   f32x4 acc[4];
-  split_logits_mfma(kc1, a.n_c1, jw, qbase, lane, kst_all[wave], acc);
+  split_logits_mfma(kc1, split_rows(a, b, false), jw, qbase, lane, kst_all[wave], acc);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int j = jw + 16 * nt + (lane & 15);
@@ -1322,7 +1338,7 @@ __global__ void __launch_bounds__(MERGE_THREADS) scores_select_merge_kernel(Spli
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = bt / a.n_q, t = bt % a.n_q;
   const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
-  const int b_p = (a.q_pos0 + t) >> 6;
+  const int b_p = (split_pos0(a, b) + t) >> 6;
   const int nb = b_p + 1;
   const int init_hi = min(a.N_init, nb);
   const int loc_lo = max(0, b_p - a.N_local + 1);
@@ -1665,6 +1681,39 @@ size_t select_fused_workspace(const infv2_problem& p, int n_c1) {
   return (size_t)p.batch * p.h_kv * ((p.n_q + SEL_TOK_WG - 1) / SEL_TOK_WG) * sizeof(int32_t);
 }
 
+// The split path of the fused selection: score sweeps that also write the
+// per-chunk candidate lists, then the per-row merge.  seq_lens: varlen batch
+// (the sizes in p and ks are then those of the longest sequence, n_kv).
+static hipError_t launch_select_split(const infv2_problem& p, const void* Q, const KeySet& ks,
+                                      const int32_t* seq_lens, float* S_cmp, int32_t* idx,
+                                      int32_t* n_sel, void* ws, int n_blk, float scale,
+                                      int budget, hipStream_t stream) {
+  SplitArgs a = split_args(p, Q, ks, S_cmp, ws, n_blk, scale);
+  a.seq_lens = seq_lens;
+  a.n_kv = p.n_kv;
+  a.cand = (uint64_t*)((char*)ws + align256(scores_workspace(p, ks)));
+  a.idx = idx;
+  a.n_sel = n_sel;
+  a.k = p.k;
+  a.kc = p.k;
+  a.N_init = p.N_init;
+  a.N_local = p.N_local;
+  a.budget = budget;
+  launch_split_scores(p, a, stream);
+  hipLaunchKernelGGL(scores_select_merge_kernel, dim3(p.h_kv, p.batch * p.n_q),
+                     dim3(MERGE_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Varlen batches (decode): the split selection with per-sequence lengths;
+// requires scores_use_split(p) and select_fused_shape(p, n_C1(n_kv)).
+hipError_t launch_select_varlen(const infv2_problem& p, const void* Q, const KeySet& ks,
+                                const int32_t* seq_lens, int32_t* idx, int32_t* n_sel, void* ws,
+                                int n_blk, float scale, int budget, hipStream_t stream) {
+  return launch_select_split(p, Q, ks, seq_lens, nullptr, idx, n_sel, ws, n_blk, scale, budget,
+                             stream);
+}
+
 hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeySet& ks,
                                float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, int n_blk,
                                float scale, int budget, hipStream_t stream) {
@@ -1680,19 +1729,8 @@ hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeyS
     launch_prefill_scores<true>(p, a, stream);
     return hipGetLastError();
   }
-  SplitArgs a = split_args(p, Q, ks, S_cmp, ws, n_blk, scale);
-  a.cand = (uint64_t*)((char*)ws + align256(scores_workspace(p, ks)));
-  a.idx = idx;
-  a.n_sel = n_sel;
-  a.k = p.k;
-  a.kc = p.k;
-  a.N_init = p.N_init;
-  a.N_local = p.N_local;
-  a.budget = budget;
-  launch_split_scores(p, a, stream);
-  hipLaunchKernelGGL(scores_select_merge_kernel, dim3(p.h_kv, p.batch * p.n_q),
-                     dim3(MERGE_THREADS), 0, stream, a);
-  return hipGetLastError();
+  return launch_select_split(p, Q, ks, nullptr, S_cmp, idx, n_sel, ws, n_blk, scale, budget,
+                             stream);
 }
 
 hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const KeySet& ks,
