@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import trainable_block_sparse_amd as tbs  # noqa: E402
-from synth import CONFIGS, make_inputs  # noqa: E402
+from synth import CONFIGS, make_inputs, paged_cache, varlen_lengths  # noqa: E402
 
 METRIC = "sparse-attn prefill tokens/s at 32k/128k + decode µs/token; % of MFMA/HBM peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
@@ -97,6 +97,18 @@ def decode_bytes(cfg, budget, lse_approx=False):
     kv = nsel * cfg.B * cfg.d * 2 * 2
     qo = 2 * cfg.G * cfg.d * 2
     return float(cfg.batch * cfg.h_kv * (kc + kv + qo))
+
+
+def decode_varlen_bytes(cfg, lens, budget):
+    """decode_bytes summed over a varlen batch: each sequence's own K^C1 and
+    selected blocks (a short sequence selects all of its causal blocks)."""
+    total = 0.0
+    for L in lens:
+        L = int(L)
+        n_c1 = (L - cfg.l_C1) // cfg.s_C1 + 1 if L >= cfg.l_C1 else 0
+        nsel = min((L - 1) // cfg.B + 1, budget)
+        total += cfg.h_kv * (n_c1 * cfg.d * 2 + nsel * cfg.B * cfg.d * 2 * 2 + 2 * cfg.G * cfg.d * 2)
+    return total
 
 
 def kernel_source_hash():
@@ -282,6 +294,65 @@ def bench_backward(cfg, steps, warmup, with_dense=True):
     return out
 
 
+def bench_decode_varlen(cfg, steps, warmup):
+    """Serving-style decode step: 16 sequences of seeded lengths up to 131072
+    (the first at full length), K/V in a shuffled page pool with a block
+    table; the step appends each sequence's newest kernel, selects and
+    attends through the varlen calls; timed as one HIP graph replay."""
+    lens = varlen_lengths(cfg.batch, cfg.n_kv, seed=cfg.seed + 100, must=(cfg.n_kv,))
+    log(f"[bench] {cfg.name} varlen paged: lengths {lens.tolist()}")
+    x = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    kp, vp, table = paged_cache(x["k"], x["v"], lens, cfg.B, cfg.seed + 101)
+    Q, K, V, table = x["q"].to(dev), kp.to(dev), vp.to(dev), table.to(dev)
+    del x, kp, vp
+    lp = problem_of(cfg, n_kv=cfg.n_kv, q_pos0=0)
+    bud = tbs.budget(lp)
+    seq = torch.tensor(lens, device=dev)
+    Kc1 = torch.empty((lp.batch, lp.h_kv, tbs.n_kernels(lp), lp.d), dtype=Q.dtype, device=dev)
+    tbs.compress_k_varlen(lp, K, seq - 1, Kc1, block_table=table)       # the cache before
+    idx = torch.empty((lp.batch, lp.h_kv, 1, bud), dtype=torch.int32, device=dev)
+    nsel = torch.empty((lp.batch, lp.h_kv, 1), dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((lp.batch, lp.h_q, 1), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(max(tbs.select_blocks_varlen_workspace(lp), 16), dtype=torch.uint8,
+                       device=dev)
+    ws_a = torch.empty(max(tbs.sparse_attn_varlen_workspace(lp), 16), dtype=torch.uint8,
+                       device=dev)
+    fns = [
+        lambda: tbs.compress_k_varlen(lp, K, seq, Kc1, block_table=table, last_n=1),
+        lambda: tbs.select_blocks_varlen(lp, Q, Kc1, seq, idx, nsel, ws_s),
+        lambda: tbs.sparse_attn_varlen(lp, Q, K, V, seq, idx, nsel, block_table=table, O=O,
+                                       lse=lse, ws=ws_a),
+    ]
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for fn in fns:
+            fn()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    nbytes = decode_varlen_bytes(cfg, lens, bud)
+    out = dict(step_us=step_ms * 1e3, us_per_token=step_ms * 1e3 / cfg.batch,
+               timing="HIP graph replay of the whole step", lengths=lens.tolist(),
+               algo_bytes=nbytes, algo_GBps=nbytes / (step_ms / 1e3) / 1e9)
+    out["frac_of_hbm_peak"] = out["algo_GBps"] / PEAK_HBM_GBS
+    del Q, K, V, Kc1, O, ws_s, ws_a
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(cfg, steps, warmup, lse_approx=False):
     log(f"[bench] {cfg.name}{' (LSE approximation)' if lse_approx else ''}: "
         "generating the KV cache")
@@ -456,7 +527,8 @@ def main():
     ap.add_argument("--no-pipeline", action="store_true",
                     help="skip the two-stream range-pipeline record of the 128k prefill")
     ap.add_argument("--only", choices=["prefill32k", "prefill128k", "decode", "dense_switch",
-                                       "copy", "backward32k", "backward128k"],
+                                       "copy", "backward32k", "backward128k",
+                                       "decode_varlen"],
                     help="run one workload alone and print its record (profiling runs); "
                          "'copy' is a plain 256 MiB device copy used to calibrate the "
                          "FETCH_SIZE / WRITE_SIZE counters")
@@ -481,6 +553,10 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
             print(json.dumps({"workload": "copy", "bytes_read": n, "bytes_written": n}), flush=True)
+            return
+        if args.only == "decode_varlen":
+            rec = bench_decode_varlen(CONFIGS["decode"], args.steps, args.warmup)
+            print(json.dumps({"workload": args.only, **rec}), flush=True)
             return
         if args.only.startswith("backward"):
             c = CONFIGS["prefill" + args.only[len("backward"):]]
@@ -539,6 +615,9 @@ def main():
         r4 = bench_decode(c4, max(20, args.steps * 5), args.warmup)
         extra["decode"] = r4
         log(f"[bench] decode: {r4['step_us']:.1f} us/step")
+        rv = bench_decode_varlen(c4, max(20, args.steps * 5), args.warmup)
+        extra["decode_varlen_paged"] = rv
+        log(f"[bench] decode varlen paged: {rv['step_us']:.1f} us/step")
         c5 = CONFIGS["dense_switch"]
         r5 = bench_dense_switch(c5, args.steps, args.warmup)
         extra["dense_switch"] = r5

@@ -100,8 +100,11 @@ def paged_cache(k: torch.Tensor, v: torch.Tensor, lengths, B: int, seed: int,
     n_pages = b * max_blocks + extra_pages
     order = rng.permutation(n_pages)
     table = order[: b * max_blocks].reshape(b, max_blocks).astype(np.int32)
-    kp = torch.from_numpy(rng.standard_normal((n_pages, B, h_kv, d), dtype=np.float32)).to(k.dtype)
-    vp = torch.from_numpy(rng.standard_normal((n_pages, B, h_kv, d), dtype=np.float32)).to(v.dtype)
+    kp = torch.empty((n_pages, B, h_kv, d), dtype=k.dtype)
+    vp = torch.empty((n_pages, B, h_kv, d), dtype=v.dtype)
+    spare = torch.from_numpy(order[b * max_blocks:].astype(np.int64))
+    kp[spare] = torch.from_numpy(rng.standard_normal((extra_pages, B, h_kv, d), dtype=np.float32)).to(k.dtype)
+    vp[spare] = torch.from_numpy(rng.standard_normal((extra_pages, B, h_kv, d), dtype=np.float32)).to(v.dtype)
     pad = max_blocks * B - cap
     kf = torch.nn.functional.pad(k, (0, 0, 0, 0, 0, pad)) if pad else k
     vf = torch.nn.functional.pad(v, (0, 0, 0, 0, 0, pad)) if pad else v

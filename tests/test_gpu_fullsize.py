@@ -9,9 +9,10 @@ import torch
 
 import oracle as orc
 import trainable_block_sparse_amd as tbs
-from synth import CONFIGS, make_inputs
+from synth import CONFIGS, make_inputs, paged_cache, varlen_lengths
 
-from parity import check_compress, check_rows, problems, run_gpu_dense, run_gpu_sparse, sample_rows
+from parity import (check_compress, check_rows, problems, run_gpu_dense, run_gpu_sparse,
+                    sample_rows, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +70,56 @@ def test_decode_full_size():
                      & set(x["needles"][b].tolist()))
                  for b in range(cfg.batch) for g in range(cfg.h_kv))
     _say(rep, "needles selected:", picked, "of", cfg.batch * cfg.h_kv * x["needles"].shape[1])
+
+
+def test_decode_varlen_paged_full_size():
+    # the serving bench's step: 16 sequences with seeded lengths up to 131072
+    # (the first at full length), pages in a shuffled pool, the new token
+    # completing or not a kernel per sequence
+    cfg = CONFIGS["decode"]
+    lens = varlen_lengths(cfg.batch, cfg.n_kv, seed=cfg.seed + 100, must=(cfg.n_kv,))
+    _say("case: varlen paged decode full size, lengths", lens.tolist())
+    x = make_inputs(cfg)
+    lp, op = problems(cfg, q_pos0=0)
+    dev = torch.device("cuda:0")
+    kp, vp, table = paged_cache(x["k"], x["v"], lens, cfg.B, cfg.seed + 101)
+    Q, K, V, table = x["q"].to(dev), kp.to(dev), vp.to(dev), table.to(dev)
+    del kp, vp
+    seq = torch.tensor(lens, device=dev)
+    Kc1 = torch.empty((cfg.batch, cfg.h_kv, tbs.n_kernels(lp), cfg.d), dtype=K.dtype, device=dev)
+    tbs.compress_k_varlen(lp, K, seq - 1, Kc1, block_table=table)       # before this step
+    tbs.compress_k_varlen(lp, K, seq, Kc1, block_table=table, last_n=1)
+    idx, n_sel = tbs.select_blocks_varlen(lp, Q, Kc1, seq)
+    O, lse = tbs.sparse_attn_varlen(lp, Q, K, V, seq, idx, n_sel, block_table=table)
+    torch.cuda.synchronize()
+    idx, n_sel, O, lse, Kc1 = idx.cpu(), n_sel.cpu(), O.cpu(), lse.cpu(), Kc1.cpu()
+    del K, V
+    # every sequence: bitwise equal to the one-sequence calls on its own rows
+    for i, L in enumerate(int(v) for v in lens):
+        p1 = tbs.Problem(batch=1, n_q=1, n_kv=L, q_pos0=L - 1, h_kv=cfg.h_kv, G=cfg.G, d=cfg.d,
+                         k=cfg.k)
+        Ki = x["k"][i:i + 1, :L].to(dev)
+        Vi = x["v"][i:i + 1, :L].to(dev)
+        K1 = tbs.compress_k(p1, Ki)
+        i1, n1 = tbs.select_blocks(p1, Q[i:i + 1], K1)
+        O1, l1 = tbs.sparse_attn(p1, Q[i:i + 1], Ki, Vi, i1, n1)
+        torch.cuda.synchronize()
+        n_c1 = tbs.n_kernels(p1)
+        assert torch.equal(K1.cpu()[0, :, :n_c1], Kc1[i, :, :n_c1]), i
+        assert torch.equal(i1.cpu()[0], idx[i]) and torch.equal(n1.cpu()[0], n_sel[i]), i
+        assert torch.equal(O1.cpu()[0], O[i]) and torch.equal(l1.cpu()[0], lse[i]), i
+        del Ki, Vi, K1
+    # the oracle on four sequences (the longest, the shortest, two others)
+    order = np.argsort(lens)
+    for i in sorted({0, int(order[0]), int(order[len(lens) // 2]), int(order[-2])}):
+        L = int(lens[i])
+        res_i = dict(idx=idx[i:i + 1], n_sel=n_sel[i:i + 1], O=O[i:i + 1], lse=lse[i:i + 1])
+        x_i = dict(q=x["q"][i:i + 1], k=x["k"][i:i + 1, :L], v=x["v"][i:i + 1, :L])
+        Kc1_ref = orc.compress_k(to_f64(x_i["k"]), op)[0]
+        np.testing.assert_array_equal(to_f64(Kc1[i, :, :Kc1_ref.shape[1]]), Kc1_ref)
+        rep = check_rows(res_i, x_i, op, L - 1, {0: np.array([0])}, check_scores=False,
+                         Kc1_ref={0: Kc1_ref})
+        _say("sequence", i, "length", L, rep)
 
 
 def test_dense_switch_full_size():

@@ -92,13 +92,20 @@ __global__ void __launch_bounds__(256) compress_k_kernel(
   for (int u0 = 0; u0 < l_C1; u0 += 32) {
     const int cnt = min(32, l_C1 - u0);
     double x[32];
+    // paged: the group's 32 tokens lie in at most two pages (B >= 32 on
+    // this path), looked up once each before the loads
+    const int tok0 = j * s_C1 + u0;
+    int pg0 = 0, pg1 = 0;
+    if (table) {
+      pg0 = min(max(table[tok0 / src_of.B], 0), src_of.n_pages - 1);
+      pg1 = min(max(table[(tok0 + cnt - 1) / src_of.B], 0), src_of.n_pages - 1);
+    }
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
-      const int tok = j * s_C1 + u0 + min(u, cnt - 1);
+      const int tok = tok0 + min(u, cnt - 1);
       size_t row = tok;   // token row of the sequence, or of its page in the pool
       if (table)
-        row = (size_t)min(max(table[tok / src_of.B], 0), src_of.n_pages - 1) * src_of.B +
-              tok % src_of.B;
+        row = (size_t)(tok / src_of.B == tok0 / src_of.B ? pg0 : pg1) * src_of.B + tok % src_of.B;
       x[u] = load_f64<T>((table ? K + col : seq_base) + row * row_stride);
     }
 #pragma unroll

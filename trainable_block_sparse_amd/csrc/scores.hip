@@ -1344,9 +1344,11 @@ __global__ void __launch_bounds__(MERGE_THREADS) scores_select_merge_kernel(Spli
   const int loc_lo = max(0, b_p - a.N_local + 1);
   const int ncand = max(0, loc_lo - init_hi);
   const int kk = min(a.k, ncand);
-  const int nch = a.nch;
+  // only the chunks that hold candidate blocks (< loc_lo) have non-zero keys:
+  // the bound and the scans below use those lists alone
+  const int nch = ncand > 0 ? min(a.nch, (loc_lo + 63) >> 6) : 1;
   const int nkeys = nch * a.kc;
-  const uint64_t* rlist = a.cand + row * nkeys;
+  const uint64_t* rlist = a.cand + row * (size_t)(a.nch * a.kc);
   for (int i = tid; i < nkeys; i += MERGE_THREADS) keys[i] = rlist[i];
   for (int i = tid; i < SELECT_MAX_CHUNKS * 2 + 2; i += MERGE_THREADS) selbits[i] = 0u;
   if (tid < 64) pick[tid] = 0ull;
