@@ -48,6 +48,8 @@ struct BwdArgs {
   float* dK;              // [b][kv_cap][h_kv][d]
   float* dV;
   float* Dsum;            // [b][h_q][n_q]
+  uint16_t* dZ;           // sparse: [b][h_kv][n_q][budget] tiles of 2 KB (dZ of a token's
+                          // selected block in the B layout of dQ^T = K^T dZ^T), or null
   int batch, n_q, q_pos0, n_kv, n_blk, h_kv, budget, nw;
   int64_t kv_cap;
   float c;                // scale * log2(e)
@@ -127,6 +129,53 @@ __global__ void __launch_bounds__(256) bwd_bitmap_kernel(BwdArgs a) {
     const int blk = sel[i];
     if (blk < 0 || blk > b_p) continue;
     atomicOr(base + (size_t)blk * a.nw, 1u << (t & 31));
+  }
+}
+
+// D = dO . O per (token, head): one wave per (token, group), lane (grp,
+// head) sums features 32ks + 8grp .. +7 (the order the dQ kernel uses), then
+// the four lane groups.  grid: x = rows / 4; 256 threads.
+__global__ void __launch_bounds__(256) bwd_dsum_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t rid = (size_t)blockIdx.x * 4 + wave;   // (b*h_kv + g)*n_q + t
+  if (rid >= (size_t)a.batch * a.h_kv * a.n_q) return;
+  const int t = (int)(rid % a.n_q);
+  const int bg = (int)(rid / a.n_q);
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int grp = lane >> 4;
+  const int hq = a.h_kv * AT_G;
+  const int head = g * AT_G + (lane & 15);
+  const size_t qoff = (((size_t)b * a.n_q + t) * hq + head) * AT_D + 8 * grp;
+  float dsum = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4 dv = *(const u32x4*)(a.dO + qoff + 32 * ks);
+    const u32x4 ov = *(const u32x4*)(a.O + qoff + 32 * ks);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dsum = __builtin_fmaf(bf16_bits_to_f32(dv[e] & 0xFFFFu), bf16_bits_to_f32(ov[e] & 0xFFFFu), dsum);
+      dsum = __builtin_fmaf(bf16_bits_to_f32(dv[e] >> 16), bf16_bits_to_f32(ov[e] >> 16), dsum);
+    }
+  }
+  dsum += __shfl_xor(dsum, 16, 64);
+  dsum += __shfl_xor(dsum, 32, 64);
+  if (grp == 0) a.Dsum[((size_t)b * hq + head) * a.n_q + t] = dsum;
+}
+
+// 4x4 transpose inside each quad of lanes: lane q's t[j] becomes the value
+// lane j held in t[q] (two exchange stages over quad_perm DPP).
+__device__ __forceinline__ void quad_transpose4(float (&t)[4], int lane) {
+  const int q = lane & 3;
+  float u[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float pv = __uint_as_float(dpp_u<0xB1>(__float_as_uint(t[j ^ 1])));   // lane ^ 1
+    u[j] = ((j ^ q) & 1) ? pv : t[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float pv = __uint_as_float(dpp_u<0x4E>(__float_as_uint(u[j ^ 2])));   // lane ^ 2
+    t[j] = ((j ^ q) & 2) ? pv : u[j];
   }
 }
 
@@ -248,6 +297,58 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// dQ from the dZ tiles the dK/dV kernel stashed (sparse path): per selected
+// block only K in the feature layout (16 KB) and the 2 KB tile are read, for
+// dQ^T += K^T dZ^T.  Mapping as attn_bwd_dq_kernel.  Deterministic.
+__global__ void __launch_bounds__(256, 4) attn_bwd_dq_stash_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_qb = (a.n_q + AT_B - 1) / AT_B;
+  const int n_bg = a.batch * a.h_kv;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, r = bid >> 3;
+  const int qbg = (r >> 4) * 8 + xcd;
+  if (qbg >= n_qb * n_bg) return;
+  const int qb = n_qb - 1 - qbg / n_bg;
+  const int bg = qbg % n_bg;
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int t = qb * AT_B + (r & 15) * 4 + wave;
+  if (t >= a.n_q) return;
+  const int b_p = (a.q_pos0 + t) / AT_B;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int hq = a.h_kv * AT_G;
+  f32x4 acc[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+  const int nblocks = a.n_sel[row];
+  const int32_t* sel = a.idx + row * a.budget;
+  const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS + lane * 8;
+  const uint16_t* dz0 = a.dZ + row * a.budget * 1024 + lane * 8;
+  for (int bi = 0; bi < nblocks; ++bi) {
+    const int blk = sel[bi];
+    if (blk < 0 || blk > b_p) continue;     // never stashed
+    const size_t boff = pack0 + (size_t)blk * PACK_ELEMS;
+    bf16x8 kvf[8][2], dzf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) dzf[ks] = as_bf16x8(*(const u32x4*)(dz0 + (size_t)bi * 1024 + ks * 512));
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        kvf[mt][ks] = as_bf16x8(*(const u32x4*)(a.Kv + boff + (2 * mt + ks) * 512));
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) acc[mt] = mfma16(kvf[mt][ks], dzf[ks], acc[mt]);
+  }
+  float* drow = a.dQ + (((size_t)b * a.n_q + t) * hq + g * AT_G + r16) * AT_D;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const f32x4 v = acc[mt] * a.scale;
+    *(f32x4*)(drow + 16 * mt + 4 * grp) = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV.  grid: x = window of BW_WIN query tokens, y = key block, z = b*h_kv.
 // Tokens go two at a time (a pair) through LDS, as row-major Q and dO (the
@@ -274,10 +375,16 @@ __device__ __forceinline__ int bwd_tslot(int d) { return (d & ~15) | ((d & 15) ^
 struct BwdStage {                    // one thread's share of a staged pair
   u32x4 r[4];                        // heads 4hq + j, features 8fo .. +7
   float ld;                          // L (Q waves) or D (dO waves) of head lane&15
+  int32_t sel;                       // with the dZ stash: entry `lane` of the token's list
 };
 
+// STASH: also write each live token's dZ for this block to its tile in a.dZ
+// (slot = the block's position in the token's list, found by a ballot over
+// the list, which the staging loads bring in with Q and dO).
+template <bool STASH>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ int toks[BW_WIN];
+  __shared__ int slot_s[2][2];                                // [buffer][token of the pair]
   __shared__ __attribute__((aligned(16))) BwdTok stg[2][2];   // [buffer][token of the pair]
   __shared__ float LD[2][2][2][AT_G];                         // [buffer][token][L, D][head]
   __shared__ int ntok_s;
@@ -346,6 +453,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) s.r[j] = *(const u32x4*)(st_src + off + j * AT_D);
     s.ld = st_ld[((size_t)b * hq + g * AT_G + (lane & 15)) * a.n_q + tt];
+    if constexpr (STASH)
+      s.sel = a.idx[(((size_t)b * a.h_kv + g) * a.n_q + tt) * a.budget + min(lane, a.budget - 1)];
   };
   auto stage_store = [&](int buf, const BwdStage& s) {
     BwdTok& T = stg[buf][st_k];
@@ -365,6 +474,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     // lanes l, l+16, l+32, l+48 hold the same value: all write it, with no
     // branch (a branch would wait for every load in flight)
     LD[buf][st_k][st_x][lane & 15] = s.ld * st_mul;
+    if constexpr (STASH) {
+      const uint64_t hit = __ballot(lane < a.budget && s.sel == blk);
+      if (st_x == 0 && lane == 0) slot_s[buf][st_k] = hit ? (int)__builtin_ctzll(hit) : -1;
+    }
   };
   f32x4 accV[8], accK[8];
 #pragma unroll
@@ -447,6 +560,27 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
       const bf16x8 bd = as_bf16x8(*(const u32x4*)&T.T[1][grp & 1][slot][0]);
       accV[nt] = mfma16(pa, bd, accV[nt]);
       accK[nt] = mfma16(za, bq, accK[nt]);
+    }
+    // (after the MFMAs are issued, so that this vector work overlaps them)
+    if constexpr (STASH) {
+      // dZ of the wave's 16 keys (key 32ks + 8m + 4(wave&1) + q sits in lane
+      // row r16 = 4m + q, ks = wave>>1) to the token's tile: after a
+      // transpose inside each quad, lane (grp, 4m + q') holds head 4grp + q'
+      // at the four keys q = 0..3 -- 8 bytes of the tile's 16-byte piece
+      // (ks, lane 16m + head), elements 4(wave&1) .. +3
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        float tz[4] = {zv[k2][0], zv[k2][1], zv[k2][2], zv[k2][3]};
+        quad_transpose4(tz, lane);
+        const int tt = k2 == 0 ? tA : tB;
+        const int slot = slot_s[buf][k2];
+        if (tt >= 0 && slot >= 0) {
+          const size_t trow = ((size_t)b * a.h_kv + g) * a.n_q + tt;
+          const int piece = (wave >> 1) * 64 + 16 * (r16 >> 2) + 4 * grp + (lane & 3);
+          *(u32x2*)(a.dZ + ((trow * a.budget + slot) * 128 + piece) * 8 + 4 * (wave & 1)) =
+              u32x2{pack_bf16x2(tz[0], tz[1]), pack_bf16x2(tz[2], tz[3])};
+        }
+      }
     }
   };
   // pipeline: pair i is read from buffer i&1; set A holds the registers of
@@ -595,13 +729,22 @@ bool attn_fast_shape(const infv2_problem& p);
 
 static size_t bwd_nw(const infv2_problem& p) { return ((size_t)p.n_q + 31) / 32; }
 
+// The sparse path stashes dZ (2 KB per selected block of every row) when a
+// row's list fits one wave's ballot.
+static bool bwd_stash(const infv2_problem& p, bool sparse) {
+  return sparse && p.N_init + p.N_local + p.k <= 64;
+}
+
 size_t attn_bwd_workspace(const infv2_problem& p, bool sparse) {
   if (!attn_fast_shape(p)) return 0;
   const size_t n_blk = ((size_t)p.n_kv + AT_B - 1) / AT_B;
   const size_t packs = 3 * (size_t)p.batch * p.h_kv * n_blk * PACK_ELEMS * sizeof(uint16_t);
   const size_t dsum = (size_t)p.batch * p.h_kv * AT_G * p.n_q * sizeof(float);
   const size_t bitmap = sparse ? (size_t)p.batch * p.h_kv * n_blk * bwd_nw(p) * sizeof(uint32_t) : 0;
-  return packs + ((dsum + 255) & ~(size_t)255) + bitmap;
+  const size_t dz = bwd_stash(p, sparse) ? (size_t)p.batch * p.h_kv * p.n_q *
+                                               (p.N_init + p.N_local + p.k) * 2048
+                                         : 0;
+  return packs + ((dsum + 255) & ~(size_t)255) + ((bitmap + 255) & ~(size_t)255) + dz;
 }
 
 size_t attn_bwd_generic_lds(const infv2_problem& p, int budget, bool sparse) {
@@ -637,6 +780,10 @@ hipError_t launch_attn_bwd(const infv2_problem& p, const void* Q, const void* K,
     a.Dsum = (float*)tail;
     const size_t dsum = (size_t)p.batch * p.h_kv * AT_G * p.n_q * sizeof(float);
     a.bitmap = sparse ? (const uint32_t*)(tail + ((dsum + 255) & ~(size_t)255)) : nullptr;
+    const size_t bitmap_bytes = sparse ? (size_t)p.batch * p.h_kv * n_blk * bwd_nw(p) * sizeof(uint32_t) : 0;
+    a.dZ = bwd_stash(p, sparse) ? (uint16_t*)(tail + ((dsum + 255) & ~(size_t)255) +
+                                              ((bitmap_bytes + 255) & ~(size_t)255))
+                                : nullptr;
     a.idx = idx;
     a.n_sel = n_sel;
     a.dQ = dQ;
@@ -667,11 +814,18 @@ hipError_t launch_attn_bwd(const infv2_problem& p, const void* Q, const void* K,
                          stream, a);
     }
     const int total_qb = ((p.n_q + AT_B - 1) / AT_B) * p.batch * p.h_kv;
-    hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3(((total_qb + 7) / 8) * 8 * 16), dim3(256), 0,
-                       stream, a);
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel,
-                       dim3((p.n_q + BW_WIN - 1) / BW_WIN, n_blk, p.batch * p.h_kv), dim3(256),
-                       0, stream, a);
+    const dim3 dq_grid(((total_qb + 7) / 8) * 8 * 16);
+    const dim3 kv_grid((p.n_q + BW_WIN - 1) / BW_WIN, n_blk, p.batch * p.h_kv);
+    if (a.dZ) {
+      // D first, then dK/dV (which stashes dZ), then dQ from the stash
+      const size_t rows = (size_t)p.batch * p.h_kv * p.n_q;
+      hipLaunchKernelGGL(bwd_dsum_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, kv_grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(attn_bwd_dq_stash_kernel, dq_grid, dim3(256), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL(attn_bwd_dq_kernel, dq_grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, kv_grid, dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
   }
   GenericBwdArgs a = {};
