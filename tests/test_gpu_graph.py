@@ -85,3 +85,58 @@ def test_fused_selection_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(idx, idx_ref), f"replay {rep}: idx differs"
         assert torch.equal(nsel, nsel_ref), f"replay {rep}: n_sel differs"
+
+
+def test_varlen_paged_decode_step_graph_replay_matches_eager():
+    # the serving step the bench times: append, varlen selection, paged
+    # attention; the lengths change between replays through the device array
+    from synth import paged_cache
+    cfg = CONFIGS["decode"]
+    lens = np.array([1, 700, 3001, 5000], np.int32)
+    b, n_max = len(lens), int(lens.max())
+    print("case: varlen paged decode graph replay", lens.tolist(), flush=True)
+    x = make_inputs(cfg, n_kv=n_max, batch=b, seed=79)
+    lp, _ = problems(cfg, n_kv=n_max, batch=b, q_pos0=0)
+    dev = torch.device("cuda:0")
+    kp, vp, table = paged_cache(x["k"], x["v"], lens, cfg.B, 80)
+    Q, K, V, table = x["q"].to(dev), kp.to(dev), vp.to(dev), table.to(dev)
+    seq = torch.tensor(lens, device=dev)
+    Kc1 = torch.zeros((b, lp.h_kv, tbs.n_kernels(lp), lp.d), dtype=torch.bfloat16, device=dev)
+    tbs.compress_k_varlen(lp, K, seq - 1, Kc1, block_table=table)
+    idx = torch.empty((b, lp.h_kv, 1, tbs.budget(lp)), dtype=torch.int32, device=dev)
+    nsel = torch.empty((b, lp.h_kv, 1), dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((b, lp.h_q, 1), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(tbs.select_blocks_varlen_workspace(lp), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(tbs.sparse_attn_varlen_workspace(lp), dtype=torch.uint8, device=dev)
+
+    def step():
+        tbs.compress_k_varlen(lp, K, seq, Kc1, block_table=table, last_n=1)
+        tbs.select_blocks_varlen(lp, Q, Kc1, seq, idx, nsel, ws_s)
+        tbs.sparse_attn_varlen(lp, Q, K, V, seq, idx, nsel, block_table=table, O=O, lse=lse,
+                               ws=ws_a)
+
+    def eager_for(lengths):
+        seq.copy_(torch.tensor(lengths, device=dev))
+        step()
+        torch.cuda.synchronize()
+        return {k: t.clone() for k, t in dict(idx=idx, nsel=nsel, O=O, lse=lse, Kc1=Kc1).items()}
+
+    other = np.minimum(lens + 16, n_max).astype(np.int32)
+    ref_a, ref_b = eager_for(lens), eager_for(other)
+    seq.copy_(torch.tensor(lens, device=dev))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        lengths, ref = (lens, ref_a) if rep % 2 == 0 else (other, ref_b)
+        for t in (O, lse, idx, nsel):
+            t.zero_()                     # eager work between replays
+        seq.copy_(torch.tensor(lengths, device=dev))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ("idx", "nsel", "O", "lse"):
+            assert torch.equal(dict(idx=idx, nsel=nsel, O=O, lse=lse)[k], ref[k]), \
+                f"replay {rep}: {k} differs"
