@@ -111,9 +111,29 @@ def decode_varlen_bytes(cfg, lens, budget):
     return total
 
 
-def kernel_source_hash():
+# the sources each kernel is built from (its own file and the headers it uses)
+KERNEL_SOURCES = {
+    "compress_k_kernel": ["compress.hip", "common.hpp"],
+    "scores_": ["scores.hip", "common.hpp"],
+    "topk_kernel": ["topk.hip", "common.hpp"],
+    "kv_pack_kernel": ["attn.hip", "attn_layout.hpp", "common.hpp"],
+    "attn_bwd": ["attn_bwd.hip", "attn_layout.hpp", "common.hpp"],
+    "bwd_": ["attn_bwd.hip", "attn_layout.hpp", "common.hpp"],
+    "attn_": ["attn.hip", "attn_layout.hpp", "common.hpp"],
+}
+
+
+def kernel_source_hash(kernel=None):
+    """sha256 prefix of the sources a kernel is built from (all sources when
+    the kernel is not listed)."""
+    files = sorted(os.listdir(CSRC))
+    if kernel is not None:
+        for prefix, fs in KERNEL_SOURCES.items():
+            if kernel.startswith(prefix):
+                files = fs
+                break
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -526,7 +546,7 @@ def traffic_for(stage, workload):
     total = 0.0
     for kernel in STAGE_KERNELS.get(stage, [stage]):
         ent = tr.get(f"{workload}/{kernel}")
-        if not ent or ent.get("source_hash") != kernel_source_hash():
+        if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
             return None
         total += ent.get("bytes_per_launch", 0.0)
     return total

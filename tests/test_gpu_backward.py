@@ -98,11 +98,12 @@ def test_bf16_sparse_backward_query_offset():
     _check(cfg, lp, op, xq, q0, False, seed=62)
 
 
-def test_bf16_sparse_backward_windows_past_1024_tokens():
-    # 3000 query tokens: three windows of the dK / dV kernel, block 0 selected
-    # by every token of every window
+def test_bf16_sparse_backward_several_token_windows():
+    # 4300 query tokens: three windows of the dK / dV kernel (2048 tokens
+    # each, the last one ragged), block 0 selected by every token of every
+    # window
     cfg = CONFIGS["prefill32k"]
-    n_kv = 3000
+    n_kv = 4300
     _say("case: bf16 sparse backward, 3 windows", n_kv)
     x = make_inputs(cfg, n_kv=n_kv, batch=1, seed=63)
     lp, op = problems(cfg, n_kv=n_kv, batch=1)

@@ -18,7 +18,7 @@
 //    S^T = K Q^T and dP^T = V dO^T (keys on the M axis, the 16 heads on N), so
 //    that dZ^T lands in the B-operand layout of dQ^T = K^T dZ^T.  It also
 //    writes D = dO.O per (token, head) for the second kernel.
-//  * attn_bwd_dkdv_kernel: one workgroup per (key block, group, window of 1024
+//  * attn_bwd_dkdv_kernel: one workgroup per (key block, group, window of 2048
 //    query tokens), 4 waves x 16 keys.  The tokens of the window that
 //    selected the block come from a bitmap (bwd_bitmap_kernel) in ascending
 //    order and are taken two at a time: S = Q K^T and dP = dO V^T with the 16
@@ -362,7 +362,7 @@ __global__ void __launch_bounds__(256, 4) attn_bwd_dq_stash_kernel(BwdArgs a) {
 // stores (rows 8 apart across lanes) and the operand reads (16 consecutive
 // rows) both fall on distinct banks.  LDS holds two pairs; the registers of
 // two more are in flight, so a load has two pairs of compute to land.
-constexpr int BW_WIN = 1024;
+constexpr int BW_WIN = 2048;   // 1024: 21% slower at 32k; 4096: slower at 32k and 128k
 constexpr int BW_RROW = AT_D + 8;   // row-major LDS row (bf16): 272 B, conflict-free reads
 
 struct BwdTok {                      // one staged token (16 896 B)
@@ -383,7 +383,7 @@ struct BwdStage {                    // one thread's share of a staged pair
 // the list, which the staging loads bring in with Q and dO).
 template <bool STASH>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ int toks[BW_WIN];
+  __shared__ uint16_t toks[BW_WIN];                           // token - t_lo
   __shared__ int slot_s[2][2];                                // [buffer][token of the pair]
   __shared__ __attribute__((aligned(16))) BwdTok stg[2][2];   // [buffer][token of the pair]
   __shared__ float LD[2][2][2][AT_G];                         // [buffer][token][L, D][head]
@@ -402,10 +402,17 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     const int w0 = t_lo >> 5;
     const int nwin = (t_hi - t_lo + 31) >> 5;
     const uint32_t* bm = a.bitmap + ((size_t)bg * a.n_blk + blk) * a.nw + w0;
-    uint32_t word = 0u;
-    if (tid < nwin) word = bm[tid];
+    constexpr int WPL = BW_WIN / 2048;     // bitmap words per lane of wave 0
+    static_assert(WPL >= 1 && BW_WIN % 2048 == 0, "one wave scans the window's bitmap");
     if (wave == 0) {
-      const int c = __popc(word);
+      uint32_t word[WPL];
+      int c = 0;
+#pragma unroll
+      for (int q = 0; q < WPL; ++q) {
+        const int wi = WPL * lane + q;
+        word[q] = wi < nwin ? bm[wi] : 0u;
+        c += __popc(word[q]);
+      }
       int incl = c;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -413,11 +420,14 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
         if (lane >= o) incl += y;
       }
       int pos = incl - c;
-      for (uint32_t wv = word; wv; wv &= wv - 1) toks[pos++] = t_lo + 32 * tid + __builtin_ctz(wv);
+#pragma unroll
+      for (int q = 0; q < WPL; ++q)
+        for (uint32_t wv = word[q]; wv; wv &= wv - 1)
+          toks[pos++] = (uint16_t)(32 * (WPL * lane + q) + __builtin_ctz(wv));
       if (lane == 63) ntok_s = incl;
     }
   } else {
-    for (int i = tid; i < t_hi - t_first; i += 256) toks[i] = t_first + i;
+    for (int i = tid; i < t_hi - t_first; i += 256) toks[i] = (uint16_t)(t_first - t_lo + i);
     if (tid == 0) ntok_s = t_hi - t_first;
   }
   __syncthreads();
@@ -448,7 +458,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   // (exact zeros) then cancel.
   auto stage_load = [&](int pair, BwdStage& s) {
     const int k = 2 * pair + st_k;
-    const int tt = toks[k < ntok ? k : 0];
+    const int tt = t_lo + toks[k < ntok ? k : 0];
     const size_t off = (((size_t)b * a.n_q + tt) * hq + g * AT_G + 4 * s_hq) * AT_D + 8 * s_fo;
 #pragma unroll
     for (int j = 0; j < 4; ++j) s.r[j] = *(const u32x4*)(st_src + off + j * AT_D);
@@ -486,8 +496,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     accK[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   auto compute = [&](int buf, int pair) {
-    const int tA = toks[2 * pair];
-    const int tB = 2 * pair + 1 < ntok ? toks[2 * pair + 1] : -1;
+    const int tA = t_lo + toks[2 * pair];
+    const int tB = 2 * pair + 1 < ntok ? t_lo + toks[2 * pair + 1] : -1;
     // the (token, head) normalisers and D of this lane's rows
     float Lr[2][4], Dr[2][4];
 #pragma unroll
