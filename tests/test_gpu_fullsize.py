@@ -11,8 +11,8 @@ import oracle as orc
 import trainable_block_sparse_amd as tbs
 from synth import CONFIGS, make_inputs, paged_cache, varlen_lengths
 
-from parity import (check_compress, check_rows, problems, run_gpu_dense, run_gpu_sparse,
-                    sample_rows, to_f64)
+from parity import (check_compress, check_rows, gpu_set, problems, run_gpu_dense,
+                    run_gpu_sparse, sample_rows, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -139,3 +139,56 @@ def test_dense_switch_full_size():
     rows = {b: sample_rows(cfg.n_q, 24, rng, must=(0, 63, 64, 4095)) for b in (0, 3, 7)}
     check_rows(de, x, op, 0, rows, dense=True)
     check_rows(sp, x, op, 0, rows)
+
+
+def test_backward_full_size_prefill32k():
+    # the bench's backward call (32k, bf16, the stash path); dQ on sampled
+    # query rows (edges included), dK / dV on the keys of two sampled blocks
+    # against the oracle's backward over exactly the rows whose GPU sets hold
+    # those blocks (every other row adds nothing to their gradients)
+    cfg = CONFIGS["prefill32k"]
+    _say("case: backward full size (prefill32k)")
+    x = make_inputs(cfg)
+    lp, op = problems(cfg)
+    dev = torch.device("cuda:0")
+    Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
+    gen = torch.Generator().manual_seed(321)
+    dO_cpu = torch.randn(Q.shape, generator=gen).to(Q.dtype)
+    dO = dO_cpu.to(dev)
+    Kc1 = tbs.compress_k(lp, K)
+    idx, n_sel = tbs.topk_select(lp, tbs.block_scores(lp, Q, Kc1))
+    O, lse = tbs.sparse_attn(lp, Q, K, V, idx, n_sel)
+    dQ, dK, dV = tbs.sparse_attn_bwd(lp, Q, K, V, idx, n_sel, O, lse, dO)
+    torch.cuda.synchronize()
+    res = dict(idx=idx.cpu(), n_sel=n_sel.cpu())
+    q_rows = np.array(sorted({0, 1, 63, 64, 65, 1215, 1216, 4096, 20000, cfg.n_q - 64,
+                              cfg.n_q - 1} | set(np.random.default_rng(9).choice(cfg.n_q, 8,
+                                                                               replace=False).tolist())))
+    blocks = (100, 317)
+    idx_np = res["idx"][0].numpy()                                   # [h_kv, n_q, budget]
+    hit = np.zeros(cfg.n_q, bool)
+    for blk in blocks:
+        hit |= (idx_np == blk).any(axis=-1).any(axis=0)
+    k_rows = np.nonzero(hit)[0]
+    rows = np.union1d(q_rows, k_rows)
+    _say("rows:", len(rows), "of which attend the sampled blocks:", len(k_rows))
+    gQ = dQ[0].cpu()
+    key_idx = np.concatenate([np.arange(blk * cfg.B, (blk + 1) * cfg.B) for blk in blocks])
+    gK = dK[0, key_idx].cpu().double().numpy()
+    gV = dV[0, key_idx].cpu().double().numpy()
+    del Q, K, V, O, lse, dO, dQ, dK, dV, Kc1
+    token_sets = [[orc.attended_tokens(gpu_set(res, 0, g, int(t)), int(t), op)
+                   for g in range(op.h_kv)] for t in rows]
+    rQ, rK, rV = orc.attention_rows_backward(to_f64(x["q"][0, rows]), to_f64(x["k"][0]),
+                                             to_f64(x["v"][0]), token_sets,
+                                             to_f64(dO_cpu[0, rows]), op)
+    pos = {int(t): i for i, t in enumerate(rows)}
+    sel = [pos[int(t)] for t in q_rows]
+    err = {}
+    got_q = gQ[q_rows].double().numpy()
+    err["dQ"] = float(np.abs(got_q - rQ[sel]).max()) / float(np.abs(rQ[sel]).max())
+    err["dK"] = float(np.abs(gK - rK[key_idx]).max()) / float(np.abs(rK[key_idx]).max())
+    err["dV"] = float(np.abs(gV - rV[key_idx]).max()) / float(np.abs(rV[key_idx]).max())
+    _say("relative errors", err)
+    for k, v in err.items():
+        assert v <= 2e-2, (k, v)
