@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -123,9 +124,17 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text):
+    """Source text without comments and whitespace (a comment edit does not
+    change a kernel)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return "".join(text.split())
+
+
 def kernel_source_hash(kernel=None):
-    """sha256 prefix of the sources a kernel is built from (all sources when
-    the kernel is not listed)."""
+    """sha256 prefix of the code of the sources a kernel is built from (all
+    sources when the kernel is not listed)."""
     files = sorted(os.listdir(CSRC))
     if kernel is not None:
         for prefix, fs in KERNEL_SOURCES.items():
@@ -134,8 +143,8 @@ def kernel_source_hash(kernel=None):
                 break
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -21,7 +21,9 @@
 //    of the math, and rescales O only when a head's running maximum grows by
 //    more than 2^8;
 //  * decode splits the selected blocks over workgroups (one block each) and
-//    merges the partial (max, sum, O) afterwards.
+//    merges the partial (max, sum, O) afterwards; for a varlen batch each
+//    sequence's positions come from a device array of lengths, and with a
+//    paged cache each selected block is read from its page (page = block).
 // A generic fp64 kernel serves fp32 I/O and other shapes.
 #include "attn_layout.hpp"
 

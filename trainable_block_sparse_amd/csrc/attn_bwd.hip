@@ -14,10 +14,16 @@
 //  * bwd_pack_kernel writes, once per call, K in the key layout (the forward's
 //    K pack), V in the key layout and K in the feature layout (attn_layout.hpp):
 //    every MFMA operand below is one coalesced 1 KB fragment load.
-//  * attn_bwd_dq_kernel: one wavefront per (token, group), as the forward:
-//    S^T = K Q^T and dP^T = V dO^T (keys on the M axis, the 16 heads on N), so
-//    that dZ^T lands in the B-operand layout of dQ^T = K^T dZ^T.  It also
-//    writes D = dO.O per (token, head) for the second kernel.
+//  * Sparse path (lists of at most 64 blocks): bwd_dsum_kernel writes
+//    D = dO.O per (token, head); attn_bwd_dkdv_kernel (below) also stashes
+//    each token's dZ for the block as a 2 KB bf16 tile in the B-operand
+//    layout of dQ^T = K^T dZ^T, at the block's slot in the token's list;
+//    attn_bwd_dq_stash_kernel (one wavefront per (token, group)) then reads
+//    per selected block only K in the feature layout and that tile.
+//  * Dense path: attn_bwd_dq_kernel, one wavefront per (token, group) as the
+//    forward, recomputes S^T = K Q^T and dP^T = V dO^T (keys on the M axis,
+//    the 16 heads on N), so that dZ^T lands in the B-operand layout of
+//    dQ^T = K^T dZ^T; it also writes D for the dK/dV kernel.
 //  * attn_bwd_dkdv_kernel: one workgroup per (key block, group, window of 2048
 //    query tokens), 4 waves x 16 keys.  The tokens of the window that
 //    selected the block come from a bitmap (bwd_bitmap_kernel) in ascending
