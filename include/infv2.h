@@ -119,7 +119,8 @@ int infv2_compress_k2(const infv2_problem* prob, const void* K, void* Kc2,
  *                 i.e. j*s_C1 + l_C1 - 1 <= p (a kernel is causal when its
  *                 last token is);
  *   S^C1[h][j]  = exp(z[h][j] - lse[h]),  lse[h] = log sum_j exp(z[h][j]);
- *   S^shared[j] = sum over the G heads of g of S^C1[h][j]   (kept on chip);
+ *   S^shared[j] = sum over the G heads of g of S^C1[h][j]   (kept on chip
+ *                 unless the caller asks for it);
  *   S^cmp[blk]  = max of S^shared over the visible kernels that intersect
  *                 block blk (-inf when there is none).
  * With prob->lse_approx the normaliser is the coarse estimate instead (the
@@ -134,12 +135,15 @@ int infv2_compress_k2(const infv2_problem* prob, const void* K, void* Kc2,
  *   S_cmp : [batch][h_kv][n_q][n_blk] fp32 (output).  Entries for blocks
  *           0..floor(p/B) are written; entries after the query's own block are
  *           left untouched.
+ *   S_shared : [batch][h_kv][n_q][n_C1] fp32 (optional output, may be NULL):
+ *           S^shared[j] for every kernel, 0 for kernels the token does not
+ *           see.  Asking for it costs one more fp32 write per kernel.
  *   ws    : workspace of infv2_block_scores_workspace(prob) bytes (may be
  *           NULL when that size is 0). */
 size_t infv2_block_scores_workspace(const infv2_problem* prob);
 int infv2_block_scores(const infv2_problem* prob, const void* Q, const void* Kc1,
-                       const void* Kc2, float* S_cmp, void* ws, size_t ws_bytes,
-                       void* stream);
+                       const void* Kc2, float* S_cmp, float* S_shared, void* ws,
+                       size_t ws_bytes, void* stream);
 
 /* Block selection (papernotes note, 关键设计 2; OpenBMB blog, Top-K块共享):
  *   I(p) = I_init  u  I_local(p)  u  top-k(p),

@@ -93,7 +93,10 @@ def test_calls_reject_null_and_misaligned_pointers_before_any_launch(L):
     assert b"aligned" in L.infv2_last_error()
     assert L.infv2_compress_k(pc, 16, 32, 0, 10 ** 6, None) == tbs.INFV2_E_ARG
     assert L.infv2_topk_select(pc, None, 16, 16, None) == tbs.INFV2_E_ARG
-    assert L.infv2_block_scores(pc, 16, 16, None, None, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_block_scores(pc, 16, 16, None, None, None, None, 0, None) == tbs.INFV2_E_ARG
+    # the optional S^shared output must be aligned like every other buffer
+    assert L.infv2_block_scores(pc, 16, 16, None, 16, 20, None, 0, None) == tbs.INFV2_E_ARG
+    assert b"S_shared" in L.infv2_last_error()
     assert L.infv2_select_blocks(pc, 16, 16, None, None, None, 16, None, 0, None) \
         == tbs.INFV2_E_ARG
     assert L.infv2_select_blocks(pc, 16, 16, None, 17, 16, 16, None, 0, None) == tbs.INFV2_E_ARG
@@ -101,7 +104,7 @@ def test_calls_reject_null_and_misaligned_pointers_before_any_launch(L):
     # the LSE approximation needs the coarse keys
     pa = _prob(lse_approx=True)
     pac = ctypes.byref(pa.to_c())
-    assert L.infv2_block_scores(pac, 16, 16, None, 16, None, 0, None) == tbs.INFV2_E_ARG
+    assert L.infv2_block_scores(pac, 16, 16, None, 16, None, None, 0, None) == tbs.INFV2_E_ARG
     assert b"Kc2" in L.infv2_last_error()
     assert L.infv2_compress_k2(pac, 16, 32, 0, tbs.n_coarse_kernels(pa) + 1, None) \
         == tbs.INFV2_E_ARG
@@ -115,7 +118,8 @@ def test_workspace_sizes_and_errors(L):
     pc = ctypes.byref(dec.to_c())
     need = L.infv2_block_scores_workspace(pc)
     assert need >= 16 * 2 * 16 * 8191 * 4
-    assert L.infv2_block_scores(pc, 16, 16, None, 16, 16, need - 1, None) == tbs.INFV2_E_WORKSPACE
+    assert L.infv2_block_scores(pc, 16, 16, None, 16, None, 16, need - 1, None) \
+        == tbs.INFV2_E_WORKSPACE
     need_a = L.infv2_sparse_attn_workspace(pc)
     assert need_a >= 16 * 2 * 19 * 16 * 128 * 4
     assert L.infv2_sparse_attn(pc, 16, 16, 16, 16, 16, 16, None, 16, 0, None) \

@@ -109,7 +109,7 @@ def lib() -> ctypes.CDLL:
             "infv2_compress_k": (ctypes.c_int, [P, vp, vp, i32, i32, vp]),
             "infv2_compress_k2": (ctypes.c_int, [P, vp, vp, i32, i32, vp]),
             "infv2_block_scores_workspace": (sz, [P]),
-            "infv2_block_scores": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
+            "infv2_block_scores": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_topk_select": (ctypes.c_int, [P, vp, vp, vp, vp]),
             "infv2_select_blocks_workspace": (sz, [P, ctypes.c_int]),
             "infv2_select_blocks": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -221,9 +221,12 @@ def block_scores_workspace(prob: Problem) -> int:
 
 def block_scores(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
                  S_cmp: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-                 stream=None, Kc2: torch.Tensor | None = None) -> torch.Tensor:
+                 stream=None, Kc2: torch.Tensor | None = None,
+                 S_shared: torch.Tensor | None = None) -> torch.Tensor:
     """Q, K^C1 (and K^C2 with prob.lse_approx) -> S^cmp [b, h_kv, n_q, n_blk]
-    fp32 (blocks after floor(p/B) untouched)."""
+    fp32 (blocks after floor(p/B) untouched).  S_shared, when given
+    ([b, h_kv, n_q, n_C1] fp32), also receives S^shared (0 where a kernel is
+    not visible)."""
     if S_cmp is None:
         S_cmp = torch.full((prob.batch, prob.h_kv, prob.n_q, n_blocks(prob)), float("nan"),
                            dtype=torch.float32, device=Q.device)
@@ -231,8 +234,8 @@ def block_scores(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
     _check(lib().infv2_block_scores(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1), _ptr(Kc2),
-                                    _ptr(S_cmp), _ptr(ws), ws.numel() if ws is not None else 0,
-                                    _stream(stream)))
+                                    _ptr(S_cmp), _ptr(S_shared), _ptr(ws),
+                                    ws.numel() if ws is not None else 0, _stream(stream)))
     return S_cmp
 
 

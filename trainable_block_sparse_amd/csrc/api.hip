@@ -32,7 +32,7 @@ bool scores_fast_shape(const infv2_problem& p);
 size_t scores_workspace(const infv2_problem& p, const KeySet& ks);
 size_t scores_generic_lds(const infv2_problem& p, int n_c1);
 hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const KeySet& ks,
-                               float* S_cmp, void* ws, int n_blk, float scale,
+                               float* S_cmp, float* S_sh, void* ws, int n_blk, float scale,
                                hipStream_t stream);
 hipError_t launch_topk(const infv2_problem& p, const float* S_cmp, int32_t* idx, int32_t* n_sel,
                        int n_blk, int budget, hipStream_t stream);
@@ -233,11 +233,13 @@ static int check_keys(const infv2_problem& p, const void* Kc1, const void* Kc2) 
 }
 
 int infv2_block_scores(const infv2_problem* p, const void* Q, const void* Kc1, const void* Kc2,
-                       float* S_cmp, void* ws, size_t ws_bytes, void* stream) {
+                       float* S_cmp, float* S_shared, void* ws, size_t ws_bytes, void* stream) {
   int st = check(p);
   if (st) return st;
   CHECK_PTR(Q);
   CHECK_PTR(S_cmp);
+  if (S_shared && !aligned16(S_shared))
+    return fail(INFV2_E_ARG, "S_shared is not 16-byte aligned");
   if ((st = check_keys(*p, Kc1, Kc2))) return st;
   const KeySet ks = keys_of(*p, Kc1, Kc2);
   const size_t need = scores_workspace(*p, ks);
@@ -246,8 +248,8 @@ int infv2_block_scores(const infv2_problem* p, const void* Q, const void* Kc1, c
     if (ws_bytes < need)
       return fail(INFV2_E_WORKSPACE, "block_scores workspace %zu < %zu bytes", ws_bytes, need);
   }
-  return hip_status(launch_block_scores(*p, Q, ks, S_cmp, ws, n_blk_of(*p), scale_of(*p),
-                                        (hipStream_t)stream),
+  return hip_status(launch_block_scores(*p, Q, ks, S_cmp, S_shared, ws, n_blk_of(*p),
+                                        scale_of(*p), (hipStream_t)stream),
                     "infv2_block_scores");
 }
 
@@ -297,7 +299,7 @@ int infv2_select_blocks(const infv2_problem* p, const void* Q, const void* Kc1, 
                       "infv2_select_blocks");
   }
   float* S = S_cmp ? S_cmp : (float*)((char*)ws + align256(scores_workspace(*p, ks)));
-  hipError_t e = launch_block_scores(*p, Q, ks, S, ws, n_blk_of(*p), scale_of(*p), s);
+  hipError_t e = launch_block_scores(*p, Q, ks, S, nullptr, ws, n_blk_of(*p), scale_of(*p), s);
   if (e == hipSuccess) e = launch_topk(*p, S, idx, n_sel, n_blk_of(*p), budget_of(*p), s);
   return hip_status(e, "infv2_select_blocks");
 }

@@ -41,6 +41,7 @@ struct ScoresArgs {
   const uint16_t* Kc1;
   const uint16_t* Kc2;   // coarse keys (LSE approximation), else null
   float* S_cmp;          // null in the selection mode unless the caller wants it
+  float* S_sh;           // S^shared [batch][h_kv][n_q][n_c1] when the caller wants it
   // selection mode (top-k streamed inside the score sweep): outputs, and one
   // mark per tile for the exact kernel (1: recompute this tile)
   int32_t* idx;
@@ -368,6 +369,19 @@ __device__ __noinline__ void scores_exact_body(const ScoresArgs a) {
         const int b_p = (a.q_pos0 + tok) >> 6;
         if (lane < 32 && a.S_cmp && tok < a.n_q && blk <= b_p)
           a.S_cmp[(((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_blk + blk] = v;
+        if (!SELECT && a.S_sh) {
+          // S^shared of the chunk's 32 kernels for the 4 tokens (0 where not seen)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int u = lane + 64 * e, ut = u >> 5, x = u & 31;
+            const int j = c * SEL_CHUNK + x;
+            if (t0 + ut < a.n_q && j < a.n_c1) {
+              const float sv = sbuf[ut][1 + x];
+              a.S_sh[(((size_t)b * a.h_kv + g) * a.n_q + t0 + ut) * a.n_c1 + j] =
+                  (sv == kNegInf) ? 0.f : sv;
+            }
+          }
+        }
         if constexpr (SELECT) {
           const bool cand = lane < 32 && tok < a.n_q && blk >= min(a.N_init, b_p + 1) &&
                             blk < max(0, b_p - a.N_local + 1);
@@ -496,6 +510,13 @@ __device__ __noinline__ void scores_exact_body(const ScoresArgs a) {
         row[blk] = kNegInf;
     }
   }
+  if (!SELECT && a.S_sh) {   // S^shared past the swept chunks
+    const int tok = t0 + (lane >> 4);
+    if (tok < a.n_q) {
+      float* row = a.S_sh + (((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_c1;
+      for (int j = nchunks * SEL_CHUNK + (lane & 15); j < a.n_c1; j += 16) row[j] = 0.f;
+    }
+  }
   if constexpr (SELECT) {
 #pragma unroll
     for (int tl = 0; tl < SEL_TOK_WAVE; ++tl) {
@@ -565,6 +586,7 @@ struct SelWave {
   int jm_l;          // the same for the token of this lane's row after the head sum
   int bp_l;          // its last causal block
   float* srow;       // its S^cmp row (null: not written)
+  float* shrow;      // its S^shared row (SHARED kernels only)
   TopkStream<2> tk;  // selection mode: streaming top-k of the wave's 2 tokens
   uint64_t* tkbuf;   // their LDS buffers [2][64]
 };
@@ -596,8 +618,10 @@ __device__ __forceinline__ void chunk_mfma(const uint8_t* kb, const SelWave& w, 
 //  PASS_SCORE: S^C1 = 2^(z*c - M) * W (LFORM: 2^(z*c - W), W holding each
 //              head's log2-normaliser), summed over the group's 16 heads,
 //              max-pooled over the kernels that intersect each block and
-//              written to S^cmp
-template <int PASS, bool MASKED, bool FIRST, bool LFORM = false, bool TOPK = false>
+//              written to S^cmp; SHR: S^shared itself is written as well
+//              (0 for the kernels the token does not see)
+template <int PASS, bool MASKED, bool FIRST, bool LFORM = false, bool TOPK = false,
+          bool SHR = false>
 __device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][2], int chunk,
                                            SelWave& w, int lane) {
   static_assert(PASS == PASS_SUM || PASS == PASS_SCORE, "fast passes");
@@ -655,6 +679,10 @@ __device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][
     float v = row_sum4(part[0][0], part[1][0], part[0][1], part[1][1]);
     const int nt = (lane >> 4) & 1;
     if constexpr (MASKED) v = (chunk * SEL_CHUNK + nt * 16 + r16 > w.jm_l) ? kNegInf : v;
+    if constexpr (SHR) {
+      const int j = chunk * SEL_CHUNK + nt * 16 + r16;
+      if (j < a.n_c1) w.shrow[j] = (v == kNegInf) ? 0.f : v;
+    }
     // block bb = 4nt + r16/4 of the chunk takes kernels 4bb-1 .. 4bb+3: the
     // max over its quad of lanes and the kernel before it (the previous lane;
     // for rows 0 and 2 at column 0, the last kernel of the previous chunk)
@@ -684,8 +712,9 @@ __device__ __forceinline__ void chunk_valu(const ScoresArgs& a, f32x4 (&acc)[2][
 // SELECT: the selection mode.  Each wave streams the top-k of its two tokens
 // through the score sweep (no S^cmp round trip; S^cmp is still written when
 // a.S_cmp is set) and writes idx / n_sel; the tile's mark tells the exact
-// kernel whether to redo it.
-template <bool APPROX, bool SELECT>
+// kernel whether to redo it.  SHARED: S^shared is written to a.S_sh too (a
+// separate instance, so that the others keep their registers).
+template <bool APPROX, bool SELECT, bool SHARED = false>
 __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2 * SEL_CHUNK_BYTES];
   __shared__ uint64_t tkbuf_all[SELECT ? FAST_WAVES : 1][2][64];
@@ -744,6 +773,7 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
     w.jm_l = last_visible_kernel(a.q_pos0 + tok);
     w.bp_l = (a.q_pos0 + tok) >> 6;
     w.srow = srows ? srows + (size_t)tok * a.n_blk : nullptr;
+    if constexpr (SHARED) w.shrow = a.S_sh + (((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_c1;
   }
   if constexpr (SELECT) {
     w.tkbuf = &tkbuf_all[wave][0][0];
@@ -813,13 +843,14 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
       chunk_mfma(slot(c), w, lane, acc);
       constexpr bool LF = APPROX && PASS == PASS_SCORE;
       constexpr bool TK = SELECT && PASS == PASS_SCORE;
+      constexpr bool SH = SHARED && PASS == PASS_SCORE;
       if (SET_REF && c == 0) {
-        if (n_full > 0) chunk_valu<PASS, false, SET_REF, LF, TK>(a, acc, c, w, lane);
-        else            chunk_valu<PASS, true, SET_REF, LF, TK>(a, acc, c, w, lane);
+        if (n_full > 0) chunk_valu<PASS, false, SET_REF, LF, TK, SH>(a, acc, c, w, lane);
+        else            chunk_valu<PASS, true, SET_REF, LF, TK, SH>(a, acc, c, w, lane);
       } else if (c < n_full) {
-        chunk_valu<PASS, false, false, LF, TK>(a, acc, c, w, lane);
+        chunk_valu<PASS, false, false, LF, TK, SH>(a, acc, c, w, lane);
       } else {
-        chunk_valu<PASS, true, false, LF, TK>(a, acc, c, w, lane);
+        chunk_valu<PASS, true, false, LF, TK, SH>(a, acc, c, w, lane);
       }
       *(u32x4*)(piece_dst + ((c + 1) & 1) * SEL_CHUNK_BYTES) = next;
       next = load_piece(c + 1 + SEL_DEPTH);
@@ -901,6 +932,14 @@ __global__ void __launch_bounds__(512, 4) scores_prefill_kernel(ScoresArgs a) {
         row[blk] = kNegInf;
     }
   }
+  // S^shared past the swept chunks: kernels no token of the tile sees
+  if constexpr (SHARED) {
+    const int tok = t0 + (lane >> 5);
+    if (tok < a.n_q) {
+      float* row = a.S_sh + (((size_t)b * a.h_kv + g) * a.n_q + tok) * a.n_c1;
+      for (int j = nchunks * SEL_CHUNK + (lane & 31); j < a.n_c1; j += 32) row[j] = 0.f;
+    }
+  }
   if constexpr (SELECT) {
     if (tid == 0) a.marks[tile_id] = 0;
 #pragma unroll
@@ -923,6 +962,7 @@ struct SplitArgs {
   const uint16_t* Kc1;
   const uint16_t* Kc2;  // coarse keys (LSE approximation), else null
   float* S_cmp;
+  float* S_sh;      // S^shared [batch][h_kv][n_q][n_c1], or null
   float* logits;    // [batch*n_q][h_kv][16][n_c1p]  (z*c, -inf when invisible)
   float2* part;     // [batch*n_q][h_kv][nch][16]    (chunk max, chunk sum)
   float2* part2;    // [batch*n_q][h_kv][nch2][16]   the same over the coarse kernels
@@ -1130,6 +1170,19 @@ __device__ __forceinline__ void head_lse_weights(const SplitArgs& a, int g, int 
   }
 }
 
+// S^shared of the chunk's kernels j0 .. j0+255 from sh (sh[x] = kernel
+// j0 - 1 + x, -inf where not visible) into the caller's row: 0 where the
+// token does not see the kernel.  256 threads, one kernel each.
+static_assert(SPLIT_CK == 256, "one thread per kernel of the chunk");
+__device__ __forceinline__ void split_write_shared(const SplitArgs& a, int b, int g, int t,
+                                                   int j0, const float* sh) {
+  const int j = j0 + (int)threadIdx.x;
+  if (j < a.n_c1) {
+    const float v = sh[1 + threadIdx.x];
+    a.S_sh[(((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_c1 + j] = (v == kNegInf) ? 0.f : v;
+  }
+}
+
 // The pool step for one chunk: merges the per-chunk (max, sum) partials of
 // every head into the exact log-sum-exp, forms S^shared for the chunk's 256
 // kernels (+ the carry kernel) and max-pools them into its 64 blocks; thread
@@ -1157,6 +1210,7 @@ __device__ __forceinline__ float split_pool_chunk(const SplitArgs& a, int chunk,
     sh[x] = v;
   }
   __syncthreads();
+  if (a.S_sh) split_write_shared(a, b, g, t, j0, sh);
   float* row = a.S_cmp ? a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_blk : nullptr;
   const int nblk_chunk = SPLIT_CK / 4;
   float out = kNegInf;
@@ -1293,6 +1347,7 @@ __global__ void __launch_bounds__(256) scores_split_fused_kernel(SplitArgs a) {
     if (lane == 0) sh[0] = carry_vis ? v : kNegInf;
   }
   __syncthreads();
+  if (a.S_sh) split_write_shared(a, b, g, t, j0, sh);
   const int b_p = p >> 6;
   float* srow = a.S_cmp ? a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_blk : nullptr;
   if (srow && chunk == a.nch - 1)
@@ -1437,6 +1492,7 @@ struct GenericScoresArgs {
   const void* Kc1;
   const void* Kc2;   // coarse keys (LSE approximation), else null
   float* S_cmp;
+  float* S_sh;       // S^shared [batch][h_kv][n_q][n_c1], or null
   int dtype, n_q, q_pos0, h_kv, G, d, n_c1, n_c2, n_blk, B, l_C1, s_C1;
   int approx;
   int64_t c1_cap, c2_cap;
@@ -1537,6 +1593,10 @@ __global__ void __launch_bounds__(256) scores_generic_kernel(GenericScoresArgs a
     shared_s[j] = acc;
   }
   __syncthreads();
+  if (a.S_sh) {   // 0 for the kernels the token does not see
+    float* srow = a.S_sh + (((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_c1;
+    for (int j = threadIdx.x; j < a.n_c1; j += blockDim.x) srow[j] = j < nv ? (float)shared_s[j] : 0.f;
+  }
   const int b_p = p / a.B;
   float* row = a.S_cmp + (((size_t)b * a.h_kv + g) * a.n_q + t) * a.n_blk;
   for (int blk = threadIdx.x; blk <= b_p; blk += blockDim.x) {
@@ -1646,18 +1706,25 @@ static ScoresArgs prefill_args(const infv2_problem& p, const void* Q, const KeyS
   return a;
 }
 
+// a.S_sh (S^shared wanted) takes the SHARED instance of the fast kernel; the
+// selection mode never writes S^shared.
 template <bool SELECT>
 static void launch_prefill_scores(const infv2_problem& p, const ScoresArgs& a,
                                   hipStream_t stream) {
   const int wgs = a.tiles * p.h_kv * p.batch;
   dim3 grid(8 % p.h_kv == 0 ? ((wgs + 7) / 8) * 8 : wgs);
+  const dim3 block(64 * FAST_WAVES);
   if (p.lse_approx) {
-    hipLaunchKernelGGL((scores_prefill_kernel<true, SELECT>), grid, dim3(64 * FAST_WAVES), 0,
-                       stream, a);
+    if (!SELECT && a.S_sh)
+      hipLaunchKernelGGL((scores_prefill_kernel<true, false, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((scores_prefill_kernel<true, SELECT>), grid, block, 0, stream, a);
     hipLaunchKernelGGL((scores_exact_kernel<true, SELECT>), dim3(wgs), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((scores_prefill_kernel<false, SELECT>), grid, dim3(64 * FAST_WAVES), 0,
-                       stream, a);
+    if (!SELECT && a.S_sh)
+      hipLaunchKernelGGL((scores_prefill_kernel<false, false, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((scores_prefill_kernel<false, SELECT>), grid, block, 0, stream, a);
     hipLaunchKernelGGL((scores_exact_kernel<false, SELECT>), dim3(wgs), dim3(256), 0, stream, a);
   }
 }
@@ -1735,15 +1802,20 @@ hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeyS
                              stream);
 }
 
+// S_sh: S^shared [batch][h_kv][n_q][n_C1] as well, or null.
 hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const KeySet& ks,
-                               float* S_cmp, void* ws, int n_blk, float scale,
+                               float* S_cmp, float* S_sh, void* ws, int n_blk, float scale,
                                hipStream_t stream) {
   if (scores_use_split(p)) {
-    launch_split_scores(p, split_args(p, Q, ks, S_cmp, ws, n_blk, scale), stream);
+    SplitArgs a = split_args(p, Q, ks, S_cmp, ws, n_blk, scale);
+    a.S_sh = S_sh;
+    launch_split_scores(p, a, stream);
     return hipGetLastError();
   }
   if (scores_fast_shape(p)) {
-    launch_prefill_scores<false>(p, prefill_args(p, Q, ks, S_cmp, n_blk, scale), stream);
+    ScoresArgs a = prefill_args(p, Q, ks, S_cmp, n_blk, scale);
+    a.S_sh = S_sh;
+    launch_prefill_scores<false>(p, a, stream);
     return hipGetLastError();
   }
   GenericScoresArgs a = {};
@@ -1751,6 +1823,7 @@ hipError_t launch_block_scores(const infv2_problem& p, const void* Q, const KeyS
   a.Kc1 = ks.Kc1;
   a.Kc2 = ks.Kc2;
   a.S_cmp = S_cmp;
+  a.S_sh = S_sh;
   a.dtype = p.dtype;
   a.n_q = p.n_q;
   a.q_pos0 = p.q_pos0;
