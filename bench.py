@@ -360,9 +360,11 @@ def bench_decode_varlen(cfg, steps, warmup):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
+    h0 = time.perf_counter()
     for _ in range(steps):
         for fn in fns:
             fn()
+    host_ms = (time.perf_counter() - h0) * 1e3 / steps
     e1.record()
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / steps
@@ -384,7 +386,8 @@ def bench_decode_varlen(cfg, steps, warmup):
     out = dict(step_us=step_ms * 1e3, us_per_token=step_ms * 1e3 / cfg.batch,
                timing=("eager launches, steps back to back" if eager_ms <= graph_ms
                        else "HIP graph replay of the whole step"),
-               eager_step_us=eager_ms * 1e3, graph_step_us=graph_ms * 1e3, lengths=lens.tolist(),
+               eager_step_us=eager_ms * 1e3, graph_step_us=graph_ms * 1e3,
+               host_enqueue_us=host_ms * 1e3, lengths=lens.tolist(),
                algo_bytes=nbytes, algo_GBps=nbytes / (step_ms / 1e3) / 1e9)
     out["frac_of_hbm_peak"] = out["algo_GBps"] / PEAK_HBM_GBS
     del Q, K, V, Kc1, O, ws_s, ws_a
@@ -445,11 +448,15 @@ def bench_decode(cfg, steps, warmup, lse_approx=False):
         timer.step(fns)
     stage = timer.collect()
     # the whole step, eager, without events in between
+    # (host_ms: the host's enqueue time per step; the eager figure is the GPU's
+    # own only while this stays below it)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
+    h0 = time.perf_counter()
     for _ in range(steps):
         for fn in fns:
             fn()
+    host_ms = (time.perf_counter() - h0) * 1e3 / steps
     e1.record()
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / steps
@@ -488,6 +495,7 @@ def bench_decode(cfg, steps, warmup, lse_approx=False):
     step_ms = min(eager_ms, graph_ms)
     out = dict(step_us=step_ms * 1e3, us_per_token=step_ms * 1e3 / cfg.batch,
                eager_step_us=eager_ms * 1e3, graph_step_us=graph_ms * 1e3,
+               host_enqueue_us=host_ms * 1e3,
                timing=("eager launches, steps back to back" if eager_ms <= graph_ms
                        else "HIP graph replay of the whole step"),
                separate_topk_step_us=sep_ms * 1e3,

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import dataclasses
 from dataclasses import dataclass
 
 import torch
@@ -81,6 +82,22 @@ class Problem:
                         self.N_local, INFV2_BF16 if self.dtype == "bf16" else INFV2_F32,
                         self.scale, self.kv_cap, self.c1_cap, self.c2_cap, int(self.lse_approx))
 
+    # The C struct and the buffer extents are built once and kept until a
+    # field changes (the calls below take them on every launch).
+    def __setattr__(self, name, value):
+        object.__setattr__(self, name, value)
+        self.__dict__.pop("_cached", None)
+
+    def _c(self) -> _Problem:
+        c = self.__dict__.get("_cached")
+        if c is None:
+            c = self.__dict__["_cached"] = (self.to_c(), _Ext(self))
+        return c[0]
+
+    def _ext(self) -> "_Ext":
+        self._c()
+        return self.__dict__["_cached"][1]
+
 
 class Infv2Error(RuntimeError):
     def __init__(self, status: int, msg: str):
@@ -142,8 +159,58 @@ def _check(status: int) -> None:
         raise Infv2Error(status, lib().infv2_last_error().decode())
 
 
-def _ptr(t) -> int | None:
-    return None if t is None else t.data_ptr()
+class _Ext:
+    """Element counts of every buffer of one problem (the layouts of
+    include/infv2.h), for the checks below."""
+    __slots__ = ("io", "q", "kv", "kc1", "kc2", "n_c1", "n_c2", "n_blk", "rows", "budget",
+                 "lse", "kv_rows")
+
+    def __init__(self, prob: "Problem"):
+        self.io = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
+        n_kv, l1, s1 = prob.n_kv, prob.l_C1, prob.s_C1
+        self.n_c1 = 0 if n_kv < l1 else (n_kv - l1) // s1 + 1
+        self.n_c2 = n_c2 = 0 if n_kv < 4 * l1 else (n_kv - 4 * l1) // (4 * s1) + 1
+        self.n_blk = -(-n_kv // prob.B) if prob.B > 0 else 0
+        self.budget = prob.N_init + prob.N_local + prob.k
+        h_q = prob.G * prob.h_kv
+        self.kv_rows = prob.kv_cap or n_kv
+        self.q = prob.batch * prob.n_q * h_q * prob.d
+        self.kv = prob.batch * self.kv_rows * prob.h_kv * prob.d
+        self.kc1 = prob.batch * prob.h_kv * (prob.c1_cap or self.n_c1) * prob.d
+        self.kc2 = prob.batch * prob.h_kv * (prob.c2_cap or n_c2) * prob.d
+        self.rows = prob.batch * prob.h_kv * prob.n_q
+        self.lse = prob.batch * h_q * prob.n_q
+
+
+def _arg(t, name: str, dtype, numel: int, optional: bool = False):
+    """Device pointer of `t` once the kernels can use it: a contiguous GPU
+    tensor of `dtype` that holds at least `numel` elements.  A host tensor,
+    a strided view or a short buffer raises here instead of reaching a kernel."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if (not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != dtype
+            or not t.is_contiguous() or t.numel() < numel):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor, not {type(t).__name__}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype} (it is {t.dtype})")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.numel() < numel:
+            raise ValueError(f"{name} holds {t.numel()} elements; the problem needs {numel}")
+        raise ValueError(f"{name} must be a GPU tensor (it is on {t.device})")
+    return t.data_ptr()
+
+
+def _ws(ws):
+    """(pointer, size in bytes) of a workspace tensor of any dtype."""
+    if ws is None:
+        return None, 0
+    if not isinstance(ws, torch.Tensor) or ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous GPU tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
 def _stream(stream=None) -> int:
@@ -154,30 +221,30 @@ def _stream(stream=None) -> int:
 # --- derived sizes ----------------------------------------------------------
 
 def n_kernels(prob: Problem) -> int:
-    return lib().infv2_n_kernels(ctypes.byref(prob.to_c()))
+    return lib().infv2_n_kernels(ctypes.byref(prob._c()))
 
 
 def n_coarse_kernels(prob: Problem) -> int:
-    return lib().infv2_n_coarse_kernels(ctypes.byref(prob.to_c()))
+    return lib().infv2_n_coarse_kernels(ctypes.byref(prob._c()))
 
 
 def n_blocks(prob: Problem) -> int:
-    return lib().infv2_n_blocks(ctypes.byref(prob.to_c()))
+    return lib().infv2_n_blocks(ctypes.byref(prob._c()))
 
 
 def budget(prob: Problem) -> int:
-    return lib().infv2_budget(ctypes.byref(prob.to_c()))
+    return lib().infv2_budget(ctypes.byref(prob._c()))
 
 
 def use_dense(prob: Problem) -> bool:
-    r = lib().infv2_use_dense(ctypes.byref(prob.to_c()))
+    r = lib().infv2_use_dense(ctypes.byref(prob._c()))
     if r < 0:
-        _check(lib().infv2_check_problem(ctypes.byref(prob.to_c())))
+        _check(lib().infv2_check_problem(ctypes.byref(prob._c())))
     return r == 1
 
 
 def check_problem(prob: Problem) -> None:
-    _check(lib().infv2_check_problem(ctypes.byref(prob.to_c())))
+    _check(lib().infv2_check_problem(ctypes.byref(prob._c())))
 
 
 def _torch_dtype(prob: Problem):
@@ -189,13 +256,14 @@ def _torch_dtype(prob: Problem):
 def compress_k(prob: Problem, K: torch.Tensor, Kc1: torch.Tensor | None = None,
                c1_begin: int = 0, c1_end: int | None = None, stream=None) -> torch.Tensor:
     """K [b, kv_cap, h_kv, d] -> K^C1 [b, h_kv, c1_cap, d] (rows c1_begin..c1_end-1)."""
-    n_c1 = n_kernels(prob)
+    e = prob._ext()
     if Kc1 is None:
-        cap = prob.c1_cap or n_c1
+        cap = prob.c1_cap or e.n_c1
         Kc1 = torch.empty((prob.batch, prob.h_kv, max(cap, 1), prob.d), dtype=K.dtype,
                           device=K.device)
-    c1_end = n_c1 if c1_end is None else c1_end
-    _check(lib().infv2_compress_k(ctypes.byref(prob.to_c()), _ptr(K), _ptr(Kc1), c1_begin, c1_end,
+    c1_end = e.n_c1 if c1_end is None else c1_end
+    _check(lib().infv2_compress_k(ctypes.byref(prob._c()), _arg(K, "K", e.io, e.kv),
+                                  _arg(Kc1, "Kc1", e.io, e.kc1), c1_begin, c1_end,
                                   _stream(stream)))
     return Kc1
 
@@ -204,19 +272,20 @@ def compress_k2(prob: Problem, K: torch.Tensor, Kc2: torch.Tensor | None = None,
                 c2_begin: int = 0, c2_end: int | None = None, stream=None) -> torch.Tensor:
     """K [b, kv_cap, h_kv, d] -> K^C2 [b, h_kv, c2_cap, d] (rows c2_begin..c2_end-1),
     the coarse keys of the LSE approximation."""
-    n_c2 = n_coarse_kernels(prob)
+    e = prob._ext()
     if Kc2 is None:
-        cap = prob.c2_cap or n_c2
+        cap = prob.c2_cap or e.n_c2
         Kc2 = torch.empty((prob.batch, prob.h_kv, max(cap, 1), prob.d), dtype=K.dtype,
                           device=K.device)
-    c2_end = n_c2 if c2_end is None else c2_end
-    _check(lib().infv2_compress_k2(ctypes.byref(prob.to_c()), _ptr(K), _ptr(Kc2), c2_begin,
-                                   c2_end, _stream(stream)))
+    c2_end = e.n_c2 if c2_end is None else c2_end
+    _check(lib().infv2_compress_k2(ctypes.byref(prob._c()), _arg(K, "K", e.io, e.kv),
+                                   _arg(Kc2, "Kc2", e.io, e.kc2), c2_begin, c2_end,
+                                   _stream(stream)))
     return Kc2
 
 
 def block_scores_workspace(prob: Problem) -> int:
-    return lib().infv2_block_scores_workspace(ctypes.byref(prob.to_c()))
+    return lib().infv2_block_scores_workspace(ctypes.byref(prob._c()))
 
 
 def block_scores(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
@@ -230,12 +299,17 @@ def block_scores(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
     if S_cmp is None:
         S_cmp = torch.full((prob.batch, prob.h_kv, prob.n_q, n_blocks(prob)), float("nan"),
                            dtype=torch.float32, device=Q.device)
-    need = block_scores_workspace(prob)
-    if ws is None and need:
+    if ws is None and (need := block_scores_workspace(prob)):
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _check(lib().infv2_block_scores(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1), _ptr(Kc2),
-                                    _ptr(S_cmp), _ptr(S_shared), _ptr(ws),
-                                    ws.numel() if ws is not None else 0, _stream(stream)))
+    e = prob._ext()
+    ws_p, ws_n = _ws(ws)
+    _check(lib().infv2_block_scores(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                    _arg(Kc1, "Kc1", e.io, e.kc1, optional=True),
+                                    _arg(Kc2, "Kc2", e.io, e.kc2, optional=True),
+                                    _arg(S_cmp, "S_cmp", torch.float32, e.rows * e.n_blk),
+                                    _arg(S_shared, "S_shared", torch.float32, e.rows * e.n_c1,
+                                         optional=True),
+                                    ws_p, ws_n, _stream(stream)))
     return S_cmp
 
 
@@ -248,13 +322,16 @@ def topk_select(prob: Problem, S_cmp: torch.Tensor, idx: torch.Tensor | None = N
     if n_sel is None:
         n_sel = torch.empty((prob.batch, prob.h_kv, prob.n_q), dtype=torch.int32,
                             device=S_cmp.device)
-    _check(lib().infv2_topk_select(ctypes.byref(prob.to_c()), _ptr(S_cmp), _ptr(idx), _ptr(n_sel),
-                                   _stream(stream)))
+    e = prob._ext()
+    _check(lib().infv2_topk_select(ctypes.byref(prob._c()),
+                                   _arg(S_cmp, "S_cmp", torch.float32, e.rows * e.n_blk),
+                                   _arg(idx, "idx", torch.int32, e.rows * e.budget),
+                                   _arg(n_sel, "n_sel", torch.int32, e.rows), _stream(stream)))
     return idx, n_sel
 
 
 def select_blocks_workspace(prob: Problem, with_scores: bool = False) -> int:
-    return lib().infv2_select_blocks_workspace(ctypes.byref(prob.to_c()), int(bool(with_scores)))
+    return lib().infv2_select_blocks_workspace(ctypes.byref(prob._c()), int(bool(with_scores)))
 
 
 def select_blocks(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
@@ -269,17 +346,23 @@ def select_blocks(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
     if n_sel is None:
         n_sel = torch.empty((prob.batch, prob.h_kv, prob.n_q), dtype=torch.int32,
                             device=Q.device)
-    need = select_blocks_workspace(prob, S_cmp is not None)
-    if ws is None and need:
+    if ws is None and (need := select_blocks_workspace(prob, S_cmp is not None)):
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _check(lib().infv2_select_blocks(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1), _ptr(Kc2),
-                                     _ptr(S_cmp), _ptr(idx), _ptr(n_sel), _ptr(ws),
-                                     ws.numel() if ws is not None else 0, _stream(stream)))
+    e = prob._ext()
+    ws_p, ws_n = _ws(ws)
+    _check(lib().infv2_select_blocks(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                     _arg(Kc1, "Kc1", e.io, e.kc1, optional=True),
+                                     _arg(Kc2, "Kc2", e.io, e.kc2, optional=True),
+                                     _arg(S_cmp, "S_cmp", torch.float32, e.rows * e.n_blk,
+                                          optional=True),
+                                     _arg(idx, "idx", torch.int32, e.rows * e.budget),
+                                     _arg(n_sel, "n_sel", torch.int32, e.rows), ws_p, ws_n,
+                                     _stream(stream)))
     return idx, n_sel
 
 
 def sparse_attn_workspace(prob: Problem) -> int:
-    return lib().infv2_sparse_attn_workspace(ctypes.byref(prob.to_c()))
+    return lib().infv2_sparse_attn_workspace(ctypes.byref(prob._c()))
 
 
 def sparse_attn(prob: Problem, Q, K, V, idx, n_sel, O=None, lse=None, ws=None,
@@ -289,17 +372,22 @@ def sparse_attn(prob: Problem, Q, K, V, idx, n_sel, O=None, lse=None, ws=None,
         O = torch.empty_like(Q)
     if lse is None and want_lse:
         lse = torch.empty((prob.batch, prob.h_q, prob.n_q), dtype=torch.float32, device=Q.device)
-    need = sparse_attn_workspace(prob)
-    if ws is None and need:
+    if ws is None and (need := sparse_attn_workspace(prob)):
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _check(lib().infv2_sparse_attn(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(K), _ptr(V),
-                                   _ptr(idx), _ptr(n_sel), _ptr(O), _ptr(lse), _ptr(ws),
-                                   ws.numel() if ws is not None else 0, _stream(stream)))
+    e = prob._ext()
+    ws_p, ws_n = _ws(ws)
+    _check(lib().infv2_sparse_attn(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                   _arg(K, "K", e.io, e.kv), _arg(V, "V", e.io, e.kv),
+                                   _arg(idx, "idx", torch.int32, e.rows * e.budget),
+                                   _arg(n_sel, "n_sel", torch.int32, e.rows),
+                                   _arg(O, "O", e.io, e.q),
+                                   _arg(lse, "lse", torch.float32, e.lse, optional=True),
+                                   ws_p, ws_n, _stream(stream)))
     return O, lse
 
 
 def dense_attn_workspace(prob: Problem) -> int:
-    return lib().infv2_dense_attn_workspace(ctypes.byref(prob.to_c()))
+    return lib().infv2_dense_attn_workspace(ctypes.byref(prob._c()))
 
 
 def dense_attn(prob: Problem, Q, K, V, O=None, lse=None, ws=None, want_lse: bool = True,
@@ -309,22 +397,36 @@ def dense_attn(prob: Problem, Q, K, V, O=None, lse=None, ws=None, want_lse: bool
         O = torch.empty_like(Q)
     if lse is None and want_lse:
         lse = torch.empty((prob.batch, prob.h_q, prob.n_q), dtype=torch.float32, device=Q.device)
-    need = dense_attn_workspace(prob)
-    if ws is None and need:
+    if ws is None and (need := dense_attn_workspace(prob)):
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _check(lib().infv2_dense_attn(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
-                                  _ptr(lse), _ptr(ws), ws.numel() if ws is not None else 0,
-                                  _stream(stream)))
+    e = prob._ext()
+    ws_p, ws_n = _ws(ws)
+    _check(lib().infv2_dense_attn(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                  _arg(K, "K", e.io, e.kv), _arg(V, "V", e.io, e.kv),
+                                  _arg(O, "O", e.io, e.q),
+                                  _arg(lse, "lse", torch.float32, e.lse, optional=True),
+                                  ws_p, ws_n, _stream(stream)))
     return O, lse
 
 
 # --- varlen batches / paged cache (decode shapes) ---------------------------
 
-def _pages(block_table, K):
-    """(pointer, max_blocks, n_pages) of a page table over the pool K."""
+def _cache(prob: Problem, e: _Ext, K, V, block_table):
+    """(K, V, block_table pointers, max_blocks, n_pages): a contiguous cache
+    [batch, kv_cap, h_kv, d], or page pools [n_pages, B, h_kv, d] (V may be
+    None for the key-only calls) with a table [batch, max_blocks]."""
     if block_table is None:
-        return None, 0, 0
-    return _ptr(block_table), block_table.shape[1], K.shape[0]
+        return (_arg(K, "K", e.io, e.kv), _arg(V, "V", e.io, e.kv, optional=True), None, 0, 0)
+    if not isinstance(K, torch.Tensor) or K.dim() != 4 or \
+            tuple(K.shape[1:]) != (prob.B, prob.h_kv, prob.d):
+        raise ValueError("a paged K must be a pool [n_pages, B, h_kv, d]")
+    if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2 or \
+            block_table.shape[0] < prob.batch:
+        raise ValueError("block_table must be [batch, max_blocks]")
+    n_pages, mb = K.shape[0], block_table.shape[1]
+    pool = n_pages * prob.B * prob.h_kv * prob.d
+    return (_arg(K, "K", e.io, pool), _arg(V, "V", e.io, pool, optional=True),
+            _arg(block_table, "block_table", torch.int32, prob.batch * mb), mb, n_pages)
 
 
 def compress_k_varlen(prob: Problem, K: torch.Tensor, seq_lens: torch.Tensor, Kc: torch.Tensor,
@@ -333,15 +435,17 @@ def compress_k_varlen(prob: Problem, K: torch.Tensor, seq_lens: torch.Tensor, Kc
     """Each sequence's last `last_n` complete kernels (all when last_n <= 0)
     of K^C1 (coarse=False) or K^C2 (coarse=True) into Kc [b, h_kv, cap, d];
     K is a page pool [n_pages, B, h_kv, d] when block_table is given."""
-    bt, mb, npg = _pages(block_table, K)
-    _check(lib().infv2_compress_k_varlen(ctypes.byref(prob.to_c()), _ptr(K), bt, mb, npg,
-                                         _ptr(seq_lens), _ptr(Kc), int(bool(coarse)), last_n,
-                                         _stream(stream)))
+    e = prob._ext()
+    k_p, _, bt, mb, npg = _cache(prob, e, K, None, block_table)
+    _check(lib().infv2_compress_k_varlen(ctypes.byref(prob._c()), k_p, bt, mb, npg,
+                                         _arg(seq_lens, "seq_lens", torch.int32, prob.batch),
+                                         _arg(Kc, "Kc", e.io, e.kc2 if coarse else e.kc1),
+                                         int(bool(coarse)), last_n, _stream(stream)))
     return Kc
 
 
 def select_blocks_varlen_workspace(prob: Problem) -> int:
-    return lib().infv2_select_blocks_varlen_workspace(ctypes.byref(prob.to_c()))
+    return lib().infv2_select_blocks_varlen_workspace(ctypes.byref(prob._c()))
 
 
 def select_blocks_varlen(prob: Problem, Q, Kc1, seq_lens, idx=None, n_sel=None, ws=None,
@@ -356,14 +460,20 @@ def select_blocks_varlen(prob: Problem, Q, Kc1, seq_lens, idx=None, n_sel=None, 
     if ws is None:
         ws = torch.empty(max(select_blocks_varlen_workspace(prob), 16), dtype=torch.uint8,
                          device=Q.device)
-    _check(lib().infv2_select_blocks_varlen(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(Kc1),
-                                            _ptr(Kc2), _ptr(seq_lens), _ptr(idx), _ptr(n_sel),
-                                            _ptr(ws), ws.numel(), _stream(stream)))
+    e = prob._ext()
+    ws_p, ws_n = _ws(ws)
+    _check(lib().infv2_select_blocks_varlen(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                            _arg(Kc1, "Kc1", e.io, e.kc1, optional=True),
+                                            _arg(Kc2, "Kc2", e.io, e.kc2, optional=True),
+                                            _arg(seq_lens, "seq_lens", torch.int32, prob.batch),
+                                            _arg(idx, "idx", torch.int32, e.rows * e.budget),
+                                            _arg(n_sel, "n_sel", torch.int32, e.rows),
+                                            ws_p, ws_n, _stream(stream)))
     return idx, n_sel
 
 
 def sparse_attn_varlen_workspace(prob: Problem) -> int:
-    return lib().infv2_sparse_attn_varlen_workspace(ctypes.byref(prob.to_c()))
+    return lib().infv2_sparse_attn_varlen_workspace(ctypes.byref(prob._c()))
 
 
 def sparse_attn_varlen(prob: Problem, Q, K, V, seq_lens, idx, n_sel, block_table=None, O=None,
@@ -377,11 +487,19 @@ def sparse_attn_varlen(prob: Problem, Q, K, V, seq_lens, idx, n_sel, block_table
     if ws is None:
         ws = torch.empty(max(sparse_attn_varlen_workspace(prob), 16), dtype=torch.uint8,
                          device=Q.device)
-    bt, mb, npg = _pages(block_table, K)
-    _check(lib().infv2_sparse_attn_varlen(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(K), _ptr(V),
-                                          bt, mb, npg, _ptr(seq_lens), _ptr(idx), _ptr(n_sel),
-                                          _ptr(O), _ptr(lse), _ptr(ws), ws.numel(),
-                                          _stream(stream)))
+    e = prob._ext()
+    if V is None:
+        raise ValueError("V is required")
+    k_p, v_p, bt, mb, npg = _cache(prob, e, K, V, block_table)
+    ws_p, ws_n = _ws(ws)
+    _check(lib().infv2_sparse_attn_varlen(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                          k_p, v_p, bt, mb, npg,
+                                          _arg(seq_lens, "seq_lens", torch.int32, prob.batch),
+                                          _arg(idx, "idx", torch.int32, e.rows * e.budget),
+                                          _arg(n_sel, "n_sel", torch.int32, e.rows),
+                                          _arg(O, "O", e.io, e.q),
+                                          _arg(lse, "lse", torch.float32, e.lse, optional=True),
+                                          ws_p, ws_n, _stream(stream)))
     return O, lse
 
 
@@ -398,7 +516,7 @@ def _bwd_outputs(prob: Problem, Q, K, dQ, dK, dV):
 
 
 def sparse_attn_bwd_workspace(prob: Problem) -> int:
-    return lib().infv2_sparse_attn_bwd_workspace(ctypes.byref(prob.to_c()))
+    return lib().infv2_sparse_attn_bwd_workspace(ctypes.byref(prob._c()))
 
 
 def sparse_attn_bwd(prob: Problem, Q, K, V, idx, n_sel, O, lse, dO, dQ=None, dK=None,
@@ -406,31 +524,41 @@ def sparse_attn_bwd(prob: Problem, Q, K, V, idx, n_sel, O, lse, dO, dQ=None, dK=
     """Gradients (dQ, dK, dV) in fp32 of the block-sparse attention with the
     selected sets held fixed."""
     dQ, dK, dV = _bwd_outputs(prob, Q, K, dQ, dK, dV)
-    need = sparse_attn_bwd_workspace(prob)
-    if ws is None and need:
+    if ws is None and (need := sparse_attn_bwd_workspace(prob)):
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _check(lib().infv2_sparse_attn_bwd(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(K), _ptr(V),
-                                       _ptr(idx), _ptr(n_sel), _ptr(O), _ptr(lse), _ptr(dO),
-                                       _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws),
-                                       ws.numel() if ws is not None else 0, _stream(stream)))
+    e = prob._ext()
+    ws_p, ws_n = _ws(ws)
+    f32 = torch.float32
+    _check(lib().infv2_sparse_attn_bwd(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                       _arg(K, "K", e.io, e.kv), _arg(V, "V", e.io, e.kv),
+                                       _arg(idx, "idx", torch.int32, e.rows * e.budget),
+                                       _arg(n_sel, "n_sel", torch.int32, e.rows),
+                                       _arg(O, "O", e.io, e.q), _arg(lse, "lse", f32, e.lse),
+                                       _arg(dO, "dO", e.io, e.q), _arg(dQ, "dQ", f32, e.q),
+                                       _arg(dK, "dK", f32, e.kv), _arg(dV, "dV", f32, e.kv),
+                                       ws_p, ws_n, _stream(stream)))
     return dQ, dK, dV
 
 
 def dense_attn_bwd_workspace(prob: Problem) -> int:
-    return lib().infv2_dense_attn_bwd_workspace(ctypes.byref(prob.to_c()))
+    return lib().infv2_dense_attn_bwd_workspace(ctypes.byref(prob._c()))
 
 
 def dense_attn_bwd(prob: Problem, Q, K, V, O, lse, dO, dQ=None, dK=None, dV=None, ws=None,
                    stream=None):
     """Gradients (dQ, dK, dV) in fp32 of dense causal attention."""
     dQ, dK, dV = _bwd_outputs(prob, Q, K, dQ, dK, dV)
-    need = dense_attn_bwd_workspace(prob)
-    if ws is None and need:
+    if ws is None and (need := dense_attn_bwd_workspace(prob)):
         ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    _check(lib().infv2_dense_attn_bwd(ctypes.byref(prob.to_c()), _ptr(Q), _ptr(K), _ptr(V),
-                                      _ptr(O), _ptr(lse), _ptr(dO), _ptr(dQ), _ptr(dK),
-                                      _ptr(dV), _ptr(ws), ws.numel() if ws is not None else 0,
-                                      _stream(stream)))
+    e = prob._ext()
+    ws_p, ws_n = _ws(ws)
+    f32 = torch.float32
+    _check(lib().infv2_dense_attn_bwd(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                      _arg(K, "K", e.io, e.kv), _arg(V, "V", e.io, e.kv),
+                                      _arg(O, "O", e.io, e.q), _arg(lse, "lse", f32, e.lse),
+                                      _arg(dO, "dO", e.io, e.q), _arg(dQ, "dQ", f32, e.q),
+                                      _arg(dK, "dK", f32, e.kv), _arg(dV, "dV", f32, e.kv),
+                                      ws_p, ws_n, _stream(stream)))
     return dQ, dK, dV
 
 
@@ -489,9 +617,9 @@ class PrefillPipeline:
                                   for i in range(1, n_chunks)})
         self.chunks = []
         for r0, r1 in zip(cuts[:-1], cuts[1:]):
-            p = Problem(**{**prob.__dict__, "n_q": r1 - r0, "q_pos0": prob.q_pos0 + r0,
-                           "n_kv": prob.q_pos0 + r1, "kv_cap": kv_cap, "c1_cap": c1_cap,
-                           "c2_cap": c2_cap})
+            p = dataclasses.replace(prob, n_q=r1 - r0, q_pos0=prob.q_pos0 + r0,
+                                    n_kv=prob.q_pos0 + r1, kv_cap=kv_cap, c1_cap=c1_cap,
+                                    c2_cap=c2_cap)
             ws_bytes = select_blocks_workspace(p) if lean else block_scores_workspace(p)
             self.chunks.append(dict(
                 p=p, r0=r0, r1=r1,
