@@ -127,6 +127,17 @@ def test_fp32_tiny_sparse_backward_generic_kernel():
     _check(cfg, lp, op, x, 0, False, seed=67)
 
 
+def test_bf16_sparse_backward_generic_kernel():
+    # G = 8, d = 64: the generic backward with bf16 loads
+    import dataclasses
+    cfg = dataclasses.replace(CONFIGS["prefill32k"], name="g8d64", h_q=32, h_kv=4, d=64, k=8,
+                              n_needles=8)
+    _say("case: bf16 G=8 d=64 sparse backward")
+    x = make_inputs(cfg, n_kv=1100, batch=1, seed=69)
+    lp, op = problems(cfg, n_kv=1100, batch=1)
+    _check(cfg, lp, op, x, 0, False, seed=70)
+
+
 def test_backward_is_repeatable():
     # dQ bitwise; dK / dV to fp32 accumulation-order rounding
     cfg = CONFIGS["prefill32k"]
