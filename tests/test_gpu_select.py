@@ -202,3 +202,23 @@ def test_fused_selection_repeated_calls_share_workspace():
         idx, n_sel = tbs.select_blocks(lp, Q, Kc1, ws=ws)
         torch.cuda.synchronize()
         assert torch.equal(idx, idx_ref) and torch.equal(n_sel, n_ref)
+
+
+@pytest.mark.parametrize("n_kv", [262144, 300001])
+def test_decode_at_and_past_the_longest_fused_selection(n_kv):
+    # 262144 keys: 16383 kernels in 64 chunks of 256, the most the fused
+    # decode selection takes; 300001 keys: past it, select_blocks runs the
+    # scores and the general top-k kernel (4688 blocks, re-read from memory)
+    cfg = CONFIGS["decode"]
+    _say("case: decode selection and attention at", n_kv)
+    x, lp, op, Q, Kc1 = _selection_inputs(cfg, n_kv, 2, 1, seed=90)
+    S = torch.full((2, lp.h_kv, 1, tbs.n_blocks(lp)), float("nan"), device=Q.device)
+    idx, n_sel = tbs.select_blocks(lp, Q, Kc1, S_cmp=S)
+    K, V = x["k"].to(Q.device), x["v"].to(Q.device)
+    O, lse = tbs.sparse_attn(lp, Q, K, V, idx, n_sel)
+    torch.cuda.synchronize()
+    res = dict(Kc1=Kc1.cpu(), S_cmp=S.cpu(), idx=idx.cpu(), n_sel=n_sel.cpu(), O=O.cpu(),
+               lse=lse.cpu())
+    del K, V
+    check_compress(res, x["k"], op)
+    _say(check_rows(res, x, op, n_kv - 1, {b: np.array([0]) for b in range(2)}))
