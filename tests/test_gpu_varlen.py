@@ -19,7 +19,7 @@ import torch
 
 import oracle as orc
 import trainable_block_sparse_amd as tbs
-from synth import CONFIGS, make_inputs, paged_cache, varlen_lengths
+from synth import CONFIGS, make_inputs, paged_cache
 
 from parity import check_rows, problems, to_f64
 
