@@ -591,9 +591,9 @@ def main():
                     help="skip the LSE-approximation records")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the path shards by KV group / batch / query range, see the design notes); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU and has no multi-GPU path (the work would shard by "
+              "KV group, batch or query range with the same kernels); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     tbs.lib()
