@@ -52,7 +52,8 @@ Sources (cited by tag in the docstrings below):
        what lets decoding (one new token per sequence) use the sparse path.
 
 Readings where the pages are silent or ambiguous are tagged READING-<n>; the
-design notes list them all:
+ones this module follows (the others concern the tests' exemption rule, the
+inputs and the GPU kernels' own sweeps):
  1 scale 1/sqrt(d) in both softmaxes          8 dense switch: ceil(n/B) <= N_init+N_local+k
  2 a kernel is visible when its last token <= p 9 top-k ties go to the lower block index
  3 group SUM (not mean) over the G heads       11 K^C1 and O rounded once (RNE) to the I/O dtype
