@@ -177,3 +177,34 @@ def test_varlen_calls_validate_before_any_launch(L):
     f32 = ctypes.byref(_prob(dtype="f32", G=4, d=64, n_q=1, n_kv=4096).to_c())
     assert L.infv2_sparse_attn_varlen(f32, 16, 16, 16, None, 0, 0, 16, 16, 16, 16, None, 16,
                                       1 << 30, None) == tbs.INFV2_E_UNSUPPORTED
+
+
+def test_error_messages_are_per_thread(L):
+    # each thread sees the message of its own last failing call, while the
+    # other threads fail in other ways at the same time
+    import threading
+    barrier = threading.Barrier(4)
+    out = {}
+
+    def worker(i):
+        p = ctypes.byref(_prob(n_kv=4096 + 64 * i, n_q=4096 + 64 * i).to_c())
+        barrier.wait()
+        for _ in range(200):
+            if i % 2:
+                st = L.infv2_compress_k(p, None, 16, 0, 1, None)      # NULL K
+                want = b"NULL"
+            else:
+                st = L.infv2_compress_k(p, 16, 17, 0, 1, None)        # misaligned Kc1
+                want = b"aligned"
+            msg = L.infv2_last_error()
+            if st != tbs.INFV2_E_ARG or want not in msg:
+                out[i] = (st, msg)
+                return
+        out[i] = "ok"
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert out == {i: "ok" for i in range(4)}, out
