@@ -88,8 +88,9 @@ int infv2_use_dense(const infv2_problem* prob);
 
 /* Checks that `prob` describes a problem the library can run (shapes, the
  * max-pool parameters l and s equal the count and stride of the kernels that
- * intersect a block, B a multiple of the attention key tile, ...).  Returns
- * INFV2_OK, INFV2_E_ARG or INFV2_E_UNSUPPORTED; enqueues nothing. */
+ * intersect a block, B a multiple of the attention key tile, batch x
+ * min(n_q, 4) <= 65535 so that one launch grid dimension holds it, ...).
+ * Returns INFV2_OK, INFV2_E_ARG or INFV2_E_UNSUPPORTED; enqueues nothing. */
 int infv2_check_problem(const infv2_problem* prob);
 
 /* Stage 1 (papernotes note, 关键设计 3; OpenBMB blog, 语义核): mean-pool the keys

@@ -179,6 +179,20 @@ def test_varlen_calls_validate_before_any_launch(L):
                                       1 << 30, None) == tbs.INFV2_E_UNSUPPORTED
 
 
+def test_batches_beyond_one_launch_are_refused(L):
+    # the batch (times up to 4 query tokens) rides in a grid dimension of at
+    # most 65535 workgroups
+    assert _status(L, _prob(batch=16383, n_q=4, n_kv=4096, q_pos0=4092)) == tbs.INFV2_OK
+    assert _status(L, _prob(batch=16384, n_q=4, n_kv=4096, q_pos0=4092)) \
+        == tbs.INFV2_E_UNSUPPORTED
+    assert b"65535" in L.infv2_last_error()
+    assert _status(L, _prob(batch=65535, n_q=1, n_kv=4096, q_pos0=4095)) == tbs.INFV2_OK
+    assert _status(L, _prob(batch=65536, n_q=1, n_kv=4096, q_pos0=4095)) \
+        == tbs.INFV2_E_UNSUPPORTED
+    assert _status(L, _prob(batch=65536, n_q=1, n_kv=4096, q_pos0=4095, dtype="f32", G=4,
+                            d=64)) == tbs.INFV2_E_UNSUPPORTED
+
+
 def test_error_messages_are_per_thread(L):
     # each thread sees the message of its own last failing call, while the
     # other threads fail in other ways at the same time

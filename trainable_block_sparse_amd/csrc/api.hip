@@ -150,6 +150,11 @@ int check(const infv2_problem* pp) {
   if (p.lse_approx != 0 && p.lse_approx != 1) return fail(INFV2_E_ARG, "lse_approx must be 0 or 1");
   if (budget_of(p) < 1) return fail(INFV2_E_ARG, "N_init + N_local + k must be >= 1");
   if ((int64_t)p.G * p.h_kv > 4096) return fail(INFV2_E_ARG, "h_q too large");
+  // launch grids carry the batch (times up to 4 query tokens on the decode
+  // paths) in a dimension of at most 65535 workgroups
+  if ((int64_t)p.batch * std::min(p.n_q, 4) > 65535)
+    return fail(INFV2_E_UNSUPPORTED, "batch (%d) x min(n_q, 4) exceeds 65535: split the batch",
+                p.batch);
   // kernel instances
   if (!is_pow2(p.l_C1))
     return fail(INFV2_E_UNSUPPORTED, "l_C1 (%d) must be a power of two (exact mean)", p.l_C1);
