@@ -511,9 +511,28 @@ def bench_decode(cfg, steps, warmup, lse_approx=False):
 # CPU baseline: the fp64 oracle, as it stands, on a bounded sample
 # --------------------------------------------------------------------------
 
-def cpu_baseline(cfg, budget_s=15.0):
+_CPU = {}
+
+
+def _cpu_rows(rows):
+    """Worker: the oracle's selection, top-k and attention for some rows."""
     import oracle as orc
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
+    c = _CPU
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        orc.forward_rows(c["Q"], c["K"], c["V"], np.asarray(rows), c["op"], Kc1=c["Kc1"],
+                         mode="sparse")
+    return len(rows), time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, budget_s=15.0):
+    """The oracle as it stands (fp64 numpy), timed on the host's cores: one
+    worker process per usable core (at most 16), each with one BLAS thread,
+    over a stratified sample of query rows that takes about budget_s of wall
+    time; compress_k runs once over all keys.  Extrapolated to every row."""
+    import multiprocessing as mp
+    import oracle as orc
     x = make_inputs(cfg)
     op = orc.Problem(G=cfg.G, h_kv=cfg.h_kv, d=cfg.d, B=cfg.B, l_C1=cfg.l_C1, s_C1=cfg.s_C1,
                      l=cfg.l, s=cfg.s, k=cfg.k, N_init=cfg.N_init, N_local=cfg.N_local,
@@ -524,22 +543,48 @@ def cpu_baseline(cfg, budget_s=15.0):
     t0 = time.perf_counter()
     Kc1 = orc.compress_k(K[None], op)[0]
     t_comp = time.perf_counter() - t0
+    _CPU.update(Q=Q, K=K, V=V, Kc1=Kc1, op=op)
+    nproc = os.cpu_count() or 1
+    usable = len(os.sched_getaffinity(0))
+    workers = max(1, min(usable, 16))
+    # calibrate: the cost of a row grows with its position, so rows are
+    # stratified over the sequence (one per stratum, jittered)
+    n_cal = 16
     rng = np.random.default_rng(0)
-    rows_done, t_rows = 0, 0.0
-    while t_rows < budget_s and rows_done < cfg.n_q:
-        rows = np.sort(rng.choice(cfg.n_q, size=16, replace=False))
-        t1 = time.perf_counter()
-        orc.forward_rows(Q, K, V, rows, op, Kc1=Kc1, mode="sparse")
-        t_rows += time.perf_counter() - t1
-        rows_done += 16
-    per_row = t_rows / rows_done
-    total = t_comp + per_row * cfg.n_q * cfg.batch
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": cfg.batch * cfg.n_q / total, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": (f"{cfg.name}: compress_k over all {cfg.n_kv} keys ({t_comp:.1f} s) + "
-                       f"{rows_done} uniformly sampled query rows (selection, top-k, attention; "
-                       f"{t_rows:.1f} s), extrapolated to {cfg.batch * cfg.n_q} rows")}
+    cal = np.sort(rng.choice(cfg.n_q, size=n_cal, replace=False))
+    _, t_cal = _cpu_rows(cal)
+    per_row = t_cal / n_cal
+    n_rows = int(max(workers * 8, min(cfg.n_q, budget_s * workers / per_row)))
+    edges = np.linspace(0, cfg.n_q, n_rows + 1).astype(np.int64)
+    rows = np.unique(np.minimum(edges[:-1] + rng.integers(0, np.maximum(1, np.diff(edges))),
+                                cfg.n_q - 1))
+    chunks = [rows[i::workers * 4] for i in range(workers * 4)]
+    ctx = mp.get_context("fork")
+    t1 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        done = pool.map(_cpu_rows, chunks)
+    t_rows = time.perf_counter() - t1
+    rows_done = sum(n for n, _ in done)
+    total = t_comp + t_rows / rows_done * cfg.n_q * cfg.batch
+    return {"value": cfg.batch * cfg.n_q / total, "unit": "tokens/s", "cores": workers,
+            "kind": "oracle", "nproc": nproc, "usable_cpus": usable,
+            "sample": (f"{cfg.name}: compress_k over all {cfg.n_kv} keys ({t_comp:.1f} s, one "
+                       f"process) + {rows_done} query rows stratified over the sequence "
+                       f"(selection, top-k, attention) on {workers} worker processes with one "
+                       f"BLAS thread each ({t_rows:.1f} s wall), extrapolated to "
+                       f"{cfg.batch * cfg.n_q} rows; host nproc {nproc}")}
+
+
+def cpu_baseline_child():
+    """cpu_baseline run in a fresh child process (this process holds the
+    GPU; the child only uses the CPU)."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only"],
+                       capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        log("[bench] cpu baseline failed:", r.stderr[-2000:])
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 # the kernels one call of each prefill stage launches (rocprofv3 names)
@@ -569,6 +614,70 @@ def traffic_for(stage, workload):
     return total
 
 
+# the kernels one call of each decode stage launches
+DECODE_STAGE_KERNELS = {
+    "compress_append": ["compress_k_kernel"],
+    "select_blocks": ["scores_split_logits_kernel", "scores_split_pool_kernel",
+                      "scores_select_merge_kernel"],
+    "sparse_attn": ["attn_split_kernel", "attn_merge_kernel"],
+}
+
+
+def prefill_roofline(res, workload):
+    """Roofline object of the dominant stage of a prefill record: algorithmic
+    flops of that stage over its event-timed duration (one launch per kernel
+    per call) against the bf16 MFMA peak; traffic = the committed counter
+    bytes of the stage's launches when they were taken on the current
+    kernel sources, else null."""
+    stages = res["stages_ms"]
+    dom = max(stages, key=stages.get)
+    flops = {"block_scores": res.get("sel_flops_2pass"), "sparse_attn": res["attn_flops"]}.get(dom)
+    if flops is None:
+        return {"kernel": dom, "bound": "mfma", "achieved": None, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": None, "traffic": None}
+    ach = flops / (stages[dom] / 1e3) / 1e12
+    return {"kernel": dom, "launches": STAGE_KERNELS.get(dom, [dom]), "bound": "mfma",
+            "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic_for(dom, workload),
+            "per_launch_algorithmic": flops, "avg_launch_ms": stages[dom]}
+
+
+def decode_roofline(res, cfg, budget, workload="decode"):
+    """Roofline object of the decode step's dominant stage (HBM-bound):
+    algorithmic bytes of that stage (select_blocks: every visible K^C1 row
+    and Q; sparse_attn: the selected K/V blocks, Q and O) over its
+    event-timed duration against the HBM peak."""
+    st = res["stages_us_eager"]
+    dom = max(st, key=st.get)
+    L = cfg.n_kv
+    n_c1 = (L - cfg.l_C1) // cfg.s_C1 + 1
+    nsel = min((L - 1) // cfg.B + 1, budget)
+    qo = cfg.G * cfg.d * 2
+    per = {"select_blocks": n_c1 * cfg.d * 2 + qo,
+           "sparse_attn": nsel * cfg.B * cfg.d * 2 * 2 + 2 * qo,
+           "compress_append": cfg.l_C1 * cfg.d * 2 + cfg.d * 2}[dom]
+    nbytes = float(cfg.batch * cfg.h_kv * per)
+    ach = nbytes / (st[dom] / 1e6) / 1e9
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        tot = 0.0
+        for kern in DECODE_STAGE_KERNELS[dom]:
+            ent = tr.get(f"{workload}/{kern}")
+            if not ent or ent.get("source_hash") != kernel_source_hash(kern):
+                tot = None
+                break
+            tot += ent.get("bytes_per_launch", 0.0)
+        traffic = tot
+    except (OSError, ValueError):
+        pass
+    return {"kernel": dom, "launches": DECODE_STAGE_KERNELS[dom], "bound": "hbm",
+            "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+            "traffic": traffic, "per_launch_algorithmic": nbytes,
+            "avg_launch_us": st[dom]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -589,7 +698,12 @@ def main():
                     help="with --only: the LSE approximation instead of the exact LSE")
     ap.add_argument("--no-approx", action="store_true",
                     help="skip the LSE-approximation records")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="only the CPU oracle baseline (no GPU use); prints its JSON object")
     args = ap.parse_args()
+    if args.cpu_baseline_only:
+        print(json.dumps(cpu_baseline(CONFIGS["prefill32k"])), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU and has no multi-GPU path (the work would shard by "
               "KV group, batch or query range with the same kernels); run with --gpus 1",
@@ -637,35 +751,19 @@ def main():
     log(f"[bench] prefill32k: {main_res['ms_per_step']:.3f} ms/step, stages {main_res['stages_ms']}")
 
     # roofline of the dominant kernel
-    stages = main_res["stages_ms"]
-    dom = max(stages, key=stages.get)
-    pos = np.arange(cfg.n_kv)
-    if dom == "block_scores":
-        flops = main_res["sel_flops_2pass"]
-    elif dom == "sparse_attn":
-        flops = main_res["attn_flops"]
-    else:
-        flops = None
-    if flops is not None:
-        ach = flops / (stages[dom] / 1e3) / 1e12
-        roof = {"kernel": dom, "launches": STAGE_KERNELS.get(dom, [dom]), "bound": "mfma",
-                "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                "traffic": traffic_for(dom, "prefill32k"),
-                "per_launch_algorithmic": flops, "avg_launch_ms": stages[dom]}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": None, "traffic": traffic_for(dom, "prefill32k")}
+    roof = prefill_roofline(main_res, "prefill32k")
 
     extra = {}
     if not args.no_extra:
         c3 = CONFIGS["prefill128k"]
         r3 = bench_prefill(c3, max(2, args.steps // 5), 1, with_dense=not args.no_dense,
                            dense_steps=1, pipeline_chunk=0 if args.no_pipeline else 8192)
+        r3["roofline"] = prefill_roofline(r3, "prefill128k")
         extra["prefill128k"] = {k: v for k, v in r3.items()}
         log(f"[bench] prefill128k: {r3['ms_per_step']:.3f} ms/step")
         c4 = CONFIGS["decode"]
         r4 = bench_decode(c4, max(20, args.steps * 5), args.warmup)
+        r4["roofline"] = decode_roofline(r4, c4, 19)
         extra["decode"] = r4
         log(f"[bench] decode: {r4['step_us']:.1f} us/step")
         rv = bench_decode_varlen(c4, max(20, args.steps * 5), args.warmup)
@@ -694,8 +792,8 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        log("[bench] cpu baseline (oracle)")
-        cpu = cpu_baseline(cfg)
+        log("[bench] cpu baseline (oracle, child process)")
+        cpu = cpu_baseline_child()
 
     line = {
         "metric": METRIC,
@@ -720,14 +818,17 @@ def main():
         "speedup_vs_dense": main_res.get("speedup_vs_dense"),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "library": tbs.library_info(),
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
 
 
 def bench_dense_switch(cfg, steps, warmup):
-    """Short sequences: the switch selects dense attention; the sparse path is
-    timed beside it on the same input (they must agree)."""
+    """Short sequences: the switch selects dense attention.  The sparse path
+    (compress_k, block_scores, topk_select, sparse_attn, whose selection
+    then covers every causal block) is timed beside it on the same input,
+    and the two outputs are compared."""
     log(f"[bench] {cfg.name}: inputs")
     x = make_inputs(cfg)
     dev = torch.device("cuda:0")
@@ -743,9 +844,40 @@ def bench_dense_switch(cfg, steps, warmup):
     for _ in range(steps):
         t.step([lambda: tbs.dense_attn(lp, Q, K, V, O, lse, ws_d)])
     dense_ms = t.collect()["dense_attn"]
+    # the sparse path on the same input
+    n_blk, bud, n_c1 = tbs.n_blocks(lp), tbs.budget(lp), tbs.n_kernels(lp)
+    Kc1 = torch.empty((lp.batch, lp.h_kv, n_c1, lp.d), dtype=Q.dtype, device=dev)
+    S = torch.empty((lp.batch, lp.h_kv, lp.n_q, n_blk), dtype=torch.float32, device=dev)
+    idx = torch.empty((lp.batch, lp.h_kv, lp.n_q, bud), dtype=torch.int32, device=dev)
+    nsel = torch.empty((lp.batch, lp.h_kv, lp.n_q), dtype=torch.int32, device=dev)
+    Os = torch.empty_like(Q)
+    lses = torch.empty_like(lse)
+    ws_s = torch.empty(max(tbs.block_scores_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(tbs.sparse_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    fns = [lambda: tbs.compress_k(lp, K, Kc1),
+           lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s),
+           lambda: tbs.topk_select(lp, S, idx, nsel),
+           lambda: tbs.sparse_attn(lp, Q, K, V, idx, nsel, Os, lses, ws_a)]
+    names = ["compress_k", "block_scores", "topk_select", "sparse_attn"]
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    ts = StageTimer(names)
+    for _ in range(steps):
+        ts.step(fns)
+    sp_stages = ts.collect()
+    sparse_ms = sum(sp_stages.values())
+    diff = float((Os.float() - O.float()).abs().max().item())
     flops = attention_flops(cfg, np.arange(cfg.n_kv), 10 ** 9)
-    return {"dense_ms": dense_ms, "tokens_per_s": cfg.batch * cfg.n_q / (dense_ms / 1e3),
-            "algo_tflops": flops / (dense_ms / 1e3) / 1e12}
+    out = {"dense_ms": dense_ms, "tokens_per_s": cfg.batch * cfg.n_q / (dense_ms / 1e3),
+           "algo_tflops": flops / (dense_ms / 1e3) / 1e12,
+           "sparse_ms": sparse_ms, "sparse_stages_ms": sp_stages,
+           "sparse_over_dense": sparse_ms / dense_ms,
+           "sparse_attn_over_dense_attn": sp_stages["sparse_attn"] / dense_ms,
+           "sparse_vs_dense_max_abs_O": diff}
+    del Q, K, V, O, Os, S, Kc1
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

@@ -192,8 +192,13 @@ int infv2_sparse_attn(const infv2_problem* prob, const void* Q, const void* K,
                       const void* V, const int32_t* idx, const int32_t* n_sel,
                       void* O, float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* Dense causal attention (the fallback of the switch, and the baseline):
- * the same as infv2_sparse_attn with T(p) = {0..p}.  Layouts as above;
+/* Dense causal attention, the dense branch of the dense-sparse switch
+ * (papernotes.org InfLLM-V2 note, 方法详解 > 整体框架 flowchart: short inputs take
+ * ordinary dense attention; OpenBMB blog "技术Blog-4 | 新一代InfLLM：可训练的稀疏
+ * 注意力机制", 动态上下文块选择 > 语义核: when the sequence fits in the selected
+ * blocks the sparse attention degenerates to dense), and the baseline it is
+ * timed against.  The same as infv2_sparse_attn with T(p) = {0..p}: every
+ * causal key.  Layouts, ownership and errors as above;
  * ws: workspace of infv2_dense_attn_workspace(prob) bytes. */
 size_t infv2_dense_attn_workspace(const infv2_problem* prob);
 int infv2_dense_attn(const infv2_problem* prob, const void* Q, const void* K,
@@ -286,6 +291,12 @@ int infv2_sparse_attn_varlen(const infv2_problem* prob, const void* Q, const voi
 
 const char* infv2_status_string(int status);
 const char* infv2_last_error(void);
+
+/* Identity of this build: the first 16 hex digits of the SHA-256 of the
+ * library's source files (csrc/ and this header), fixed when the library was
+ * compiled.  A caller compares it with the sources it holds to know that the
+ * loaded library was built from them.  Static string, never NULL. */
+const char* infv2_build_id(void);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ def _prob(**kw):
                                 dict(n_kv=1000, n_q=1000, kv_cap=1500, c1_cap=99, c2_cap=20)])
 def test_extents_follow_the_library(kw):
     p = _prob(**kw)
-    e = tbs._Ext(p)
+    e = p._ext()
     assert e.n_c1 == tbs.n_kernels(p)
     assert e.n_blk == tbs.n_blocks(p)
     assert e.budget == tbs.budget(p)
@@ -54,7 +54,7 @@ def test_arg_checks_in_order():
 
 def test_wrappers_refuse_host_tensors_before_any_launch():
     p = _prob()
-    e = tbs._Ext(p)
+    e = p._ext()
     Q = torch.zeros(e.q, dtype=torch.bfloat16).view(p.batch, p.n_q, p.h_q, p.d)
     K = torch.zeros(e.kv, dtype=torch.bfloat16).view(p.batch, p.n_kv, p.h_kv, p.d)
     idx = torch.zeros(e.rows * e.budget, dtype=torch.int32)
@@ -71,7 +71,7 @@ def test_wrappers_refuse_host_tensors_before_any_launch():
 
 def test_paged_pool_shape_is_checked():
     p = _prob(batch=2, n_q=1, n_kv=4096, q_pos0=4095)
-    e = tbs._Ext(p)
+    e = p._ext()
     pool = torch.zeros(10, 32, p.h_kv, p.d, dtype=torch.bfloat16)     # pages of 32 rows, B = 64
     table = torch.zeros(2, 64, dtype=torch.int32)
     with pytest.raises(ValueError, match="pool"):

@@ -15,7 +15,9 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libinfv2.so")
+# INFV2_LIB names another build of the same library (the host-ASan build of
+# the CPU tests); by default the package's own libinfv2.so.
+LIB_PATH = os.environ.get("INFV2_LIB") or os.path.join(_PKG, "libinfv2.so")
 
 INFV2_OK, INFV2_E_ARG, INFV2_E_UNSUPPORTED, INFV2_E_WORKSPACE, INFV2_E_HIP = 0, -1, -2, -3, -4
 INFV2_BF16, INFV2_F32 = 0, 1
@@ -31,7 +33,7 @@ EXPORTED = (
     "infv2_compress_k_varlen", "infv2_select_blocks_varlen_workspace",
     "infv2_select_blocks_varlen", "infv2_sparse_attn_varlen_workspace",
     "infv2_sparse_attn_varlen",
-    "infv2_status_string", "infv2_last_error",
+    "infv2_status_string", "infv2_last_error", "infv2_build_id",
 )
 
 
@@ -91,7 +93,8 @@ class Problem:
     def _c(self) -> _Problem:
         c = self.__dict__.get("_cached")
         if c is None:
-            c = self.__dict__["_cached"] = (self.to_c(), _Ext(self))
+            cs = self.to_c()
+            c = self.__dict__["_cached"] = (cs, _Ext(self, cs))
         return c[0]
 
     def _ext(self) -> "_Ext":
@@ -146,12 +149,28 @@ def lib() -> ctypes.CDLL:
                                          + [sz, vp]),
             "infv2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "infv2_last_error": (ctypes.c_char_p, []),
+            "infv2_build_id": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
             fn.restype, fn.argtypes = res, args
         _lib = L
     return _lib
+
+
+def build_id() -> str:
+    """Source hash the loaded library was compiled from (infv2_build_id)."""
+    return lib().infv2_build_id().decode()
+
+
+def library_info() -> dict:
+    """The loaded library's path and build id, and whether that id is the
+    hash of the library sources in this tree (the library is current)."""
+    from .build import source_hash
+    cur = source_hash()
+    bid = build_id()
+    return {"path": os.path.relpath(LIB_PATH, os.path.dirname(_PKG)), "build_id": bid,
+            "source_hash": cur, "built_from_these_sources": bid == cur}
 
 
 def _check(status: int) -> None:
@@ -165,13 +184,15 @@ class _Ext:
     __slots__ = ("io", "q", "kv", "kc1", "kc2", "n_c1", "n_c2", "n_blk", "rows", "budget",
                  "lse", "kv_rows")
 
-    def __init__(self, prob: "Problem"):
+    def __init__(self, prob: "Problem", c: _Problem):
+        # the sizes come from the library's own helpers (one copy of the rules)
         self.io = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
-        n_kv, l1, s1 = prob.n_kv, prob.l_C1, prob.s_C1
-        self.n_c1 = 0 if n_kv < l1 else (n_kv - l1) // s1 + 1
-        self.n_c2 = n_c2 = 0 if n_kv < 4 * l1 else (n_kv - 4 * l1) // (4 * s1) + 1
-        self.n_blk = -(-n_kv // prob.B) if prob.B > 0 else 0
-        self.budget = prob.N_init + prob.N_local + prob.k
+        L, ref = lib(), ctypes.byref(c)
+        n_kv = prob.n_kv
+        self.n_c1 = max(L.infv2_n_kernels(ref), 0)
+        self.n_c2 = n_c2 = max(L.infv2_n_coarse_kernels(ref), 0)
+        self.n_blk = max(L.infv2_n_blocks(ref), 0)
+        self.budget = max(L.infv2_budget(ref), 0)
         h_q = prob.G * prob.h_kv
         self.kv_rows = prob.kv_cap or n_kv
         self.q = prob.batch * prob.n_q * h_q * prob.d

@@ -87,16 +87,20 @@ int hip_status(hipError_t e, const char* what) {
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// The size helpers return 0 for a problem whose strides are not positive
+// (check() rejects such a problem; the helpers only must not divide by zero).
 int n_c1_of(const infv2_problem& p) {
+  if (p.s_C1 <= 0 || p.l_C1 <= 0) return 0;
   return p.n_kv < p.l_C1 ? 0 : (p.n_kv - p.l_C1) / p.s_C1 + 1;
 }
 // coarse kernels of the LSE approximation: l_C2 = 4 l_C1, s_C2 = 4 s_C1
 int l_c2_of(const infv2_problem& p) { return 4 * p.l_C1; }
 int s_c2_of(const infv2_problem& p) { return 4 * p.s_C1; }
 int n_c2_of(const infv2_problem& p) {
+  if (p.s_C1 <= 0 || p.l_C1 <= 0) return 0;
   return p.n_kv < l_c2_of(p) ? 0 : (p.n_kv - l_c2_of(p)) / s_c2_of(p) + 1;
 }
-int n_blk_of(const infv2_problem& p) { return (p.n_kv + p.B - 1) / p.B; }
+int n_blk_of(const infv2_problem& p) { return p.B <= 0 ? 0 : (p.n_kv + p.B - 1) / p.B; }
 int budget_of(const infv2_problem& p) { return p.N_init + p.N_local + p.k; }
 int64_t kv_cap_of(const infv2_problem& p) { return p.kv_cap ? p.kv_cap : p.n_kv; }
 int64_t c1_cap_of(const infv2_problem& p) { return p.c1_cap ? p.c1_cap : n_c1_of(p); }
@@ -530,5 +534,10 @@ const char* infv2_status_string(int status) {
 }
 
 const char* infv2_last_error(void) { return g_last_error.c_str(); }
+
+#ifndef INFV2_SOURCE_HASH
+#define INFV2_SOURCE_HASH "unknown"
+#endif
+const char* infv2_build_id(void) { return INFV2_SOURCE_HASH; }
 
 }  // extern "C"

@@ -15,8 +15,9 @@
 //    2^(z*c - M) with M the exact row maximum of the first chunk (an extra
 //    maximum sweep runs only if a later logit overflows that reference); the
 //    second forms S^C1, sums the 16 heads (8 in-lane + one cross-half
-//    exchange), max-pools into blocks and writes S^cmp.  Neither S^C1 nor
-//    S^shared is written to memory.
+//    exchange), max-pools into blocks and writes S^cmp.  S^C1 is never
+//    written to memory; S^shared is written only by the SHARED instance,
+//    when the caller passes a buffer for it.
 //  * scores_split_{logits,pool}_kernel -- few query tokens (decode): the kernel
 //    axis is split over workgroups; the first writes scaled logits and
 //    per-chunk (max, sum) partials, the second merges the partials into the
