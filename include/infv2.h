@@ -13,8 +13,9 @@
  *    row-major and contiguous with the layouts stated per call; every device
  *    pointer must be 16-byte aligned.
  *  - The caller owns and frees every buffer, workspaces included.  The
- *    library keeps no state besides a thread-local error string: it never
- *    allocates, never synchronises and never writes an input.
+ *    library keeps no state besides a thread-local error string (and, for
+ *    infv2_sparse_attn_noalloc alone, one static scratch array per GPU): it
+ *    never allocates, never synchronises and never writes an input.
  *  - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *    the default stream).  Calls return once the work is enqueued.
  *  - Return value: INFV2_OK, or a negative status; infv2_last_error() then
@@ -291,6 +292,27 @@ int infv2_sparse_attn_varlen(const infv2_problem* prob, const void* Q, const voi
 
 const char* infv2_status_string(int status);
 const char* infv2_last_error(void);
+
+/* infv2_sparse_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and outputs, bit for bit, but
+ * its workspace is a static device array of INFV2_NOALLOC_SCRATCH_BYTES
+ * inside the library (one copy per GPU, held until the process ends) instead
+ * of a caller buffer.  It calls no hipMalloc / hipFree and nothing that
+ * allocates.  The caller still passes every input and output, as for
+ * infv2_sparse_attn.
+ *  - A problem whose infv2_sparse_attn_workspace(prob) exceeds the scratch
+ *    is refused with INFV2_E_WORKSPACE before anything is enqueued.
+ *  - The scratch's address is looked up once per GPU, on the first call
+ *    with that GPU current; `stream` must belong to the current GPU
+ *    (INFV2_E_ARG otherwise), and a failed lookup returns INFV2_E_HIP.
+ *  - All calls on one GPU share its scratch and no call clears it (the
+ *    kernels write every byte they read).  Calls that can overlap on one
+ *    GPU (other streams, other threads) race on it: serialise them. */
+#define INFV2_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int infv2_sparse_attn_noalloc(const infv2_problem* prob, const void* Q, const void* K,
+                              const void* V, const int32_t* idx, const int32_t* n_sel,
+                              void* O, float* lse, void* stream);
 
 /* Identity of this build: the first 16 hex digits of the SHA-256 of the
  * library's source files (csrc/ and this header), fixed when the library was

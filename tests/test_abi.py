@@ -222,3 +222,25 @@ def test_error_messages_are_per_thread(L):
     for t in threads:
         t.join()
     assert out == {i: "ok" for i in range(4)}, out
+
+
+def test_noalloc_refuses_problems_past_its_scratch(L):
+    # the size check comes before any device call: a problem whose workspace
+    # exceeds the static scratch is refused, with the sizes in the message
+    p = _prob(n_kv=131072, n_q=131072)
+    assert tbs.sparse_attn_workspace(p) > tbs.NOALLOC_SCRATCH_BYTES
+    one = ctypes.c_void_p(256)
+    st = L.infv2_sparse_attn_noalloc(ctypes.byref(p.to_c()), one, one, one, one, one, one, None,
+                                     None)
+    assert st == tbs.INFV2_E_WORKSPACE
+    assert "static scratch" in L.infv2_last_error().decode()
+    st = L.infv2_sparse_attn_noalloc(ctypes.byref(p.to_c()), None, one, one, one, one, one, None,
+                                     None)
+    assert st == tbs.INFV2_E_ARG
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define INFV2_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "INFV2_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == tbs.NOALLOC_SCRATCH_BYTES

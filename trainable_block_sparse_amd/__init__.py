@@ -33,8 +33,11 @@ EXPORTED = (
     "infv2_compress_k_varlen", "infv2_select_blocks_varlen_workspace",
     "infv2_select_blocks_varlen", "infv2_sparse_attn_varlen_workspace",
     "infv2_sparse_attn_varlen",
+    "infv2_sparse_attn_noalloc",
     "infv2_status_string", "infv2_last_error", "infv2_build_id",
 )
+# static scratch of infv2_sparse_attn_noalloc (INFV2_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class _Problem(ctypes.Structure):
@@ -135,6 +138,7 @@ def lib() -> ctypes.CDLL:
             "infv2_select_blocks": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_sparse_attn_workspace": (sz, [P]),
             "infv2_sparse_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "infv2_sparse_attn_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
             "infv2_dense_attn_workspace": (sz, [P]),
             "infv2_dense_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_sparse_attn_bwd_workspace": (sz, [P]),
@@ -404,6 +408,21 @@ def sparse_attn(prob: Problem, Q, K, V, idx, n_sel, O=None, lse=None, ws=None,
                                    _arg(O, "O", e.io, e.q),
                                    _arg(lse, "lse", torch.float32, e.lse, optional=True),
                                    ws_p, ws_n, _stream(stream)))
+    return O, lse
+
+
+def sparse_attn_noalloc(prob: Problem, Q, K, V, idx, n_sel, O, lse=None, stream=None):
+    """sparse_attn with the library's static per-GPU scratch as its workspace
+    (infv2_sparse_attn_noalloc): nothing is allocated, O (and lse, optional)
+    are the caller's.  Calls that overlap on one GPU race on the scratch."""
+    e = prob._ext()
+    _check(lib().infv2_sparse_attn_noalloc(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                           _arg(K, "K", e.io, e.kv), _arg(V, "V", e.io, e.kv),
+                                           _arg(idx, "idx", torch.int32, e.rows * e.budget),
+                                           _arg(n_sel, "n_sel", torch.int32, e.rows),
+                                           _arg(O, "O", e.io, e.q),
+                                           _arg(lse, "lse", torch.float32, e.lse, optional=True),
+                                           _stream(stream)))
     return O, lse
 
 

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.hpp"
@@ -339,6 +340,71 @@ int infv2_sparse_attn(const infv2_problem* p, const void* Q, const void* K, cons
   return hip_status(launch_attn(*p, Q, K, V, idx, n_sel, O, lse, ws, budget_of(*p), kv_cap_of(*p),
                                 scale_of(*p), (hipStream_t)stream),
                     "infv2_sparse_attn");
+}
+
+// Workspace of infv2_sparse_attn_noalloc: one copy on every GPU the library
+// runs on.  Host code never uses this name as an address: the per-device
+// address from hipGetSymbolAddress is what kernels receive.
+static __device__ __align__(256) unsigned char scratch[INFV2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// Address of this GPU's scratch; looked up once per device, with the device
+// current.  The stream must belong to the current device.
+int scratch_of(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(INFV2_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(INFV2_E_UNSUPPORTED, "device %d is past the %d the scratch table holds", dev,
+                kMaxDevices);
+  if (stream != nullptr) {
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(INFV2_E_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(INFV2_E_ARG, "stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(INFV2_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return INFV2_OK;
+}
+}  // namespace
+
+int infv2_sparse_attn_noalloc(const infv2_problem* p, const void* Q, const void* K,
+                              const void* V, const int32_t* idx, const int32_t* n_sel, void* O,
+                              float* lse, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(Q);
+  CHECK_PTR(K);
+  CHECK_PTR(V);
+  CHECK_PTR(idx);
+  CHECK_PTR(n_sel);
+  CHECK_PTR(O);
+  if (lse && !aligned16(lse)) return fail(INFV2_E_ARG, "lse is not 16-byte aligned");
+  const size_t need = attn_workspace(*p, budget_of(*p), true);
+  if (need > INFV2_NOALLOC_SCRATCH_BYTES)
+    return fail(INFV2_E_WORKSPACE,
+                "sparse_attn_noalloc: this problem needs %zu bytes of workspace, more than the "
+                "%zu-byte static scratch",
+                need, (size_t)INFV2_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need && (st = scratch_of((hipStream_t)stream, &ws))) return st;
+  return hip_status(launch_attn(*p, Q, K, V, idx, n_sel, O, lse, ws, budget_of(*p), kv_cap_of(*p),
+                                scale_of(*p), (hipStream_t)stream),
+                    "infv2_sparse_attn_noalloc");
 }
 
 size_t infv2_dense_attn_workspace(const infv2_problem* p) {
