@@ -244,3 +244,33 @@ def test_k_zero_selects_init_and_local_blocks_only():
             assert res["idx"][b, g, 0, :n].tolist() == [0, b_p - 1, b_p]
     rep = check_rows(res, x, op, n_kv - 1, {b: np.array([0]) for b in range(batch)})
     _say(rep)
+
+
+# From 1024 key blocks (65536 keys) on, the sparse prefill attention splits
+# the keys into ranges of 128 blocks (8192 keys): a token whose blocks span
+# several ranges is attended range by range and its partial results merged.
+# These sizes span nine ranges; the rows sampled include the range edges and
+# a tile that straddles one.
+RANGE_EDGE_ROWS = (0, 63, 64, 8127, 8190, 8191, 8192, 8193, 8255, 8256, 16383, 16384, 16447,
+                   40959, 40960, 65535, 65536, 65537)
+
+
+@pytest.mark.parametrize("n_kv,batch,q0", [
+    (70000, 1, 0),         # nine ranges
+    (66000, 2, 0),         # two sequences
+    (70000, 1, 60005),     # a query offset that is not a multiple of the tile
+])
+def test_bf16_sparse_prefill_key_ranges(n_kv, batch, q0):
+    cfg = CONFIGS["prefill32k"]
+    _say(f"case: key ranges n_kv={n_kv} batch={batch} q0={q0}")
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=31 + n_kv + q0)
+    xq = dict(x)
+    xq["q"] = x["q"][:, q0:].contiguous()
+    lp, op = problems(cfg, n_kv=n_kv, batch=batch, n_q=n_kv - q0, q_pos0=q0)
+    res = run_gpu_sparse(lp, xq["q"], x["k"], x["v"])
+    rng = np.random.default_rng(n_kv + batch)
+    n_q = n_kv - q0
+    must = tuple(t - q0 for t in RANGE_EDGE_ROWS) + (n_q - 1, n_q - 64)
+    rows = {b: sample_rows(n_q, 30, rng, must=must) for b in range(batch)}
+    rep = check_rows(res, xq, op, q0, rows)
+    _say(rep)

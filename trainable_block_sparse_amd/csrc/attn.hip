@@ -25,6 +25,8 @@
 //    sequence's positions come from a device array of lengths, and with a
 //    paged cache each selected block is read from its page (page = block).
 // A generic fp64 kernel serves fp32 I/O and other shapes.
+#include <algorithm>
+
 #include "attn_layout.hpp"
 
 namespace infv2 {
@@ -325,6 +327,378 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
   if (a.lse && grp == 0)
     __builtin_nontemporal_store((m_run + fast_log2(l_run)) * kLn2,
                                 a.lse + ((size_t)b * hq + g * AT_G + r16) * a.n_q + t);
+}
+
+// ---------------------------------------------------------------------------
+// Key-range split of the sparse prefill attention.
+//
+// With per-token selections spread over the whole causal prefix, a
+// token-major gather re-reads K/V blocks from wherever they happen to live:
+// at 131072 keys the packs of one group (64 MB) are 16x one XCD's L2, and
+// every L2 miss is served at ~7 TB/s whether or not the data sits in the
+// Infinity Cache.  Here the keys are split into ranges of W blocks (W = 128:
+// 4 MB of packs per group, one XCD's L2) and a work item is (sequence, group,
+// range r, tile of query tokens): it attends each token of the tile to its
+// selected blocks inside range r only.  Work items are numbered range by
+// range and every XCD takes a contiguous stretch of the numbering, so an XCD
+// works through one range at a time and its gathers hit L2.
+//
+// A token whose blocks all lie in one range gets its output here; any other
+// token leaves one partial per range it touches -- the running maximum m and
+// sum l of every head (log2 domain, as in attn_softmax) and O/l rounded to
+// bf16 -- in slot (rank of r among the token's ranges), and
+// attn_range_merge_kernel combines them:
+//   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  O = sum_s (l_s 2^(m_s - M) / L) O_s.
+// (The one extra bf16 rounding of each partial adds at most 2^-8 of that
+// partial's magnitude, a convex combination of V rows, before the final
+// rounding of O.)
+//
+// Per wave: TPW consecutive query tokens.  Their block lists (ascending) are
+// read once; the entries inside range r form one contiguous run per token,
+// found with ballots, and all (token, block) pairs of the wave are listed in
+// LDS so that the loads run two pairs ahead across token boundaries, as in
+// attn_prefill_kernel.  Q of the next token is loaded while the current one
+// is computed.
+// ---------------------------------------------------------------------------
+constexpr int RG_WAVES = 4;
+constexpr int RG_MAX_TPW = 4;             // tokens per wave (at most)
+constexpr int RG_MAX_LIST = 64;           // block-list entries per token (budget)
+constexpr int RG_PART_O_BYTES = AT_G * AT_D * 2;   // bf16 O of one (token, range)
+constexpr int RG_PART_ML_BYTES = AT_G * 8;         // (m, l) per head
+
+struct RangeArgs {
+  AttnArgs a;
+  u32x4* part_o;          // [rows][max_slots][4][64 lanes] x 16 B (bf16 O)
+  float2* part_ml;        // [rows][max_slots][16]
+  int W;                  // blocks per key range
+  int tpw;                // tokens per wave
+  int t_base, n_ct;       // first query token of this chunk, tokens in the chunk
+  int n_qt;               // query tiles (RG_WAVES * tpw tokens) in the chunk
+  int items_bg;           // work items per (sequence, group)
+  int segment;            // work items per XCD
+  int max_slots;          // partial slots per row
+};
+
+// First tile (within the chunk) whose last token reaches block r*W.
+__device__ __host__ inline int rg_first_tile(int r, int W, int pos_base, int tile) {
+  const int need = r * W * AT_B - pos_base - (tile - 1);
+  return need <= 0 ? 0 : (need + tile - 1) / tile;
+}
+
+// Buffer descriptor over `bytes` bytes from `base` (raw, dword data): loads
+// take their block offset in a scalar register and the lane's 16-byte offset
+// in one vector register, and read 0 past `bytes`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pack_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+}
+
+// Two workgroups per CU (two waves per SIMD, one block of K/V in registers
+// per wave).
+__global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
+  const AttnArgs& a = ra.a;
+  // Q fragments of the wave's tokens (the 4 k-steps of one token are 4 KB in
+  // lane order) and the wave's (token << 16 | block) pairs
+  __shared__ u32x4 qlds[RG_WAVES][RG_MAX_TPW][4][64];
+  __shared__ int prs[RG_WAVES][RG_MAX_TPW * RG_MAX_LIST];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int item = (blockIdx.x & 7) * ra.segment + (blockIdx.x >> 3);
+  if (item >= ra.items_bg * a.batch * a.h_kv) return;
+  const int bg = item / ra.items_bg;
+  int rem = item % ra.items_bg;
+  const int tile = RG_WAVES * ra.tpw;
+  const int pos_base = a.q_pos0 + ra.t_base;
+  int r = 0, qt = 0;
+  for (;; ++r) {
+    const int first = rg_first_tile(r, ra.W, pos_base, tile);
+    const int cnt = max(0, ra.n_qt - first);
+    if (rem < cnt) {
+      qt = first + rem;
+      break;
+    }
+    rem -= cnt;
+  }
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int hq = a.h_kv * AT_G;
+  const int tc0 = qt * tile + wave * ra.tpw;          // first chunk token of this wave
+  // --- the wave's block lists: lane u holds entry u of token j in e[j]
+  // (the list and its length are loaded together; entries past n_sel are
+  // masked by the length below)
+  int nsel_l = 0;
+  if (lane < ra.tpw && tc0 + lane < ra.n_ct) {
+    const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + ra.t_base + tc0 + lane;
+    nsel_l = min(a.n_sel[row], a.budget);
+  }
+  int e[RG_MAX_TPW];
+#pragma unroll
+  for (int j = 0; j < RG_MAX_TPW; ++j) {
+    e[j] = -1;
+    if (j < ra.tpw && tc0 + j < ra.n_ct && lane < a.budget) {
+      const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + ra.t_base + tc0 + j;
+      e[j] = a.idx[row * a.budget + lane];
+    }
+  }
+  // --- per token: the run inside range r, its slot, the token's range count;
+  // Q of every token with a run goes to LDS
+  int slot_l = 0, nparts_l = 0;                       // lane j holds token j's values
+  int total = 0;
+#pragma unroll
+  for (int j = 0; j < RG_MAX_TPW; ++j) {
+    if (j >= ra.tpw) break;
+    const int nsj = __builtin_amdgcn_readlane(nsel_l, j);
+    const int p = pos_base + tc0 + j;
+    const int b_p = p / AT_B;
+    const bool ok = lane < nsj && e[j] >= 0 && e[j] <= b_p;
+    const int rg = ok ? e[j] / ra.W : 0x7fffffff;
+    const int prev = __shfl_up(rg, 1, 64);
+    const bool first = ok && (lane == 0 || rg != prev);
+    const int s = __builtin_popcountll(__ballot(rg < r));
+    const int c = __builtin_popcountll(__ballot(rg == r));
+    const int sl = __builtin_popcountll(__ballot(first && rg < r));
+    const int np = __builtin_popcountll(__ballot(first));
+    if (lane == j) {
+      slot_l = sl;
+      nparts_l = np;
+    }
+    // pairs of token j: (j << 16) | block, blocks of the run in order (a
+    // list that breaks the ascending-causal contract still reads blocks
+    // within 0..b_p only)
+    const int blk = __shfl(e[j], min(s + lane, 63), 64);
+    if (lane < c) prs[wave][total + lane] = (j << 16) | min(max(blk, 0), b_p);
+    total += c;
+    if (c > 0) {
+      const uint16_t* q = a.Q + (((size_t)b * a.n_q + ra.t_base + tc0 + j) * hq + g * AT_G +
+                                 (lane & 15)) * AT_D;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qlds[wave][j][ks][lane] =
+            __builtin_nontemporal_load((const u32x4*)(q + 32 * ks + 8 * (lane >> 4)));
+    }
+  }
+  if (total == 0) return;                             // (no barrier below)
+  const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS;
+  const uint32_t pack_bytes = (uint32_t)a.n_blk * PACK_ELEMS * 2;
+  const __amdgpu_buffer_rsrc_t rk = pack_rsrc(a.Kp + pack0, pack_bytes);
+  const __amdgpu_buffer_rsrc_t rv = pack_rsrc(a.Vp + pack0, pack_bytes);
+  const int lane_off = lane * 16;
+  const int grp = lane >> 4, r16 = lane & 15;
+  // fragment f of block blk: 1 KB at blk * 16 KB + f * 1 KB, lane l's 16 B at l * 16
+  auto load_k = [&](int blk, bf16x8 (&kf)[4][4]) {
+    const int so = blk * (PACK_ELEMS * 2);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kf[tt][ks] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, so + (4 * tt + ks) * 1024, 0));
+  };
+  auto load_v = [&](int blk, bf16x8 (&vf)[8][2]) {
+    const int so = blk * (PACK_ELEMS * 2);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        vf[mt][ks] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, so + (2 * mt + ks) * 1024, 0));
+  };
+  // the pair list, 64 entries per lane register at a time (reading the next
+  // pair is a lane read; the list is re-read from LDS every 64 pairs)
+  int pbase = 0;
+  int preg = prs[wave][min(lane, total - 1)];
+  auto pair_at = [&](int i) -> int {
+    i = min(i, total - 1);
+    if (i >= pbase + 64) {
+      pbase = i & ~63;
+      preg = prs[wave][min(pbase + lane, total - 1)];
+    }
+    return __builtin_amdgcn_readlane(preg, i - pbase);
+  };
+  bf16x8 qc[4];
+  auto load_q = [&](int j) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qc[ks] = as_bf16x8(qlds[wave][j][ks][lane]);
+  };
+  f32x4 o[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+  int cur = pair_at(0);
+  int tok = cur >> 16;
+  int p_tok = pos_base + tc0 + tok;
+  int bp_tok = p_tok / AT_B;
+  load_q(tok);
+  // finish the current token: its output (one range) or its partial
+  auto finish = [&]() {
+    float l = l_run;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / l;
+    const int tq = ra.t_base + tc0 + tok;
+    const int np = __builtin_amdgcn_readlane(nparts_l, tok);
+    if (np <= 1) {
+      uint16_t* orow = a.O + (((size_t)b * a.n_q + tq) * hq + g * AT_G + r16) * AT_D;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const uint32_t w0 = pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv);
+        __builtin_nontemporal_store(u32x2{w0, w1}, (u32x2*)(orow + 16 * mt + 4 * grp));
+      }
+      if (a.lse && grp == 0)
+        __builtin_nontemporal_store((m_run + fast_log2(l)) * kLn2,
+                                    a.lse + ((size_t)b * hq + g * AT_G + r16) * a.n_q + tq);
+    } else {
+      const int slot = __builtin_amdgcn_readlane(slot_l, tok);
+      const size_t prow = (((size_t)b * a.h_kv + g) * ra.n_ct + tc0 + tok) * ra.max_slots + slot;
+      // piece q of the lane: features 16 mt + 4 grp + i for mt = 2q, 2q + 1
+      u32x4* dst = ra.part_o + prow * 256 + lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m0 = 2 * q, m1 = 2 * q + 1;
+        __builtin_nontemporal_store(
+            u32x4{pack_bf16x2(o[m0][0] * inv, o[m0][1] * inv), pack_bf16x2(o[m0][2] * inv, o[m0][3] * inv),
+                  pack_bf16x2(o[m1][0] * inv, o[m1][1] * inv), pack_bf16x2(o[m1][2] * inv, o[m1][3] * inv)},
+            dst + 64 * q);
+      }
+      if (grp == 0)
+        __builtin_nontemporal_store(f32x2{m_run, l}, (f32x2*)(ra.part_ml + prow * AT_G + r16));
+    }
+  };
+  bf16x8 kf[4][4], vf[8][2], pf[2];
+  load_k(cur & 0xffff, kf);
+  load_v(cur & 0xffff, vf);
+  for (int i = 0; i < total; ++i) {
+    const bool last = i + 1 >= total;
+    const int nx = pair_at(i + 1);
+    const int blk = cur & 0xffff;
+    const int kv0 = blk * AT_B;
+    // scores S^T = K Q^T; each tile's K fragments are refilled with the next
+    // pair's as soon as its MFMAs have issued, and each V fragment after the
+    // PV MFMAs that read it, so the loads have about a whole pair to land
+    const int so_nx = (nx & 0xffff) * (PACK_ELEMS * 2);
+    f32x4 sc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sc[t] = mfma16(kf[t][ks], qc[ks], sc[t]);
+      if (!last) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          kf[t][ks] = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, so_nx + (4 * t + ks) * 1024, 0));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (blk == bp_tok)
+      attn_softmax<true>(sc, o, m_run, l_run, kv0, p_tok, a.c, lane, pf);
+    else
+      attn_softmax<false>(sc, o, m_run, l_run, kv0, p_tok, a.c, lane, pf);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) o[mt] = mfma16(vf[mt][ks], pf[ks], o[mt]);
+      if (!last) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          vf[mt][ks] = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, so_nx + (2 * mt + ks) * 1024, 0));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (last || (nx >> 16) != tok) {
+      finish();
+      if (!last) {
+        tok = nx >> 16;
+        p_tok = pos_base + tc0 + tok;
+        bp_tok = p_tok / AT_B;
+        load_q(tok);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = kNegInf;
+        l_run = 0.f;
+      }
+    }
+    cur = nx;
+  }
+}
+
+// Merge of the range partials of one (token, group) row: one wave per row,
+// four rows per workgroup.  The row's range count comes from its block list
+// (as in attn_range_kernel); rows with one range were written there.
+__global__ void __launch_bounds__(256) attn_range_merge_kernel(RangeArgs ra) {
+  const AttnArgs& a = ra.a;
+  const int lane = threadIdx.x & 63;
+  const int rix = blockIdx.x * 4 + (threadIdx.x >> 6);     // row in the chunk
+  const int rows = a.batch * a.h_kv * ra.n_ct;
+  if (rix >= rows) return;
+  const int tc = rix % ra.n_ct, bg = rix / ra.n_ct;
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int tq = ra.t_base + tc;
+  const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + tq;
+  const int nsel = min(a.n_sel[row], a.budget);
+  const int p = a.q_pos0 + tq;
+  const int b_p = p / AT_B;
+  const int ev = lane < nsel ? a.idx[row * a.budget + lane] : -1;
+  const bool ok = lane < nsel && ev >= 0 && ev <= b_p;
+  const int rg = ok ? ev / ra.W : 0x7fffffff;
+  const int prev = __shfl_up(rg, 1, 64);
+  const int np = __builtin_popcountll(__ballot(ok && (lane == 0 || rg != prev)));
+  if (np <= 1) return;
+  const int nparts = min(np, ra.max_slots);
+  const size_t prow = ((size_t)bg * ra.n_ct + tc) * ra.max_slots;
+  const int r16 = lane & 15, grp = lane >> 4;
+  // one pass, four slots at a time, with the running maximum
+  float M = kNegInf, L = 0.f;
+  float acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < nparts; s0 += 4) {
+    u32x4 ov[4][4];
+    float2 mlv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = min(s0 + u, nparts - 1);
+      mlv[u] = ra.part_ml[(prow + s) * AT_G + r16];
+      const u32x4* src = ra.part_o + (prow + s) * 256 + lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ov[u][q] = __builtin_nontemporal_load(src + 64 * q);
+    }
+    float mx = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + u < nparts) mx = fmaxf(mx, mlv[u].x);
+    const float wo = fast_exp2(M - mx);               // M = -inf gives 0
+    L *= wo;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] *= wo;
+    M = mx;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s0 + u >= nparts) break;
+      const float wgt = mlv[u].y * fast_exp2(mlv[u].x - M);
+      L += wgt;
+      // piece q word c: features 16 mt + 4 grp + {2(c&1), +1}, mt = 2q + (c >> 1)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t wd = ov[u][q][c];
+          acc[8 * q + 2 * c] += wgt * bf16_bits_to_f32(wd & 0xffffu);
+          acc[8 * q + 2 * c + 1] += wgt * bf16_bits_to_f32(wd >> 16);
+        }
+    }
+  }
+  const float inv = 1.0f / L;
+  const int hq = a.h_kv * AT_G;
+  uint16_t* orow = a.O + (((size_t)b * a.n_q + tq) * hq + g * AT_G + r16) * AT_D;
+  // acc[4 mt + i] is feature 16 mt + 4 grp + i (the lane layout of o[mt][i])
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const uint32_t w0 = pack_bf16x2(acc[4 * mt] * inv, acc[4 * mt + 1] * inv);
+    const uint32_t w1 = pack_bf16x2(acc[4 * mt + 2] * inv, acc[4 * mt + 3] * inv);
+    __builtin_nontemporal_store(u32x2{w0, w1}, (u32x2*)(orow + 16 * mt + 4 * grp));
+  }
+  if (a.lse && grp == 0)
+    a.lse[((size_t)b * hq + g * AT_G + r16) * a.n_q + tq] = (M + fast_log2(L)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -754,6 +1128,55 @@ bool attn_fast_shape(const infv2_problem& p) {
 }
 bool attn_use_split(const infv2_problem& p) { return attn_fast_shape(p) && p.n_q <= 4; }
 
+// The key-range split of the sparse prefill attention (attn_range_kernel):
+// range width, partial slots per row and the query chunk whose partials fit
+// the workspace bound.  Used when the lists fit the kernel's LDS and blocks
+// fit 16 bits.
+#ifndef INFV2_RG_W_BLOCKS
+#define INFV2_RG_W_BLOCKS 128
+#endif
+#ifndef INFV2_RG_SPLIT_MIN_BLOCKS
+#define INFV2_RG_SPLIT_MIN_BLOCKS 1024
+#endif
+constexpr int RG_W_BLOCKS = INFV2_RG_W_BLOCKS;          // 4 MB of K+V packs per group
+// the keys are split only from this many blocks on (below, one range)
+constexpr int RG_SPLIT_MIN_BLOCKS = INFV2_RG_SPLIT_MIN_BLOCKS;
+constexpr size_t RG_PART_BUDGET = (size_t)2 << 30;      // partial bytes per call (at most)
+struct RangePlan {
+  bool use;
+  int W, R, max_slots, tpw, chunk;
+};
+static RangePlan range_plan(const infv2_problem& p, int budget) {
+  RangePlan pl{};
+  const int n_blk = (p.n_kv + AT_B - 1) / AT_B;
+  // below RG_SPLIT_MIN_BLOCKS the token-major kernel (attn_prefill_kernel) is
+  // faster: the packs mostly stay in L2 and a range split would only add the
+  // per-(token, range) set-up and the merge
+  pl.use = budget <= RG_MAX_LIST && n_blk < 65536 && n_blk >= RG_SPLIT_MIN_BLOCKS;
+  if (!pl.use) return pl;
+  pl.W = RG_W_BLOCKS;
+  pl.R = (n_blk + pl.W - 1) / pl.W;
+  pl.max_slots = pl.R > 1 ? std::min(pl.R, budget) : 0;
+  // RG_MAX_TPW tokens per wave; fewer when that would leave the chip with
+  // too few workgroups
+  const long tiles16 = (long)p.batch * p.h_kv * ((p.n_q + 63) / 64);
+  pl.tpw = tiles16 >= 1024 ? RG_MAX_TPW : 4;
+  const int tile = RG_WAVES * pl.tpw;
+  pl.chunk = p.n_q;
+  if (pl.R > 1) {
+    const size_t per_tok = (size_t)p.batch * p.h_kv * pl.max_slots *
+                           (RG_PART_O_BYTES + RG_PART_ML_BYTES);
+    const size_t fit = RG_PART_BUDGET / per_tok;
+    if (fit < (size_t)p.n_q) pl.chunk = std::max(tile, (int)(fit / tile) * tile);
+  }
+  return pl;
+}
+static size_t range_part_bytes(const infv2_problem& p, const RangePlan& pl) {
+  if (!pl.use || pl.R <= 1) return 0;
+  const size_t slots = (size_t)p.batch * p.h_kv * pl.chunk * pl.max_slots;
+  return (slots * RG_PART_O_BYTES + 255) / 256 * 256 + slots * RG_PART_ML_BYTES;
+}
+
 size_t attn_workspace(const infv2_problem& p, int budget, bool sparse) {
   if (!attn_fast_shape(p)) return 0;
   if (sparse && attn_use_split(p)) {
@@ -761,7 +1184,44 @@ size_t attn_workspace(const infv2_problem& p, int budget, bool sparse) {
     return slots * AT_G * AT_D * sizeof(float) + slots * AT_G * sizeof(float2);
   }
   const size_t n_blk = ((size_t)p.n_kv + AT_B - 1) / AT_B;
-  return 2 * (size_t)p.batch * p.h_kv * n_blk * PACK_ELEMS * sizeof(uint16_t);
+  const size_t packs = 2 * (size_t)p.batch * p.h_kv * n_blk * PACK_ELEMS * sizeof(uint16_t);
+  if (!sparse) return packs;
+  return packs + range_part_bytes(p, range_plan(p, budget));
+}
+
+// The range-split attention over one query chunk at a time (the partial
+// slots are reused by the next chunk after its merge).
+static void launch_attn_ranges(const infv2_problem& p, const AttnArgs& a, void* part_ws,
+                               const RangePlan& pl, hipStream_t stream) {
+  RangeArgs ra;
+  ra.a = a;
+  ra.W = pl.W;
+  ra.tpw = pl.tpw;
+  ra.max_slots = std::max(pl.max_slots, 1);
+  const size_t slots = (size_t)p.batch * p.h_kv * pl.chunk * pl.max_slots;
+  ra.part_o = (u32x4*)part_ws;
+  ra.part_ml = (float2*)((char*)part_ws + (slots * RG_PART_O_BYTES + 255) / 256 * 256);
+  const int tile = RG_WAVES * pl.tpw;
+  for (int t0 = 0; t0 < p.n_q; t0 += pl.chunk) {
+    ra.t_base = t0;
+    ra.n_ct = std::min(pl.chunk, p.n_q - t0);
+    ra.n_qt = (ra.n_ct + tile - 1) / tile;
+    const int pos_base = p.q_pos0 + t0;
+    const int last_rg = ((pos_base + ra.n_ct - 1) / AT_B) / pl.W;
+    long items = 0;
+    for (int r = 0; r <= last_rg; ++r)
+      items += std::max(0, ra.n_qt - rg_first_tile(r, pl.W, pos_base, tile));
+    ra.items_bg = (int)items;
+    const long total = items * p.batch * p.h_kv;
+    ra.segment = (int)((total + 7) / 8);
+    hipLaunchKernelGGL(attn_range_kernel, dim3(8 * ra.segment), dim3(64 * RG_WAVES), 0, stream,
+                       ra);
+    if (pl.R > 1) {
+      const int rows = p.batch * p.h_kv * ra.n_ct;
+      hipLaunchKernelGGL(attn_range_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream,
+                         ra);
+    }
+  }
 }
 
 static AttnArgs fast_args(const infv2_problem& p, const void* Q, const void* K, const void* V,
@@ -840,6 +1300,13 @@ hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, con
     hipLaunchKernelGGL(kv_pack_kernel, dim3(a.n_blk, p.h_kv, p.batch), dim3(256), 0, stream,
                        (const uint16_t*)K, (const uint16_t*)V, (uint16_t*)a.Kp, (uint16_t*)a.Vp,
                        p.n_kv, a.n_blk, p.h_kv, kv_cap);
+    if (sparse) {
+      const RangePlan pl = range_plan(p, budget);
+      if (pl.use) {
+        launch_attn_ranges(p, a, (uint16_t*)ws + 2 * pack, pl, stream);
+        return hipGetLastError();
+      }
+    }
     const int total_qb = ((p.n_q + AT_B - 1) / AT_B) * p.batch * p.h_kv;
     dim3 grid(((total_qb + 7) / 8) * 8 * 16);
     if (sparse && budget > 64) {
