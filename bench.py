@@ -307,7 +307,8 @@ def bench_backward(cfg, steps, warmup, with_dense=True):
     pos = np.arange(cfg.n_kv)
     flops = 2.5 * attention_flops(cfg, pos, bud)
     out = dict(ms=ms, tokens_per_s=cfg.batch * cfg.n_q / (ms / 1e3), algo_flops=flops,
-               algo_tflops=flops / (ms / 1e3) / 1e12)
+               algo_tflops=flops / (ms / 1e3) / 1e12,
+               workspace_bytes=tbs.sparse_attn_bwd_workspace(lp))
     out["frac_of_bf16_peak"] = out["algo_tflops"] / PEAK_BF16_TFLOPS
     if with_dense:
         Od, lsed = tbs.dense_attn(lp, Q, K, V)

@@ -244,3 +244,18 @@ def test_noalloc_scratch_size_matches_header():
     m = re.search(r"#define INFV2_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m, "INFV2_NOALLOC_SCRATCH_BYTES not found"
     assert int(m.group(1)) << int(m.group(2)) == tbs.NOALLOC_SCRATCH_BYTES
+
+
+def test_backward_refuses_grids_past_65535_before_any_launch(L):
+    # the fast backward's dK/dV grid takes the key blocks in y and batch x
+    # h_kv in z: larger problems are refused up front, nothing enqueued
+    one = ctypes.c_void_p(256)
+    p = _prob(n_kv=65536 * 64 + 64, n_q=1, q_pos0=65536 * 64 + 63)      # 65537 blocks
+    st = L.infv2_sparse_attn_bwd(ctypes.byref(p.to_c()), one, one, one, one, one, one, one,
+                                 one, one, one, one, one, ctypes.c_size_t(1 << 62), None)
+    assert st == tbs.INFV2_E_UNSUPPORTED
+    assert "65535" in L.infv2_last_error().decode()
+    p = _prob(batch=40000, h_kv=2, n_kv=256, n_q=256)                    # batch x h_kv = 80000
+    st = L.infv2_dense_attn_bwd(ctypes.byref(p.to_c()), one, one, one, one, one, one, one,
+                                one, one, one, ctypes.c_size_t(1 << 62), None)
+    assert st == tbs.INFV2_E_UNSUPPORTED

@@ -3,6 +3,8 @@ times (same calls, same shapes), on outputs the oracle computes one by one:
 K^C1 everywhere (bit-exact), and the selection, S^cmp, O and LSE of sampled
 query rows that include the edge rows (first tokens, block boundaries, the
 last token)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -178,13 +180,18 @@ def test_dense_switch_full_size():
     check_rows(sp, x, op, 0, rows)
 
 
-def test_backward_full_size_prefill32k():
+@pytest.mark.parametrize("batch", [1, 2])
+def test_backward_full_size_prefill32k(batch):
     # the bench's backward call (32k, bf16, the stash path); dQ on sampled
     # query rows (edges included), dK / dV on the keys of two sampled blocks
     # against the oracle's backward over exactly the rows whose GPU sets hold
-    # those blocks (every other row adds nothing to their gradients)
-    cfg = CONFIGS["prefill32k"]
-    _say("case: backward full size (prefill32k)")
+    # those blocks (every other row adds nothing to their gradients).  Batch 1
+    # is the bench's launch; at either batch the dZ stash of the whole
+    # sequence does not fit the workspace budget, so the backward runs query
+    # chunk by chunk.  At batch 2 the second sequence is the one checked.
+    cfg = dataclasses.replace(CONFIGS["prefill32k"], batch=batch)
+    sb = batch - 1
+    _say(f"case: backward full size (prefill32k, batch {batch})")
     x = make_inputs(cfg)
     lp, op = problems(cfg)
     dev = torch.device("cuda:0")
@@ -198,27 +205,33 @@ def test_backward_full_size_prefill32k():
     dQ, dK, dV = tbs.sparse_attn_bwd(lp, Q, K, V, idx, n_sel, O, lse, dO)
     torch.cuda.synchronize()
     res = dict(idx=idx.cpu(), n_sel=n_sel.cpu())
+    # 2 KB of dZ per selected block of every (query, group) row
+    whole_stash = cfg.batch * lp.h_kv * cfg.n_q * (lp.N_init + lp.N_local + lp.k) * 2048
+    ws = tbs.sparse_attn_bwd_workspace(lp)
+    _say("workspace bytes:", ws, "a whole-sequence stash:", whole_stash)
+    assert ws <= 1 << 30
+    assert ws < whole_stash              # the stash holds part of the queries
     q_rows = np.array(sorted({0, 1, 63, 64, 65, 1215, 1216, 4096, 20000, cfg.n_q - 64,
                               cfg.n_q - 1} | set(np.random.default_rng(9).choice(cfg.n_q, 8,
                                                                                replace=False).tolist())))
     blocks = (100, 317)
-    idx_np = res["idx"][0].numpy()                                   # [h_kv, n_q, budget]
+    idx_np = res["idx"][sb].numpy()                                  # [h_kv, n_q, budget]
     hit = np.zeros(cfg.n_q, bool)
     for blk in blocks:
         hit |= (idx_np == blk).any(axis=-1).any(axis=0)
     k_rows = np.nonzero(hit)[0]
     rows = np.union1d(q_rows, k_rows)
     _say("rows:", len(rows), "of which attend the sampled blocks:", len(k_rows))
-    gQ = dQ[0].cpu()
+    gQ = dQ[sb].cpu()
     key_idx = np.concatenate([np.arange(blk * cfg.B, (blk + 1) * cfg.B) for blk in blocks])
-    gK = dK[0, key_idx].cpu().double().numpy()
-    gV = dV[0, key_idx].cpu().double().numpy()
+    gK = dK[sb, key_idx].cpu().double().numpy()
+    gV = dV[sb, key_idx].cpu().double().numpy()
     del Q, K, V, O, lse, dO, dQ, dK, dV, Kc1
-    token_sets = [[orc.attended_tokens(gpu_set(res, 0, g, int(t)), int(t), op)
+    token_sets = [[orc.attended_tokens(gpu_set(res, sb, g, int(t)), int(t), op)
                    for g in range(op.h_kv)] for t in rows]
-    rQ, rK, rV = orc.attention_rows_backward(to_f64(x["q"][0, rows]), to_f64(x["k"][0]),
-                                             to_f64(x["v"][0]), token_sets,
-                                             to_f64(dO_cpu[0, rows]), op)
+    rQ, rK, rV = orc.attention_rows_backward(to_f64(x["q"][sb, rows]), to_f64(x["k"][sb]),
+                                             to_f64(x["v"][sb]), token_sets,
+                                             to_f64(dO_cpu[sb, rows]), op)
     pos = {int(t): i for i, t in enumerate(rows)}
     sel = [pos[int(t)] for t in q_rows]
     err, err_abs, err_mixed, big = {}, {}, {}, {}

@@ -463,6 +463,14 @@ static int attn_bwd_common(const infv2_problem* p, const void* Q, const void* K,
     return fail(INFV2_E_UNSUPPORTED,
                 "%s: %s for the generic backward kernel (shape G=%d d=%d dtype=%d)", what,
                 sparse ? "budget * B too large" : "n_kv too large", p->G, p->d, p->dtype);
+  // the fast kernels launch (window, key block, batch * h_kv) grids and
+  // (key block, h_kv, batch) pack grids: y and z hold at most 65535
+  // (the sparse dK/dV grid adds 7 sub-windows per init block to y)
+  if (attn_fast_shape(*p) &&
+      ((int64_t)n_blk_of(*p) + 7 * (int64_t)p->N_init > 65535 || (int64_t)p->batch * p->h_kv > 65535))
+    return fail(INFV2_E_UNSUPPORTED,
+                "%s: ceil(n_kv/B) + 7 N_init (%lld) and batch x h_kv (%lld) must be at most 65535",
+                what, (long long)n_blk_of(*p) + 7LL * p->N_init, (long long)p->batch * p->h_kv);
   const size_t need = attn_bwd_workspace(*p, sparse);
   if (need) {
     CHECK_PTR(ws);

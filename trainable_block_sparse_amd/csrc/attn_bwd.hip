@@ -35,6 +35,8 @@
 //    (their order between windows is not fixed: the last bits of dK / dV can
 //    vary between runs; dQ is deterministic).
 // A generic fp64 kernel serves fp32 I/O and other shapes.
+#include <algorithm>
+
 #include "attn_layout.hpp"
 
 namespace infv2 {
@@ -54,9 +56,15 @@ struct BwdArgs {
   float* dK;              // [b][kv_cap][h_kv][d]
   float* dV;
   float* Dsum;            // [b][h_q][n_q]
-  uint16_t* dZ;           // sparse: [b][h_kv][n_q][budget] tiles of 2 KB (dZ of a token's
-                          // selected block in the B layout of dQ^T = K^T dZ^T), or null
+  uint16_t* dZ;           // sparse: [b][h_kv][stash_tokens][budget] tiles of 2 KB (dZ of a
+                          // token's selected block in the B layout of dQ^T = K^T dZ^T) for
+                          // the query chunk t_base .. t_base+stash_tokens-1, or null
   int batch, n_q, q_pos0, n_kv, n_blk, h_kv, budget, nw;
+  int win_base;           // first window of this dK/dV launch (the chunk's)
+  int n_init, init_split; // the first n_init blocks (selected by every token) take their
+                          // windows in init_split sub-windows, one workgroup each
+  int t_base, t_end;      // the query chunk of this launch (dQ from the stash)
+  int stash_tokens;       // query tokens the stash holds per (sequence, group)
   int64_t kv_cap;
   float c;                // scale * log2(e)
   float scale;
@@ -308,17 +316,18 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 // dQ^T += K^T dZ^T.  Mapping as attn_bwd_dq_kernel.  Deterministic.
 __global__ void __launch_bounds__(256, 4) attn_bwd_dq_stash_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_qb = (a.n_q + AT_B - 1) / AT_B;
+  const int qb_base = a.t_base / AT_B;                 // (t_base is a multiple of 64)
+  const int n_qb = (a.t_end - a.t_base + AT_B - 1) / AT_B;
   const int n_bg = a.batch * a.h_kv;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, r = bid >> 3;
   const int qbg = (r >> 4) * 8 + xcd;
   if (qbg >= n_qb * n_bg) return;
-  const int qb = n_qb - 1 - qbg / n_bg;
+  const int qb = qb_base + n_qb - 1 - qbg / n_bg;
   const int bg = qbg % n_bg;
   const int g = bg % a.h_kv, b = bg / a.h_kv;
   const int t = qb * AT_B + (r & 15) * 4 + wave;
-  if (t >= a.n_q) return;
+  if (t >= a.t_end) return;
   const int b_p = (a.q_pos0 + t) / AT_B;
   const int grp = lane >> 4, r16 = lane & 15;
   const int hq = a.h_kv * AT_G;
@@ -329,7 +338,8 @@ __global__ void __launch_bounds__(256, 4) attn_bwd_dq_stash_kernel(BwdArgs a) {
   const int nblocks = a.n_sel[row];
   const int32_t* sel = a.idx + row * a.budget;
   const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS + lane * 8;
-  const uint16_t* dz0 = a.dZ + row * a.budget * 1024 + lane * 8;
+  const size_t srow = ((size_t)b * a.h_kv + g) * a.stash_tokens + (t - a.t_base);
+  const uint16_t* dz0 = a.dZ + srow * a.budget * 1024 + lane * 8;
   for (int bi = 0; bi < nblocks; ++bi) {
     const int blk = sel[bi];
     if (blk < 0 || blk > b_p) continue;     // never stashed
@@ -369,6 +379,7 @@ __global__ void __launch_bounds__(256, 4) attn_bwd_dq_stash_kernel(BwdArgs a) {
 // rows) both fall on distinct banks.  LDS holds two pairs; the registers of
 // two more are in flight, so a load has two pairs of compute to land.
 constexpr int BW_WIN = 2048;   // 1024: 21% slower at 32k; 4096: slower at 32k and 128k
+constexpr int BW_INIT_SPLIT = 8;   // sub-windows of 256 tokens for the init blocks
 constexpr int BW_RROW = AT_D + 8;   // row-major LDS row (bf16): 272 B, conflict-free reads
 
 struct BwdTok {                      // one staged token (16 896 B)
@@ -395,10 +406,25 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ float LD[2][2][2][AT_G];                         // [buffer][token][L, D][head]
   __shared__ int ntok_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int win = blockIdx.x, blk = blockIdx.y, bg = blockIdx.z;
+  const int win = blockIdx.x + a.win_base, bg = blockIdx.z;
   const int g = bg % a.h_kv, b = bg / a.h_kv;
-  const int t_lo = win * BW_WIN;
-  const int t_hi = min(t_lo + BW_WIN, a.n_q);
+  // grid y: the key blocks, then (init_split - 1) more sub-windows of each
+  // init block (every token selects those, so a whole window would make one
+  // long workgroup)
+  int blk = blockIdx.y, sub = 0, nsub = 1;
+  if (a.init_split > 1) {
+    if (blk >= a.n_blk) {
+      const int e = blk - a.n_blk;
+      blk = e / (a.init_split - 1);
+      sub = e % (a.init_split - 1) + 1;
+      nsub = a.init_split;
+    } else if (blk < a.n_init) {
+      nsub = a.init_split;
+    }
+  }
+  const int span = BW_WIN / nsub;                    // a multiple of 32 tokens
+  const int t_lo = win * BW_WIN + sub * span;
+  const int t_hi = min(min(t_lo + span, win * BW_WIN + BW_WIN), a.n_q);
   // query tokens that can see a key of the block: p >= 64 * blk
   const int t_first = max(t_lo, blk * AT_B - a.q_pos0);
   if (t_first >= t_hi) return;
@@ -591,7 +617,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
         const int tt = k2 == 0 ? tA : tB;
         const int slot = slot_s[buf][k2];
         if (tt >= 0 && slot >= 0) {
-          const size_t trow = ((size_t)b * a.h_kv + g) * a.n_q + tt;
+          const size_t trow = ((size_t)b * a.h_kv + g) * a.stash_tokens + (tt - a.t_base);
           const int piece = (wave >> 1) * 64 + 16 * (r16 >> 2) + 4 * grp + (lane & 3);
           *(u32x2*)(a.dZ + ((trow * a.budget + slot) * 128 + piece) * 8 + 4 * (wave & 1)) =
               u32x2{pack_bf16x2(tz[0], tz[1]), pack_bf16x2(tz[2], tz[3])};
@@ -750,17 +776,35 @@ static size_t bwd_nw(const infv2_problem& p) { return ((size_t)p.n_q + 31) / 32;
 static bool bwd_stash(const infv2_problem& p, bool sparse) {
   return sparse && p.N_init + p.N_local + p.k <= 64;
 }
-
-size_t attn_bwd_workspace(const infv2_problem& p, bool sparse) {
-  if (!attn_fast_shape(p)) return 0;
+// Workspace apart from the dZ stash: K/V packs, the dO.O row sums and the
+// sparse path's block-to-query bitmap.
+static size_t bwd_fixed_bytes(const infv2_problem& p, bool sparse) {
   const size_t n_blk = ((size_t)p.n_kv + AT_B - 1) / AT_B;
   const size_t packs = 3 * (size_t)p.batch * p.h_kv * n_blk * PACK_ELEMS * sizeof(uint16_t);
   const size_t dsum = (size_t)p.batch * p.h_kv * AT_G * p.n_q * sizeof(float);
   const size_t bitmap = sparse ? (size_t)p.batch * p.h_kv * n_blk * bwd_nw(p) * sizeof(uint32_t) : 0;
-  const size_t dz = bwd_stash(p, sparse) ? (size_t)p.batch * p.h_kv * p.n_q *
+  return packs + ((dsum + 255) & ~(size_t)255) + ((bitmap + 255) & ~(size_t)255);
+}
+// The stash holds a chunk of whole BW_WIN-token windows of queries, as many
+// as keep the whole workspace within BWD_WS_BUDGET bytes (at least one
+// window); the backward runs chunk by chunk (dK/dV with the stash, then dQ
+// from it).
+constexpr size_t BWD_WS_BUDGET = (size_t)1 << 30;
+static int bwd_stash_tokens(const infv2_problem& p) {
+  const size_t per_tok = (size_t)p.batch * p.h_kv * (p.N_init + p.N_local + p.k) * 2048;
+  const size_t fixed = bwd_fixed_bytes(p, true);
+  const size_t room = fixed < BWD_WS_BUDGET ? BWD_WS_BUDGET - fixed : 0;
+  const size_t fit = room / per_tok / BW_WIN * BW_WIN;
+  const size_t chunk = fit < (size_t)BW_WIN ? (size_t)BW_WIN : fit;
+  return (int)(chunk < (size_t)p.n_q ? chunk : (size_t)p.n_q);
+}
+
+size_t attn_bwd_workspace(const infv2_problem& p, bool sparse) {
+  if (!attn_fast_shape(p)) return 0;
+  const size_t dz = bwd_stash(p, sparse) ? (size_t)p.batch * p.h_kv * bwd_stash_tokens(p) *
                                                (p.N_init + p.N_local + p.k) * 2048
                                          : 0;
-  return packs + ((dsum + 255) & ~(size_t)255) + ((bitmap + 255) & ~(size_t)255) + dz;
+  return bwd_fixed_bytes(p, sparse) + dz;
 }
 
 size_t attn_bwd_generic_lds(const infv2_problem& p, int budget, bool sparse) {
@@ -833,11 +877,25 @@ hipError_t launch_attn_bwd(const infv2_problem& p, const void* Q, const void* K,
     const dim3 dq_grid(((total_qb + 7) / 8) * 8 * 16);
     const dim3 kv_grid((p.n_q + BW_WIN - 1) / BW_WIN, n_blk, p.batch * p.h_kv);
     if (a.dZ) {
-      // D first, then dK/dV (which stashes dZ), then dQ from the stash
+      // D first, then per query chunk: dK/dV (which stashes dZ), then dQ
+      // from the stash
       const size_t rows = (size_t)p.batch * p.h_kv * p.n_q;
       hipLaunchKernelGGL(bwd_dsum_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
-      hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, kv_grid, dim3(256), 0, stream, a);
-      hipLaunchKernelGGL(attn_bwd_dq_stash_kernel, dq_grid, dim3(256), 0, stream, a);
+      a.stash_tokens = bwd_stash_tokens(p);
+      a.n_init = std::min(p.N_init, n_blk);
+      a.init_split = BW_INIT_SPLIT;
+      for (int t0 = 0; t0 < p.n_q; t0 += a.stash_tokens) {
+        a.t_base = t0;
+        a.t_end = std::min(p.n_q, t0 + a.stash_tokens);
+        a.win_base = t0 / BW_WIN;
+        const int n_win = (a.t_end - t0 + BW_WIN - 1) / BW_WIN;
+        const int chunk_qb = ((a.t_end - t0 + AT_B - 1) / AT_B) * p.batch * p.h_kv;
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>,
+                           dim3(n_win, n_blk + a.n_init * (BW_INIT_SPLIT - 1), p.batch * p.h_kv),
+                           dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(attn_bwd_dq_stash_kernel, dim3(((chunk_qb + 7) / 8) * 8 * 16),
+                           dim3(256), 0, stream, a);
+      }
     } else {
       hipLaunchKernelGGL(attn_bwd_dq_kernel, dq_grid, dim3(256), 0, stream, a);
       hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, kv_grid, dim3(256), 0, stream, a);
