@@ -588,32 +588,16 @@ def cpu_baseline_child():
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
-# the kernels one call of each prefill stage launches (rocprofv3 names)
+# the kernels one call of each prefill stage can launch (rocprofv3 name
+# prefixes; which of them run depends on the shape: the key-range split of the
+# attention from 1024 blocks on)
 STAGE_KERNELS = {
     "compress_k": ["compress_k_kernel"],
     "block_scores": ["scores_prefill_kernel", "scores_exact_kernel"],
     "topk_select": ["topk_kernel"],
-    "sparse_attn": ["kv_pack_kernel", "attn_prefill_kernel"],
+    "sparse_attn": ["kv_pack_kernel", "attn_prefill_kernel", "attn_range_kernel",
+                    "attn_range_merge_kernel"],
 }
-
-
-def traffic_for(stage, workload):
-    """HBM bytes of one call of a stage (the sum over the kernels it
-    launches) from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel sources."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-    except (OSError, ValueError):
-        return None
-    total = 0.0
-    for kernel in STAGE_KERNELS.get(stage, [stage]):
-        ent = tr.get(f"{workload}/{kernel}")
-        if not ent or ent.get("source_hash") != kernel_source_hash(kernel):
-            return None
-        total += ent.get("bytes_per_launch", 0.0)
-    return total
-
 
 # the kernels one call of each decode stage launches
 DECODE_STAGE_KERNELS = {
@@ -622,6 +606,35 @@ DECODE_STAGE_KERNELS = {
                       "scores_select_merge_kernel"],
     "sparse_attn": ["attn_split_kernel", "attn_merge_kernel"],
 }
+
+
+def stage_traffic(workload, prefixes):
+    """(HBM bytes of one stage call, the kernels counted) from the committed
+    rocprofv3 counter summary: every kernel of the workload's profiled run
+    whose name starts with one of the prefixes, each entry's bytes per launch
+    times its launches per call.  None when an entry was taken on other kernel
+    sources than the current ones, or when none is there."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None, []
+    total, kernels = 0.0, []
+    for key, ent in tr.items():
+        if not key.startswith(workload + "/"):
+            continue
+        kern = key.split("/", 1)[1]
+        if not any(kern.startswith(pre) for pre in prefixes):
+            continue
+        if ent.get("source_hash") != kernel_source_hash(kern):
+            return None, []
+        total += ent.get("bytes_per_call", ent.get("bytes_per_launch", 0.0))
+        kernels.append(kern)
+    return (total, kernels) if kernels else (None, [])
+
+
+def traffic_for(stage, workload):
+    return stage_traffic(workload, STAGE_KERNELS.get(stage, [stage]))[0]
 
 
 def prefill_roofline(res, workload):
@@ -637,9 +650,10 @@ def prefill_roofline(res, workload):
         return {"kernel": dom, "bound": "mfma", "achieved": None, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": None, "traffic": None}
     ach = flops / (stages[dom] / 1e3) / 1e12
-    return {"kernel": dom, "launches": STAGE_KERNELS.get(dom, [dom]), "bound": "mfma",
+    traffic, kernels = stage_traffic(workload, STAGE_KERNELS.get(dom, [dom]))
+    return {"kernel": dom, "launches": kernels or STAGE_KERNELS.get(dom, [dom]), "bound": "mfma",
             "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic_for(dom, workload),
+            "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic,
             "per_launch_algorithmic": flops, "avg_launch_ms": stages[dom]}
 
 
@@ -659,21 +673,8 @@ def decode_roofline(res, cfg, budget, workload="decode"):
            "compress_append": cfg.l_C1 * cfg.d * 2 + cfg.d * 2}[dom]
     nbytes = float(cfg.batch * cfg.h_kv * per)
     ach = nbytes / (st[dom] / 1e6) / 1e9
-    traffic = None
-    try:
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        tot = 0.0
-        for kern in DECODE_STAGE_KERNELS[dom]:
-            ent = tr.get(f"{workload}/{kern}")
-            if not ent or ent.get("source_hash") != kernel_source_hash(kern):
-                tot = None
-                break
-            tot += ent.get("bytes_per_launch", 0.0)
-        traffic = tot
-    except (OSError, ValueError):
-        pass
-    return {"kernel": dom, "launches": DECODE_STAGE_KERNELS[dom], "bound": "hbm",
+    traffic, kernels = stage_traffic(workload, DECODE_STAGE_KERNELS[dom])
+    return {"kernel": dom, "launches": kernels or DECODE_STAGE_KERNELS[dom], "bound": "hbm",
             "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
             "traffic": traffic, "per_launch_algorithmic": nbytes,
             "avg_launch_us": st[dom]}
