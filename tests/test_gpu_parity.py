@@ -201,13 +201,14 @@ def test_extreme_logits_take_exact_pass():
     _say(rep)
 
 
-@pytest.mark.parametrize("lean", [False, True])
-def test_prefill_pipeline_matches_one_shot(lean):
+@pytest.mark.parametrize("n_kv,lean", [(2600, False), (2600, True), (70000, False)])
+def test_prefill_pipeline_matches_one_shot(n_kv, lean):
     # the two-stream range pipeline computes every row exactly as the one-shot
     # path: O and LSE bitwise equal, and both match the oracle (lean: the
-    # streamed top-k selection, no S^cmp buffers)
+    # streamed top-k selection, no S^cmp buffers; 70000 keys = 1094 blocks:
+    # the attention splits the keys into ranges, in the one-shot call and in
+    # every range call alike)
     cfg = CONFIGS["prefill32k"]
-    n_kv = 2600
     _say("case: prefill pipeline, n_kv", n_kv, "lean", lean)
     x = make_inputs(cfg, n_kv=n_kv, batch=1, seed=23)
     lp, op = problems(cfg, n_kv=n_kv, batch=1)
@@ -218,14 +219,17 @@ def test_prefill_pipeline_matches_one_shot(lean):
     O = torch.empty_like(Q)
     lse = torch.empty((1, lp.h_q, lp.n_q), dtype=torch.float32, device=dev)
     pipe = tbs.PrefillPipeline(lp, 3, lean=lean)
-    assert [c["r0"] for c in pipe.chunks] == [0, 896, 1728]
+    if n_kv == 2600:
+        assert [c["r0"] for c in pipe.chunks] == [0, 896, 1728]
     for _ in range(2):                  # a second run reuses every buffer
         pipe.run(Q, K, V, Kc1, O, lse)
     torch.cuda.synchronize()
     assert torch.equal(O.cpu(), ref["O"])
     assert torch.equal(lse.cpu(), ref["lse"])
     assert torch.equal(Kc1.cpu(), ref["Kc1"])
-    rows = sample_rows(n_kv, 40, np.random.default_rng(3), must=(0, 895, 896, 1727, 1728, 2599))
+    cuts = [c["r0"] for c in pipe.chunks[1:]]
+    rows = sample_rows(n_kv, 40 if n_kv < 10000 else 12, np.random.default_rng(3),
+                       must=(0, n_kv - 1, *cuts, *(r - 1 for r in cuts)))
     res = dict(ref, O=O.cpu(), lse=lse.cpu())
     _say(check_rows(res, x, op, 0, {0: rows}))
 

@@ -632,8 +632,12 @@ class PrefillPipeline:
     matrix unit) is enqueued on one stream while the block-sparse attention of
     range i (bound by the K/V gather) runs on another; an event per range
     orders the two.  Each range is an ordinary call of the C ABI with
-    q_pos0/n_q/n_kv of that range, so every output row is computed exactly as
-    in the one-shot path (bitwise the same O and LSE).  Buffers and workspaces
+    q_pos0/n_q of that range (the selection with n_kv of the range, the
+    attention with the whole sequence's n_kv, so that the library takes the
+    same attention plan for every range as for the one-shot call: from 1024
+    blocks on it splits the keys into ranges, which rounds differently), so
+    every output row is computed exactly as in the one-shot path (bitwise the
+    same O and LSE).  Buffers and workspaces
     are allocated once here; ``run`` allocates nothing.  With ``lean`` the
     selection streams the top-k through the score sweep (select_blocks), so
     no S^cmp buffer is held (2.1 GB at 128k); the two-call selection is
@@ -660,16 +664,17 @@ class PrefillPipeline:
             p = dataclasses.replace(prob, n_q=r1 - r0, q_pos0=prob.q_pos0 + r0,
                                     n_kv=prob.q_pos0 + r1, kv_cap=kv_cap, c1_cap=c1_cap,
                                     c2_cap=c2_cap)
+            p_att = dataclasses.replace(p, n_kv=prob.n_kv)
             ws_bytes = select_blocks_workspace(p) if lean else block_scores_workspace(p)
             self.chunks.append(dict(
-                p=p, r0=r0, r1=r1,
+                p=p, p_att=p_att, r0=r0, r1=r1,
                 S=None if lean else torch.empty((1, p.h_kv, p.n_q, n_blocks(p)),
                                                 dtype=torch.float32, device=device),
                 idx=torch.empty((1, p.h_kv, p.n_q, budget(p)), dtype=torch.int32, device=device),
                 n_sel=torch.empty((1, p.h_kv, p.n_q), dtype=torch.int32, device=device),
                 lse=torch.empty((1, p.h_q, p.n_q), dtype=torch.float32, device=device),
                 ws_s=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device),
-                ws_a=torch.empty(max(sparse_attn_workspace(p), 16), dtype=torch.uint8,
+                ws_a=torch.empty(max(sparse_attn_workspace(p_att), 16), dtype=torch.uint8,
                                  device=device),
                 ready=torch.cuda.Event()))
         self.sel_stream = torch.cuda.Stream(device=device)
@@ -708,7 +713,7 @@ class PrefillPipeline:
             s_att.wait_event(c["ready"])
             if attn_events is not None:
                 attn_events[i][0].record(s_att)
-            sparse_attn(c["p"], Q[:, c["r0"]:c["r1"]], K, V, c["idx"], c["n_sel"],
+            sparse_attn(c["p_att"], Q[:, c["r0"]:c["r1"]], K, V, c["idx"], c["n_sel"],
                         O[:, c["r0"]:c["r1"]], c["lse"], c["ws_a"], stream=s_att)
             if attn_events is not None:
                 attn_events[i][1].record(s_att)
