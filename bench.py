@@ -5,9 +5,10 @@ Default workload (the headline line): MiniCPM-style GQA layer prefill at 32k
 tokens (b=1, n=32768, h_q=32, h_kv=2, d=128, bf16, B=64, l_C1=32, s_C1=16,
 l=5, s=4, N_init=1, N_local=2, k=16) on seeded synthetic inputs with planted
 needle blocks.  One step = the whole hot path: compress_k -> block_scores ->
-topk_select -> sparse_attn (decode: compress append -> select_blocks, the
-scores with the top-k fused in -> sparse_attn), inputs resident in HBM,
-outputs preallocated.
+topk_select -> sparse_attn (decode: select_blocks_append -- the step's new
+K^C1 kernel formed inside the selection's score sweep, the top-k fused into
+the pooling -- then sparse_attn), inputs resident in HBM, outputs
+preallocated.
 The same JSON line also carries the 128k prefill and the 16-sequence decode
 step (both secondary, fewer steps), the dense-attention time on the same
 input, the roofline of the dominant kernel, and the fp64 CPU oracle timed on a
@@ -424,21 +425,31 @@ def bench_decode(cfg, steps, warmup, lse_approx=False):
     ws_s = torch.empty(max(tbs.select_blocks_workspace(lp), tbs.block_scores_workspace(lp), 16),
                        dtype=torch.uint8, device=dev)
     ws_a = torch.empty(max(tbs.sparse_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
-    # the step: scores and top-k in one call (the top-k fused into the pooling
-    # kernel); S^cmp is not stored
-    fns = [
+    # the step as three calls: the append, scores and top-k in one call (the
+    # top-k fused into the pooling kernel; S^cmp is not stored), attention
+    fns3 = [
         lambda: tbs.compress_k(lp, K, Kc1, c1_begin=n_prev, c1_end=n_c1),
         lambda: tbs.select_blocks(lp, Q, Kc1, None, idx, nsel, ws_s, Kc2=Kc2),
         lambda: tbs.sparse_attn(lp, Q, K, V, idx, nsel, O, lse, ws_a),
     ]
-    names = ["compress_append", "select_blocks", "sparse_attn"]
+    names3 = ["compress_append", "select_blocks", "sparse_attn"]
     if lse_approx and n_c2 > n_prev2:
         # this step also completes a coarse kernel (every 64th token)
-        fns.insert(1, lambda: tbs.compress_k2(lp, K, Kc2, c2_begin=n_prev2, c2_end=n_c2))
-        names.insert(1, "compress2_append")
+        fns3.insert(1, lambda: tbs.compress_k2(lp, K, Kc2, c2_begin=n_prev2, c2_end=n_c2))
+        names3.insert(1, "compress2_append")
     # the same step with the separate score and top-k calls, for comparison
-    fns_sep = fns[:-2] + [lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s, Kc2=Kc2),
-                          lambda: tbs.topk_select(lp, S, idx, nsel), fns[-1]]
+    fns_sep = fns3[:-2] + [lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s, Kc2=Kc2),
+                           lambda: tbs.topk_select(lp, S, idx, nsel), fns3[-1]]
+    if lse_approx:
+        fns, names = fns3, names3
+    else:
+        # the timed step: the append inside the selection's score sweep, then
+        # the attention (two calls)
+        fns = [
+            lambda: tbs.select_blocks_append(lp, Q, K, Kc1, n_prev, n_c1, idx, nsel, ws_s),
+            fns3[-1],
+        ]
+        names = ["select_blocks_append", "sparse_attn"]
     for _ in range(warmup):
         for fn in fns:
             fn()
@@ -476,6 +487,19 @@ def bench_decode(cfg, steps, warmup, lse_approx=False):
     e1.record()
     torch.cuda.synchronize()
     step_ms = e0.elapsed_time(e1) / steps
+    three_ms = None
+    if fns is not fns3:
+        for _ in range(warmup):
+            for fn in fns3:
+                fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            for fn in fns3:
+                fn()
+        e1.record()
+        torch.cuda.synchronize()
+        three_ms = e0.elapsed_time(e1) / steps
     graph_sep = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph_sep):
         for fn in fns_sep:
@@ -500,6 +524,7 @@ def bench_decode(cfg, steps, warmup, lse_approx=False):
                timing=("eager launches, steps back to back" if eager_ms <= graph_ms
                        else "HIP graph replay of the whole step"),
                separate_topk_step_us=sep_ms * 1e3,
+               three_call_step_us=None if three_ms is None else three_ms * 1e3,
                stages_us_eager={k: v * 1e3 for k, v in stage.items()}, algo_bytes=nbytes,
                algo_GBps=nbytes / (step_ms / 1e3) / 1e9)
     out["frac_of_hbm_peak"] = out["algo_GBps"] / PEAK_HBM_GBS
@@ -604,6 +629,8 @@ DECODE_STAGE_KERNELS = {
     "compress_append": ["compress_k_kernel"],
     "select_blocks": ["scores_split_logits_kernel", "scores_split_pool_kernel",
                       "scores_select_merge_kernel"],
+    "select_blocks_append": ["scores_split_logits_kernel", "scores_split_pool_kernel",
+                             "scores_select_merge_kernel"],
     "sparse_attn": ["attn_split_kernel", "attn_merge_kernel"],
 }
 
@@ -669,6 +696,8 @@ def decode_roofline(res, cfg, budget, workload="decode"):
     nsel = min((L - 1) // cfg.B + 1, budget)
     qo = cfg.G * cfg.d * 2
     per = {"select_blocks": n_c1 * cfg.d * 2 + qo,
+           # the selection's bytes plus the appended kernel's keys and its row
+           "select_blocks_append": n_c1 * cfg.d * 2 + qo + cfg.l_C1 * cfg.d * 2 + cfg.d * 2,
            "sparse_attn": nsel * cfg.B * cfg.d * 2 * 2 + 2 * qo,
            "compress_append": cfg.l_C1 * cfg.d * 2 + cfg.d * 2}[dom]
     nbytes = float(cfg.batch * cfg.h_kv * per)

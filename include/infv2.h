@@ -179,6 +179,29 @@ int infv2_select_blocks(const infv2_problem* prob, const void* Q, const void* Kc
                         const void* Kc2, float* S_cmp, int32_t* idx, int32_t* n_sel,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* The decode step's K^C1 append and the block selection in one call:
+ * kernels [c1_begin, c1_end) of every sequence are formed from K exactly as
+ * infv2_compress_k forms them (papernotes note, 关键设计 3: the mean of the
+ * kernel's keys, rounded once) and written to Kc1, and the selection runs as
+ * infv2_select_blocks with S_cmp = NULL and no K^C2; the appended kernels are
+ * formed inside the score sweep that reads them, so the step needs no
+ * separate compress launch (OpenBMB blog, 查询和键值词元的不同粒度: token-level
+ * queries make decode sparse, so the per-step work is what matters).  Kc1,
+ * idx and n_sel are bitwise those of infv2_compress_k(c1_begin, c1_end)
+ * followed by infv2_select_blocks.
+ *   K     : [batch][kv_cap][h_kv][d] (input)
+ *   Kc1   : [batch][h_kv][c1_cap][d] (input; rows [c1_begin, c1_end) are
+ *           written and are not read)
+ *   c1_begin, c1_end : 0 <= c1_begin <= c1_end <= n_C1 (else INFV2_E_ARG)
+ *   idx, n_sel, ws, ws_bytes : as in infv2_select_blocks (workspace of
+ *           infv2_select_blocks_workspace(prob, 0) bytes)
+ * Serves the decode shapes of infv2_select_blocks (bf16, G = 16, d = 128,
+ * n_q <= 4, k <= 32) with the exact LSE; anything else is refused with
+ * INFV2_E_UNSUPPORTED before any work is enqueued. */
+int infv2_select_blocks_append(const infv2_problem* prob, const void* Q, const void* K,
+                               void* Kc1, int32_t c1_begin, int32_t c1_end, int32_t* idx,
+                               int32_t* n_sel, void* ws, size_t ws_bytes, void* stream);
+
 /* Block-sparse attention (paperlayer.ai summary, A IMPLEMENTATION DETAIL):
  * for each query token and head, softmax attention over the keys
  * T(p) = {t <= p : floor(t/B) in I(p)}, returning O and the natural-log LSE.

@@ -259,3 +259,30 @@ def test_backward_refuses_grids_past_65535_before_any_launch(L):
     st = L.infv2_dense_attn_bwd(ctypes.byref(p.to_c()), one, one, one, one, one, one, one,
                                 one, one, one, ctypes.c_size_t(1 << 62), None)
     assert st == tbs.INFV2_E_UNSUPPORTED
+
+
+def test_select_blocks_append_validates_before_any_launch(L):
+    # shape, range, pointer and workspace errors are returned before anything
+    # is enqueued (no GPU is needed to reach them)
+    one = ctypes.c_void_p(256)
+    big = ctypes.c_size_t(1 << 62)
+    pre = _prob()                                                        # prefill shape
+    st = L.infv2_select_blocks_append(ctypes.byref(pre.to_c()), one, one, one, 0, 1, one, one,
+                                      one, big, None)
+    assert st == tbs.INFV2_E_UNSUPPORTED
+    assert "decode shapes" in L.infv2_last_error().decode()
+    dec = _prob(n_kv=131072, n_q=1, q_pos0=131071)
+    dc = ctypes.byref(dec.to_c())
+    n_c1 = tbs.n_kernels(dec)
+    assert L.infv2_select_blocks_append(dc, one, one, one, n_c1, n_c1 + 1, one, one, one, big,
+                                        None) == tbs.INFV2_E_ARG
+    assert "c1_begin" in L.infv2_last_error().decode()
+    assert L.infv2_select_blocks_append(dc, one, one, one, 5, 4, one, one, one, big,
+                                        None) == tbs.INFV2_E_ARG
+    assert L.infv2_select_blocks_append(dc, one, None, one, n_c1 - 1, n_c1, one, one, one, big,
+                                        None) == tbs.INFV2_E_ARG
+    assert L.infv2_select_blocks_append(dc, one, one, one, n_c1 - 1, n_c1, one, one, one,
+                                        ctypes.c_size_t(16), None) == tbs.INFV2_E_WORKSPACE
+    approx = _prob(n_kv=131072, n_q=1, q_pos0=131071, lse_approx=True)
+    assert L.infv2_select_blocks_append(ctypes.byref(approx.to_c()), one, one, one, 0, 1, one,
+                                        one, one, big, None) == tbs.INFV2_E_UNSUPPORTED

@@ -56,9 +56,10 @@ def test_decode_full_size():
     lp.c1_cap = prev.c1_cap = n_now
     Kc1 = torch.empty((cfg.batch, cfg.h_kv, n_now, cfg.d), dtype=K.dtype, device=dev)
     tbs.compress_k(prev, K, Kc1)
-    # the step exactly as bench.py launches it: the append, the fused
-    # selection (scores and top-k in one call, S^cmp not stored) with a
-    # preallocated workspace, then the attention
+    # the step exactly as bench.py launches it: the append fused into the
+    # selection (the new kernel formed inside the score sweep; scores and
+    # top-k in one call, S^cmp not stored) with a preallocated workspace,
+    # then the attention; the appended row is NaN beforehand
     ws_s = torch.empty(max(tbs.select_blocks_workspace(lp), tbs.block_scores_workspace(lp), 16),
                        dtype=torch.uint8, device=dev)
     ws_a = torch.empty(max(tbs.sparse_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
@@ -67,8 +68,8 @@ def test_decode_full_size():
     n_sel = torch.empty((cfg.batch, cfg.h_kv, 1), dtype=torch.int32, device=dev)
     O = torch.empty_like(Q)
     lse = torch.empty((cfg.batch, lp.h_q, 1), dtype=torch.float32, device=dev)
-    tbs.compress_k(lp, K, Kc1, c1_begin=n_prev, c1_end=n_now)
-    tbs.select_blocks(lp, Q, Kc1, None, idx, n_sel, ws_s)
+    Kc1[:, :, n_prev:n_now] = float("nan")
+    tbs.select_blocks_append(lp, Q, K, Kc1, n_prev, n_now, idx, n_sel, ws_s)
     tbs.sparse_attn(lp, Q, K, V, idx, n_sel, O, lse, ws_a)
     # S^cmp for the score check, and the two-call selection, bitwise the same
     S = tbs.block_scores(lp, Q, Kc1)

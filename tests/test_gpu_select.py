@@ -222,3 +222,55 @@ def test_decode_at_and_past_the_longest_fused_selection(n_kv):
     del K, V
     check_compress(res, x["k"], op)
     _say(check_rows(res, x, op, n_kv - 1, {b: np.array([0]) for b in range(2)}))
+
+
+@pytest.mark.parametrize("n_kv,batch,n_q,c1_back", [
+    (5000, 3, 1, 1),        # the decode step: the newest kernel
+    (4130, 2, 2, 7),        # several kernels across a 256-kernel chunk edge, two query rows
+    (131072, 16, 1, 1),     # the bench's decode launch (16 x 131072)
+    (999, 1, 1, 0),         # nothing to append
+])
+def test_select_blocks_append_equals_compress_then_select(n_kv, batch, n_q, c1_back):
+    # infv2_select_blocks_append forms the appended K^C1 rows inside the
+    # logits sweep: Kc1, idx and n_sel must be bitwise those of compress_k on
+    # the same rows followed by select_blocks; the rows are NaN beforehand so
+    # a read of the stale rows would show
+    cfg = CONFIGS["decode"]
+    _say(f"case: select_blocks_append n_kv={n_kv} batch={batch} n_q={n_q} rows back={c1_back}")
+    x, lp, op, Q, Kc1_ref = _selection_inputs(cfg, n_kv, batch, n_q, seed=41)
+    K = x["k"].to(Q.device)
+    n_c1 = tbs.n_kernels(lp)
+    c1_begin, c1_end = n_c1 - c1_back, n_c1
+    idx_ref, ns_ref = tbs.select_blocks(lp, Q, Kc1_ref)
+    Kc1 = Kc1_ref.clone()
+    Kc1[:, :, c1_begin:c1_end] = float("nan")
+    idx, ns = tbs.select_blocks_append(lp, Q, K, Kc1, c1_begin, c1_end)
+    torch.cuda.synchronize()
+    assert torch.equal(Kc1.cpu(), Kc1_ref.cpu())
+    assert torch.equal(idx.cpu(), idx_ref.cpu())
+    assert torch.equal(ns.cpu(), ns_ref.cpu())
+    if n_kv <= 5000:
+        # and the appended rows against the oracle's exact mean
+        res = dict(Kc1=Kc1.cpu(), idx=idx.cpu(), n_sel=ns.cpu())
+        check_compress(res, x["k"], op)
+
+
+def test_select_blocks_append_refuses_other_shapes():
+    cfg = CONFIGS["prefill32k"]
+    lp, _ = problems(cfg, n_kv=2000, batch=1)           # a prefill shape
+    dev = torch.device("cuda:0")
+    e = lp._ext()
+    Q = torch.zeros(e.q, dtype=torch.bfloat16, device=dev)
+    K = torch.zeros(e.kv, dtype=torch.bfloat16, device=dev)
+    Kc1 = torch.zeros(e.kc1, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(tbs.Infv2Error, match="decode shapes"):
+        tbs.select_blocks_append(lp, Q, K, Kc1, 0, 1)
+    dcfg = CONFIGS["decode"]
+    dp, _ = problems(dcfg, n_kv=3000, batch=1)
+    n_c1 = tbs.n_kernels(dp)
+    e = dp._ext()
+    Q = torch.zeros(e.q, dtype=torch.bfloat16, device=dev)
+    K = torch.zeros(e.kv, dtype=torch.bfloat16, device=dev)
+    Kc1 = torch.zeros(e.kc1, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(tbs.Infv2Error, match="c1_begin"):
+        tbs.select_blocks_append(dp, Q, K, Kc1, n_c1 - 1, n_c1 + 1)

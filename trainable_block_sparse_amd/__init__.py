@@ -26,7 +26,7 @@ EXPORTED = (
     "infv2_use_dense", "infv2_check_problem", "infv2_compress_k", "infv2_compress_k2",
     "infv2_block_scores_workspace",
     "infv2_block_scores", "infv2_topk_select", "infv2_select_blocks_workspace",
-    "infv2_select_blocks", "infv2_sparse_attn_workspace",
+    "infv2_select_blocks", "infv2_select_blocks_append", "infv2_sparse_attn_workspace",
     "infv2_sparse_attn", "infv2_dense_attn_workspace", "infv2_dense_attn",
     "infv2_sparse_attn_bwd_workspace", "infv2_sparse_attn_bwd",
     "infv2_dense_attn_bwd_workspace", "infv2_dense_attn_bwd",
@@ -136,6 +136,8 @@ def lib() -> ctypes.CDLL:
             "infv2_topk_select": (ctypes.c_int, [P, vp, vp, vp, vp]),
             "infv2_select_blocks_workspace": (sz, [P, ctypes.c_int]),
             "infv2_select_blocks": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "infv2_select_blocks_append": (ctypes.c_int,
+                                           [P, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]),
             "infv2_sparse_attn_workspace": (sz, [P]),
             "infv2_sparse_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_sparse_attn_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
@@ -383,6 +385,32 @@ def select_blocks(prob: Problem, Q: torch.Tensor, Kc1: torch.Tensor,
                                      _arg(idx, "idx", torch.int32, e.rows * e.budget),
                                      _arg(n_sel, "n_sel", torch.int32, e.rows), ws_p, ws_n,
                                      _stream(stream)))
+    return idx, n_sel
+
+
+def select_blocks_append(prob: Problem, Q: torch.Tensor, K: torch.Tensor, Kc1: torch.Tensor,
+                         c1_begin: int, c1_end: int, idx: torch.Tensor | None = None,
+                         n_sel: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                         stream=None):
+    """Decode: K^C1 rows c1_begin..c1_end-1 formed from K and written to Kc1
+    inside the selection's score sweep, then (idx, n_sel) as select_blocks
+    (bitwise compress_k(c1_begin, c1_end) followed by select_blocks)."""
+    if idx is None:
+        idx = torch.empty((prob.batch, prob.h_kv, prob.n_q, budget(prob)), dtype=torch.int32,
+                          device=Q.device)
+    if n_sel is None:
+        n_sel = torch.empty((prob.batch, prob.h_kv, prob.n_q), dtype=torch.int32,
+                            device=Q.device)
+    if ws is None and (need := select_blocks_workspace(prob, False)):
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    e = prob._ext()
+    ws_p, ws_n = _ws(ws)
+    _check(lib().infv2_select_blocks_append(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                            _arg(K, "K", e.io, e.kv),
+                                            _arg(Kc1, "Kc1", e.io, e.kc1), c1_begin, c1_end,
+                                            _arg(idx, "idx", torch.int32, e.rows * e.budget),
+                                            _arg(n_sel, "n_sel", torch.int32, e.rows), ws_p,
+                                            ws_n, _stream(stream)))
     return idx, n_sel
 
 

@@ -42,6 +42,10 @@ size_t select_fused_workspace(const infv2_problem& p, int n_c1);
 hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeySet& ks,
                                float* S_cmp, int32_t* idx, int32_t* n_sel, void* ws, int n_blk,
                                float scale, int budget, hipStream_t stream);
+hipError_t launch_select_append(const infv2_problem& p, const void* Q, const void* K, void* Kc1,
+                                int c1_begin, int c1_end, int64_t kv_cap, const KeySet& ks,
+                                int32_t* idx, int32_t* n_sel, void* ws, int n_blk, float scale,
+                                int budget, hipStream_t stream);
 bool attn_fast_shape(const infv2_problem& p);
 size_t attn_workspace(const infv2_problem& p, int budget, bool sparse);
 hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, const void* V,
@@ -312,6 +316,37 @@ int infv2_select_blocks(const infv2_problem* p, const void* Q, const void* Kc1, 
   hipError_t e = launch_block_scores(*p, Q, ks, S, nullptr, ws, n_blk_of(*p), scale_of(*p), s);
   if (e == hipSuccess) e = launch_topk(*p, S, idx, n_sel, n_blk_of(*p), budget_of(*p), s);
   return hip_status(e, "infv2_select_blocks");
+}
+
+int infv2_select_blocks_append(const infv2_problem* p, const void* Q, const void* K, void* Kc1,
+                               int32_t c1_begin, int32_t c1_end, int32_t* idx, int32_t* n_sel,
+                               void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(Q);
+  CHECK_PTR(K);
+  CHECK_PTR(idx);
+  CHECK_PTR(n_sel);
+  if (p->lse_approx || !scores_use_split(*p) || !select_fused_shape(*p, n_c1_of(*p)))
+    return fail(INFV2_E_UNSUPPORTED,
+                "select_blocks_append serves the decode shapes of infv2_select_blocks (bf16, "
+                "G=16, d=128, n_q<=4, k<=32, exact LSE)");
+  if ((st = check_keys(*p, Kc1, nullptr))) return st;
+  const KeySet ks = keys_of(*p, Kc1, nullptr);
+  if (c1_begin < 0 || c1_begin > c1_end || c1_end > ks.n_c1)
+    return fail(INFV2_E_ARG, "need 0 <= c1_begin <= c1_end <= n_C1 (%d..%d, n_C1=%d)",
+                c1_begin, c1_end, ks.n_c1);
+  const size_t need = infv2_select_blocks_workspace(p, 0);
+  if (need) {
+    CHECK_PTR(ws);
+    if (ws_bytes < need)
+      return fail(INFV2_E_WORKSPACE, "select_blocks_append workspace %zu < %zu bytes", ws_bytes,
+                  need);
+  }
+  return hip_status(launch_select_append(*p, Q, K, Kc1, c1_begin, c1_end, kv_cap_of(*p), ks, idx,
+                                         n_sel, ws, n_blk_of(*p), scale_of(*p), budget_of(*p),
+                                         (hipStream_t)stream),
+                    "infv2_select_blocks_append");
 }
 
 size_t infv2_sparse_attn_workspace(const infv2_problem* p) {

@@ -7,32 +7,11 @@
 //
 // The kernel is HBM-bound: every key row is read by l_C1/s_C1 kernels, so the
 // second read hits L2.  Threads run along d so that each 32-token segment is
-// read as contiguous rows.  The sum of the l_C1 keys is carried as an fp64
-// pair (hi, lo) with TwoSum: exact unless the kernel's values span more than
-// about 78 binades (never for bf16 or fp32 data of one attention layer in
-// practice), and rounded ONCE to the I/O dtype, to nearest even.
-#include "common.hpp"
+// read as contiguous rows.  The exact mean and its single rounding are in
+// kc1_mean.hpp (shared with the decode logits kernel's on-the-fly append).
+#include "kc1_mean.hpp"
 
 namespace infv2 {
-
-// Round (hi + lo) to a binary format with P significant bits and fp32's
-// exponent range, to nearest even; |lo| <= ulp(hi)/2 (a TwoSum pair).
-template <int P>
-__device__ __forceinline__ double round_pair(double hi, double lo) {
-  if (hi == 0.0 || !__builtin_isfinite(hi)) return hi + lo;
-  int e;
-  (void)__builtin_frexp(hi, &e);             // hi = m * 2^e, 0.5 <= |m| < 1
-  int qexp = e - P;
-  if (qexp < -126 - P + 1) qexp = -126 - P + 1;   // subnormal quantum
-  const double scaled = __builtin_ldexp(hi, -qexp);
-  double r = __builtin_rint(scaled);         // ties to even
-  const double delta = scaled - r;           // exact
-  if ((delta == 0.5 || delta == -0.5) && lo != 0.0) {
-    // hi sits exactly on a midpoint: the sign of lo decides the direction.
-    if ((lo > 0.0) == (delta > 0.0)) r += (delta > 0.0) ? 1.0 : -1.0;
-  }
-  return __builtin_ldexp(r, qexp);
-}
 
 template <typename T> __device__ __forceinline__ double load_f64(const T* p);
 template <> __device__ __forceinline__ double load_f64<uint16_t>(const uint16_t* p) {
@@ -44,8 +23,7 @@ template <> __device__ __forceinline__ double load_f64<float>(const float* p) {
 
 template <typename T> __device__ __forceinline__ void store_rounded(T* p, double hi, double lo);
 template <> __device__ __forceinline__ void store_rounded<uint16_t>(uint16_t* p, double hi, double lo) {
-  const float r = (float)round_pair<8>(hi, lo);      // exact: 8 bits fit fp32
-  *p = (uint16_t)(__float_as_uint(r) >> 16);          // exact: low half is zero
+  *p = kmean_bf16(hi, lo);
 }
 template <> __device__ __forceinline__ void store_rounded<float>(float* p, double hi, double lo) {
   *p = (float)round_pair<24>(hi, lo);                 // exact conversion
@@ -110,21 +88,15 @@ __global__ void __launch_bounds__(256) compress_k_kernel(
     }
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
-      // (a predicate, not a break: the unrolled loop keeps x in registers)
-      const double xu = u < cnt ? x[u] : -0.0;   // -0 is the exact identity of +
-      const double t = hi + xu;
-      const double bp = t - hi;
-      lo += (hi - (t - bp)) + (xu - bp);    // TwoSum error, accumulated exactly
-      hi = t;                               // for the magnitudes of one kernel
+      // (a predicate, not a break: the unrolled loop keeps x in registers;
+      // -0 is the exact identity of +)
+      kmean_add(hi, lo, u < cnt ? x[u] : -0.0);
     }
   }
-  // renormalise the pair so that |lo| <= ulp(hi)/2, then scale by 1/l_C1
-  // (a power of two: exact)
-  const double t = hi + lo;
-  const double bp = t - hi;
-  const double e = (hi - (t - bp)) + (lo - bp);
+  double rh, rl;
+  kmean_finish(hi, lo, inv_l, rh, rl);
   T* dst = Kc1 + (((size_t)b * h_kv + g) * c1_cap + j) * d + di;
-  store_rounded<T>(dst, t * inv_l, e * inv_l);
+  store_rounded<T>(dst, rh, rl);
 }
 
 // Kernels of length l_len at stride s_len (K^C1: l_C1, s_C1; K^C2: 4 l_C1, 4 s_C1).

@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "kc1_mean.hpp"
 
 namespace infv2 {
 
@@ -981,6 +982,15 @@ struct SplitArgs {
   // n_q; n_c1, n_c2, nch, nch2 are then those of the longest, n_kv
   const int32_t* seq_lens;
   int n_kv;
+  // kernels [app_begin, app_end) of every sequence are formed from K here
+  // (the decode step's append, infv2_select_blocks_append) instead of read:
+  // the logits sweep uses them and the workgroups of query token 0 write
+  // them to Kc1_out.  K [b][kv_cap][h_kv][d]; app_end <= app_begin: none.
+  const uint16_t* K;
+  uint16_t* Kc1_out;
+  int64_t kv_cap;
+  int app_begin, app_end, l_C1, s_C1;
+  double inv_l1;
 };
 
 // position of sequence b's first query token
@@ -1001,15 +1011,40 @@ __device__ __forceinline__ int split_rows(const SplitArgs& a, int b, bool coarse
 // n_rows-1 are clamped to it (the caller masks them); with no row at all
 // nothing is read.  C layout: acc[nt][i] is head 4*(lane>>4)+i, row
 // jw + 16*nt + (lane&15).
+// The rows of the decode step's append: where in K the sequence's keys of
+// this group start (kcol: offset to the lane's two features 2 lane, 2 lane +
+// 1), the row range, and where to write them (null: only use them).
+struct SplitAppend {
+  const uint16_t* kcol;
+  size_t row_stride;
+  uint16_t* out;           // K^C1 rows of this sequence and group, or null
+  int begin, end, l_len, s_len;
+  double inv_l;
+};
+
 __device__ __forceinline__ void split_logits_mfma(const uint16_t* keys, int n_rows, int jw,
                                                   const uint16_t* qrow_base, int lane,
-                                                  uint8_t* kst, f32x4 (&acc)[4]) {
+                                                  uint8_t* kst, f32x4 (&acc)[4],
+                                                  bool appending = false,
+                                                  const SplitAppend app = {}) {
   u32x4 v[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int j = min(jw + 4 * i + (lane >> 4), n_rows - 1);
     v[i] = n_rows > 0 ? *(const u32x4*)(keys + (size_t)j * SEL_D + 8 * (lane & 15))
                       : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // the wave's first appended kernel, formed while the rows above are in
+  // flight (its keys' loads overlap theirs); any further one is formed below
+  int j_app = -1;
+  uint32_t w_app = 0u;
+  if (appending) {
+    const int jb = max(app.begin, jw), je = min(min(app.end, jw + 64), n_rows);
+    if (jb < je) {
+      j_app = jb;
+      w_app = kmean_pair_bf16(app.kcol, app.row_stride, jb, app.l_len, app.s_len, app.inv_l);
+    }
   }
   // A operand: Q rows = heads (lane & 15), k = d
   bf16x8 qf[4];
@@ -1023,6 +1058,21 @@ __device__ __forceinline__ void split_logits_mfma(const uint16_t* keys, int n_ro
     for (int i = 8 * h; i < 8 * h + 8; ++i) {
       const int row = 4 * i + (lane >> 4) - 32 * h, c16 = lane & 15;
       *(u32x4*)(kst + row * SEL_ROW_BYTES + ((c16 ^ (row & 15)) << 4)) = v[i];
+    }
+    // appended kernels of this half: formed from the keys (all 64 lanes, two
+    // features each) in place of the rows just staged (not yet written in
+    // memory), and written back by one query token's workgroups
+    const int j_lo = jw + 32 * h;
+    if (appending && j_lo < app.end && j_lo + 32 > app.begin) {
+      const int r1 = min(min(app.end, j_lo + 32), n_rows);
+      for (int j = max(app.begin, j_lo); j < r1; ++j) {
+        const uint32_t w = j == j_app ? w_app
+                                      : kmean_pair_bf16(app.kcol, app.row_stride, j, app.l_len,
+                                                        app.s_len, app.inv_l);
+        const int row = j - j_lo, c16 = lane >> 2;
+        *(uint32_t*)(kst + row * SEL_ROW_BYTES + ((c16 ^ (row & 15)) << 4) + 4 * (lane & 3)) = w;
+        if (app.out) *(uint32_t*)(app.out + (size_t)j * SEL_D + 2 * lane) = w;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -1091,12 +1141,25 @@ __device__ __forceinline__ void split_chunk_partials(const f32x4 (&acc)[4], int 
 // Fine: writes z*c (-inf when not visible) to the logits buffer and the
 // chunk's per-head (max, sum).  COARSE: the same sweep over the coarse
 // kernels for the LSE approximation, partials only.
-template <bool COARSE>
+// APPEND: kernels [a.app_begin, a.app_end) are formed from K in the sweep
+// (the decode step's append) -- a separate instance, so that the others keep
+// their registers.
+template <bool COARSE, bool APPEND = false>
 __global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
   __shared__ float red_m[4][16], red_s[4][16];
   __shared__ __attribute__((aligned(16))) uint8_t kst_all[4][32 * SEL_ROW_BYTES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+  int chunk = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+  if constexpr (APPEND) {
+    // chunks from the last one down, every row's before the next chunk: the
+    // workgroups that form the appended kernels (the last chunks) start first
+    const int rows = gridDim.y * gridDim.z;
+    const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    chunk = gridDim.x - 1 - lin / rows;
+    const int r = lin % rows;
+    g = r % gridDim.y;
+    bt = r / gridDim.y;
+  }
   const int b = bt / a.n_q, t = bt % a.n_q;
   const int p = split_pos0(a, b) + t;
   const int jmax = COARSE ? last_visible_coarse(p) : last_visible_kernel(p);
@@ -1106,8 +1169,20 @@ __global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
   const int n_rows = split_rows(a, b, COARSE);
   const int jw = chunk * SPLIT_CK + wave * 64;
   f32x4 acc[4];
+  SplitAppend app = {};
+  const bool appending = APPEND && a.app_end > a.app_begin;
+  if (appending) {
+    app.kcol = a.K + ((size_t)b * a.kv_cap * a.h_kv + g) * SEL_D + 2 * lane;
+    app.row_stride = (size_t)a.h_kv * SEL_D;
+    app.out = t == 0 ? a.Kc1_out + ((size_t)b * a.h_kv + g) * a.c1_cap * SEL_D : nullptr;
+    app.begin = a.app_begin;
+    app.end = a.app_end;
+    app.l_len = a.l_C1;
+    app.s_len = a.s_C1;
+    app.inv_l = a.inv_l1;
+  }
   split_logits_mfma(keys, n_rows, jw, a.Q + (((size_t)b * a.n_q + t) * hq + g * SEL_G) * SEL_D,
-                    lane, kst_all[wave], acc);
+                    lane, kst_all[wave], acc, appending, app);
   float* lrow = a.logits + ((size_t)bt * a.h_kv + g) * SEL_G * a.n_c1p;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1681,7 +1756,10 @@ static void launch_split_scores(const infv2_problem& p, const SplitArgs& a, hipS
     else
       hipLaunchKernelGGL(scores_split_fused_kernel<false>, grid, dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(scores_split_logits_kernel<false>, grid, dim3(256), 0, stream, a);
+    if (a.app_end > a.app_begin)
+      hipLaunchKernelGGL((scores_split_logits_kernel<false, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(scores_split_logits_kernel<false>, grid, dim3(256), 0, stream, a);
     hipLaunchKernelGGL(scores_split_pool_kernel, grid, dim3(256), 0, stream, a);
   }
 }
@@ -1757,8 +1835,19 @@ size_t select_fused_workspace(const infv2_problem& p, int n_c1) {
 static hipError_t launch_select_split(const infv2_problem& p, const void* Q, const KeySet& ks,
                                       const int32_t* seq_lens, float* S_cmp, int32_t* idx,
                                       int32_t* n_sel, void* ws, int n_blk, float scale,
-                                      int budget, hipStream_t stream) {
+                                      int budget, hipStream_t stream,
+                                      const SplitArgs* append = nullptr) {
   SplitArgs a = split_args(p, Q, ks, S_cmp, ws, n_blk, scale);
+  if (append) {
+    a.K = append->K;
+    a.Kc1_out = append->Kc1_out;
+    a.kv_cap = append->kv_cap;
+    a.app_begin = append->app_begin;
+    a.app_end = append->app_end;
+    a.l_C1 = append->l_C1;
+    a.s_C1 = append->s_C1;
+    a.inv_l1 = append->inv_l1;
+  }
   a.seq_lens = seq_lens;
   a.n_kv = p.n_kv;
   a.cand = (uint64_t*)((char*)ws + align256(scores_workspace(p, ks)));
@@ -1801,6 +1890,27 @@ hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeyS
   }
   return launch_select_split(p, Q, ks, nullptr, S_cmp, idx, n_sel, ws, n_blk, scale, budget,
                              stream);
+}
+
+// The decode selection with the step's append fused into the logits sweep:
+// kernels [c1_begin, c1_end) of every sequence are formed from K inside the
+// sweep and written to Kc1 (bit for bit what launch_compress_k writes).
+// Requires scores_use_split(p), select_fused_shape(p, n_C1), exact LSE.
+hipError_t launch_select_append(const infv2_problem& p, const void* Q, const void* K, void* Kc1,
+                                int c1_begin, int c1_end, int64_t kv_cap, const KeySet& ks,
+                                int32_t* idx, int32_t* n_sel, void* ws, int n_blk, float scale,
+                                int budget, hipStream_t stream) {
+  SplitArgs app = {};
+  app.K = (const uint16_t*)K;
+  app.Kc1_out = (uint16_t*)Kc1;
+  app.kv_cap = kv_cap;
+  app.app_begin = c1_begin;
+  app.app_end = c1_end;
+  app.l_C1 = p.l_C1;
+  app.s_C1 = p.s_C1;
+  app.inv_l1 = 1.0 / (double)p.l_C1;
+  return launch_select_split(p, Q, ks, nullptr, nullptr, idx, n_sel, ws, n_blk, scale, budget,
+                             stream, &app);
 }
 
 // S_sh: S^shared [batch][h_kv][n_q][n_C1] as well, or null.
