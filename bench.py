@@ -627,10 +627,12 @@ STAGE_KERNELS = {
 # the kernels one call of each decode stage launches
 DECODE_STAGE_KERNELS = {
     "compress_append": ["compress_k_kernel"],
-    "select_blocks": ["scores_split_logits_kernel", "scores_split_pool_kernel",
+    # (the profiled run also times the three-call step, so the logits
+    # kernel's two instances are named apart)
+    "select_blocks": ["scores_split_logits_kernel<false,false>", "scores_split_pool_kernel",
                       "scores_select_merge_kernel"],
-    "select_blocks_append": ["scores_split_logits_kernel", "scores_split_pool_kernel",
-                             "scores_select_merge_kernel"],
+    "select_blocks_append": ["scores_split_logits_kernel<false,true>",
+                             "scores_split_pool_kernel", "scores_select_merge_kernel"],
     "sparse_attn": ["attn_split_kernel", "attn_merge_kernel"],
 }
 
