@@ -140,3 +140,52 @@ def test_varlen_paged_decode_step_graph_replay_matches_eager():
         for k in ("idx", "nsel", "O", "lse"):
             assert torch.equal(dict(idx=idx, nsel=nsel, O=O, lse=lse)[k], ref[k]), \
                 f"replay {rep}: {k} differs"
+
+
+def test_two_call_decode_step_graph_replay_matches_eager():
+    # the bench's decode step (the append inside the selection, then the
+    # attention) captured once; the appended K^C1 row is cleared to NaN
+    # between replays so that every replay must form it again
+    cfg = CONFIGS["decode"]
+    n_kv, batch = 9000, 3
+    print("case: two-call decode graph replay", n_kv, batch, flush=True)
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=79)
+    lp, op = problems(cfg, n_kv=n_kv, batch=batch)
+    dev = torch.device("cuda:0")
+    Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
+    n_c1, bud = tbs.n_kernels(lp), tbs.budget(lp)
+    Kc1 = tbs.compress_k(lp, K)
+    Kc1_ref = Kc1.clone()
+    idx = torch.empty((batch, lp.h_kv, 1, bud), dtype=torch.int32, device=dev)
+    nsel = torch.empty((batch, lp.h_kv, 1), dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((batch, lp.h_q, 1), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(max(tbs.select_blocks_workspace(lp), 16), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(tbs.sparse_attn_workspace(lp), 16), dtype=torch.uint8, device=dev)
+
+    def step():
+        tbs.select_blocks_append(lp, Q, K, Kc1, n_c1 - 1, n_c1, idx, nsel, ws_s)
+        tbs.sparse_attn(lp, Q, K, V, idx, nsel, O, lse, ws_a)
+
+    Kc1[:, :, n_c1 - 1] = float("nan")
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(Kc1, Kc1_ref)
+    ref = {k: t.clone() for k, t in dict(idx=idx, nsel=nsel, O=O, lse=lse).items()}
+    res = dict(Kc1=Kc1.cpu(), idx=idx.cpu(), n_sel=nsel.cpu(), O=O.cpu(), lse=lse.cpu())
+    check_rows(res, x, op, n_kv - 1, {b: np.array([0]) for b in range(batch)},
+               check_scores=False)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (O, lse, idx, nsel):
+            t.zero_()                     # eager work between replays
+        Kc1[:, :, n_c1 - 1] = float("nan")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Kc1, Kc1_ref), f"replay {rep}: Kc1 differs"
+        for k, t in dict(idx=idx, nsel=nsel, O=O, lse=lse).items():
+            assert torch.equal(t, ref[k]), f"replay {rep}: {k} differs"
