@@ -1143,9 +1143,10 @@ __device__ __forceinline__ void split_chunk_partials(const f32x4 (&acc)[4], int 
 // kernels for the LSE approximation, partials only.
 // APPEND: kernels [a.app_begin, a.app_end) are formed from K in the sweep
 // (the decode step's append) -- a separate instance, so that the others keep
-// their registers.
+// their registers; held to 128 VGPRs (four waves per SIMD) so that its 1024
+// workgroups fit the chip in one round, as the plain instance's do.
 template <bool COARSE, bool APPEND = false>
-__global__ void __launch_bounds__(256) scores_split_logits_kernel(SplitArgs a) {
+__global__ void __launch_bounds__(256, APPEND ? 4 : 1) scores_split_logits_kernel(SplitArgs a) {
   __shared__ float red_m[4][16], red_s[4][16];
   __shared__ __attribute__((aligned(16))) uint8_t kst_all[4][32 * SEL_ROW_BYTES];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
