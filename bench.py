@@ -620,8 +620,8 @@ STAGE_KERNELS = {
     "compress_k": ["compress_k_kernel"],
     "block_scores": ["scores_prefill_kernel", "scores_exact_kernel"],
     "topk_select": ["topk_kernel"],
-    "sparse_attn": ["kv_pack_kernel", "attn_prefill_kernel", "attn_range_kernel",
-                    "attn_range_merge_kernel"],
+    "sparse_attn": ["kv_pack_kernel", "attn_prefill_kernel", "attn_prefill_seq_kernel",
+                    "attn_range_kernel", "attn_range_merge_kernel"],
 }
 
 # the kernels one call of each decode stage launches

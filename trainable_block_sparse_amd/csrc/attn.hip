@@ -29,6 +29,12 @@
 
 #include "attn_layout.hpp"
 
+// tokens per wave of the sparse prefill attention below the key-range split
+// (1: attn_prefill_kernel; 2 or 4: attn_prefill_seq_kernel)
+#ifndef INFV2_ATTN_TPW
+#define INFV2_ATTN_TPW 2
+#endif
+
 namespace infv2 {
 
 
@@ -327,6 +333,167 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
   if (a.lse && grp == 0)
     __builtin_nontemporal_store((m_run + fast_log2(l_run)) * kLn2,
                                 a.lse + ((size_t)b * hq + g * AT_G + r16) * a.n_q + t);
+}
+
+// The sparse prefill (lists of at most 64 entries) with TPW consecutive
+// tokens per wave, taken one after the other: the wave walks the pairs
+// (token, list entry) of its tokens as one sequence, so that the loads run
+// two pairs ahead across the token boundaries and the next token starts with
+// its first blocks already in flight (a workgroup that starts cold waits a
+// list read and a block read before its first MFMA).  Every token is computed
+// exactly as in attn_prefill_kernel (same blocks, same order, same
+// arithmetic): O and LSE are bitwise the same.  Q of the wave's tokens is
+// staged in LDS; one wave per SIMD as there.
+template <int TPW>
+__global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
+  __shared__ u32x4 qlds[4][TPW][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_qb = (a.n_q + AT_B - 1) / AT_B;
+  const int n_bg = a.batch * a.h_kv;
+  constexpr int WPQ = 16 / TPW;                        // workgroups per query block
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, r = bid >> 3;
+  const int qbg = (r / WPQ) * 8 + xcd;                 // query block, global order
+  if (qbg >= n_qb * n_bg) return;
+  const int qb = n_qb - 1 - qbg / n_bg;                // late tokens (long rows) first
+  const int bg = qbg % n_bg;
+  const int g = bg % a.h_kv, b = bg / a.h_kv;
+  const int t0 = qb * AT_B + (r % WPQ) * (4 * TPW) + wave * TPW;
+  if (t0 >= a.n_q) return;
+  const int hq = a.h_kv * AT_G;
+  const int grp = lane >> 4, r16 = lane & 15;
+  // the wave's tokens: list entry `lane` of token j in E[j], pair counts,
+  // the pair index where each token starts; Q to LDS
+  int E[TPW], start[TPW + 1];
+  start[0] = 0;
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = t0 + j;
+    int nb = 0;
+    E[j] = -1;
+    if (t < a.n_q) {
+      const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+      nb = min(a.n_sel[row], a.budget);
+      E[j] = lane < nb ? a.idx[row * a.budget + lane] : -1;
+      const uint16_t* q = a.Q + (((size_t)b * a.n_q + t) * hq + g * AT_G + r16) * AT_D;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qlds[wave][j][ks][lane] = __builtin_nontemporal_load((const u32x4*)(q + 32 * ks + 8 * grp));
+    }
+    start[j + 1] = start[j] + nb;
+  }
+  const int ntok = min(TPW, a.n_q - t0);
+  const int total = start[TPW];
+  auto token_of = [&](int i) -> int {                  // (uniform)
+    int j = 0;
+#pragma unroll
+    for (int k = 1; k < TPW; ++k) j += (i >= start[k]) ? 1 : 0;
+    return j;
+  };
+  // block of pair i, or -1 when the entry is not a causal block of its token
+  auto block_at = [&](int i) -> int {
+    const int j = token_of(i);
+    int ev = E[0];
+#pragma unroll
+    for (int k = 1; k < TPW; ++k) ev = (j == k) ? E[k] : ev;
+    const int blk = __builtin_amdgcn_readlane(ev, i - start[j]);
+    const int bpj = (a.q_pos0 + t0 + j) / AT_B;
+    return (blk < 0 || blk > bpj) ? -1 : blk;
+  };
+  const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS + lane * 8;
+  const uint16_t* kbase = a.Kp + pack0;
+  const uint16_t* vbase = a.Vp + pack0;
+  auto load_k = [&](int blk, bf16x8 (&kf)[4][4]) {
+    const uint16_t* src = kbase + (uint32_t)blk * PACK_ELEMS;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[tt][ks] = as_bf16x8(*(const u32x4*)(src + (4 * tt + ks) * 512));
+  };
+  auto load_v = [&](int blk, bf16x8 (&vf)[8][2]) {
+    const uint16_t* src = vbase + (uint32_t)blk * PACK_ELEMS;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) vf[mt][ks] = as_bf16x8(*(const u32x4*)(src + (2 * mt + ks) * 512));
+  };
+  // the current token's state
+  bf16x8 qf[4];
+  f32x4 o[8];
+  float m_run = kNegInf, l_run = 0.f;
+  int cur = -1, p = 0, b_p = 0;
+  auto begin_token = [&](int j) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(qlds[wave][j][ks][lane]);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = kNegInf;
+    l_run = 0.f;
+    cur = j;
+    p = a.q_pos0 + t0 + j;
+    b_p = p / AT_B;
+  };
+  auto finish_token = [&]() {
+    float l = l_run;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.0f / l;
+    const int t = t0 + cur;
+    uint16_t* orow = a.O + (((size_t)b * a.n_q + t) * hq + g * AT_G + r16) * AT_D;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const uint32_t w0 = pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv);
+      __builtin_nontemporal_store(u32x2{w0, w1}, (u32x2*)(orow + 16 * mt + 4 * grp));
+    }
+    if (a.lse && grp == 0)
+      __builtin_nontemporal_store((m_run + fast_log2(l)) * kLn2,
+                                  a.lse + ((size_t)b * hq + g * AT_G + r16) * a.n_q + t);
+  };
+  // make pair i's token the current one (tokens without pairs in between
+  // are finished as they come: O and LSE as for an empty list)
+  auto reach = [&](int j) {
+    while (cur < j) {
+      if (cur >= 0) finish_token();
+      begin_token(cur + 1);
+    }
+  };
+  bf16x8 kA[4][4], vA[8][2], kB[4][4], vB[8][2], pf[2];
+  auto step = [&](int blk, bf16x8 (&kf)[4][4], bf16x8 (&vf)[8][2], int nxt) {
+    const int kv0 = max(blk, 0) * AT_B;
+    if (blk == b_p)
+      attn_scores<true>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+    else if (blk < 0)
+      attn_scores<true>(qf, kf, o, m_run, l_run, kv0, -1, a.c, lane, pf);
+    else
+      attn_scores<false>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+    load_k(max(nxt, 0), kf);
+    __builtin_amdgcn_sched_barrier(0);
+    attn_pv(vf, pf, o);
+    load_v(max(nxt, 0), vf);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (total > 0) {
+    int b0 = block_at(0);
+    int b1 = block_at(min(1, total - 1));
+    load_k(max(b0, 0), kA);
+    load_v(max(b0, 0), vA);
+    load_k(max(b1, 0), kB);
+    load_v(max(b1, 0), vB);
+    for (int bi = 0; bi < total; bi += 2) {
+      const int n2 = block_at(min(bi + 2, total - 1));
+      reach(token_of(bi));
+      step(b0, kA, vA, n2);
+      if (bi + 1 >= total) break;
+      const int n3 = block_at(min(bi + 3, total - 1));
+      reach(token_of(bi + 1));
+      step(b1, kB, vB, n3);
+      b0 = n2;
+      b1 = n3;
+    }
+  }
+  reach(ntok - 1);
+  finish_token();
 }
 
 // ---------------------------------------------------------------------------
@@ -1311,6 +1478,10 @@ hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, con
     dim3 grid(((total_qb + 7) / 8) * 8 * 16);
     if (sparse && budget > 64) {
       hipLaunchKernelGGL((attn_prefill_kernel<true, true>), grid, dim3(256), 0, stream, a);
+    } else if (sparse && INFV2_ATTN_TPW > 1) {
+      constexpr int TPW = INFV2_ATTN_TPW;
+      const dim3 grid_seq(((total_qb + 7) / 8) * 8 * (16 / TPW));
+      hipLaunchKernelGGL(attn_prefill_seq_kernel<TPW>, grid_seq, dim3(256), 0, stream, a);
     } else if (sparse) {
       hipLaunchKernelGGL((attn_prefill_kernel<true, false>), grid, dim3(256), 0, stream, a);
     } else {
