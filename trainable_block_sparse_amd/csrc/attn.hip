@@ -223,7 +223,10 @@ __device__ __forceinline__ void load_qfrag(const AttnArgs& a, int b, int t, int 
 // time; the common case never touches memory for the list inside the loop.
 template <bool SPARSE, bool LONG>
 __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (the wave index and the list length are made uniform: a loop whose bound
+  // the compiler takes as per-lane gets exec-masked paths, and the wait counts
+  // of its loads become conservative)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_qb = (a.n_q + AT_B - 1) / AT_B;
   const int n_bg = a.batch * a.h_kv;
   const int bid = blockIdx.x;
@@ -244,7 +247,7 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
   for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
   const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
-  const int nblocks = SPARSE ? a.n_sel[row] : b_p + 1;
+  const int nblocks = __builtin_amdgcn_readfirstlane(SPARSE ? a.n_sel[row] : b_p + 1);
   const int32_t* sel = SPARSE ? a.idx + row * a.budget : nullptr;
   const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS + lane * 8;
   const uint16_t* kbase = a.Kp + pack0;
@@ -283,14 +286,17 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) vf[mt][ks] = as_bf16x8(*(const u32x4*)(src + (2 * mt + ks) * 512));
   };
-  // Every iteration issues the loads of the next entry unconditionally (the
-  // last one re-reads its own block), so the loads in flight are the same on
-  // every path and the waits stay precise.  A non-causal entry is processed as
-  // block 0 with every key masked: it adds nothing.
   // Two register sets (A: even list entries, B: odd ones): the K and V of
-  // entries i+1 and i+2 are in flight while entry i is computed.
+  // entries i+1 and i+2 are in flight while entry i is computed.  Inside the
+  // loop every step issues the loads of the entry two ahead unconditionally
+  // (past the end, its own block again), so the loads in flight are the same
+  // on every path; the loop has no other exit than its end test (an exit
+  // between the two steps gives the compiler a path that skips set B's loads,
+  // and its wait counts for set A turn conservative), and an odd last entry
+  // is computed after it, with nothing left to load.  A non-causal entry is
+  // processed as block 0 with every key masked: it adds nothing.
   bf16x8 kA[4][4], vA[8][2], kB[4][4], vB[8][2], pf[2];
-  auto step = [&](int blk, bf16x8 (&kf)[4][4], bf16x8 (&vf)[8][2], int nxt) {
+  auto score = [&](int blk, bf16x8 (&kf)[4][4]) {
     const int kv0 = max(blk, 0) * AT_B;
     if (blk == b_p)
       attn_scores<true>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
@@ -298,6 +304,9 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
       attn_scores<true>(qf, kf, o, m_run, l_run, kv0, -1, a.c, lane, pf);
     else
       attn_scores<false>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+  };
+  auto step = [&](int blk, bf16x8 (&kf)[4][4], bf16x8 (&vf)[8][2], int nxt) {
+    score(blk, kf);
     load_k(max(nxt, 0), kf);
     __builtin_amdgcn_sched_barrier(0);
     attn_pv(vf, pf, o);
@@ -306,18 +315,30 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
   };
   int b0 = block_at(0);
   int b1 = block_at(min(1, nblocks - 1));
+  // issued in the loop's order (the scheduling barriers keep the scheduler
+  // from reordering them: the wait counts at the loop head merge this order
+  // with the loop's, and any other order makes every step wait for all loads
+  // in flight, the prefetch included)
   load_k(max(b0, 0), kA);
+  __builtin_amdgcn_sched_barrier(0);
   load_v(max(b0, 0), vA);
+  __builtin_amdgcn_sched_barrier(0);
   load_k(max(b1, 0), kB);
+  __builtin_amdgcn_sched_barrier(0);
   load_v(max(b1, 0), vB);
-  for (int bi = 0; bi < nblocks; bi += 2) {
+  __builtin_amdgcn_sched_barrier(0);
+  int bi = 0;
+  for (; bi + 1 < nblocks; bi += 2) {
     const int n2 = block_at(min(bi + 2, nblocks - 1));
     step(b0, kA, vA, n2);
-    if (bi + 1 >= nblocks) break;
     const int n3 = block_at(min(bi + 3, nblocks - 1));
     step(b1, kB, vB, n3);
     b0 = n2;
     b1 = n3;
+  }
+  if (bi < nblocks) {
+    score(b0, kA);
+    attn_pv(vA, pf, o);
   }
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
@@ -347,7 +368,8 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
 template <int TPW>
 __global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
   __shared__ u32x4 qlds[4][TPW][4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // (uniform wave index and counts, as in attn_prefill_kernel)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n_qb = (a.n_q + AT_B - 1) / AT_B;
   const int n_bg = a.batch * a.h_kv;
   constexpr int WPQ = 16 / TPW;                        // workgroups per query block
@@ -373,7 +395,7 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
     E[j] = -1;
     if (t < a.n_q) {
       const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
-      nb = min(a.n_sel[row], a.budget);
+      nb = __builtin_amdgcn_readfirstlane(min(a.n_sel[row], a.budget));
       E[j] = lane < nb ? a.idx[row * a.budget + lane] : -1;
       const uint16_t* q = a.Q + (((size_t)b * a.n_q + t) * hq + g * AT_G + r16) * AT_D;
 #pragma unroll
@@ -450,16 +472,25 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
       __builtin_nontemporal_store((m_run + fast_log2(l)) * kLn2,
                                   a.lse + ((size_t)b * hq + g * AT_G + r16) * a.n_q + t);
   };
-  // make pair i's token the current one (tokens without pairs in between
-  // are finished as they come: O and LSE as for an empty list)
-  auto reach = [&](int j) {
-    while (cur < j) {
+  // tokens without pairs: O and LSE as the one-token kernel leaves them for
+  // an empty list (written here, so that the loop only ever moves forward to
+  // a token that has pairs)
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+    if (j < ntok && start[j + 1] == start[j]) {
+      begin_token(j);
+      finish_token();
+    }
+  cur = -1;
+  // make token j (uniform) the current one
+  auto switch_to = [&](int j) {
+    if (j != cur) {
       if (cur >= 0) finish_token();
-      begin_token(cur + 1);
+      begin_token(j);
     }
   };
   bf16x8 kA[4][4], vA[8][2], kB[4][4], vB[8][2], pf[2];
-  auto step = [&](int blk, bf16x8 (&kf)[4][4], bf16x8 (&vf)[8][2], int nxt) {
+  auto score = [&](int blk, bf16x8 (&kf)[4][4]) {
     const int kv0 = max(blk, 0) * AT_B;
     if (blk == b_p)
       attn_scores<true>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
@@ -467,32 +498,43 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
       attn_scores<true>(qf, kf, o, m_run, l_run, kv0, -1, a.c, lane, pf);
     else
       attn_scores<false>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+  };
+  auto step = [&](int blk, bf16x8 (&kf)[4][4], bf16x8 (&vf)[8][2], int nxt) {
+    score(blk, kf);
     load_k(max(nxt, 0), kf);
     __builtin_amdgcn_sched_barrier(0);
     attn_pv(vf, pf, o);
     load_v(max(nxt, 0), vf);
     __builtin_amdgcn_sched_barrier(0);
   };
-  if (total > 0) {
-    int b0 = block_at(0);
-    int b1 = block_at(min(1, total - 1));
-    load_k(max(b0, 0), kA);
-    load_v(max(b0, 0), vA);
-    load_k(max(b1, 0), kB);
-    load_v(max(b1, 0), vB);
-    for (int bi = 0; bi < total; bi += 2) {
-      const int n2 = block_at(min(bi + 2, total - 1));
-      reach(token_of(bi));
-      step(b0, kA, vA, n2);
-      if (bi + 1 >= total) break;
-      const int n3 = block_at(min(bi + 3, total - 1));
-      reach(token_of(bi + 1));
-      step(b1, kB, vB, n3);
-      b0 = n2;
-      b1 = n3;
-    }
+  if (total == 0) return;
+  // the loop's structure, load order and odd tail as in attn_prefill_kernel
+  int b0 = block_at(0);
+  int b1 = block_at(min(1, total - 1));
+  load_k(max(b0, 0), kA);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v(max(b0, 0), vA);
+  __builtin_amdgcn_sched_barrier(0);
+  load_k(max(b1, 0), kB);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v(max(b1, 0), vB);
+  __builtin_amdgcn_sched_barrier(0);
+  int bi = 0;
+  for (; bi + 1 < total; bi += 2) {
+    const int n2 = block_at(min(bi + 2, total - 1));
+    switch_to(token_of(bi));
+    step(b0, kA, vA, n2);
+    const int n3 = block_at(min(bi + 3, total - 1));
+    switch_to(token_of(bi + 1));
+    step(b1, kB, vB, n3);
+    b0 = n2;
+    b1 = n3;
   }
-  reach(ntok - 1);
+  if (bi < total) {
+    switch_to(token_of(bi));
+    score(b0, kA);
+    attn_pv(vA, pf, o);
+  }
   finish_token();
 }
 
