@@ -315,7 +315,7 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(BwdArgs a) {
 // block only K in the feature layout (16 KB) and the 2 KB tile are read, for
 // dQ^T += K^T dZ^T.  Mapping as attn_bwd_dq_kernel.  Deterministic.
 __global__ void __launch_bounds__(256, 4) attn_bwd_dq_stash_kernel(BwdArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qb_base = a.t_base / AT_B;                 // (t_base is a multiple of 64)
   const int n_qb = (a.t_end - a.t_base + AT_B - 1) / AT_B;
   const int n_bg = a.batch * a.h_kv;
@@ -335,13 +335,22 @@ __global__ void __launch_bounds__(256, 4) attn_bwd_dq_stash_kernel(BwdArgs a) {
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
-  const int nblocks = a.n_sel[row];
+  // (uniform count; the list is read into lanes 64 entries at a time, so
+  // that an entry costs a lane read, not a memory round trip before its
+  // block's loads)
+  const int nblocks = __builtin_amdgcn_readfirstlane(a.n_sel[row]);
   const int32_t* sel = a.idx + row * a.budget;
   const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS + lane * 8;
   const size_t srow = ((size_t)b * a.h_kv + g) * a.stash_tokens + (t - a.t_base);
   const uint16_t* dz0 = a.dZ + srow * a.budget * 1024 + lane * 8;
+  int list_base = 0;
+  int my_entry = lane < nblocks ? sel[lane] : -1;
   for (int bi = 0; bi < nblocks; ++bi) {
-    const int blk = sel[bi];
+    if (bi >= list_base + 64) {
+      list_base = bi;
+      my_entry = bi + lane < nblocks ? sel[bi + lane] : -1;
+    }
+    const int blk = __builtin_amdgcn_readlane(my_entry, bi - list_base);
     if (blk < 0 || blk > b_p) continue;     // never stashed
     const size_t boff = pack0 + (size_t)blk * PACK_ELEMS;
     bf16x8 kvf[8][2], dzf[2];
@@ -463,7 +472,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
     if (tid == 0) ntok_s = t_hi - t_first;
   }
   __syncthreads();
-  const int ntok = ntok_s;
+  // (uniform: a loop bound the compiler takes as per-lane gets exec-masked
+  // paths, and the wait counts of the loads in the loop become conservative)
+  const int ntok = __builtin_amdgcn_readfirstlane(ntok_s);
   if (ntok == 0) return;
   const int npairs = (ntok + 1) >> 1;
   const int grp = lane >> 4, r16 = lane & 15;
@@ -629,25 +640,33 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   // even pairs, set B of odd pairs, loaded two pairs ahead.  Loads and stores
   // are unconditional (pair indices past the end are clamped to the last
   // pair, whose copies are never read): a load under a branch would make the
-  // compiler wait for all loads in flight where the branch joins.
+  // compiler wait for all loads in flight where the branch joins.  For the
+  // same reason the loop has no exit between its two halves (an odd last
+  // pair is computed after it) and the first loads are issued in the loop's
+  // order (the scheduling barriers keep them so).
   const int last = npairs - 1;
   BwdStage sa, sb;
   stage_load(0, sa);
+  __builtin_amdgcn_sched_barrier(0);
   stage_load(min(1, last), sb);
+  __builtin_amdgcn_sched_barrier(0);
   stage_store(0, sa);
+  __builtin_amdgcn_sched_barrier(0);
   stage_load(min(2, last), sa);
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
-  for (int i = 0; i < npairs; i += 2) {
+  int i = 0;
+  for (; i + 1 < npairs; i += 2) {
     compute(0, i);
     stage_store(1, sb);
     stage_load(min(i + 3, last), sb);
     __syncthreads();
-    if (i + 1 >= npairs) break;
     compute(1, i + 1);
     stage_store(0, sa);
     stage_load(min(i + 4, last), sa);
     __syncthreads();
   }
+  if (i < npairs) compute(0, i);
   // C layout: rows = keys tile_key(wave, 4grp + j), column = feature 16nt + r16
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
