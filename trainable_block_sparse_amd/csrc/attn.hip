@@ -772,8 +772,10 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
     }
   };
   bf16x8 kf[4][4], vf[8][2], pf[2];
-  load_k(cur & 0xffff, kf);
+  load_k(cur & 0xffff, kf);                           // (in the loop's order)
+  __builtin_amdgcn_sched_barrier(0);
   load_v(cur & 0xffff, vf);
+  __builtin_amdgcn_sched_barrier(0);
   for (int i = 0; i < total; ++i) {
     const bool last = i + 1 >= total;
     const int nx = pair_at(i + 1);
@@ -781,7 +783,10 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
     const int kv0 = blk * AT_B;
     // scores S^T = K Q^T; each tile's K fragments are refilled with the next
     // pair's as soon as its MFMAs have issued, and each V fragment after the
-    // PV MFMAs that read it, so the loads have about a whole pair to land
+    // PV MFMAs that read it, so the loads have about a whole pair to land.
+    // The refills are unconditional (the last pair re-reads its own block):
+    // a load under a branch makes the compiler's waits count it as absent,
+    // and the first P*V would then also wait for a refill of the next pair.
     const int so_nx = (nx & 0xffff) * (PACK_ELEMS * 2);
     f32x4 sc[4];
 #pragma unroll
@@ -789,12 +794,10 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
       sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) sc[t] = mfma16(kf[t][ks], qc[ks], sc[t]);
-      if (!last) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kf[t][ks] = __builtin_bit_cast(
-              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, so_nx + (4 * t + ks) * 1024, 0));
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        kf[t][ks] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, so_nx + (4 * t + ks) * 1024, 0));
     }
     __builtin_amdgcn_sched_barrier(0);
     if (blk == bp_tok)
@@ -805,12 +808,10 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
     for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) o[mt] = mfma16(vf[mt][ks], pf[ks], o[mt]);
-      if (!last) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          vf[mt][ks] = __builtin_bit_cast(
-              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, so_nx + (2 * mt + ks) * 1024, 0));
-      }
+      for (int ks = 0; ks < 2; ++ks)
+        vf[mt][ks] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, so_nx + (2 * mt + ks) * 1024, 0));
     }
     __builtin_amdgcn_sched_barrier(0);
     if (last || (nx >> 16) != tok) {
