@@ -288,33 +288,48 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
   };
   // Two register sets (A: even list entries, B: odd ones): the K and V of
   // entries i+1 and i+2 are in flight while entry i is computed.  Inside the
-  // loop every step issues the loads of the entry two ahead unconditionally
-  // (past the end, its own block again), so the loads in flight are the same
-  // on every path; the loop has no other exit than its end test (an exit
-  // between the two steps gives the compiler a path that skips set B's loads,
-  // and its wait counts for set A turn conservative), and an odd last entry
-  // is computed after it, with nothing left to load.  A non-causal entry is
-  // processed as block 0 with every key masked: it adds nothing.
+  // loop every step issues its loads unconditionally (past the end, the last
+  // entry's block again), so the loads in flight are the same on every path;
+  // the loop has no other exit than its end test (an exit between the two
+  // steps gives the compiler a path that skips set B's loads, and its wait
+  // counts for set A turn conservative).  The pipeline is skewed by one
+  // entry: step i issues the score MFMAs of entry i, then the P*V MFMAs of
+  // entry i-1, then the softmax of entry i, so that with one wave per SIMD
+  // neither the softmax nor a P*V waits on the MFMAs just before it; O, m and
+  // l see the same operations in the same order as unskewed (bitwise the
+  // same output).  Entry i's K set is refilled with entry i+2 after its score
+  // MFMAs, entry i-1's V set with entry i+1 after its P*V.  A non-causal entry
+  // is processed as block 0 with every key masked: it adds nothing.
   bf16x8 kA[4][4], vA[8][2], kB[4][4], vB[8][2], pf[2];
-  auto score = [&](int blk, bf16x8 (&kf)[4][4]) {
+  auto score_mfma = [&](bf16x8 (&kf)[4][4], f32x4 (&sc)[4]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sc[tt] = mfma16(kf[tt][ks], qf[ks], sc[tt]);
+    }
+  };
+  auto softmax_of = [&](int blk, f32x4 (&sc)[4]) {
     const int kv0 = max(blk, 0) * AT_B;
     if (blk == b_p)
-      attn_scores<true>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+      attn_softmax<true>(sc, o, m_run, l_run, kv0, p, a.c, lane, pf);
     else if (blk < 0)
-      attn_scores<true>(qf, kf, o, m_run, l_run, kv0, -1, a.c, lane, pf);
+      attn_softmax<true>(sc, o, m_run, l_run, kv0, -1, a.c, lane, pf);
     else
-      attn_scores<false>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+      attn_softmax<false>(sc, o, m_run, l_run, kv0, p, a.c, lane, pf);
   };
-  auto step = [&](int blk, bf16x8 (&kf)[4][4], bf16x8 (&vf)[8][2], int nxt) {
-    score(blk, kf);
-    load_k(max(nxt, 0), kf);
+  auto step = [&](int blk, bf16x8 (&kx)[4][4], bf16x8 (&vy)[8][2], int nk, int nv) {
+    f32x4 sc[4];
+    score_mfma(kx, sc);
+    load_k(max(nk, 0), kx);
     __builtin_amdgcn_sched_barrier(0);
-    attn_pv(vf, pf, o);
-    load_v(max(nxt, 0), vf);
+    attn_pv(vy, pf, o);
+    load_v(max(nv, 0), vy);
     __builtin_amdgcn_sched_barrier(0);
+    softmax_of(blk, sc);
   };
-  int b0 = block_at(0);
-  int b1 = block_at(min(1, nblocks - 1));
+  const int b0 = block_at(0);
+  int bcur = block_at(min(1, nblocks - 1));
   // issued in the loop's order (the scheduling barriers keep the scheduler
   // from reordering them: the wait counts at the loop head merge this order
   // with the loop's, and any other order makes every step wait for all loads
@@ -323,22 +338,31 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   load_v(max(b0, 0), vA);
   __builtin_amdgcn_sched_barrier(0);
-  load_k(max(b1, 0), kB);
+  load_k(max(bcur, 0), kB);
   __builtin_amdgcn_sched_barrier(0);
-  load_v(max(b1, 0), vB);
+  load_v(max(bcur, 0), vB);
   __builtin_amdgcn_sched_barrier(0);
-  int bi = 0;
-  for (; bi + 1 < nblocks; bi += 2) {
-    const int n2 = block_at(min(bi + 2, nblocks - 1));
-    step(b0, kA, vA, n2);
-    const int n3 = block_at(min(bi + 3, nblocks - 1));
-    step(b1, kB, vB, n3);
-    b0 = n2;
-    b1 = n3;
-  }
-  if (bi < nblocks) {
-    score(b0, kA);
-    attn_pv(vA, pf, o);
+  if (nblocks > 0) {
+    // entry 0: scores and softmax (its P*V goes with entry 1)
+    f32x4 sc[4];
+    score_mfma(kA, sc);
+    load_k(max(block_at(min(2, nblocks - 1)), 0), kA);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_of(b0, sc);
+    int bi = 1;
+    for (; bi + 1 < nblocks; bi += 2) {
+      const int bnx = block_at(bi + 1);
+      const int b2 = block_at(min(bi + 2, nblocks - 1));
+      step(bcur, kB, vA, b2, bnx);
+      step(bnx, kA, vB, block_at(min(bi + 3, nblocks - 1)), b2);
+      bcur = b2;
+    }
+    if (bi < nblocks) {
+      step(bcur, kB, vA, bcur, bcur);     // an odd last entry (set B)
+      attn_pv(vB, pf, o);
+    } else {
+      attn_pv(vA, pf, o);                 // the last entry is even (set A)
+    }
   }
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
@@ -444,9 +468,11 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
   f32x4 o[8];
   float m_run = kNegInf, l_run = 0.f;
   int cur = -1, p = 0, b_p = 0;
-  auto begin_token = [&](int j) {
+  auto load_q = [&](int j) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(qlds[wave][j][ks][lane]);
+  };
+  auto reset_token = [&](int j) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run = kNegInf;
@@ -478,62 +504,93 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < TPW; ++j)
     if (j < ntok && start[j + 1] == start[j]) {
-      begin_token(j);
+      reset_token(j);
       finish_token();
     }
   cur = -1;
-  // make token j (uniform) the current one
-  auto switch_to = [&](int j) {
-    if (j != cur) {
-      if (cur >= 0) finish_token();
-      begin_token(j);
+  bf16x8 kA[4][4], vA[8][2], kB[4][4], vB[8][2], pf[2];
+  auto score_mfma = [&](bf16x8 (&kf)[4][4], f32x4 (&sc)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sc[t] = mfma16(kf[t][ks], qf[ks], sc[t]);
     }
   };
-  bf16x8 kA[4][4], vA[8][2], kB[4][4], vB[8][2], pf[2];
-  auto score = [&](int blk, bf16x8 (&kf)[4][4]) {
+  auto softmax_of = [&](int blk, f32x4 (&sc)[4]) {
     const int kv0 = max(blk, 0) * AT_B;
     if (blk == b_p)
-      attn_scores<true>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+      attn_softmax<true>(sc, o, m_run, l_run, kv0, p, a.c, lane, pf);
     else if (blk < 0)
-      attn_scores<true>(qf, kf, o, m_run, l_run, kv0, -1, a.c, lane, pf);
+      attn_softmax<true>(sc, o, m_run, l_run, kv0, -1, a.c, lane, pf);
     else
-      attn_scores<false>(qf, kf, o, m_run, l_run, kv0, p, a.c, lane, pf);
+      attn_softmax<false>(sc, o, m_run, l_run, kv0, p, a.c, lane, pf);
   };
-  auto step = [&](int blk, bf16x8 (&kf)[4][4], bf16x8 (&vf)[8][2], int nxt) {
-    score(blk, kf);
-    load_k(max(nxt, 0), kf);
+  // The pipeline is skewed by one pair, as in attn_range_kernel: step i
+  // issues the score MFMAs of pair i, then the P*V MFMAs of pair i-1, then
+  // the softmax of pair i, so that with one wave per SIMD neither the
+  // softmax nor a P*V waits on the MFMAs just before it.  Each token's O, m
+  // and l see the same operations in the same order as unskewed: the output
+  // is bitwise the same.  Pair i's K and V are in set (i even ? A : B); its K
+  // set is refilled with pair i+2 after its score MFMAs, and pair i-1's V set
+  // with pair i+1 after its P*V.  At a token change the new token's Q comes
+  // in before pair i's score MFMAs, and the old token is finished after the
+  // P*V of its last pair.
+  auto step = [&](int i, int blk, bf16x8 (&kx)[4][4], bf16x8 (&vy)[8][2], int nk, int nv) {
+    const int j = token_of(i);
+    const bool sw = j != cur;
+    if (sw) load_q(j);
+    f32x4 sc[4];
+    score_mfma(kx, sc);
+    load_k(max(nk, 0), kx);
     __builtin_amdgcn_sched_barrier(0);
-    attn_pv(vf, pf, o);
-    load_v(max(nxt, 0), vf);
+    attn_pv(vy, pf, o);
+    load_v(max(nv, 0), vy);
     __builtin_amdgcn_sched_barrier(0);
+    if (sw) {
+      finish_token();
+      reset_token(j);
+    }
+    softmax_of(blk, sc);
   };
   if (total == 0) return;
-  // the loop's structure, load order and odd tail as in attn_prefill_kernel
-  int b0 = block_at(0);
-  int b1 = block_at(min(1, total - 1));
+  // first loads in the loop's order (see attn_prefill_kernel)
+  const int b0 = block_at(0);
+  int bcur = block_at(min(1, total - 1));
   load_k(max(b0, 0), kA);
   __builtin_amdgcn_sched_barrier(0);
   load_v(max(b0, 0), vA);
   __builtin_amdgcn_sched_barrier(0);
-  load_k(max(b1, 0), kB);
+  load_k(max(bcur, 0), kB);
   __builtin_amdgcn_sched_barrier(0);
-  load_v(max(b1, 0), vB);
+  load_v(max(bcur, 0), vB);
   __builtin_amdgcn_sched_barrier(0);
-  int bi = 0;
+  {
+    // pair 0: its token, scores and softmax (its P*V goes with pair 1)
+    const int j = token_of(0);
+    load_q(j);
+    reset_token(j);
+    f32x4 sc[4];
+    score_mfma(kA, sc);
+    load_k(max(block_at(min(2, total - 1)), 0), kA);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_of(b0, sc);
+  }
+  // whole pairs of steps (B: odd pairs, A: even ones); no exit in between
+  int bi = 1;
   for (; bi + 1 < total; bi += 2) {
-    const int n2 = block_at(min(bi + 2, total - 1));
-    switch_to(token_of(bi));
-    step(b0, kA, vA, n2);
-    const int n3 = block_at(min(bi + 3, total - 1));
-    switch_to(token_of(bi + 1));
-    step(b1, kB, vB, n3);
-    b0 = n2;
-    b1 = n3;
+    const int bnx = block_at(bi + 1);
+    const int b2 = block_at(min(bi + 2, total - 1));
+    step(bi, bcur, kB, vA, b2, bnx);
+    step(bi + 1, bnx, kA, vB, block_at(min(bi + 3, total - 1)), b2);
+    bcur = b2;
   }
   if (bi < total) {
-    switch_to(token_of(bi));
-    score(b0, kA);
-    attn_pv(vA, pf, o);
+    // an odd last pair (set B), with nothing left to load
+    step(bi, bcur, kB, vA, bcur, bcur);
+    attn_pv(vB, pf, o);
+  } else {
+    attn_pv(vA, pf, o);                 // the last pair is even (set A)
   }
   finish_token();
 }
@@ -646,8 +703,7 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
       e[j] = a.idx[row * a.budget + lane];
     }
   }
-  // --- per token: the run inside range r, its slot, the token's range count;
-  // Q of every token with a run goes to LDS
+  // --- per token: the run inside range r, its slot, the token's range count
   int slot_l = 0, nparts_l = 0;                       // lane j holds token j's values
   int total = 0;
 #pragma unroll
@@ -674,16 +730,22 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
     const int blk = __shfl(e[j], min(s + lane, 63), 64);
     if (lane < c) prs[wave][total + lane] = (j << 16) | min(max(blk, 0), b_p);
     total += c;
-    if (c > 0) {
-      const uint16_t* q = a.Q + (((size_t)b * a.n_q + ra.t_base + tc0 + j) * hq + g * AT_G +
-                                 (lane & 15)) * AT_D;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qlds[wave][j][ks][lane] =
-            __builtin_nontemporal_load((const u32x4*)(q + 32 * ks + 8 * (lane >> 4)));
-    }
   }
   if (total == 0) return;                             // (no barrier below)
+  // Q of the wave's tokens into registers now, to LDS once the first pair's
+  // K and V loads are issued: the Q and K/V round trips overlap (a token
+  // without a run in r is loaded and never read; one past the chunk reads
+  // the chunk's last token)
+  u32x4 qr[RG_MAX_TPW][4];
+#pragma unroll
+  for (int j = 0; j < RG_MAX_TPW; ++j) {
+    if (j >= ra.tpw) break;
+    const int tq = ra.t_base + min(tc0 + j, ra.n_ct - 1);
+    const uint16_t* q = a.Q + (((size_t)b * a.n_q + tq) * hq + g * AT_G + (lane & 15)) * AT_D;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qr[j][ks] = __builtin_nontemporal_load((const u32x4*)(q + 32 * ks + 8 * (lane >> 4)));
+  }
   const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS;
   const uint32_t pack_bytes = (uint32_t)a.n_blk * PACK_ELEMS * 2;
   const __amdgpu_buffer_rsrc_t rk = pack_rsrc(a.Kp + pack0, pack_bytes);
@@ -734,7 +796,6 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
   int tok = cur >> 16;
   int p_tok = pos_base + tc0 + tok;
   int bp_tok = p_tok / AT_B;
-  load_q(tok);
   // finish the current token: its output (one range) or its partial
   auto finish = [&]() {
     float l = l_run;
@@ -776,19 +837,25 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
   __builtin_amdgcn_sched_barrier(0);
   load_v(cur & 0xffff, vf);
   __builtin_amdgcn_sched_barrier(0);
-  for (int i = 0; i < total; ++i) {
-    const bool last = i + 1 >= total;
-    const int nx = pair_at(i + 1);
-    const int blk = cur & 0xffff;
-    const int kv0 = blk * AT_B;
-    // scores S^T = K Q^T; each tile's K fragments are refilled with the next
-    // pair's as soon as its MFMAs have issued, and each V fragment after the
-    // PV MFMAs that read it, so the loads have about a whole pair to land.
-    // The refills are unconditional (the last pair re-reads its own block):
-    // a load under a branch makes the compiler's waits count it as absent,
-    // and the first P*V would then also wait for a refill of the next pair.
-    const int so_nx = (nx & 0xffff) * (PACK_ELEMS * 2);
-    f32x4 sc[4];
+#pragma unroll
+  for (int j = 0; j < RG_MAX_TPW; ++j) {
+    if (j >= ra.tpw) break;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qlds[wave][j][ks][lane] = qr[j][ks];
+  }
+  load_q(tok);
+  // The pipeline is skewed by one pair: step i issues the score MFMAs of
+  // pair i, then the P*V MFMAs of pair i-1, then the softmax of pair i, so
+  // that neither the softmax (which reads the score MFMAs' results) nor a
+  // P*V (which reads the softmax's probabilities) waits on the instruction
+  // just before it.  Every token's O, m and l see the same operations in the
+  // same order as unskewed (softmax i, P*V i, softmax i+1, ...): the output
+  // is bitwise the same.  Each tile's K fragments are refilled with the next
+  // pair's as soon as its MFMAs have issued, each V fragment with pair i's
+  // after the P*V of pair i-1 has read it.  The refills are unconditional
+  // (the last pair re-reads its own block): a load under a branch makes the
+  // compiler's waits count it as absent.
+  auto scores_refill = [&](int so_next, f32x4 (&sc)[4]) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -797,13 +864,33 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         kf[t][ks] = __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, so_nx + (4 * t + ks) * 1024, 0));
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, lane_off, so_next + (4 * t + ks) * 1024, 0));
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto softmax_of = [&](int blk, f32x4 (&sc)[4]) {
+    const int kv0 = blk * AT_B;
     if (blk == bp_tok)
       attn_softmax<true>(sc, o, m_run, l_run, kv0, p_tok, a.c, lane, pf);
     else
       attn_softmax<false>(sc, o, m_run, l_run, kv0, p_tok, a.c, lane, pf);
+  };
+  {
+    // pair 0: scores and softmax (its P*V goes with the next step)
+    const int nx = pair_at(1);
+    f32x4 sc[4];
+    scores_refill((nx & 0xffff) * (PACK_ELEMS * 2), sc);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_of(cur & 0xffff, sc);
+    cur = nx;
+  }
+  for (int i = 1; i < total; ++i) {
+    const int nx = pair_at(i + 1);
+    const int blk = cur & 0xffff, tk = cur >> 16;
+    if (tk != tok) load_q(tk);        // (O, m and l are still the previous token's)
+    f32x4 sc[4];
+    scores_refill((nx & 0xffff) * (PACK_ELEMS * 2), sc);
+    __builtin_amdgcn_sched_barrier(0);
+    const int so_cur = blk * (PACK_ELEMS * 2);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
@@ -811,24 +898,28 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
         vf[mt][ks] = __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, so_nx + (2 * mt + ks) * 1024, 0));
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, so_cur + (2 * mt + ks) * 1024, 0));
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (last || (nx >> 16) != tok) {
+    if (tk != tok) {
       finish();
-      if (!last) {
-        tok = nx >> 16;
-        p_tok = pos_base + tc0 + tok;
-        bp_tok = p_tok / AT_B;
-        load_q(tok);
+      tok = tk;
+      p_tok = pos_base + tc0 + tok;
+      bp_tok = p_tok / AT_B;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run = kNegInf;
-        l_run = 0.f;
-      }
+      for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run = kNegInf;
+      l_run = 0.f;
     }
+    softmax_of(blk, sc);
     cur = nx;
   }
+  // P*V of the last pair, then its token's output
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) o[mt] = mfma16(vf[mt][ks], pf[ks], o[mt]);
+  finish();
 }
 
 // Merge of the range partials of one (token, group) row: one wave per row,
