@@ -251,11 +251,11 @@ def test_k_zero_selects_init_and_local_blocks_only():
 
 
 # From 1024 key blocks (65536 keys) on, the sparse prefill attention splits
-# the keys into ranges of 192 blocks (12288 keys): a token whose blocks span
+# the keys into ranges of 128 blocks (8192 keys): a token whose blocks span
 # several ranges is attended range by range and its partial results merged.
-# These sizes span six ranges; the rows sampled include the range edges, a
+# These sizes span nine ranges; the rows sampled include the range edges, a
 # tile that straddles one, and the split threshold.
-RANGE_KEYS = 192 * 64
+RANGE_KEYS = 128 * 64
 RANGE_EDGE_ROWS = (0, 63, 64, RANGE_KEYS - 65, RANGE_KEYS - 2, RANGE_KEYS - 1, RANGE_KEYS,
                    RANGE_KEYS + 1, RANGE_KEYS + 63, RANGE_KEYS + 64, 2 * RANGE_KEYS - 1,
                    2 * RANGE_KEYS, 2 * RANGE_KEYS + 63, 5 * RANGE_KEYS - 1, 5 * RANGE_KEYS,
@@ -263,7 +263,7 @@ RANGE_EDGE_ROWS = (0, 63, 64, RANGE_KEYS - 65, RANGE_KEYS - 2, RANGE_KEYS - 1, R
 
 
 @pytest.mark.parametrize("n_kv,batch,q0", [
-    (70000, 1, 0),         # six ranges
+    (70000, 1, 0),         # nine ranges
     (66000, 2, 0),         # two sequences
     (70000, 1, 60005),     # a query offset that is not a multiple of the tile
 ])

@@ -602,9 +602,9 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
 // token-major gather re-reads K/V blocks from wherever they happen to live:
 // at 131072 keys the packs of one group (64 MB) are 16x one XCD's L2, and
 // every L2 miss is served at ~7 TB/s whether or not the data sits in the
-// Infinity Cache.  Here the keys are split into ranges of W blocks (W = 192:
-// 6 MB of packs per group, about one and a half XCD L2s; 160 to 192 measured
-// best, 128 3% and 256 6% slower) and a work item is (sequence, group,
+// Infinity Cache.  Here the keys are split into ranges of W blocks (W = 128:
+// 4 MB of packs per group, one XCD's L2; 160 or 192 run ~3% faster but move
+// 39% / 73% more bytes past L2) and a work item is (sequence, group,
 // range r, tile of query tokens): it attends each token of the tile to its
 // selected blocks inside range r only.  Work items are numbered range by
 // range and every XCD takes a contiguous stretch of the numbering, so an XCD
@@ -1435,12 +1435,12 @@ bool attn_use_split(const infv2_problem& p) { return attn_fast_shape(p) && p.n_q
 // the workspace bound.  Used when the lists fit the kernel's LDS and blocks
 // fit 16 bits.
 #ifndef INFV2_RG_W_BLOCKS
-#define INFV2_RG_W_BLOCKS 192
+#define INFV2_RG_W_BLOCKS 128
 #endif
 #ifndef INFV2_RG_SPLIT_MIN_BLOCKS
 #define INFV2_RG_SPLIT_MIN_BLOCKS 1024
 #endif
-constexpr int RG_W_BLOCKS = INFV2_RG_W_BLOCKS;          // 6 MB of K+V packs per group
+constexpr int RG_W_BLOCKS = INFV2_RG_W_BLOCKS;          // 4 MB of K+V packs per group
 // the keys are split only from this many blocks on (below, one range)
 constexpr int RG_SPLIT_MIN_BLOCKS = INFV2_RG_SPLIT_MIN_BLOCKS;
 constexpr size_t RG_PART_BUDGET = (size_t)2 << 30;      // partial bytes per call (at most)
