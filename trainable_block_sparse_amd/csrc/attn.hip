@@ -219,7 +219,7 @@ __device__ __forceinline__ void load_qfrag(const AttnArgs& a, int b, int t, int 
 // 12.9 ms at 128k against two waves per SIMD with one block in flight.
 // Loads run two list entries ahead: after the scores of entry i its K set is
 // refilled with entry i+2, after its PV the V set.
-// LONG: block lists of more than 64 entries (budget > 64) are re-read 64 at a
+// LONG: block lists of more than 64 entries (budget and n_blk > 64) are re-read 64 at a
 // time; the common case never touches memory for the list inside the loop.
 template <bool SPARSE, bool LONG>
 __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
@@ -1611,7 +1611,8 @@ hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, con
     }
     const int total_qb = ((p.n_q + AT_B - 1) / AT_B) * p.batch * p.h_kv;
     dim3 grid(((total_qb + 7) / 8) * 8 * 16);
-    if (sparse && budget > 64) {
+    // a list holds distinct causal blocks: at most min(budget, n_blk) entries
+    if (sparse && std::min(budget, a.n_blk) > 64) {
       hipLaunchKernelGGL((attn_prefill_kernel<true, true>), grid, dim3(256), 0, stream, a);
     } else if (sparse && INFV2_ATTN_TPW > 1) {
       constexpr int TPW = INFV2_ATTN_TPW;
