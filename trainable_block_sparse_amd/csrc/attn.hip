@@ -1175,11 +1175,16 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
   const int b = bt / a.n_q, t = bt % a.n_q;
   const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
   const size_t prow = row * a.budget + slot;
+  // the list length, the entry (slot < budget: in bounds), the sequence
+  // length and Q are independent reads: all issued before the first use, so
+  // that they cost one memory round trip, not one each
   const int nsel = a.n_sel[row];
-  if (slot >= nsel) return;
-  const int n_kv = a.seq_lens ? seq_len_of(a.seq_lens, b, a.n_q, a.n_kv) : a.n_kv;
-  const int p = (a.seq_lens ? n_kv - a.n_q : a.q_pos0) + t;
   const int blk = a.idx[row * a.budget + slot];
+  const int n_kv = a.seq_lens ? seq_len_of(a.seq_lens, b, a.n_q, a.n_kv) : a.n_kv;
+  bf16x8 qf[4];
+  load_qfrag(a, b, t, g, lane, qf);
+  if (slot >= nsel) return;
+  const int p = (a.seq_lens ? n_kv - a.n_q : a.q_pos0) + t;
   if (blk < 0 || blk > p / AT_B) {                  // only causal blocks
     if (lane < AT_G) a.part_ml[prow * AT_G + lane] = make_float2(kNegInf, 0.f);
     return;
@@ -1224,8 +1229,6 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
     for (int q = 0; q < 8; ++q) *(u32x4*)&vt2[kg][vt_row(8 * c + q)][0] = out[q];
   }
   __syncthreads();
-  bf16x8 qf[4];
-  load_qfrag(a, b, t, g, lane, qf);
   f32x4 o[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
