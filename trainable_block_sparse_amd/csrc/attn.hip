@@ -247,8 +247,10 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
   for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
   const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
-  const int nblocks = __builtin_amdgcn_readfirstlane(SPARSE ? a.n_sel[row] : b_p + 1);
   const int32_t* sel = SPARSE ? a.idx + row * a.budget : nullptr;
+  // (the first 64 entries are read with the length, not after it)
+  const int raw0 = (SPARSE && lane < a.budget) ? sel[lane] : -1;
+  const int nblocks = __builtin_amdgcn_readfirstlane(SPARSE ? a.n_sel[row] : b_p + 1);
   const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS + lane * 8;
   const uint16_t* kbase = a.Kp + pack0;
   const uint16_t* vbase = a.Vp + pack0;
@@ -256,7 +258,7 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_kernel(AttnArgs a) {
   // The block list is held one entry per lane, 64 entries at a time, so that
   // reading the next entry (a uniform lane read) never waits on memory.
   int list_base = 0;
-  int my_entry = (SPARSE && lane < nblocks) ? sel[lane] : -1;
+  int my_entry = lane < nblocks ? raw0 : -1;
   // block of list entry bi, or -1 when the entry is not a causal block
   auto block_at = [&](int bi) -> int {
     int blk = bi;
@@ -410,22 +412,30 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
   const int grp = lane >> 4, r16 = lane & 15;
   // the wave's tokens: list entry `lane` of token j in E[j], pair counts,
   // the pair index where each token starts; Q to LDS
-  int E[TPW], start[TPW + 1];
+  // (every read of the set-up -- entries, lengths, Q -- is issued before
+  // the first is used: one memory round trip, not one after another; a
+  // token past n_q reads token n_q - 1 and is never used)
+  int E[TPW], start[TPW + 1], nsr[TPW];
+  u32x4 qr[TPW][4];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int t = min(t0 + j, a.n_q - 1);
+    const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+    E[j] = lane < a.budget ? a.idx[row * a.budget + lane] : -1;
+    nsr[j] = a.n_sel[row];
+    const uint16_t* q = a.Q + (((size_t)b * a.n_q + t) * hq + g * AT_G + r16) * AT_D;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qr[j][ks] = __builtin_nontemporal_load((const u32x4*)(q + 32 * ks + 8 * grp));
+  }
+  __builtin_amdgcn_sched_barrier(0);
   start[0] = 0;
 #pragma unroll
   for (int j = 0; j < TPW; ++j) {
-    const int t = t0 + j;
-    int nb = 0;
-    E[j] = -1;
-    if (t < a.n_q) {
-      const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
-      nb = __builtin_amdgcn_readfirstlane(min(a.n_sel[row], a.budget));
-      E[j] = lane < nb ? a.idx[row * a.budget + lane] : -1;
-      const uint16_t* q = a.Q + (((size_t)b * a.n_q + t) * hq + g * AT_G + r16) * AT_D;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qlds[wave][j][ks][lane] = __builtin_nontemporal_load((const u32x4*)(q + 32 * ks + 8 * grp));
-    }
+    for (int ks = 0; ks < 4; ++ks) qlds[wave][j][ks][lane] = qr[j][ks];
+    const int nb = t0 + j < a.n_q ? __builtin_amdgcn_readfirstlane(min(nsr[j], a.budget)) : 0;
+    E[j] = lane < nb ? E[j] : -1;
     start[j + 1] = start[j] + nb;
   }
   const int ntok = min(TPW, a.n_q - t0);
