@@ -623,8 +623,9 @@ __global__ void __launch_bounds__(256, 1) attn_prefill_seq_kernel(AttnArgs a) {
 // A token whose blocks all lie in one range gets its output here; any other
 // token leaves one partial per range it touches -- the running maximum m and
 // sum l of every head (log2 domain, as in attn_softmax) and O/l rounded to
-// bf16 -- in slot (rank of r among the token's ranges), and
-// attn_range_merge_kernel combines them:
+// bf16 -- in slot (rank of r among the token's ranges), and the merge
+// combines them (in the tail rounds of the next query chunk's launch, the
+// last chunk's in attn_range_merge_kernel):
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  O = sum_s (l_s 2^(m_s - M) / L) O_s.
 // (The one extra bf16 rounding of each partial adds at most 2^-8 of that
 // partial's magnitude, a convex combination of V rows, before the final
@@ -669,16 +670,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pack_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
 }
 
-// Two workgroups per CU (two waves per SIMD, one block of K/V in registers
-// per wave).
-__global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
+// One work item of the range attention; bid plays the part of blockIdx.x
+// (8 consecutive ids, one per XCD, form a round).  Run by workgroups of two
+// per CU (two waves per SIMD, one block of K/V in registers per wave).
+__device__ __forceinline__ void attn_range_item(const RangeArgs& ra, int bid) {
   const AttnArgs& a = ra.a;
   // Q fragments of the wave's tokens (the 4 k-steps of one token are 4 KB in
   // lane order) and the wave's (token << 16 | block) pairs
   __shared__ u32x4 qlds[RG_WAVES][RG_MAX_TPW][4][64];
   __shared__ int prs[RG_WAVES][RG_MAX_TPW * RG_MAX_LIST];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int item = (blockIdx.x & 7) * ra.segment + (blockIdx.x >> 3);
+  const int item = (bid & 7) * ra.segment + (bid >> 3);
   if (item >= ra.items_bg * a.batch * a.h_kv) return;
   const int bg = item / ra.items_bg;
   int rem = item % ra.items_bg;
@@ -936,10 +938,10 @@ __global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra) {
 // Merge of the range partials of one (token, group) row: one wave per row,
 // four rows per workgroup.  The row's range count comes from its block list
 // (as in attn_range_kernel); rows with one range were written there.
-__global__ void __launch_bounds__(256) attn_range_merge_kernel(RangeArgs ra) {
+__device__ __forceinline__ void attn_range_merge_rows(const RangeArgs& ra, int bid) {
   const AttnArgs& a = ra.a;
   const int lane = threadIdx.x & 63;
-  const int rix = blockIdx.x * 4 + (threadIdx.x >> 6);     // row in the chunk
+  const int rix = bid * 4 + (threadIdx.x >> 6);           // row in the chunk
   const int rows = a.batch * a.h_kv * ra.n_ct;
   if (rix >= rows) return;
   const int tc = rix % ra.n_ct, bg = rix / ra.n_ct;
@@ -1011,6 +1013,31 @@ __global__ void __launch_bounds__(256) attn_range_merge_kernel(RangeArgs ra) {
   }
   if (a.lse && grp == 0)
     a.lse[((size_t)b * hq + g * AT_G + r16) * a.n_q + tq] = (M + fast_log2(L)) * kLn2;
+}
+
+// The range attention of one query chunk, with the merge of the previous
+// chunk's partials in the same launch, as its last rounds: the merge
+// workgroups are dispatched once every range item has been, so they fill the
+// range kernel's tail instead of running as a separate launch after it.
+// (Spread evenly through the grid instead, they ran side by side with the
+// range items the whole time and made the call slower: the partials they
+// stream pass through the L2 that the gathers live on.)  The two chunks'
+// partials sit in different buffers and their rows are disjoint.  The grid is
+// rounds of 8 workgroups, one per XCD: the first total_rounds - merge_rounds
+// keep the range kernel's item order per XCD, the rest merge 4 rows each.
+__global__ void __launch_bounds__(256, 2) attn_range_kernel(RangeArgs ra, RangeArgs rm,
+                                                            int merge_rounds, int total_rounds) {
+  const int k = blockIdx.x >> 3, x = blockIdx.x & 7;
+  const int range_rounds = total_rounds - merge_rounds;
+  if (k < range_rounds)
+    attn_range_item(ra, k * 8 + x);
+  else
+    attn_range_merge_rows(rm, (k - range_rounds) * 8 + x);
+}
+
+// The merge of the last chunk (nothing left to run beside it).
+__global__ void __launch_bounds__(256) attn_range_merge_kernel(RangeArgs ra) {
+  attn_range_merge_rows(ra, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -1456,7 +1483,7 @@ bool attn_use_split(const infv2_problem& p) { return attn_fast_shape(p) && p.n_q
 constexpr int RG_W_BLOCKS = INFV2_RG_W_BLOCKS;          // 4 MB of K+V packs per group
 // the keys are split only from this many blocks on (below, one range)
 constexpr int RG_SPLIT_MIN_BLOCKS = INFV2_RG_SPLIT_MIN_BLOCKS;
-constexpr size_t RG_PART_BUDGET = (size_t)2 << 30;      // partial bytes per call (at most)
+constexpr size_t RG_PART_BUDGET = (size_t)2 << 30;      // bytes of one chunk's partials (at most)
 struct RangePlan {
   bool use;
   int W, R, max_slots, tpw, chunk;
@@ -1486,10 +1513,16 @@ static RangePlan range_plan(const infv2_problem& p, int budget) {
   }
   return pl;
 }
+// Bytes of one chunk's partial buffer (O pieces, then (m, l)).
+static size_t range_buf_bytes(const infv2_problem& p, const RangePlan& pl) {
+  const size_t slots = (size_t)p.batch * p.h_kv * pl.chunk * pl.max_slots;
+  return ((slots * RG_PART_O_BYTES + 255) / 256 * 256 + slots * RG_PART_ML_BYTES + 255) / 256 * 256;
+}
+// Two buffers when the queries take several chunks: chunk i writes buffer
+// i & 1 while the merge of chunk i - 1 reads the other.
 static size_t range_part_bytes(const infv2_problem& p, const RangePlan& pl) {
   if (!pl.use || pl.R <= 1) return 0;
-  const size_t slots = (size_t)p.batch * p.h_kv * pl.chunk * pl.max_slots;
-  return (slots * RG_PART_O_BYTES + 255) / 256 * 256 + slots * RG_PART_ML_BYTES;
+  return range_buf_bytes(p, pl) * (pl.chunk < p.n_q ? 2 : 1);
 }
 
 size_t attn_workspace(const infv2_problem& p, int budget, bool sparse) {
@@ -1514,13 +1547,21 @@ static void launch_attn_ranges(const infv2_problem& p, const AttnArgs& a, void* 
   ra.tpw = pl.tpw;
   ra.max_slots = std::max(pl.max_slots, 1);
   const size_t slots = (size_t)p.batch * p.h_kv * pl.chunk * pl.max_slots;
-  ra.part_o = (u32x4*)part_ws;
-  ra.part_ml = (float2*)((char*)part_ws + (slots * RG_PART_O_BYTES + 255) / 256 * 256);
+  const size_t buf = range_buf_bytes(p, pl);
+  auto use_buffer = [&](RangeArgs& r, int i) {
+    char* base = (char*)part_ws + (i & 1) * buf;
+    r.part_o = (u32x4*)base;
+    r.part_ml = (float2*)(base + (slots * RG_PART_O_BYTES + 255) / 256 * 256);
+  };
   const int tile = RG_WAVES * pl.tpw;
-  for (int t0 = 0; t0 < p.n_q; t0 += pl.chunk) {
+  RangeArgs rm = ra;               // the previous chunk, whose partials are merged
+  int merge_rows = 0;              // 0: nothing to merge
+  int i = 0;
+  for (int t0 = 0; t0 < p.n_q; t0 += pl.chunk, ++i) {
     ra.t_base = t0;
     ra.n_ct = std::min(pl.chunk, p.n_q - t0);
     ra.n_qt = (ra.n_ct + tile - 1) / tile;
+    use_buffer(ra, i);
     const int pos_base = p.q_pos0 + t0;
     const int last_rg = ((pos_base + ra.n_ct - 1) / AT_B) / pl.W;
     long items = 0;
@@ -1529,14 +1570,18 @@ static void launch_attn_ranges(const infv2_problem& p, const AttnArgs& a, void* 
     ra.items_bg = (int)items;
     const long total = items * p.batch * p.h_kv;
     ra.segment = (int)((total + 7) / 8);
-    hipLaunchKernelGGL(attn_range_kernel, dim3(8 * ra.segment), dim3(64 * RG_WAVES), 0, stream,
-                       ra);
+    const int merge_rounds = (merge_rows + 31) / 32;        // 8 workgroups x 4 rows
+    const int rounds = ra.segment + merge_rounds;
+    hipLaunchKernelGGL(attn_range_kernel, dim3(8 * rounds), dim3(64 * RG_WAVES), 0, stream, ra,
+                       rm, merge_rounds, rounds);
     if (pl.R > 1) {
-      const int rows = p.batch * p.h_kv * ra.n_ct;
-      hipLaunchKernelGGL(attn_range_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream,
-                         ra);
+      rm = ra;
+      merge_rows = p.batch * p.h_kv * ra.n_ct;
     }
   }
+  if (merge_rows > 0)
+    hipLaunchKernelGGL(attn_range_merge_kernel, dim3((merge_rows + 3) / 4), dim3(256), 0, stream,
+                       rm);
 }
 
 static AttnArgs fast_args(const infv2_problem& p, const void* Q, const void* K, const void* V,
