@@ -1483,7 +1483,10 @@ bool attn_use_split(const infv2_problem& p) { return attn_fast_shape(p) && p.n_q
 constexpr int RG_W_BLOCKS = INFV2_RG_W_BLOCKS;          // 4 MB of K+V packs per group
 // the keys are split only from this many blocks on (below, one range)
 constexpr int RG_SPLIT_MIN_BLOCKS = INFV2_RG_SPLIT_MIN_BLOCKS;
-constexpr size_t RG_PART_BUDGET = (size_t)2 << 30;      // bytes of one chunk's partials (at most)
+#ifndef INFV2_RG_PART_MIB
+#define INFV2_RG_PART_MIB 1024
+#endif
+constexpr size_t RG_PART_BUDGET = (size_t)INFV2_RG_PART_MIB << 20;   // bytes of one chunk's partials (at most)
 struct RangePlan {
   bool use;
   int W, R, max_slots, tpw, chunk;
