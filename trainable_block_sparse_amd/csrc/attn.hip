@@ -719,6 +719,7 @@ __device__ __forceinline__ void attn_range_item(const RangeArgs& ra, int bid) {
   // --- per token: the run inside range r, its slot, the token's range count
   int slot_l = 0, nparts_l = 0;                       // lane j holds token j's values
   int total = 0;
+  uint32_t has_run = 0u;                              // bit j: token j has blocks in r
 #pragma unroll
   for (int j = 0; j < RG_MAX_TPW; ++j) {
     if (j >= ra.tpw) break;
@@ -743,21 +744,33 @@ __device__ __forceinline__ void attn_range_item(const RangeArgs& ra, int bid) {
     const int blk = __shfl(e[j], min(s + lane, 63), 64);
     if (lane < c) prs[wave][total + lane] = (j << 16) | min(max(blk, 0), b_p);
     total += c;
+    has_run |= (c > 0 ? 1u : 0u) << j;
   }
   if (total == 0) return;                             // (no barrier below)
   // Q of the wave's tokens into registers now, to LDS once the first pair's
-  // K and V loads are issued: the Q and K/V round trips overlap (a token
-  // without a run in r is loaded and never read; one past the chunk reads
-  // the chunk's last token)
+  // K and V loads are issued: the Q and K/V round trips overlap.  The loads
+  // go through a buffer descriptor over the wave's tokens; a token without a
+  // run in r gets an offset past its end, which reads 0 without a memory
+  // access (one in six tokens at 128k), and every load is still issued, so
+  // the waits stay exact.  A token past the chunk reads the chunk's last.
   u32x4 qr[RG_MAX_TPW][4];
+  {
+    // (wave-uniform: the descriptor lives in scalar registers)
+    const int tq0 = __builtin_amdgcn_readfirstlane(ra.t_base + tc0);
+    const int nt = __builtin_amdgcn_readfirstlane(min(ra.tpw, ra.n_ct - tc0));
+    const uint32_t tok_bytes = (uint32_t)hq * AT_D * 2;
+    const __amdgpu_buffer_rsrc_t rq = pack_rsrc(a.Q + ((size_t)b * a.n_q + tq0) * hq * AT_D,
+                                                (uint32_t)nt * tok_bytes);
+    const uint32_t lane_off_q = ((uint32_t)(g * AT_G + (lane & 15)) * AT_D + 8 * (lane >> 4)) * 2;
 #pragma unroll
-  for (int j = 0; j < RG_MAX_TPW; ++j) {
-    if (j >= ra.tpw) break;
-    const int tq = ra.t_base + min(tc0 + j, ra.n_ct - 1);
-    const uint16_t* q = a.Q + (((size_t)b * a.n_q + tq) * hq + g * AT_G + (lane & 15)) * AT_D;
+    for (int j = 0; j < RG_MAX_TPW; ++j) {
+      if (j >= ra.tpw) break;
+      const uint32_t off = ((has_run >> j) & 1u) ? (uint32_t)min(j, nt - 1) * tok_bytes + lane_off_q
+                                                 : 0x80000000u;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qr[j][ks] = __builtin_nontemporal_load((const u32x4*)(q + 32 * ks + 8 * (lane >> 4)));
+      for (int ks = 0; ks < 4; ++ks)
+        qr[j][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 64 * ks, 2));
+    }
   }
   const size_t pack0 = ((size_t)b * a.h_kv + g) * a.n_blk * PACK_ELEMS;
   const uint32_t pack_bytes = (uint32_t)a.n_blk * PACK_ELEMS * 2;
