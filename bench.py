@@ -440,16 +440,20 @@ def bench_decode(cfg, steps, warmup, lse_approx=False):
     # the same step with the separate score and top-k calls, for comparison
     fns_sep = fns3[:-2] + [lambda: tbs.block_scores(lp, Q, Kc1, S, ws_s, Kc2=Kc2),
                            lambda: tbs.topk_select(lp, S, idx, nsel), fns3[-1]]
+    # the step as two calls: the append inside the selection's score sweep,
+    # then the attention
+    fns2 = [
+        lambda: tbs.select_blocks_append(lp, Q, K, Kc1, n_prev, n_c1, idx, nsel, ws_s),
+        fns3[-1],
+    ]
     if lse_approx:
         fns, names = fns3, names3
     else:
-        # the timed step: the append inside the selection's score sweep, then
-        # the attention (two calls)
-        fns = [
-            lambda: tbs.select_blocks_append(lp, Q, K, Kc1, n_prev, n_c1, idx, nsel, ws_s),
-            fns3[-1],
-        ]
-        names = ["select_blocks_append", "sparse_attn"]
+        # the timed step: one call (infv2_decode_step: the two calls' work,
+        # with the selection's list merge inside the attention launch)
+        ws_d = torch.empty(tbs.decode_step_workspace(lp), dtype=torch.uint8, device=dev)
+        fns = [lambda: tbs.decode_step(lp, Q, K, V, Kc1, n_prev, n_c1, idx, nsel, O, lse, ws_d)]
+        names = ["decode_step"]
     for _ in range(warmup):
         for fn in fns:
             fn()
@@ -500,6 +504,19 @@ def bench_decode(cfg, steps, warmup, lse_approx=False):
         e1.record()
         torch.cuda.synchronize()
         three_ms = e0.elapsed_time(e1) / steps
+    two_ms = None
+    if not lse_approx:
+        for _ in range(warmup):
+            for fn in fns2:
+                fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            for fn in fns2:
+                fn()
+        e1.record()
+        torch.cuda.synchronize()
+        two_ms = e0.elapsed_time(e1) / steps
     graph_sep = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph_sep):
         for fn in fns_sep:
@@ -525,6 +542,7 @@ def bench_decode(cfg, steps, warmup, lse_approx=False):
                        else "HIP graph replay of the whole step"),
                separate_topk_step_us=sep_ms * 1e3,
                three_call_step_us=None if three_ms is None else three_ms * 1e3,
+               two_call_step_us=None if two_ms is None else two_ms * 1e3,
                stages_us_eager={k: v * 1e3 for k, v in stage.items()}, algo_bytes=nbytes,
                algo_GBps=nbytes / (step_ms / 1e3) / 1e9)
     out["frac_of_hbm_peak"] = out["algo_GBps"] / PEAK_HBM_GBS
@@ -634,6 +652,8 @@ DECODE_STAGE_KERNELS = {
     "select_blocks_append": ["scores_split_logits_kernel<false,true>",
                              "scores_split_pool_kernel", "scores_select_merge_kernel"],
     "sparse_attn": ["attn_split_kernel", "attn_merge_kernel"],
+    "decode_step": ["scores_split_logits_kernel<false,true>", "scores_split_pool_kernel",
+                    "attn_split_select_kernel", "attn_merge_kernel"],
 }
 
 
@@ -689,8 +709,9 @@ def prefill_roofline(res, workload):
 def decode_roofline(res, cfg, budget, workload="decode"):
     """Roofline object of the decode step's dominant stage (HBM-bound):
     algorithmic bytes of that stage (select_blocks: every visible K^C1 row
-    and Q; sparse_attn: the selected K/V blocks, Q and O) over its
-    event-timed duration against the HBM peak."""
+    and Q; sparse_attn: the selected K/V blocks, Q and O; decode_step, the
+    one-call step: both) over its event-timed duration against the HBM
+    peak."""
     st = res["stages_us_eager"]
     dom = max(st, key=st.get)
     L = cfg.n_kv
@@ -701,7 +722,10 @@ def decode_roofline(res, cfg, budget, workload="decode"):
            # the selection's bytes plus the appended kernel's keys and its row
            "select_blocks_append": n_c1 * cfg.d * 2 + qo + cfg.l_C1 * cfg.d * 2 + cfg.d * 2,
            "sparse_attn": nsel * cfg.B * cfg.d * 2 * 2 + 2 * qo,
-           "compress_append": cfg.l_C1 * cfg.d * 2 + cfg.d * 2}[dom]
+           "compress_append": cfg.l_C1 * cfg.d * 2 + cfg.d * 2}
+    # the one-call step: the append's selection and the attention together
+    per["decode_step"] = per["select_blocks_append"] + per["sparse_attn"]
+    per = per[dom]
     nbytes = float(cfg.batch * cfg.h_kv * per)
     ach = nbytes / (st[dom] / 1e6) / 1e9
     traffic, kernels = stage_traffic(workload, DECODE_STAGE_KERNELS[dom])

@@ -216,6 +216,27 @@ int infv2_sparse_attn(const infv2_problem* prob, const void* Q, const void* K,
                       const void* V, const int32_t* idx, const int32_t* n_sel,
                       void* O, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole decode step in one call (OpenBMB blog, 查询和键值词元的不同粒度:
+ * with token-level queries the per-step selection and attention are the
+ * decode cost): infv2_select_blocks_append followed by infv2_sparse_attn,
+ * with the selection's last stage -- merging the per-chunk candidate lists
+ * into I(p) -- done by the attention's split workgroups themselves, so the
+ * step has one launch fewer.  Kc1, idx, n_sel, O and lse are bitwise those of
+ * the two calls.
+ *   Q, K, V, Kc1, c1_begin, c1_end : as in infv2_select_blocks_append (V as
+ *           in infv2_sparse_attn)
+ *   idx, n_sel : [batch][h_kv][n_q][budget], [batch][h_kv][n_q] (output)
+ *   O, lse : as in infv2_sparse_attn (output; lse may be NULL)
+ *   ws    : workspace of infv2_decode_step_workspace(prob) bytes.
+ * Serves the decode shapes of both calls (bf16, G = 16, d = 128, B = 64,
+ * n_q <= 4, k <= 32, exact LSE, one length for all sequences); anything else
+ * is refused with INFV2_E_UNSUPPORTED before any work is enqueued. */
+size_t infv2_decode_step_workspace(const infv2_problem* prob);
+int infv2_decode_step(const infv2_problem* prob, const void* Q, const void* K, const void* V,
+                      void* Kc1, int32_t c1_begin, int32_t c1_end, int32_t* idx,
+                      int32_t* n_sel, void* O, float* lse, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* Dense causal attention, the dense branch of the dense-sparse switch
  * (papernotes.org InfLLM-V2 note, 方法详解 > 整体框架 flowchart: short inputs take
  * ordinary dense attention; OpenBMB blog "技术Blog-4 | 新一代InfLLM：可训练的稀疏

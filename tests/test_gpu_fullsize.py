@@ -74,10 +74,24 @@ def test_decode_full_size():
     # S^cmp for the score check, and the two-call selection, bitwise the same
     S = tbs.block_scores(lp, Q, Kc1)
     idx2, n_sel2 = tbs.topk_select(lp, S)
+    # the one-call step (infv2_decode_step, the list merge inside the
+    # attention launch), on its own copy of the cache's K^C1: bitwise the same
+    # Kc1, sets, O and LSE; its outputs are the ones checked below
+    Kc1_s = Kc1.clone()
+    Kc1_s[:, :, n_prev:n_now] = float("nan")
+    ws_d = torch.empty(tbs.decode_step_workspace(lp), dtype=torch.uint8, device=dev)
+    idx_s = torch.full_like(idx, 12345)
+    n_sel_s = torch.full_like(n_sel, -7)
+    O_s = torch.full_like(O, float("nan"))
+    lse_s = torch.full_like(lse, float("nan"))
+    tbs.decode_step(lp, Q, K, V, Kc1_s, n_prev, n_now, idx_s, n_sel_s, O_s, lse_s, ws_d)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2) and torch.equal(n_sel, n_sel2)
-    res = dict(Kc1=Kc1.cpu(), S_cmp=S.cpu(), idx=idx.cpu(), n_sel=n_sel.cpu(), O=O.cpu(),
-               lse=lse.cpu())
+    assert torch.equal(Kc1_s, Kc1) and torch.equal(idx_s, idx) and torch.equal(n_sel_s, n_sel)
+    assert torch.equal(O_s.view(torch.int16), O.view(torch.int16))
+    assert torch.equal(lse_s.view(torch.int32), lse.view(torch.int32))
+    res = dict(Kc1=Kc1_s.cpu(), S_cmp=S.cpu(), idx=idx_s.cpu(), n_sel=n_sel_s.cpu(),
+               O=O_s.cpu(), lse=lse_s.cpu())
     del Q, K, V
     Kc1_ref = check_compress(res, x["k"], op)
     rep = check_rows(res, x, op, cfg.n_kv - 1, {b: np.array([0]) for b in range(cfg.batch)},

@@ -189,3 +189,50 @@ def test_two_call_decode_step_graph_replay_matches_eager():
         assert torch.equal(Kc1, Kc1_ref), f"replay {rep}: Kc1 differs"
         for k, t in dict(idx=idx, nsel=nsel, O=O, lse=lse).items():
             assert torch.equal(t, ref[k]), f"replay {rep}: {k} differs"
+
+
+def test_one_call_decode_step_graph_replay_matches_eager():
+    # infv2_decode_step captured once and replayed: the appended K^C1 row is
+    # cleared to NaN and the outputs zeroed between replays, so every replay
+    # must form the row, merge the lists and attend again
+    cfg = CONFIGS["decode"]
+    n_kv, batch = 9000, 3
+    print("case: one-call decode graph replay", n_kv, batch, flush=True)
+    x = make_inputs(cfg, n_kv=n_kv, batch=batch, seed=83)
+    lp, op = problems(cfg, n_kv=n_kv, batch=batch)
+    dev = torch.device("cuda:0")
+    Q, K, V = (x[k].to(dev) for k in ("q", "k", "v"))
+    n_c1, bud = tbs.n_kernels(lp), tbs.budget(lp)
+    Kc1 = tbs.compress_k(lp, K)
+    Kc1_ref = Kc1.clone()
+    idx = torch.empty((batch, lp.h_kv, 1, bud), dtype=torch.int32, device=dev)
+    nsel = torch.empty((batch, lp.h_kv, 1), dtype=torch.int32, device=dev)
+    O = torch.empty_like(Q)
+    lse = torch.empty((batch, lp.h_q, 1), dtype=torch.float32, device=dev)
+    ws = torch.empty(tbs.decode_step_workspace(lp), dtype=torch.uint8, device=dev)
+
+    def step():
+        tbs.decode_step(lp, Q, K, V, Kc1, n_c1 - 1, n_c1, idx, nsel, O, lse, ws)
+
+    Kc1[:, :, n_c1 - 1] = float("nan")
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(Kc1, Kc1_ref)
+    ref = {k: t.clone() for k, t in dict(idx=idx, nsel=nsel, O=O, lse=lse).items()}
+    res = dict(Kc1=Kc1.cpu(), idx=idx.cpu(), n_sel=nsel.cpu(), O=O.cpu(), lse=lse.cpu())
+    check_rows(res, x, op, n_kv - 1, {b: np.array([0]) for b in range(batch)},
+               check_scores=False)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (O, lse, idx, nsel):
+            t.zero_()                     # eager work between replays
+        Kc1[:, :, n_c1 - 1] = float("nan")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Kc1, Kc1_ref), f"replay {rep}: Kc1 differs"
+        for k, t in dict(idx=idx, nsel=nsel, O=O, lse=lse).items():
+            assert torch.equal(t, ref[k]), f"replay {rep}: {k} differs"

@@ -274,3 +274,88 @@ def test_select_blocks_append_refuses_other_shapes():
     Kc1 = torch.zeros(e.kc1, dtype=torch.bfloat16, device=dev)
     with pytest.raises(tbs.Infv2Error, match="c1_begin"):
         tbs.select_blocks_append(dp, Q, K, Kc1, n_c1 - 1, n_c1 + 1)
+
+
+@pytest.mark.parametrize("n_kv,batch,n_q,k,c1_back", [
+    (131072, 16, 1, 16, 1),  # the bench's decode step (16 x 131072)
+    (131072, 1, 4, 32, 1),   # k = 32: 32 x 32 candidate keys, four query rows
+    (40000, 3, 2, 16, 3),    # ragged last chunk, kernels across a chunk edge
+    (5000, 2, 3, 16, 1),     # fewer chunks than k: several keys per list
+    (600, 2, 1, 16, 1),      # one chunk, 10 blocks: fewer candidates than k
+    (100, 1, 4, 16, 1),      # early tokens with no candidate at all
+    (33, 1, 1, 16, 1),       # one kernel
+    (20, 1, 1, 16, 0),       # no kernel yet, nothing to append
+    (70000, 1, 1, 0, 1),     # k = 0: init and local blocks only
+])
+def test_decode_step_equals_append_then_attention(n_kv, batch, n_q, k, c1_back):
+    # infv2_decode_step merges the candidate lists inside the attention's
+    # split workgroups: Kc1, idx, n_sel, O and LSE must be bitwise those of
+    # select_blocks_append followed by sparse_attn (the appended rows are NaN
+    # beforehand in both); small shapes also against the oracle
+    cfg = CONFIGS["decode"]
+    _say(f"case: decode_step n_kv={n_kv} batch={batch} n_q={n_q} k={k} rows back={c1_back}")
+    x, lp, op, Q, Kc1_ref = _selection_inputs(cfg, n_kv, batch, n_q, seed=53, k=k)
+    K, V = x["k"].to(Q.device), x["v"].to(Q.device)
+    n_c1 = tbs.n_kernels(lp)
+    c1_begin, c1_end = max(n_c1 - c1_back, 0), n_c1
+    Kc1_a = Kc1_ref.clone()
+    Kc1_a[:, :, c1_begin:c1_end] = float("nan")
+    idx_r, ns_r = tbs.select_blocks_append(lp, Q, K, Kc1_a, c1_begin, c1_end)
+    O_r, lse_r = tbs.sparse_attn(lp, Q, K, V, idx_r, ns_r)
+    Kc1_b = Kc1_ref.clone()
+    Kc1_b[:, :, c1_begin:c1_end] = float("nan")
+    # outputs prefilled with garbage: every element must be written
+    idx = torch.full_like(idx_r, 12345)
+    ns = torch.full_like(ns_r, -7)
+    O = torch.full_like(O_r, float("nan"))
+    lse = torch.full_like(lse_r, float("nan"))
+    tbs.decode_step(lp, Q, K, V, Kc1_b, c1_begin, c1_end, idx, ns, O, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(Kc1_b.cpu(), Kc1_a.cpu())
+    assert torch.equal(idx.cpu(), idx_r.cpu())
+    assert torch.equal(ns.cpu(), ns_r.cpu())
+    assert torch.equal(O.cpu().view(torch.int16), O_r.cpu().view(torch.int16))
+    assert torch.equal(lse.cpu().view(torch.int32), lse_r.cpu().view(torch.int32))
+    if n_kv <= 5000 and k > 0:
+        q0 = n_kv - n_q
+        xq = dict(x, q=Q.cpu())
+        res = dict(Kc1=Kc1_b.cpu(), idx=idx.cpu(), n_sel=ns.cpu(), O=O.cpu(), lse=lse.cpu())
+        rep = check_rows(res, xq, op, q0, {b: np.arange(n_q) for b in range(batch)},
+                         check_scores=False)
+        _say(rep)
+
+
+def test_decode_step_refuses_other_shapes():
+    cfg = CONFIGS["prefill32k"]
+    lp, _ = problems(cfg, n_kv=2000, batch=1)           # a prefill shape
+    dev = torch.device("cuda:0")
+    e = lp._ext()
+    Q = torch.zeros(e.q, dtype=torch.bfloat16, device=dev)
+    K = torch.zeros(e.kv, dtype=torch.bfloat16, device=dev)
+    Kc1 = torch.zeros(e.kc1, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(tbs.Infv2Error, match="decode shapes"):
+        tbs.decode_step(lp, Q, K, K, Kc1, 0, 1)
+
+
+@pytest.mark.parametrize("n_kv", [40000, 131072])
+def test_decode_step_all_ties(n_kv):
+    # Q = 0: every block scores the same, so the set is init, the lowest
+    # candidate blocks and local; far more than 64 keys reach the merge's
+    # bound, which takes the ranking path
+    cfg = CONFIGS["decode"]
+    _say(f"case: decode_step all ties n_kv={n_kv}")
+    x, lp, op, Q, Kc1 = _selection_inputs(cfg, n_kv, 2, 1, seed=57)
+    Q = torch.zeros_like(Q)
+    K, V = x["k"].to(Q.device), x["v"].to(Q.device)
+    n_c1 = tbs.n_kernels(lp)
+    Kc1_a = Kc1.clone()
+    idx_r, ns_r = tbs.select_blocks_append(lp, Q, K, Kc1_a, n_c1 - 1, n_c1)
+    O_r, lse_r = tbs.sparse_attn(lp, Q, K, V, idx_r, ns_r)
+    Kc1_b = Kc1.clone()
+    idx, ns, O, lse = tbs.decode_step(lp, Q, K, V, Kc1_b, n_c1 - 1, n_c1)
+    torch.cuda.synchronize()
+    assert torch.equal(idx.cpu(), idx_r.cpu()) and torch.equal(ns.cpu(), ns_r.cpu())
+    assert torch.equal(O.cpu().view(torch.int16), O_r.cpu().view(torch.int16))
+    b_p = (n_kv - 1) // lp.B
+    want = list(range(lp.N_init + lp.k)) + [b_p - 1, b_p]
+    assert idx[0, 0, 0, :int(ns[0, 0, 0])].cpu().tolist() == want

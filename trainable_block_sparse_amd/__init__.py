@@ -26,7 +26,8 @@ EXPORTED = (
     "infv2_use_dense", "infv2_check_problem", "infv2_compress_k", "infv2_compress_k2",
     "infv2_block_scores_workspace",
     "infv2_block_scores", "infv2_topk_select", "infv2_select_blocks_workspace",
-    "infv2_select_blocks", "infv2_select_blocks_append", "infv2_sparse_attn_workspace",
+    "infv2_select_blocks", "infv2_select_blocks_append", "infv2_decode_step_workspace",
+    "infv2_decode_step", "infv2_sparse_attn_workspace",
     "infv2_sparse_attn", "infv2_dense_attn_workspace", "infv2_dense_attn",
     "infv2_sparse_attn_bwd_workspace", "infv2_sparse_attn_bwd",
     "infv2_dense_attn_bwd_workspace", "infv2_dense_attn_bwd",
@@ -138,6 +139,9 @@ def lib() -> ctypes.CDLL:
             "infv2_select_blocks": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_select_blocks_append": (ctypes.c_int,
                                            [P, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]),
+            "infv2_decode_step_workspace": (sz, [P]),
+            "infv2_decode_step": (ctypes.c_int,
+                                  [P, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_sparse_attn_workspace": (sz, [P]),
             "infv2_sparse_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
             "infv2_sparse_attn_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
@@ -412,6 +416,41 @@ def select_blocks_append(prob: Problem, Q: torch.Tensor, K: torch.Tensor, Kc1: t
                                             _arg(n_sel, "n_sel", torch.int32, e.rows), ws_p,
                                             ws_n, _stream(stream)))
     return idx, n_sel
+
+
+def decode_step_workspace(prob: Problem) -> int:
+    return lib().infv2_decode_step_workspace(ctypes.byref(prob._c()))
+
+
+def decode_step(prob: Problem, Q, K, V, Kc1, c1_begin: int, c1_end: int, idx=None, n_sel=None,
+                O=None, lse=None, ws=None, want_lse: bool = True, stream=None):
+    """The decode step in one call (infv2_decode_step): K^C1 rows
+    c1_begin..c1_end-1 appended, the selection, and the attention, with the
+    selection's list merge inside the attention launch -> (idx, n_sel, O, lse),
+    bitwise select_blocks_append followed by sparse_attn."""
+    if idx is None:
+        idx = torch.empty((prob.batch, prob.h_kv, prob.n_q, budget(prob)), dtype=torch.int32,
+                          device=Q.device)
+    if n_sel is None:
+        n_sel = torch.empty((prob.batch, prob.h_kv, prob.n_q), dtype=torch.int32,
+                            device=Q.device)
+    if O is None:
+        O = torch.empty_like(Q)
+    if lse is None and want_lse:
+        lse = torch.empty((prob.batch, prob.h_q, prob.n_q), dtype=torch.float32, device=Q.device)
+    if ws is None:
+        ws = torch.empty(max(decode_step_workspace(prob), 1), dtype=torch.uint8, device=Q.device)
+    e = prob._ext()
+    ws_p, ws_n = _ws(ws)
+    _check(lib().infv2_decode_step(ctypes.byref(prob._c()), _arg(Q, "Q", e.io, e.q),
+                                   _arg(K, "K", e.io, e.kv), _arg(V, "V", e.io, e.kv),
+                                   _arg(Kc1, "Kc1", e.io, e.kc1), c1_begin, c1_end,
+                                   _arg(idx, "idx", torch.int32, e.rows * e.budget),
+                                   _arg(n_sel, "n_sel", torch.int32, e.rows),
+                                   _arg(O, "O", e.io, e.q),
+                                   _arg(lse, "lse", torch.float32, e.lse, optional=True),
+                                   ws_p, ws_n, _stream(stream)))
+    return idx, n_sel, O, lse
 
 
 def sparse_attn_workspace(prob: Problem) -> int:

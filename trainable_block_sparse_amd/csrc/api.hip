@@ -9,6 +9,7 @@
 #include <string>
 
 #include "common.hpp"
+#include "select_merge.hpp"
 
 namespace infv2 {
 hipError_t launch_compress_k(const infv2_problem& p, const void* K, void* Kc1, int c1_begin,
@@ -45,7 +46,11 @@ hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeyS
 hipError_t launch_select_append(const infv2_problem& p, const void* Q, const void* K, void* Kc1,
                                 int c1_begin, int c1_end, int64_t kv_cap, const KeySet& ks,
                                 int32_t* idx, int32_t* n_sel, void* ws, int n_blk, float scale,
-                                int budget, hipStream_t stream);
+                                int budget, hipStream_t stream, CandLists* lists = nullptr);
+hipError_t launch_attn_decode_select(const infv2_problem& p, const void* Q, const void* K,
+                                     const void* V, const CandLists& lists, int32_t* idx,
+                                     int32_t* n_sel, void* O, float* lse, void* ws, int budget,
+                                     int64_t kv_cap, float scale, hipStream_t stream);
 bool attn_fast_shape(const infv2_problem& p);
 size_t attn_workspace(const infv2_problem& p, int budget, bool sparse);
 hipError_t launch_attn(const infv2_problem& p, const void* Q, const void* K, const void* V,
@@ -347,6 +352,49 @@ int infv2_select_blocks_append(const infv2_problem* p, const void* Q, const void
                                          n_sel, ws, n_blk_of(*p), scale_of(*p), budget_of(*p),
                                          (hipStream_t)stream),
                     "infv2_select_blocks_append");
+}
+
+size_t infv2_decode_step_workspace(const infv2_problem* p) {
+  if (check(p) != INFV2_OK) return 0;
+  return align256(infv2_select_blocks_workspace(p, 0)) + attn_workspace(*p, budget_of(*p), true);
+}
+
+int infv2_decode_step(const infv2_problem* p, const void* Q, const void* K, const void* V,
+                      void* Kc1, int32_t c1_begin, int32_t c1_end, int32_t* idx, int32_t* n_sel,
+                      void* O, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = check(p);
+  if (st) return st;
+  CHECK_PTR(Q);
+  CHECK_PTR(K);
+  CHECK_PTR(V);
+  CHECK_PTR(idx);
+  CHECK_PTR(n_sel);
+  CHECK_PTR(O);
+  CHECK_PTR(ws);
+  if (lse && !aligned16(lse)) return fail(INFV2_E_ARG, "lse is not 16-byte aligned");
+  if (p->lse_approx || !scores_use_split(*p) || !attn_use_split(*p) ||
+      !select_fused_shape(*p, n_c1_of(*p)))
+    return fail(INFV2_E_UNSUPPORTED,
+                "decode_step serves the decode shapes of infv2_select_blocks_append and "
+                "infv2_sparse_attn (bf16, G=16, d=128, B=64, n_q<=4, k<=32, exact LSE)");
+  if ((st = check_keys(*p, Kc1, nullptr))) return st;
+  const KeySet ks = keys_of(*p, Kc1, nullptr);
+  if (c1_begin < 0 || c1_begin > c1_end || c1_end > ks.n_c1)
+    return fail(INFV2_E_ARG, "need 0 <= c1_begin <= c1_end <= n_C1 (%d..%d, n_C1=%d)",
+                c1_begin, c1_end, ks.n_c1);
+  const size_t need = infv2_decode_step_workspace(p);
+  if (ws_bytes < need)
+    return fail(INFV2_E_WORKSPACE, "decode_step workspace %zu < %zu bytes", ws_bytes, need);
+  const hipStream_t s = (hipStream_t)stream;
+  CandLists lists{};
+  hipError_t e = launch_select_append(*p, Q, K, Kc1, c1_begin, c1_end, kv_cap_of(*p), ks, idx,
+                                      n_sel, ws, n_blk_of(*p), scale_of(*p), budget_of(*p), s,
+                                      &lists);
+  if (e == hipSuccess)
+    e = launch_attn_decode_select(*p, Q, K, V, lists, idx, n_sel, O, lse,
+                                  (char*)ws + align256(infv2_select_blocks_workspace(p, 0)),
+                                  budget_of(*p), kv_cap_of(*p), scale_of(*p), s);
+  return hip_status(e, "infv2_decode_step");
 }
 
 size_t infv2_sparse_attn_workspace(const infv2_problem* p) {

@@ -28,6 +28,7 @@
 #include <algorithm>
 
 #include "attn_layout.hpp"
+#include "select_merge.hpp"
 
 // tokens per wave of the sparse prefill attention below the key-range split
 // (1: attn_prefill_kernel; 2 or 4: attn_prefill_seq_kernel)
@@ -1217,24 +1218,13 @@ __device__ __forceinline__ void transpose8x8_bf16(const u32x4 (&in)[8], u32x4 (&
 //  feature) read it, without bank conflicts.
 __device__ __forceinline__ int vt_row(int d) { return d ^ ((d >> 3) & 7); }
 
-__global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t kst[AT_B * AT_D * 2];
-  __shared__ __attribute__((aligned(16))) uint16_t vt2[8][AT_D][8];
+// The split attention of one (token, group, list entry) once its block blk
+// is known: the block's K and V through LDS, the scores, the softmax and P*V
+// of its 64 keys, and the partial (O, max, sum) of every head at prow.
+__device__ __forceinline__ void attn_split_block(const AttnArgs& a, int g, int b, size_t prow,
+                                                 int blk, int n_kv, int p, const bf16x8 (&qf)[4],
+                                                 uint8_t* kst, uint16_t (*vt2)[AT_D][8]) {
   const int lane = threadIdx.x;
-  const int slot = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
-  const int b = bt / a.n_q, t = bt % a.n_q;
-  const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
-  const size_t prow = row * a.budget + slot;
-  // the list length, the entry (slot < budget: in bounds), the sequence
-  // length and Q are independent reads: all issued before the first use, so
-  // that they cost one memory round trip, not one each
-  const int nsel = a.n_sel[row];
-  const int blk = a.idx[row * a.budget + slot];
-  const int n_kv = a.seq_lens ? seq_len_of(a.seq_lens, b, a.n_q, a.n_kv) : a.n_kv;
-  bf16x8 qf[4];
-  load_qfrag(a, b, t, g, lane, qf);
-  if (slot >= nsel) return;
-  const int p = (a.seq_lens ? n_kv - a.n_q : a.q_pos0) + t;
   if (blk < 0 || blk > p / AT_B) {                  // only causal blocks
     if (lane < AT_G) a.part_ml[prow * AT_G + lane] = make_float2(kNegInf, 0.f);
     return;
@@ -1311,6 +1301,61 @@ __global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
   for (int mt = 0; mt < 8; ++mt)
     *(f32x4*)(po + (size_t)r16 * AT_D + 16 * mt + 4 * grp) = o[mt];
   if (grp == 0) a.part_ml[prow * AT_G + r16] = make_float2(m_run, l_run);
+}
+
+__global__ void __launch_bounds__(64) attn_split_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kst[AT_B * AT_D * 2];
+  __shared__ __attribute__((aligned(16))) uint16_t vt2[8][AT_D][8];
+  const int lane = threadIdx.x;
+  const int slot = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+  const int b = bt / a.n_q, t = bt % a.n_q;
+  const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+  // the list length, the entry (slot < budget: in bounds), the sequence
+  // length and Q are independent reads: all issued before the first use, so
+  // that they cost one memory round trip, not one each
+  const int nsel = a.n_sel[row];
+  const int blk = a.idx[row * a.budget + slot];
+  const int n_kv = a.seq_lens ? seq_len_of(a.seq_lens, b, a.n_q, a.n_kv) : a.n_kv;
+  bf16x8 qf[4];
+  load_qfrag(a, b, t, g, lane, qf);
+  if (slot >= nsel) return;
+  const int p = (a.seq_lens ? n_kv - a.n_q : a.q_pos0) + t;
+  attn_split_block(a, g, b, row * a.budget + slot, blk, n_kv, p, qf, kst, vt2);
+}
+
+// The decode step's last selection stage and the split attention in one
+// launch: every workgroup of a (token, group) row merges the row's per-chunk
+// candidate lists itself (one wave, sel_merge_wave: the same set as
+// scores_select_merge_kernel, ascending), takes the block of its own list
+// entry and attends it; the row's entry-0 workgroup also writes idx and
+// n_sel.  The separate merge launch and the round trip of idx between the
+// two are gone.  One sequence length (no varlen, no paged cache).
+struct DecodeSel {
+  const uint64_t* cand;   // [rows][nch][kc] candidate keys (scores_split_pool_kernel)
+  int32_t* idx;           // [rows][budget] out
+  int32_t* n_sel;         // [rows] out
+  int nch, kc, k, N_init, N_local;
+};
+__global__ void __launch_bounds__(64) attn_split_select_kernel(AttnArgs a, DecodeSel ds) {
+  __shared__ __attribute__((aligned(16))) uint8_t kst[AT_B * AT_D * 2];
+  __shared__ __attribute__((aligned(16))) uint16_t vt2[8][AT_D][8];
+  __shared__ uint64_t pick[64];
+  const int lane = threadIdx.x;
+  const int slot = blockIdx.x, g = blockIdx.y, bt = blockIdx.z;
+  const int b = bt / a.n_q, t = bt % a.n_q;
+  const size_t row = ((size_t)b * a.h_kv + g) * a.n_q + t;
+  bf16x8 qf[4];
+  load_qfrag(a, b, t, g, lane, qf);
+  const int p = a.q_pos0 + t;
+  const RowSel rs = sel_merge_wave(ds.cand + row * (size_t)(ds.nch * ds.kc), ds.nch, ds.kc,
+                                   ds.k, ds.N_init, ds.N_local, p / AT_B, lane, pick);
+  if (slot == 0) {
+    sel_write_list(rs, ds.idx + row * a.budget, a.budget, lane);
+    if (lane == 0) ds.n_sel[row] = rs.n_sel;
+  }
+  if (slot >= rs.n_sel) return;
+  attn_split_block(a, g, b, row * a.budget + slot, row_sel_block(rs, slot), a.n_kv, p, qf, kst,
+                   vt2);
 }
 
 // grid: x = head within the group, y = h_kv, z = batch*n_q; 64 threads, two
@@ -1649,6 +1694,34 @@ hipError_t launch_attn_varlen(const infv2_problem& p, const void* Q, const void*
   a.part_ml = (float2*)((char*)ws + slots * AT_G * AT_D * sizeof(float));
   hipLaunchKernelGGL(attn_split_kernel, dim3(budget, p.h_kv, p.batch * p.n_q), dim3(64), 0,
                      stream, a);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(AT_G, p.h_kv, p.batch * p.n_q), dim3(64), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+// The decode step's attention with the selection's last stage inside
+// (attn_split_select_kernel): the candidate lists as the selection's pool
+// stage left them; writes idx and n_sel as well.  Requires attn_use_split(p)
+// and one sequence length.
+hipError_t launch_attn_decode_select(const infv2_problem& p, const void* Q, const void* K,
+                                     const void* V, const CandLists& lists, int32_t* idx,
+                                     int32_t* n_sel, void* O, float* lse, void* ws, int budget,
+                                     int64_t kv_cap, float scale, hipStream_t stream) {
+  AttnArgs a = fast_args(p, Q, K, V, idx, n_sel, O, lse, budget, kv_cap, scale);
+  const size_t slots = (size_t)p.batch * p.h_kv * p.n_q * budget;
+  a.part_o = (float*)ws;
+  a.part_ml = (float2*)((char*)ws + slots * AT_G * AT_D * sizeof(float));
+  DecodeSel ds;
+  ds.cand = lists.cand;
+  ds.idx = idx;
+  ds.n_sel = n_sel;
+  ds.nch = lists.nch;
+  ds.kc = lists.kc;
+  ds.k = p.k;
+  ds.N_init = p.N_init;
+  ds.N_local = p.N_local;
+  hipLaunchKernelGGL(attn_split_select_kernel, dim3(budget, p.h_kv, p.batch * p.n_q), dim3(64),
+                     0, stream, a, ds);
   hipLaunchKernelGGL(attn_merge_kernel, dim3(AT_G, p.h_kv, p.batch * p.n_q), dim3(64), 0, stream,
                      a);
   return hipGetLastError();

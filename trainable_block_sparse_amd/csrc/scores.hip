@@ -28,6 +28,7 @@
 
 #include "common.hpp"
 #include "kc1_mean.hpp"
+#include "select_merge.hpp"
 
 namespace infv2 {
 
@@ -1837,7 +1838,8 @@ static hipError_t launch_select_split(const infv2_problem& p, const void* Q, con
                                       const int32_t* seq_lens, float* S_cmp, int32_t* idx,
                                       int32_t* n_sel, void* ws, int n_blk, float scale,
                                       int budget, hipStream_t stream,
-                                      const SplitArgs* append = nullptr) {
+                                      const SplitArgs* append = nullptr,
+                                      CandLists* lists_only = nullptr) {
   SplitArgs a = split_args(p, Q, ks, S_cmp, ws, n_blk, scale);
   if (append) {
     a.K = append->K;
@@ -1860,6 +1862,13 @@ static hipError_t launch_select_split(const infv2_problem& p, const void* Q, con
   a.N_local = p.N_local;
   a.budget = budget;
   launch_split_scores(p, a, stream);
+  if (lists_only) {
+    // the caller merges the lists itself (attn_split_select_kernel)
+    lists_only->cand = a.cand;
+    lists_only->nch = a.nch;
+    lists_only->kc = a.kc;
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(scores_select_merge_kernel, dim3(p.h_kv, p.batch * p.n_q),
                      dim3(MERGE_THREADS), 0, stream, a);
   return hipGetLastError();
@@ -1897,10 +1906,12 @@ hipError_t launch_select_fused(const infv2_problem& p, const void* Q, const KeyS
 // kernels [c1_begin, c1_end) of every sequence are formed from K inside the
 // sweep and written to Kc1 (bit for bit what launch_compress_k writes).
 // Requires scores_use_split(p), select_fused_shape(p, n_C1), exact LSE.
+// With lists set, the selection stops at the per-chunk candidate lists (in
+// ws; *lists says where): idx and n_sel are not written.
 hipError_t launch_select_append(const infv2_problem& p, const void* Q, const void* K, void* Kc1,
                                 int c1_begin, int c1_end, int64_t kv_cap, const KeySet& ks,
                                 int32_t* idx, int32_t* n_sel, void* ws, int n_blk, float scale,
-                                int budget, hipStream_t stream) {
+                                int budget, hipStream_t stream, CandLists* lists) {
   SplitArgs app = {};
   app.K = (const uint16_t*)K;
   app.Kc1_out = (uint16_t*)Kc1;
@@ -1911,7 +1922,7 @@ hipError_t launch_select_append(const infv2_problem& p, const void* Q, const voi
   app.s_C1 = p.s_C1;
   app.inv_l1 = 1.0 / (double)p.l_C1;
   return launch_select_split(p, Q, ks, nullptr, nullptr, idx, n_sel, ws, n_blk, scale, budget,
-                             stream, &app);
+                             stream, &app, lists);
 }
 
 // S_sh: S^shared [batch][h_kv][n_q][n_C1] as well, or null.
