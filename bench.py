@@ -115,13 +115,13 @@ def decode_varlen_bytes(cfg, lens, budget):
 
 # the sources each kernel is built from (its own file and the headers it uses)
 KERNEL_SOURCES = {
-    "compress_k_kernel": ["compress.hip", "common.hpp"],
-    "scores_": ["scores.hip", "common.hpp"],
+    "compress_k_kernel": ["compress.hip", "common.hpp", "kc1_mean.hpp"],
+    "scores_": ["scores.hip", "common.hpp", "kc1_mean.hpp", "select_merge.hpp"],
     "topk_kernel": ["topk.hip", "common.hpp"],
-    "kv_pack_kernel": ["attn.hip", "attn_layout.hpp", "common.hpp"],
+    "kv_pack_kernel": ["attn.hip", "attn_layout.hpp", "common.hpp", "select_merge.hpp"],
     "attn_bwd": ["attn_bwd.hip", "attn_layout.hpp", "common.hpp"],
     "bwd_": ["attn_bwd.hip", "attn_layout.hpp", "common.hpp"],
-    "attn_": ["attn.hip", "attn_layout.hpp", "common.hpp"],
+    "attn_": ["attn.hip", "attn_layout.hpp", "common.hpp", "select_merge.hpp"],
 }
 
 
