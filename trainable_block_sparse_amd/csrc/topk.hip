@@ -15,8 +15,10 @@
 //      are >= K0 -- massive ties -- a bisection over the key range finds s*.)
 // Selected: init/local blocks, candidates with key > s*, and, of the
 // candidates with key == s*, the lowest-index ones up to kk in total -- ties
-// go to the lower block index.  The ascending index list comes from a
-// ballot/popcount compaction over the blocks in order.
+// go to the lower block index.  When the keys >= K0 were gathered (with their
+// blocks, in block order), the list is written straight from them: init
+// blocks, the selected gathered ones, local blocks.  Otherwise (bisection) the
+// ascending list comes from a ballot/popcount compaction over every block.
 // The sorts use lane moves of the data-parallel primitives and the permlane
 // swaps only (no LDS round trips); every cross-lane read runs with all lanes
 // active.
@@ -37,10 +39,12 @@ struct TopkArgs {
 template <int NI>
 __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
   __shared__ uint32_t gather_all[4][64];
+  __shared__ int gblk_all[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wave;
   if (row >= a.rows) return;                 // whole wave leaves together
   uint32_t* gather = gather_all[wave];
+  int* gblk = gblk_all[wave];
   const int t = row % a.n_q;
   const int p = a.q_pos0 + t;
   const int b_p = p / a.B;
@@ -91,6 +95,7 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
 
   uint32_t sstar = 0u;       // the kk-th largest candidate key
   const bool all = (kk == ncand);  // every candidate is selected
+  int gathered = -1;         // >= 0: every key >= s* is in gather/gblk (that many)
   if (!all && kk > 0) {
     if (kk > 64) {
       sstar = bisect(1u);    // every candidate key is >= 1
@@ -119,28 +124,60 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // (with their blocks: gathered in block order, so gblk ascends)
         int base = 0;
-        auto put = [&](uint32_t kv) {
+        auto put = [&](uint32_t kv, int blk) {
           const bool hit = kv >= k0;
           const uint64_t bal = __ballot(hit);
-          if (hit) gather[base + (int)__popcll(bal & ((1ull << lane) - 1ull))] = kv;
+          if (hit) {
+            const int at = base + (int)__popcll(bal & ((1ull << lane) - 1ull));
+            gather[at] = kv;
+            gblk[at] = blk;
+          }
           base += (int)__popcll(bal);
         };
         if constexpr (NI > 0) {
 #pragma unroll
-          for (int i = 0; i < NI; ++i) put(kr[i]);
+          for (int i = 0; i < NI; ++i) put(kr[i], lane + 64 * i);
         } else {
-          for (int i = 0; i < niter; ++i) put(key_at(i));
+          for (int i = 0; i < niter; ++i) put(key_at(i), lane + 64 * i);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const uint32_t s2 = wave_sort_desc<uint32_t>(gather[lane], lane);
         sstar = (uint32_t)__builtin_amdgcn_readlane((int)s2, kk - 1);
+        gathered = total;
       } else {
         sstar = bisect(k0);                   // count(>= k0) >= kk holds
       }
     }
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  if (all || kk == 0 || gathered >= 0) {
+    // the list is init blocks, the selected candidates (ascending), local
+    // blocks: written directly, without a pass over every block.  With every
+    // candidate selected (also when there is none: the local window then
+    // reaches the init blocks) it is every block 0 .. b_p; otherwise
+    // init_hi < loc_lo.
+    const int n_sel = all ? nb : init_hi + kk + (nb - loc_lo);
+    for (int j = lane; j < (all ? nb : init_hi); j += 64) out[j] = j;
+    if (!all && kk > 0) {
+      // of the gathered keys (block order): those > s*, and of those == s*
+      // the lowest-index ones up to kk in total
+      const uint32_t gk = lane < gathered ? gather[lane] : 0u;
+      const bool gt = lane < gathered && gk > sstar;
+      const bool eq = lane < gathered && gk == sstar;
+      const int eq_take = kk - (int)__popcll(__ballot(gt));
+      const bool sel = gt || (eq && (int)__popcll(__ballot(eq) & below) < eq_take);
+      const int pos = init_hi + (int)__popcll(__ballot(sel) & below);
+      if (sel) out[pos] = gblk[lane];
+    }
+    if (!all)
+      for (int j = lane; j < nb - loc_lo; j += 64) out[init_hi + kk + j] = loc_lo + j;
+    for (int i = n_sel + lane; i < a.budget; i += 64) out[i] = -1;
+    if (lane == 0) a.n_sel[row] = n_sel;
+    return;
   }
   // how many candidates equal to s* are taken (the lowest-index ones)
   int eq_left = 0;
@@ -154,9 +191,8 @@ __global__ void __launch_bounds__(256) topk_kernel(TopkArgs a) {
     }
     eq_left = kk - wave_sum_i(c);
   }
-  // ascending compaction of the selected blocks
+  // ascending compaction of the selected blocks (the bisection cases)
   int written = 0;
-  const uint64_t below = (1ull << lane) - 1ull;
   auto emit = [&](int i) {
     const int blk = lane + 64 * i;
     const uint32_t kv = key_at(i);
